@@ -1,0 +1,441 @@
+/*
+ * CPU oracle for the routed-expert MoE layer forward -- TEST INFRASTRUCTURE ONLY.
+ *
+ * Plain, slow, fp64 C.  Only the test suite, the package's smoke check and the
+ * benchmark's CPU-baseline leg may load this library; the product path never
+ * does.  It shares no code, header, table or helper with the HIP library: it
+ * has its own decoders for every weight format and its own LRU.
+ *
+ * What the layer computes, and where the pages say so:
+ *  - A router scores every expert for every token and picks a few of them
+ *    (Mixture of experts VRAM: total vs active parameters, section "How current
+ *    MoE models route each token").  The pages name no scoring function; the
+ *    reading taken here is softmax over the router logits (x . Wg_e + b_e),
+ *    restricted to the top k and renormalised.
+ *  - An expert is a gated FFN with gate, up and down projections whose gate
+ *    branch goes through SiLU (pith.science verdict on FloE, arXiv 2505.05950:
+ *    referee_report.summary and pith_extraction.core_discovery).  Reading:
+ *    y = W_down (SiLU(W_gate x) * (W_up x)), SiLU(z) = z / (1 + e^-z), no biases.
+ *  - Experts are stored at 4 bits (FP4 / INT4) but computed at higher precision
+ *    (Mixture of experts VRAM..., "How current MoE models route each token",
+ *    last paragraph).  Formats: OCP MXFP4 (E2M1 elements, E8M0 block scale, 32
+ *    per block) and symmetric INT4 with one bf16 scale per 32 weights along K.
+ *  - Tokens choosing the same expert are grouped so one weight read serves them
+ *    all (Understanding MoE Inference Costs on Galactus, "Prompt processing is a
+ *    different phase").  Reading: a stable grouping by expert id, tokens in
+ *    ascending flat index t*k+j inside each expert.
+ *  - Results are collected back per token (Mixture of experts VRAM..., "Expert
+ *    parallelism on RTX PRO 6000 and H200 NVL", dispatch and combine).  Reading:
+ *    out[t] = sum_j w[t,j] * y[t,j], plus the always-on shared expert with
+ *    weight 1 where the model has one (same page, routing section).
+ *  - A least-recently-used expert cache can serve most lookups (theflow.svmpsp.dev
+ *    related-abstracts list, the router-locality study of Qwen3-235B); weights
+ *    are addressed through stable logical slots while physical residency moves
+ *    (What expert offloading actually costs, "Inside expert paging").
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* activation / plain-weight element types */
+enum { ODT_F32 = 0, ODT_BF16 = 1 };
+/* expert weight formats */
+enum { OFMT_F32 = 0, OFMT_BF16 = 1, OFMT_MXFP4 = 2, OFMT_INT4G32 = 3 };
+
+typedef struct {
+  int fmt;
+  const void* w[3]; /* gate [I][H], up [I][H], down [H][I]; row-major, K contiguous */
+  const void* s[3]; /* block scales [rows][K/32]; NULL for plain formats */
+} oracle_expert;
+
+/* ---------------------------------------------------------------- decoders */
+
+static double f32_val(uint32_t u) {
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+/* bfloat16 is the top half of an IEEE binary32 */
+static double bf16_val(uint16_t h) { return f32_val((uint32_t)h << 16); }
+
+/* OCP MXFP4 element: 1 sign bit, 2 exponent bits (bias 1), 1 mantissa bit */
+static double e2m1_val(unsigned code) {
+  unsigned s = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+  double mag = (e == 0) ? 0.5 * m : ldexp(1.0 + 0.5 * m, (int)e - 1);
+  return s ? -mag : mag;
+}
+
+/* OCP E8M0 scale: 2^(x - 127); 0xFF is NaN */
+static double e8m0_val(uint8_t x) { return x == 0xFF ? NAN : ldexp(1.0, (int)x - 127); }
+
+/* two's-complement nibble */
+static int int4_val(unsigned nib) { return (nib & 8) ? (int)nib - 16 : (int)nib; }
+
+static unsigned nibble(const uint8_t* codes, int64_t K, int64_t r, int64_t k) {
+  uint8_t b = codes[r * (K / 2) + k / 2];
+  return (k & 1) ? (b >> 4) : (b & 15);
+}
+
+/* element (r, k) of a [rows][K] matrix stored in format fmt */
+static double weight_at(int fmt, const void* w, const void* s, int64_t K, int64_t r, int64_t k) {
+  switch (fmt) {
+    case OFMT_F32: return f32_val(((const uint32_t*)w)[r * K + k]);
+    case OFMT_BF16: return bf16_val(((const uint16_t*)w)[r * K + k]);
+    case OFMT_MXFP4:
+      return e2m1_val(nibble((const uint8_t*)w, K, r, k)) * e8m0_val(((const uint8_t*)s)[r * (K / 32) + k / 32]);
+    case OFMT_INT4G32:
+      return int4_val(nibble((const uint8_t*)w, K, r, k)) * bf16_val(((const uint16_t*)s)[r * (K / 32) + k / 32]);
+  }
+  return NAN;
+}
+
+static void decode_row(int fmt, const void* w, const void* s, int64_t K, int64_t r, double* out) {
+  for (int64_t k = 0; k < K; ++k) out[k] = weight_at(fmt, w, s, K, r, k);
+}
+
+static double act_at(int dt, const void* x, int64_t i) {
+  return dt == ODT_F32 ? f32_val(((const uint32_t*)x)[i]) : bf16_val(((const uint16_t*)x)[i]);
+}
+
+/* Decode a whole [rows][K] weight matrix to fp64 (the exact value of every weight). */
+void oracle_decode(int fmt, const void* w, const void* s, int64_t rows, int64_t K, double* out) {
+  for (int64_t r = 0; r < rows; ++r) decode_row(fmt, w, s, K, r, out + r * K);
+}
+
+void oracle_decode_act(int dt, const void* x, int64_t n, double* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = act_at(dt, x, i);
+}
+
+/* ------------------------------------------------------------------ router */
+
+/* logits[t][e] = sum_h x[t][h] * Wg[e][h] + b[e], summed in order of h */
+void oracle_router_logits(int dt, const void* x, const void* wg, const float* bias, int64_t T, int64_t H, int64_t E,
+                          double* logits) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t t = 0; t < T; ++t) {
+    for (int64_t e = 0; e < E; ++e) {
+      double acc = 0.0;
+      for (int64_t h = 0; h < H; ++h) acc += act_at(dt, x, t * H + h) * act_at(dt, wg, e * H + h);
+      logits[t * E + e] = acc + (bias ? (double)bias[e] : 0.0);
+    }
+  }
+}
+
+typedef struct {
+  double v;
+  int32_t e;
+} scored;
+
+/* larger logit first; equal logits: lower expert id first */
+static int by_score(const void* a, const void* b) {
+  const scored *x = (const scored*)a, *y = (const scored*)b;
+  if (x->v > y->v) return -1;
+  if (x->v < y->v) return 1;
+  return (x->e > y->e) - (x->e < y->e);
+}
+
+/*
+ * Top-k by a full sort of the E experts, then the gate weights: softmax over the
+ * k chosen logits, w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0), which equals the
+ * softmax over all E logits renormalised over the chosen k.
+ */
+void oracle_topk_gates(const double* logits, int64_t T, int64_t E, int k, int32_t* ids, double* w) {
+#pragma omp parallel
+  {
+    scored* s = (scored*)malloc(sizeof(scored) * (size_t)E);
+#pragma omp for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+      for (int64_t e = 0; e < E; ++e) {
+        s[e].v = logits[t * E + e];
+        s[e].e = (int32_t)e;
+      }
+      qsort(s, (size_t)E, sizeof(scored), by_score);
+      double z = 0.0;
+      for (int j = 0; j < k; ++j) z += exp(s[j].v - s[0].v);
+      for (int j = 0; j < k; ++j) {
+        ids[t * k + j] = s[j].e;
+        w[t * k + j] = exp(s[j].v - s[0].v) / z;
+      }
+    }
+    free(s);
+  }
+}
+
+/* ------------------------------------------------------------- permutation */
+
+typedef struct {
+  int32_t e, i;
+} tagged;
+
+static int by_expert_then_index(const void* a, const void* b) {
+  const tagged *x = (const tagged*)a, *y = (const tagged*)b;
+  if (x->e != y->e) return (x->e > y->e) - (x->e < y->e);
+  return (x->i > y->i) - (x->i < y->i);
+}
+
+/*
+ * Group the T*k (token, slot) pairs by expert: perm_src lists the flat indices
+ * t*k+j sorted by (expert id, flat index) -- a stable sort by expert --
+ * counts[e] is the group size, offsets its exclusive prefix sum (E+1 entries),
+ * inv_perm the position of each flat index in perm_src.
+ */
+void oracle_permute(const int32_t* ids, int64_t T, int k, int64_t E, int32_t* counts, int32_t* offsets,
+                    int32_t* perm_src, int32_t* inv_perm) {
+  int64_t n = T * k;
+  tagged* a = (tagged*)malloc(sizeof(tagged) * (size_t)(n ? n : 1));
+  for (int64_t i = 0; i < n; ++i) {
+    a[i].e = ids[i];
+    a[i].i = (int32_t)i;
+  }
+  qsort(a, (size_t)n, sizeof(tagged), by_expert_then_index);
+  for (int64_t e = 0; e < E; ++e) counts[e] = 0;
+  for (int64_t i = 0; i < n; ++i) counts[ids[i]]++;
+  offsets[0] = 0;
+  for (int64_t e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+  for (int64_t p = 0; p < n; ++p) {
+    perm_src[p] = a[p].i;
+    inv_perm[a[p].i] = (int32_t)p;
+  }
+  free(a);
+}
+
+/* ---------------------------------------------------------------- expert FFN */
+
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+/*
+ * y[r] = W_down (SiLU(W_gate x[r]) * (W_up x[r])) for n rows x[r] of length H,
+ * one expert with intermediate size I.  Every dot product is a sequential fp64
+ * sum over the contraction index.
+ */
+void oracle_ffn(const oracle_expert* ex, int64_t H, int64_t I, const double* x, int64_t n, double* y) {
+  double* h = (double*)malloc(sizeof(double) * (size_t)(n * I + 1));
+#pragma omp parallel
+  {
+    double* g = (double*)malloc(sizeof(double) * (size_t)H);
+    double* u = (double*)malloc(sizeof(double) * (size_t)H);
+#pragma omp for schedule(static)
+    for (int64_t i = 0; i < I; ++i) {
+      decode_row(ex->fmt, ex->w[0], ex->s[0], H, i, g);
+      decode_row(ex->fmt, ex->w[1], ex->s[1], H, i, u);
+      for (int64_t r = 0; r < n; ++r) {
+        double ag = 0.0, au = 0.0;
+        for (int64_t c = 0; c < H; ++c) {
+          ag += g[c] * x[r * H + c];
+          au += u[c] * x[r * H + c];
+        }
+        h[r * I + i] = silu(ag) * au;
+      }
+    }
+    free(g);
+    free(u);
+    double* d = (double*)malloc(sizeof(double) * (size_t)I);
+#pragma omp for schedule(static)
+    for (int64_t o = 0; o < H; ++o) {
+      decode_row(ex->fmt, ex->w[2], ex->s[2], I, o, d);
+      for (int64_t r = 0; r < n; ++r) {
+        double acc = 0.0;
+        for (int64_t i = 0; i < I; ++i) acc += d[i] * h[r * I + i];
+        y[r * H + o] = acc;
+      }
+    }
+    free(d);
+  }
+  free(h);
+}
+
+/* ------------------------------------------------------------- whole layer */
+
+/*
+ * Layer output for the tokens listed in sample[0..n_sample):
+ *   out[s] = sum_{j<k} w[t,j] * FFN_{ids[t,j]}(x[t]) (+ FFN_shared(x[t])),   t = sample[s]
+ * with routing from oracle_router_logits + oracle_topk_gates.  Routing is per
+ * token, so a sample of tokens gives exactly those tokens' outputs.  Expert
+ * outputs are summed in slot order j = 0..k-1, then the shared expert.
+ * ids_out [n_sample][k] and w_out [n_sample][k] receive the routing.
+ * experts: E descriptors (any format); shared: NULL or one descriptor, inter I_sh.
+ */
+int oracle_moe_layer(int dt, const void* x, int64_t T, int64_t H, const void* wg, const float* bias, int64_t E, int k,
+                     int64_t I, const oracle_expert* experts, const oracle_expert* shared, int64_t I_sh,
+                     const int64_t* sample, int64_t n_sample, double* out, int32_t* ids_out, double* w_out) {
+  (void)T;
+  double* xs = (double*)malloc(sizeof(double) * (size_t)(n_sample * H + 1));
+  double* lg = (double*)malloc(sizeof(double) * (size_t)(n_sample * E + 1));
+  for (int64_t s = 0; s < n_sample; ++s)
+    for (int64_t c = 0; c < H; ++c) xs[s * H + c] = act_at(dt, x, sample[s] * H + c);
+  /* router on the sampled rows: same sum as oracle_router_logits */
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t s = 0; s < n_sample; ++s) {
+    for (int64_t e = 0; e < E; ++e) {
+      double acc = 0.0;
+      for (int64_t c = 0; c < H; ++c) acc += xs[s * H + c] * act_at(dt, wg, e * H + c);
+      lg[s * E + e] = acc + (bias ? (double)bias[e] : 0.0);
+    }
+  }
+  oracle_topk_gates(lg, n_sample, E, k, ids_out, w_out);
+
+  /* y[s][j] = FFN of expert ids[s][j] at x[sample[s]]; each expert evaluated once on its rows */
+  double* y = (double*)malloc(sizeof(double) * (size_t)(n_sample * k * H + 1));
+  int64_t* rows = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n_sample * k + 1));
+  double* xin = (double*)malloc(sizeof(double) * (size_t)(n_sample * k * H + 1));
+  double* yout = (double*)malloc(sizeof(double) * (size_t)(n_sample * k * H + 1));
+  for (int64_t e = 0; e < E; ++e) {
+    int64_t n = 0;
+    for (int64_t q = 0; q < n_sample * k; ++q)
+      if (ids_out[q] == e) rows[n++] = q;
+    if (!n) continue;
+    for (int64_t r = 0; r < n; ++r) memcpy(xin + r * H, xs + (rows[r] / k) * H, sizeof(double) * (size_t)H);
+    oracle_ffn(&experts[e], H, I, xin, n, yout);
+    for (int64_t r = 0; r < n; ++r) memcpy(y + rows[r] * H, yout + r * H, sizeof(double) * (size_t)H);
+  }
+  double* ysh = NULL;
+  if (shared) {
+    ysh = (double*)malloc(sizeof(double) * (size_t)(n_sample * H + 1));
+    oracle_ffn(shared, H, I_sh, xs, n_sample, ysh);
+  }
+  for (int64_t s = 0; s < n_sample; ++s) {
+    for (int64_t c = 0; c < H; ++c) {
+      double acc = 0.0;
+      for (int j = 0; j < k; ++j) acc += w_out[s * k + j] * y[(s * k + j) * H + c];
+      if (ysh) acc += ysh[s * H + c];
+      out[s * H + c] = acc;
+    }
+  }
+  free(xs);
+  free(lg);
+  free(y);
+  free(rows);
+  free(xin);
+  free(yout);
+  free(ysh);
+  return 0;
+}
+
+/* -------------------------------------------------------------- expert cache */
+
+/*
+ * Least-recently-used cache over keys (layer * E + expert) with `capacity`
+ * slots, starting empty.  Lookups come in groups (one group = one layer of one
+ * decode step); inside a group duplicate keys count once.  A distinct key found
+ * resident is a hit, otherwise a miss that takes a free slot or evicts.  Every
+ * key touched by a group gets that group's index as its recency tick; the
+ * victim is the resident key, not in the current group, with the smallest
+ * (tick, key).  A group with more distinct keys than the capacity is an error
+ * (returns -1).
+ * group_off[g]..group_off[g+1] delimit the raw keys of group g.
+ * Outputs per group: hits[g], misses[g]; victims (in eviction order) go to
+ * victims[], their count per group to n_victims[g].
+ */
+int oracle_lru(int64_t capacity, int64_t n_groups, const int64_t* group_off, const int64_t* keys, int64_t* hits,
+               int64_t* misses, int64_t* victims, int64_t* n_victims) {
+  int64_t max_key = 0;
+  for (int64_t i = 0; i < group_off[n_groups]; ++i)
+    if (keys[i] > max_key) max_key = keys[i];
+  int64_t nk = max_key + 1;
+  int64_t* tick = (int64_t*)malloc(sizeof(int64_t) * (size_t)nk); /* -1 = not resident */
+  int64_t* in_group = (int64_t*)malloc(sizeof(int64_t) * (size_t)nk);
+  for (int64_t i = 0; i < nk; ++i) tick[i] = -1, in_group[i] = -1;
+  int64_t resident = 0, nv = 0, rc = 0;
+  for (int64_t g = 0; g < n_groups && rc == 0; ++g) {
+    int64_t distinct = 0;
+    for (int64_t i = group_off[g]; i < group_off[g + 1]; ++i)
+      if (in_group[keys[i]] != g) in_group[keys[i]] = g, distinct++;
+    if (distinct > capacity) {
+      rc = -1;
+      break;
+    }
+    hits[g] = misses[g] = n_victims[g] = 0;
+    /* visit the group's distinct keys in ascending order */
+    for (int64_t key = 0; key < nk; ++key) {
+      if (in_group[key] != g) continue;
+      if (tick[key] >= 0) {
+        hits[g]++;
+      } else {
+        misses[g]++;
+        if (resident == capacity) {
+          int64_t best = -1;
+          for (int64_t c = 0; c < nk; ++c) {
+            if (tick[c] < 0 || in_group[c] == g) continue;
+            if (best < 0 || tick[c] < tick[best] || (tick[c] == tick[best] && c < best)) best = c;
+          }
+          tick[best] = -1;
+          resident--;
+          victims[nv++] = best;
+          n_victims[g]++;
+        }
+        resident++;
+      }
+      tick[key] = g;
+    }
+  }
+  free(tick);
+  free(in_group);
+  return (int)rc;
+}
+
+/*
+ * Belady's MIN on the same groups: on a miss with a full cache, evict the
+ * resident key (not in the current group) whose next use lies farthest ahead
+ * (never = infinitely far; ties: smallest key).  Gives the largest hit count
+ * any policy can reach; used only as a bound.
+ */
+int oracle_belady(int64_t capacity, int64_t n_groups, const int64_t* group_off, const int64_t* keys, int64_t* hits,
+                  int64_t* misses) {
+  int64_t n = group_off[n_groups], max_key = 0;
+  for (int64_t i = 0; i < n; ++i)
+    if (keys[i] > max_key) max_key = keys[i];
+  int64_t nk = max_key + 1;
+  /* nu[i]: index of the first group after the one holding position i that uses keys[i] */
+  int64_t* nu = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n + 1));
+  int64_t* last = (int64_t*)malloc(sizeof(int64_t) * (size_t)nk);
+  for (int64_t c = 0; c < nk; ++c) last[c] = INT64_MAX;
+  for (int64_t g = n_groups - 1; g >= 0; --g) {
+    for (int64_t i = group_off[g]; i < group_off[g + 1]; ++i) nu[i] = last[keys[i]];
+    for (int64_t i = group_off[g]; i < group_off[g + 1]; ++i) last[keys[i]] = g;
+  }
+  char* res = (char*)calloc((size_t)nk, 1);
+  int64_t* next = (int64_t*)malloc(sizeof(int64_t) * (size_t)nk);
+  int64_t* in_group = (int64_t*)malloc(sizeof(int64_t) * (size_t)nk);
+  int64_t* pos = (int64_t*)malloc(sizeof(int64_t) * (size_t)nk);
+  for (int64_t c = 0; c < nk; ++c) in_group[c] = -1, next[c] = INT64_MAX;
+  int64_t resident = 0, rc = 0;
+  for (int64_t g = 0; g < n_groups; ++g) {
+    int64_t distinct = 0;
+    for (int64_t i = group_off[g]; i < group_off[g + 1]; ++i)
+      if (in_group[keys[i]] != g) in_group[keys[i]] = g, pos[keys[i]] = i, distinct++;
+    if (distinct > capacity) {
+      rc = -1;
+      break;
+    }
+    hits[g] = misses[g] = 0;
+    for (int64_t key = 0; key < nk; ++key) {
+      if (in_group[key] != g) continue;
+      if (res[key]) {
+        hits[g]++;
+      } else {
+        misses[g]++;
+        if (resident == capacity) {
+          int64_t best = -1;
+          for (int64_t c = 0; c < nk; ++c) {
+            if (!res[c] || in_group[c] == g) continue;
+            if (best < 0 || next[c] > next[best]) best = c;
+          }
+          res[best] = 0;
+          resident--;
+        }
+        res[key] = 1;
+        resident++;
+      }
+      next[key] = nu[pos[key]];
+    }
+  }
+  free(nu);
+  free(last);
+  free(res);
+  free(next);
+  free(in_group);
+  free(pos);
+  return (int)rc;
+}
