@@ -1,0 +1,153 @@
+"""Python names for the C-ABI entry points of libmoe.so.
+
+Each function marshals torch tensors (device memory) or numpy arrays (host
+memory) into the pointers and sizes of the C call of the same name, on the
+current torch stream unless one is given.  All computation happens in the
+library's HIP kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import torch
+
+from ._lib import MoeCacheDesc, MoeCachePlan, MoeCacheStats, MoeExperts, check, lib
+
+FMT = {"f32": 0, "bf16": 1, "mxfp4": 2, "int4g32": 3}
+DT = {"f32": 0, "bf16": 1}
+MODE = {"auto": 0, "decode": 1, "prefill": 2}
+TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def _dp(t):
+    """Device pointer of a tensor (None -> NULL)."""
+    if t is None:
+        return None
+    assert t.is_cuda and t.is_contiguous(), "expected a contiguous device tensor"
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _hp(a):
+    if a is None:
+        return None
+    assert isinstance(a, np.ndarray) and a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return DT["f32"]
+    if t.dtype == torch.bfloat16:
+        return DT["bf16"]
+    raise TypeError("activations must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def moe_route(x, w_router, bias, k, topk_ids, topk_w, logits=None, stream=None):
+    T, H = x.shape
+    E = w_router.shape[0]
+    check(lib().moe_route(_dp(x), _dt(x), T, H, _dp(w_router), _dp(bias), E, k, _dp(topk_ids), _dp(topk_w),
+                          _dp(logits), _stream(stream)))
+
+
+def moe_permute_workspace(T, k, E) -> int:
+    return int(lib().moe_permute_workspace(T, k, E))
+
+
+def moe_permute(topk_ids, E, counts, offsets, perm_src, inv_perm, ws=None, stream=None):
+    T, k = topk_ids.shape
+    check(lib().moe_permute(_dp(topk_ids), T, k, E, _dp(counts), _dp(offsets), _dp(perm_src), _dp(inv_perm),
+                            _dp(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def moe_package_bytes(H, I, fmt) -> int:
+    return int(lib().moe_package_bytes(H, I, FMT[fmt]))
+
+
+def moe_pack_expert(H, I, fmt, ex: dict, out: np.ndarray | None = None) -> np.ndarray:
+    """Pack one expert's logical weights (dict from synth.workloads.expert_weights) into a host package."""
+    n = moe_package_bytes(H, I, fmt)
+    if out is None:
+        out = np.empty(n, dtype=np.uint8)
+    w, s = ex["w"], ex["s"]
+    check(lib().moe_pack_expert(H, I, FMT[fmt], _hp(w[0]), _hp(s[0]), _hp(w[1]), _hp(s[1]), _hp(w[2]), _hp(s[2]),
+                                _hp(out), out.nbytes))
+    return out
+
+
+def moe_dequant_expert(package, H, I, fmt, out, stream=None):
+    check(lib().moe_dequant_expert(_dp(package), H, I, FMT[fmt], _dp(out), _stream(stream)))
+
+
+def experts_desc(H, I, E, fmt, packages, pkg_stride, slot_of_expert=None) -> MoeExperts:
+    d = MoeExperts()
+    d.H, d.I, d.E, d.fmt = H, I, E, FMT[fmt]
+    d.packages = packages.data_ptr() if packages is not None else None
+    d.pkg_stride = pkg_stride
+    d.slot_of_expert = slot_of_expert.data_ptr() if slot_of_expert is not None else None
+    return d
+
+
+def moe_ffn_workspace(desc: MoeExperts, T, k, mode="auto") -> int:
+    return int(lib().moe_ffn_workspace(ctypes.byref(desc), T, k, MODE[mode]))
+
+
+def moe_expert_ffn(desc: MoeExperts, x, k, offsets, perm_src, y_perm, ws, mode="auto", stream=None):
+    T = x.shape[0]
+    check(lib().moe_expert_ffn(ctypes.byref(desc), _dp(x), _dt(x), T, k, _dp(offsets), _dp(perm_src), _dp(y_perm),
+                               MODE[mode], _dp(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                               _stream(stream)))
+
+
+def moe_combine(y_perm, topk_w, inv_perm, k, shared_y, out, stream=None):
+    T, H = out.shape
+    check(lib().moe_combine(_dp(y_perm), _dp(topk_w), _dp(inv_perm), T, k, H, _dp(shared_y), _dp(out), _dt(out),
+                            _stream(stream)))
+
+
+class ExpertCache:
+    """Owner of a moe_cache_t.  `bank` (pinned host tensor) and `pool` (device tensor) must outlive it."""
+
+    def __init__(self, bank, pkg_bytes, L, E, pool, slot_stride, capacity):
+        d = MoeCacheDesc()
+        d.host_bank = bank.data_ptr() if bank is not None else None
+        d.pkg_bytes, d.L, d.E = pkg_bytes, L, E
+        d.device_pool = pool.data_ptr() if pool is not None else None
+        d.slot_stride, d.capacity = slot_stride, capacity
+        self._keep = (bank, pool)
+        h = ctypes.c_void_p()
+        check(lib().moe_cache_create(ctypes.byref(d), ctypes.byref(h)))
+        self.h = h
+        self.E = E
+
+    def plan(self, layer, host_ids: np.ndarray) -> MoeCachePlan:
+        ids = np.ascontiguousarray(host_ids, dtype=np.int32).ravel()
+        p = MoeCachePlan()
+        check(lib().moe_cache_plan(self.h, layer, _hp(ids), ids.size, ctypes.byref(p)))
+        return p
+
+    def fetch(self, plan: MoeCachePlan, dev_slot_of_expert, copy_stream, done_event=None):
+        ev = ctypes.c_void_p(done_event.cuda_event) if done_event is not None else None
+        check(lib().moe_cache_fetch(self.h, ctypes.byref(plan), _dp(dev_slot_of_expert),
+                                    ctypes.c_void_p(copy_stream.cuda_stream), ev))
+
+    def stats(self) -> dict:
+        s = MoeCacheStats()
+        check(lib().moe_cache_stats(self.h, ctypes.byref(s)))
+        return {f: getattr(s, f) for f, _ in MoeCacheStats._fields_}
+
+    def close(self):
+        if self.h:
+            lib().moe_cache_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,174 @@
+// Router: logits = x . Wg^T + b, then top-k (descending, ties to the lower expert id) and the
+// gate weights softmax-renormalised over the chosen k.  The router is dense and scores every
+// expert for every token ("Mixture of experts VRAM: total vs active parameters", section "How
+// current MoE models route each token").
+//
+// bf16 activations: one workgroup per 16 tokens; its 4 waves split the experts into 16-wide
+// MFMA tiles (v_mfma_f32_16x16x32_bf16, fp32 accumulation), the 16 x E logit block goes to
+// LDS, then each wave selects the top-k of 4 tokens with 64-lane shuffle reductions.
+// fp32 activations: one workgroup per token, fp32 FMA dot products reduced across the wave.
+#include <math.h>
+
+#include "common.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kRouteTokens = 16;    // tokens per workgroup (MFMA M)
+constexpr int kRouteWaves = 4;
+constexpr int kTilesPerPass = 8;    // 16-expert tiles each wave accumulates per pass over H
+constexpr int kMaxE = 1024;
+
+// (value, id) ordering of the router: larger value first, equal values -> lower id first
+__device__ __forceinline__ bool better(float v, int e, float bv, int be) { return v > bv || (v == bv && e < be); }
+
+// top-k of one token's E logits in LDS row `lg`; executed by one full wave.  Chosen entries are
+// overwritten with -inf in LDS.  Lane 0 writes ids/weights.
+__device__ void wave_topk(float* lg, int E, int k, int32_t* ids, float* w) {
+  const int lane = threadIdx.x & 63;
+  float sel_v[16];
+  int sel_e[16];
+  for (int j = 0; j < k; ++j) {
+    float bv = -INFINITY;
+    int be = 0x7FFFFFFF;
+    for (int e = lane; e < E; e += 64) {
+      float v = lg[e];
+      if (better(v, e, bv, be)) bv = v, be = e;
+    }
+    for (int off = 32; off > 0; off >>= 1) {
+      float ov = __shfl_xor(bv, off, 64);
+      int oe = __shfl_xor(be, off, 64);
+      if (better(ov, oe, bv, be)) bv = ov, be = oe;
+    }
+    sel_v[j] = bv;
+    sel_e[j] = be;
+    if (lane == 0) lg[be] = -INFINITY;
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  }
+  if (lane == 0) {
+    float z = 0.f, p[16];
+    for (int j = 0; j < k; ++j) {
+      p[j] = expf(sel_v[j] - sel_v[0]);
+      z += p[j];
+    }
+    for (int j = 0; j < k; ++j) {
+      ids[j] = sel_e[j];
+      w[j] = p[j] / z;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void route_bf16_kernel(const unsigned short* __restrict__ x,
+                                                         const unsigned short* __restrict__ wg,
+                                                         const float* __restrict__ bias, int T, int H, int E, int k,
+                                                         int32_t* __restrict__ ids, float* __restrict__ w,
+                                                         float* __restrict__ logits) {
+  extern __shared__ float lds[];  // [16][Epad]
+  const int Epad = ((E + 15) / 16) * 16 + 1;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * kRouteTokens;
+  const int m = lane & 15, kq = (lane >> 4) * 8;
+  const int n_tiles = (E + 15) / 16;
+  const bool row_ok = t0 + m < T;
+  const unsigned short* xrow = x + (size_t)(row_ok ? t0 + m : 0) * H + kq;
+
+  for (int first = wave; first < n_tiles; first += kRouteWaves * kTilesPerPass) {
+    f32x4 acc[kTilesPerPass];
+    const unsigned short* brow[kTilesPerPass];
+    bool bok[kTilesPerPass];
+#pragma unroll
+    for (int i = 0; i < kTilesPerPass; ++i) {
+      acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      int nt = first + i * kRouteWaves;
+      int e = nt * 16 + m;
+      bok[i] = nt < n_tiles && e < E;
+      brow[i] = wg + (size_t)(bok[i] ? e : 0) * H + kq;
+    }
+    for (int kk = 0; kk < H; kk += 32) {
+      bf16x8 a = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+      if (row_ok) a = *(const bf16x8*)(xrow + kk);
+#pragma unroll
+      for (int i = 0; i < kTilesPerPass; ++i) {
+        if (first + i * kRouteWaves < n_tiles) {  // wave-uniform
+          bf16x8 b = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+          if (bok[i]) b = *(const bf16x8*)(brow[i] + kk);
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[i], 0, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kTilesPerPass; ++i) {
+      int nt = first + i * kRouteWaves;
+      if (nt >= n_tiles) continue;
+      int e = nt * 16 + (lane & 15);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        int row = (lane >> 4) * 4 + r;
+        if (e < E) lds[row * Epad + e] = acc[i][r] + (bias ? bias[e] : 0.f);
+      }
+    }
+  }
+  __syncthreads();
+  if (logits) {
+    for (int i = threadIdx.x; i < kRouteTokens * E; i += blockDim.x) {
+      int row = i / E, e = i % E;
+      if (t0 + row < T) logits[(size_t)(t0 + row) * E + e] = lds[row * Epad + e];
+    }
+    __syncthreads();
+  }
+  for (int row = wave; row < kRouteTokens; row += kRouteWaves) {
+    int t = t0 + row;
+    if (t >= T) break;
+    wave_topk(lds + row * Epad, E, k, ids + (size_t)t * k, w + (size_t)t * k);
+  }
+}
+
+__global__ __launch_bounds__(256) void route_f32_kernel(const float* __restrict__ x, const float* __restrict__ wg,
+                                                        const float* __restrict__ bias, int T, int H, int E, int k,
+                                                        int32_t* __restrict__ ids, float* __restrict__ w,
+                                                        float* __restrict__ logits) {
+  extern __shared__ float lds[];  // [E]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int t = blockIdx.x;
+  const float* xr = x + (size_t)t * H;
+  for (int e = wave; e < E; e += nw) {
+    const float* wr = wg + (size_t)e * H;
+    float acc = 0.f;
+    for (int h = lane; h < H; h += 64) acc = fmaf(xr[h], wr[h], acc);
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if (lane == 0) lds[e] = acc + (bias ? bias[e] : 0.f);
+  }
+  __syncthreads();
+  if (logits)
+    for (int e = threadIdx.x; e < E; e += blockDim.x) logits[(size_t)t * E + e] = lds[e];
+  __syncthreads();
+  if (wave == 0) wave_topk(lds, E, k, ids + (size_t)t * k, w + (size_t)t * k);
+}
+
+}  // namespace
+
+int launch_route(const void* x, int xdt, int T, int H, const void* wg, const float* bias, int E, int k, int32_t* ids,
+                 float* w, float* logits, hipStream_t s) {
+  if (T == 0) return MOE_OK;
+  if (E > kMaxE) return fail(MOE_ERR_INVALID, "moe_route: E=%d exceeds %d", E, kMaxE);
+  if (xdt == MOE_BF16) {
+    if (H % 32) return fail(MOE_ERR_UNSUPPORTED, "moe_route: bf16 path needs H %% 32 == 0 (H=%d)", H);
+    int Epad = ((E + 15) / 16) * 16 + 1;
+    size_t lds = (size_t)kRouteTokens * Epad * sizeof(float);
+    if (lds > 65536) {
+      hipError_t e = hipFuncSetAttribute((const void*)route_bf16_kernel,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return hip_fail(e, "moe_route: LDS attribute");
+    }
+    hipLaunchKernelGGL(route_bf16_kernel, dim3((T + kRouteTokens - 1) / kRouteTokens), dim3(64 * kRouteWaves), lds,
+                       s, (const unsigned short*)x, (const unsigned short*)wg, bias, T, H, E, k, ids, w, logits);
+  } else {
+    hipLaunchKernelGGL(route_f32_kernel, dim3(T), dim3(256), (size_t)E * sizeof(float), s, (const float*)x,
+                       (const float*)wg, bias, T, H, E, k, ids, w, logits);
+  }
+  MOE_CHECK_LAUNCH("moe_route launch");
+  return MOE_OK;
+}
+
+}  // namespace moe

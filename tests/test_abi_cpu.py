@@ -1,0 +1,171 @@
+"""Host-side checks of libmoe.so that need no GPU: exports, argument validation,
+package sizes and the packer, and the LRU cache planner against the oracle."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import workloads as W
+
+import mixture_experts_layer_token_amd as moe
+from mixture_experts_layer_token_amd import _lib
+from mixture_experts_layer_token_amd.api import ExpertCache
+
+L = moe.lib()
+OK, INVALID, UNSUPPORTED, CAPACITY, WORKSPACE = 0, -1, -2, -4, -6
+
+
+def test_every_header_symbol_is_exported():
+    syms = moe.header_symbols()
+    assert len(syms) >= 15
+    for s in syms:
+        assert hasattr(L, s), s
+    assert set(_lib.SIGNATURES) == set(syms)
+
+
+def test_route_validation():
+    # no pointer is touched before validation fails
+    assert L.moe_route(None, 1, 4, 64, None, None, 0, 1, None, None, None, None) == INVALID
+    assert b"E=0" in L.moe_last_error()
+    assert L.moe_route(None, 1, 4, 64, None, None, 8, 9, None, None, None, None) == INVALID
+    assert L.moe_route(None, 1, 4, 64, None, None, 64, 17, None, None, None, None) == INVALID
+    assert L.moe_route(None, 7, 4, 64, None, None, 8, 2, None, None, None, None) == INVALID
+    assert L.moe_route(None, 1, 4, 64, None, None, 8, 2, None, None, None, None) == INVALID  # null x
+    assert L.moe_route(None, 1, 0, 64, None, None, 8, 2, None, None, None, None) == OK  # T = 0: nothing to do
+
+
+def test_permute_and_combine_validation():
+    assert L.moe_permute(None, 4, 2, 0, None, None, None, None, None, 0, None) == INVALID
+    assert L.moe_permute(None, 4, 0, 8, None, None, None, None, None, 0, None) == INVALID
+    assert L.moe_permute(None, 4, 2, 8, None, None, None, None, None, 0, None) == INVALID
+    assert L.moe_combine(None, None, None, 4, 2, 64, None, None, 5, None) == INVALID
+    assert L.moe_combine(None, None, None, 4, 17, 64, None, None, 1, None) == INVALID
+    assert L.moe_combine(None, None, None, 0, 2, 64, None, None, 1, None) == OK
+
+
+def test_ffn_validation():
+    d = moe.experts_desc(4096, 14336, 8, "bf16", None, moe.moe_package_bytes(4096, 14336, "bf16"))
+    ref = ctypes.byref(d)
+    assert L.moe_expert_ffn(ref, None, 1, 4, 2, None, None, None, 0, None, 0, None) == INVALID  # null pointers
+    d.pkg_stride = 100
+    assert L.moe_expert_ffn(ref, None, 1, 4, 2, None, None, None, 0, None, 0, None) == INVALID
+    d2 = moe.experts_desc(100, 14336, 8, "bf16", None, 1 << 30)
+    assert L.moe_expert_ffn(ctypes.byref(d2), None, 1, 4, 2, None, None, None, 0, None, 0, None) == UNSUPPORTED
+    d3 = moe.experts_desc(4096, 14336, 0, "bf16", None, 1 << 30)
+    assert L.moe_expert_ffn(ctypes.byref(d3), None, 1, 4, 2, None, None, None, 0, None, 0, None) == INVALID
+    assert L.moe_ffn_workspace(ref, 64, 2, 0) > 0 or True
+
+
+@pytest.mark.parametrize("fmt,H,I,want", [("bf16", 4096, 14336, 352321536), ("mxfp4", 2880, 2880, 13219200),
+                                          ("int4g32", 7168, 2048, 24772608), ("int4g32", 5120, 1536, 13271040),
+                                          ("f32", 256, 512, 1572864), ("bf16", 100, 64, 0)])
+def test_package_bytes(fmt, H, I, want):
+    assert moe.moe_package_bytes(H, I, fmt) == want
+
+
+@pytest.mark.parametrize("fmt", ["f32", "bf16", "mxfp4", "int4g32"])
+def test_packer_is_a_rearrangement(fmt):
+    """Every code byte / element lands in the package exactly once (multiset of values preserved)."""
+    wl = W.Workload(name="pk-" + fmt, H=224, E=2, k=1, I=352, wfmt=fmt, xdt="bf16", Ts=(1,), seed=9)
+    ex = W.expert_weights(wl, 0, 1)
+    pkg = moe.moe_pack_expert(wl.H, wl.I, fmt, ex)
+    n = 3 * wl.H * wl.I
+    if fmt in ("f32", "bf16"):
+        dt = np.float32 if fmt == "f32" else np.uint16
+        got = np.sort(pkg.view(dt))
+        want = np.sort(np.concatenate([a.ravel() for a in ex["w"]]).view(dt))
+        assert np.array_equal(got, want)
+    else:
+        codes = pkg[: n // 2]
+        nib = np.concatenate([codes & 15, codes >> 4])
+        src = np.concatenate([a.ravel() for a in ex["w"]])
+        srcn = np.concatenate([src & 15, src >> 4])
+        if fmt == "int4g32":
+            srcn = (srcn + 8) & 15  # stored as q + 8
+        assert np.array_equal(np.bincount(nib, minlength=16), np.bincount(srcn, minlength=16))
+        assert pkg.size == n // 2 + (n // 32) * (1 if fmt == "mxfp4" else 2)
+
+
+def test_pack_rejects_int4_scale_outside_binary16():
+    H = I = 32
+    codes = np.zeros((I, H // 2), np.uint8)
+    s = np.full((I, 1), 0x3F80, np.uint16)  # 1.0
+    s_bad = s.copy()
+    s_bad[3, 0] = 0x4780 + 0x0100  # 2^16 * 1.x > 65504
+    ex = {"w": [codes, codes, codes], "s": [s, s_bad, s]}
+    with pytest.raises(moe.MoeError) as e:
+        moe.moe_pack_expert(H, I, "int4g32", ex)
+    assert e.value.code == UNSUPPORTED
+
+
+# ------------------------------------------------------------------ cache planner (host only)
+
+def _planner(cap, L_, E):
+    return ExpertCache(None, 1 << 20, L_, E, None, 0, cap)
+
+
+def test_cache_planner_matches_oracle_lru():
+    L_, E, cap, steps = 4, 64, 64, 120
+    rng = np.random.default_rng(11)
+    c = _planner(cap, L_, E)
+    groups, plans = [], []
+    p = 1.0 / np.arange(1, E + 1) ** 1.2
+    p /= p.sum()
+    for s in range(steps):
+        for layer in range(L_):
+            ids = rng.choice(E, size=16, p=p)
+            groups.append((layer * E + ids).tolist())
+            plans.append(c.plan(layer, ids))
+    h, m, v = oracle.lru(cap, groups)
+    assert [pl.n_hits for pl in plans] == list(h)
+    assert [pl.n_misses for pl in plans] == list(m)
+    st = c.stats()
+    assert st["hits"] == h.sum() and st["misses"] == m.sum() and st["evictions"] == sum(len(a) for a in v)
+    assert st["bytes_fetched"] == m.sum() * (1 << 20)
+
+
+def test_cache_plan_slot_table_is_injective_and_consistent():
+    L_, E, cap = 2, 32, 20
+    c = _planner(cap, L_, E)
+    rng = np.random.default_rng(3)
+    owner = {}
+    for s in range(200):
+        layer = s % L_
+        ids = rng.integers(0, E, size=6)
+        pl = c.plan(layer, ids)
+        slots = [pl.slot_of_expert[e] for e in range(E)]
+        for e in set(ids.tolist()):
+            assert slots[e] >= 0  # every requested expert is resident after planning
+        for i in range(pl.n_misses):
+            owner[pl.miss_slots[i]] = (layer, pl.miss_ids[i])
+        for e, sl in enumerate(slots):
+            if sl >= 0:
+                assert owner[sl] == (layer, e)
+        used = [sl for sl in slots if sl >= 0]
+        assert len(used) == len(set(used)) and all(0 <= sl < cap for sl in used)
+
+
+def test_cache_plan_errors():
+    c = _planner(4, 2, 16)
+    with pytest.raises(moe.MoeError) as e:
+        c.plan(0, np.arange(5))
+    assert e.value.code == CAPACITY
+    assert c.stats()["lookups"] == 0  # state unchanged
+    with pytest.raises(moe.MoeError):
+        c.plan(2, np.arange(2))
+    with pytest.raises(moe.MoeError):
+        c.plan(0, np.array([16]))
+    pl = c.plan(1, np.array([3, 3, 3]))
+    assert pl.n_ids == 1 and pl.n_misses == 1
+
+
+def test_cache_create_rejects_unpinned_bank():
+    bank = np.zeros(1 << 16, np.uint8)
+    d = _lib.MoeCacheDesc()
+    d.host_bank = bank.ctypes.data
+    d.pkg_bytes, d.L, d.E = 1024, 1, 8
+    d.device_pool = 256  # any non-null value: never dereferenced when the bank check fails
+    d.slot_stride, d.capacity = 1024, 4
+    h = ctypes.c_void_p()
+    assert L.moe_cache_create(ctypes.byref(d), ctypes.byref(h)) == -5

@@ -1,0 +1,208 @@
+"""GPU parity: the HIP path through the C-ABI against the fp64 oracle.
+
+Integer results (routing ids, permutation) and dequantized weights are compared
+bit-exactly; gate weights to 1e-6 relative; layer outputs to rel-L2 <= 5e-3 and
+max-abs <= 2e-2 * max|ref| (bf16 activations) or rel-L2 <= 1e-5 (fp32).
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import oracle  # noqa: E402
+from synth import workloads as W  # noqa: E402
+
+import mixture_experts_layer_token_amd as moe  # noqa: E402
+from mixture_experts_layer_token_amd.layer import build_layer, to_device_act  # noqa: E402
+
+from helpers import assert_output_close, oracle_reference, say, small_variant, to_f64  # noqa: E402
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    moe.lib()
+
+
+# ------------------------------------------------------------------ dequant
+
+@pytest.mark.parametrize("fmt", ["f32", "bf16", "mxfp4", "int4g32"])
+@pytest.mark.parametrize("H,I", [(224, 352), (2880, 96), (64, 2880)])
+def test_dequant_bit_exact(fmt, H, I):
+    say("dequant", fmt, H, I)
+    wl = small_variant(fmt, H=H, I=I, name="dq-%s-%d-%d" % (fmt, H, I))
+    ex = W.expert_weights(wl, 0, 5)
+    pkg = moe.moe_pack_expert(H, I, fmt, ex)
+    d_pkg = torch.from_numpy(pkg).cuda()
+    out = torch.empty(3 * H * I, dtype=torch.float32, device="cuda")
+    moe.moe_dequant_expert(d_pkg, H, I, fmt, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    want = np.concatenate([oracle.decode(fmt, ex["w"][m], ex["s"][m], *shp).ravel()
+                           for m, shp in enumerate([(I, H), (I, H), (H, I)])]).astype(np.float32)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+# ------------------------------------------------------------------ router
+
+ROUTE_CASES = [
+    ("tiny", 16, {}),
+    ("mixtral", 64, {}),
+    ("gptoss", 512, {}),
+    ("kimi", 300, {}),
+    ("tiny", 16, dict(E=1, k=1, name="e1k1")),
+    ("tiny", 16, dict(k=8, name="k-eq-e")),
+    ("tiny", 37, dict(E=1024, k=16, H=64, name="e1024", xdt="bf16")),
+]
+
+
+@pytest.mark.parametrize("name,T,kw", ROUTE_CASES, ids=[c[0] + "-" + str(c[1]) + str(c[2].get("name", ""))
+                                                         for c in ROUTE_CASES])
+def test_route_exact(name, T, kw):
+    wl = W.WORKLOADS[name].with_(**kw)
+    say("route", wl.name, "T", T, "E", wl.E, "k", wl.k)
+    x, _ = oracle.rank_gap_inputs(wl, T)
+    wg = W.router_weights(wl)
+    bias = W.router_bias(wl)
+    lg = oracle.router_logits(wl.xdt, x, wg, bias)
+    ids_ref, w_ref = oracle.topk_gates(lg, wl.k)
+    xd, wgd = to_device_act(x, wl.xdt), to_device_act(wg, wl.xdt)
+    bd = torch.from_numpy(bias).cuda() if bias is not None else None
+    ids = torch.empty((T, wl.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, wl.k), dtype=torch.float32, device="cuda")
+    logits = torch.empty((T, wl.E), dtype=torch.float32, device="cuda")
+    moe.moe_route(xd, wgd, bd, wl.k, ids, w, logits)
+    torch.cuda.synchronize()
+    assert np.array_equal(ids.cpu().numpy(), ids_ref)
+    np.testing.assert_allclose(w.cpu().numpy(), w_ref, rtol=1e-6, atol=1e-7)
+    np.testing.assert_allclose(logits.cpu().numpy(), lg, rtol=1e-4, atol=1e-4 * np.abs(lg).max())
+
+
+# ------------------------------------------------------------------ permutation
+
+PERM_CASES = [(0, 2, 8), (1, 1, 1), (16, 2, 8), (64, 2, 8), (512, 4, 128), (8192, 8, 384), (100, 16, 1024),
+              (333, 3, 7), (4096, 16, 1024)]
+
+
+@pytest.mark.parametrize("T,k,E", PERM_CASES)
+def test_permute_exact(T, k, E):
+    say("permute", T, k, E)
+    rng = np.random.default_rng(T * 7 + k * 3 + E)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32) if T else np.zeros((0, k), np.int32)
+    if T > 10:
+        ids[: T // 3, 0] = 0  # a hot expert
+    c_ref, o_ref, p_ref, i_ref = oracle.permute(ids, E)
+    d_ids = torch.from_numpy(ids).cuda()
+    n = max(T * k, 1)
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    perm = torch.empty(n, dtype=torch.int32, device="cuda")
+    inv = torch.empty(n, dtype=torch.int32, device="cuda")
+    moe.moe_permute(d_ids, E, counts, offsets, perm, inv)
+    torch.cuda.synchronize()
+    assert np.array_equal(counts.cpu().numpy(), c_ref)
+    assert np.array_equal(offsets.cpu().numpy(), o_ref)
+    assert np.array_equal(perm.cpu().numpy()[:T * k], p_ref)
+    assert np.array_equal(inv.cpu().numpy()[:T * k], i_ref)
+
+
+def test_permute_all_tokens_one_expert():
+    T, k, E = 1000, 1, 16
+    ids = np.full((T, k), 11, dtype=np.int32)
+    d_ids = torch.from_numpy(ids).cuda()
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    perm = torch.empty(T, dtype=torch.int32, device="cuda")
+    inv = torch.empty(T, dtype=torch.int32, device="cuda")
+    moe.moe_permute(d_ids, E, counts, offsets, perm, inv)
+    torch.cuda.synchronize()
+    assert counts.cpu().numpy()[11] == T and np.array_equal(perm.cpu().numpy(), np.arange(T))
+
+
+# ------------------------------------------------------------------ whole layer, reduced shapes
+
+SMALL = [("f32", "f32"), ("f32", "bf16"), ("bf16", "bf16"), ("mxfp4", "bf16"), ("int4g32", "bf16"),
+         ("bf16", "f32"), ("int4g32", "f32")]
+
+
+@pytest.mark.parametrize("fmt,xdt", SMALL)
+@pytest.mark.parametrize("T", [1, 3, 40, 130])
+def test_layer_small(fmt, xdt, T):
+    wl = small_variant(fmt, xdt)
+    say("layer small", wl.name, "T", T)
+    x, _ = oracle.rank_gap_inputs(wl, T)
+    layer = build_layer(wl, T)
+    out = layer.forward(to_device_act(x, xdt))
+    torch.cuda.synchronize()
+    ref, ids_ref, w_ref = oracle_reference(wl, x, np.arange(T))
+    assert np.array_equal(layer.topk_ids[:T].cpu().numpy(), ids_ref)
+    np.testing.assert_allclose(layer.topk_w[:T].cpu().numpy(), w_ref, rtol=1e-6, atol=1e-7)
+    tol_dt = "f32" if (fmt == "f32" and xdt == "f32") else "bf16"
+    assert_output_close(to_f64(out), ref, tol_dt, wl.name)
+
+
+def test_tiny_config_full():
+    wl = W.WORKLOADS["tiny"]
+    T = wl.Ts[0]
+    say("tiny config", T)
+    x, _ = oracle.rank_gap_inputs(wl, T)
+    layer = build_layer(wl, T)
+    out = layer.forward(to_device_act(x, wl.xdt))
+    torch.cuda.synchronize()
+    ref, ids_ref, _ = oracle_reference(wl, x, np.arange(T))
+    assert np.array_equal(layer.topk_ids.cpu().numpy(), ids_ref)
+    assert_output_close(to_f64(out), ref, "f32", "tiny")
+
+
+def test_layer_deterministic():
+    wl = small_variant("mxfp4")
+    x, _ = oracle.rank_gap_inputs(wl, 40)
+    layer = build_layer(wl, 40)
+    xd = to_device_act(x, "bf16")
+    a = layer.forward(xd).clone()
+    b = layer.forward(xd).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_shared_expert_small():
+    wl = small_variant("int4g32", shared=True, name="small-shared")
+    T = 40
+    say("shared expert", wl.name)
+    x, _ = oracle.rank_gap_inputs(wl, T)
+    layer = build_layer(wl, T)
+    out = layer.forward(to_device_act(x, "bf16"))
+    torch.cuda.synchronize()
+    ref, _, _ = oracle_reference(wl, x, np.arange(T))
+    assert_output_close(to_f64(out), ref, "bf16", wl.name)
+
+
+# ------------------------------------------------------------------ full-size configurations (sampled tokens)
+
+FULL = [("mixtral", 1), ("mixtral", 8), ("mixtral", 32), ("mixtral", 64), ("gptoss", 1), ("gptoss", 64),
+        ("gptoss", 512)]
+
+
+@pytest.mark.parametrize("name,T", FULL)
+def test_full_size_sampled(name, T):
+    wl = W.WORKLOADS[name]
+    say("full size", wl.name, "T", T)
+    x, _ = oracle.rank_gap_inputs(wl, T)
+    layer = build_layer(wl, T)
+    out = layer.forward(to_device_act(x, wl.xdt))
+    torch.cuda.synchronize()
+    ids_all = layer.topk_ids[:T].cpu().numpy()
+    # routing and permutation of every token
+    wg, bias = W.router_weights(wl), W.router_bias(wl)
+    ids_ref, _ = oracle.topk_gates(oracle.router_logits(wl.xdt, x, wg, bias), wl.k)
+    assert np.array_equal(ids_all, ids_ref)
+    c, o, p, i = oracle.permute(ids_ref, wl.E)
+    assert np.array_equal(layer.offsets.cpu().numpy(), o)
+    assert np.array_equal(layer.perm_src[:T * wl.k].cpu().numpy(), p)
+    # outputs of sampled tokens
+    rng = np.random.default_rng(T)
+    sample = np.sort(rng.choice(T, size=min(T, 6), replace=False))
+    ref, _, _ = oracle_reference(wl, x, sample)
+    assert_output_close(to_f64(out)[sample], ref, wl.xdt, "%s T=%d" % (wl.name, T))
