@@ -23,11 +23,11 @@ constexpr int kMaxE = 1024;
 __device__ __forceinline__ bool better(float v, int e, float bv, int be) { return v > bv || (v == bv && e < be); }
 
 // top-k of one token's E logits in LDS row `lg`; executed by one full wave.  Chosen entries are
-// overwritten with -inf in LDS.  Lane 0 writes ids/weights.
+// overwritten with -inf in LDS.  Lane j keeps the j-th choice and writes ids[j], w[j].
 __device__ void wave_topk(float* lg, int E, int k, int32_t* ids, float* w) {
   const int lane = threadIdx.x & 63;
-  float sel_v[16];
-  int sel_e[16];
+  float my_v = -INFINITY;
+  int my_e = 0;
   for (int j = 0; j < k; ++j) {
     float bv = -INFINITY;
     int be = 0x7FFFFFFF;
@@ -40,22 +40,19 @@ __device__ void wave_topk(float* lg, int E, int k, int32_t* ids, float* w) {
       int oe = __shfl_xor(be, off, 64);
       if (better(ov, oe, bv, be)) bv = ov, be = oe;
     }
-    sel_v[j] = bv;
-    sel_e[j] = be;
+    if (lane == j) my_v = bv, my_e = be;
     if (lane == 0) lg[be] = -INFINITY;
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   }
-  if (lane == 0) {
-    float z = 0.f, p[16];
-    for (int j = 0; j < k; ++j) {
-      p[j] = expf(sel_v[j] - sel_v[0]);
-      z += p[j];
-    }
-    for (int j = 0; j < k; ++j) {
-      ids[j] = sel_e[j];
-      w[j] = p[j] / z;
-    }
+  // softmax over the k chosen logits (max = the first choice)
+  const float v0 = __shfl(my_v, 0, 64);
+  float p = lane < k ? expf(my_v - v0) : 0.f;
+  float z = p;
+  for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off, 64);
+  if (lane < k) {
+    ids[lane] = my_e;
+    w[lane] = p / z;
   }
 }
 

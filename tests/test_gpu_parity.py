@@ -1,8 +1,10 @@
 """GPU parity: the HIP path through the C-ABI against the fp64 oracle.
 
 Integer results (routing ids, permutation) and dequantized weights are compared
-bit-exactly; gate weights to 1e-6 relative; layer outputs to rel-L2 <= 5e-3 and
-max-abs <= 2e-2 * max|ref| (bf16 activations) or rel-L2 <= 1e-5 (fp32).
+bit-exactly; gate weights to 1e-5 relative (a gate's relative error is at most
+twice the largest logit error, and fp32 accumulation of H <= 8192 exact products
+leaves logit errors near 1e-6); layer outputs to rel-L2 <= 5e-3 and max-abs <=
+2e-2 * max|ref| (bf16 activations) or rel-L2 <= 1e-5 (fp32).
 """
 import numpy as np
 import pytest
@@ -17,6 +19,9 @@ import mixture_experts_layer_token_amd as moe  # noqa: E402
 from mixture_experts_layer_token_amd.layer import build_layer, to_device_act  # noqa: E402
 
 from helpers import assert_output_close, oracle_reference, say, small_variant, to_f64  # noqa: E402
+
+
+GATE_RTOL, GATE_ATOL = 1e-5, 1e-6
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -76,7 +81,7 @@ def test_route_exact(name, T, kw):
     moe.moe_route(xd, wgd, bd, wl.k, ids, w, logits)
     torch.cuda.synchronize()
     assert np.array_equal(ids.cpu().numpy(), ids_ref)
-    np.testing.assert_allclose(w.cpu().numpy(), w_ref, rtol=1e-6, atol=1e-7)
+    np.testing.assert_allclose(w.cpu().numpy(), w_ref, rtol=GATE_RTOL, atol=GATE_ATOL)
     np.testing.assert_allclose(logits.cpu().numpy(), lg, rtol=1e-4, atol=1e-4 * np.abs(lg).max())
 
 
@@ -138,7 +143,7 @@ def test_layer_small(fmt, xdt, T):
     torch.cuda.synchronize()
     ref, ids_ref, w_ref = oracle_reference(wl, x, np.arange(T))
     assert np.array_equal(layer.topk_ids[:T].cpu().numpy(), ids_ref)
-    np.testing.assert_allclose(layer.topk_w[:T].cpu().numpy(), w_ref, rtol=1e-6, atol=1e-7)
+    np.testing.assert_allclose(layer.topk_w[:T].cpu().numpy(), w_ref, rtol=GATE_RTOL, atol=GATE_ATOL)
     tol_dt = "f32" if (fmt == "f32" and xdt == "f32") else "bf16"
     assert_output_close(to_f64(out), ref, tol_dt, wl.name)
 
