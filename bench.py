@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-expert MoE layer forward on one MI355X.
+
+One step = one pass of the whole layer (router + top-k, permutation, grouped
+SwiGLU expert FFN, weighted combine) over one batch of synthetic tokens, with
+weights and inputs resident in HBM.  The default workload is the
+Mixtral-8x7B-shaped bf16 layer (hidden 4096, 8 experts, top-2, inter 14336) at
+decode batch T=64; T in {1, 8, 32} are measured too and reported under
+"sweep".
+
+Prints one JSON line: MoE-layer tokens/s (whole step), the roofline of the
+dominant kernel (the gate/up weight-streaming GEMM, timed live with HIP events
+recorded by the library on the launch stream), and the CPU oracle timed on a
+bounded token sample on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+
+
+# ------------------------------------------------------------------ byte accounting
+
+def expert_bytes(wl, part: str) -> int:
+    """Bytes of one expert's gate+up ('gu') or down ('d') weights, block scales included."""
+    n = (2 if part == "gu" else 1) * wl.H * wl.I
+    return {"f32": 4 * n, "bf16": 2 * n, "mxfp4": n // 2 + n // 32, "int4g32": n // 2 + 2 * (n // 32)}[wl.wfmt]
+
+
+def step_bytes(wl, T: int, touched: int) -> dict:
+    """Algorithmic HBM bytes of one step: every touched expert's weights read once, activations once."""
+    a = 2 if wl.xdt == "bf16" else 4
+    hb = 4 if wl.wfmt == "f32" else 2
+    n = T * wl.k
+    gu = touched * expert_bytes(wl, "gu") + T * wl.H * a + n * wl.I * hb
+    down = touched * expert_bytes(wl, "d") + n * wl.I * hb + n * wl.H * 4
+    route = wl.E * wl.H * a + T * wl.H * a + n * 8
+    combine = n * wl.H * 4 + T * wl.H * a
+    return {"gu": gu, "down": down, "route": route, "combine": combine,
+            "total": gu + down + route + combine}
+
+
+def cost_model(C_s: float, S_s: float) -> dict:
+    """Seconds per token T = C + S (S: streaming term B / W, C: everything else) and the implied rate."""
+    T_s = C_s + S_s
+    return {"T_s": T_s, "tokens_per_s": 1.0 / T_s}
+
+
+def streaming_time(bytes_: float, bandwidth: float) -> float:
+    """S = B / W."""
+    return bytes_ / bandwidth
+
+
+# ------------------------------------------------------------------ measurement
+
+def measure(layer, xs, steps: int, warmup: int, trace: bool, max_traced: int = 32):
+    """Time `steps` steps between two events; on up to `max_traced` evenly spaced steps the library
+    also records events around the gate/up and down kernels (on the launch stream)."""
+    import torch
+
+    from mixture_experts_layer_token_amd import _lib
+
+    L = _lib.lib()
+    R = len(xs)
+    for i in range(warmup):
+        layer.forward(xs[i % R])
+    stride = max(1, steps // max_traced) if trace else steps + 1
+    traced = list(range(0, steps, stride)) if trace else []
+    ev = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in traced}
+    for trio in ev.values():  # create the underlying HIP events
+        for e in trio:
+            e.record()
+    handles = {i: ctypes_arr(trio) for i, trio in ev.items()}
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t0.record()
+    for i in range(steps):
+        h = handles.get(i)
+        if h is not None:
+            L.moe_ffn_trace_events(h)
+        layer.forward(xs[i % R])
+        if h is not None:
+            L.moe_ffn_trace_events(None)
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t0.elapsed_time(t1)
+    gu_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in traced]
+    dn_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in traced]
+    return total_ms, wall, gu_ms, dn_ms, traced
+
+
+def ctypes_arr(trio):
+    import ctypes
+
+    arr = (ctypes.c_void_p * 3)(*[e.cuda_event for e in trio])
+    return arr
+
+
+def touched_per_batch(layer, xs, E):
+    import torch
+
+    out = []
+    for x in xs:
+        layer.forward(x)
+        torch.cuda.synchronize()
+        out.append(int((layer.counts.cpu().numpy() > 0).sum()))
+    return out
+
+
+def cpu_baseline(wl, x_host: np.ndarray, n_tokens: int):
+    """The oracle on the first n_tokens of a batch, on the host cores (touched experts generated untimed)."""
+    import oracle
+    from synth import workloads as W
+
+    wg, bias = W.router_weights(wl), W.router_bias(wl)
+    sample = np.arange(n_tokens, dtype=np.int64)
+    lg = oracle.router_logits(wl.xdt, np.ascontiguousarray(x_host[:n_tokens]), wg, bias)
+    ids, _ = oracle.topk_gates(lg, wl.k)
+    experts = [None] * wl.E
+    for e in sorted(set(ids.ravel().tolist())):
+        experts[e] = W.expert_weights(wl, 0, e)
+    shared = W.shared_weights(wl)
+    t = time.perf_counter()
+    oracle.moe_layer(wl.xdt, x_host, wg, bias, wl.k, wl.I, experts, shared, wl.I if shared else 0, sample=sample)
+    dt = time.perf_counter() - t
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of %d tokens of the timed workload, full layer (route, top-k, %d experts' SwiGLU FFN, "
+                      "combine), fp64, %.1f s" % (n_tokens, x_host.shape[0], len(set(ids.ravel().tolist())), dt)}
+
+
+def run(args):
+    import torch
+
+    from synth import workloads as W
+
+    from mixture_experts_layer_token_amd.layer import build_layer, to_device_act
+
+    wl = W.WORKLOADS[args.workload]
+    Ts = sorted(set([args.T] + (list(wl.Ts) if args.sweep else [])))
+    layer = build_layer(wl, max(Ts))
+    results = {}
+    for T in Ts:
+        xs_host = [W.activations(wl, T, 0, 1000 + r) for r in range(args.batches)]
+        xs = [to_device_act(a, wl.xdt) for a in xs_host]
+        touched = touched_per_batch(layer, xs, wl.E)
+        steps = args.steps if T == args.T else max(20, args.steps // 4)
+        total_ms, wall, gu_ms, dn_ms, traced = measure(layer, xs, steps, args.warmup, trace=True)
+        b = [step_bytes(wl, T, touched[i % len(xs)]) for i in range(steps)]
+        tot_bytes = sum(x["total"] for x in b)
+        gu_bytes = sum(b[i]["gu"] for i in traced)  # bytes of the traced launches only
+        dn_bytes = sum(b[i]["down"] for i in traced)
+        ms = total_ms / steps
+        results[T] = dict(T=T, ms_per_step=ms, tokens_per_s=T * steps / (total_ms / 1e3),
+                          gu_us=1e3 * float(np.mean(gu_ms)), down_us=1e3 * float(np.mean(dn_ms)),
+                          gu_gbps=gu_bytes / (sum(gu_ms) / 1e3) / 1e9,
+                          down_gbps=dn_bytes / (sum(dn_ms) / 1e3) / 1e9,
+                          ffn_gbps=(gu_bytes + dn_bytes) / ((sum(gu_ms) + sum(dn_ms)) / 1e3) / 1e9,
+                          step_gbps=tot_bytes / (total_ms / 1e3) / 1e9,
+                          touched_mean=float(np.mean(touched)), gu_bytes_per_launch=gu_bytes / len(traced),
+                          traced=len(traced),
+                          steps=steps, wall_s=wall, xs_host=xs_host)
+    head = results[args.T]
+    out = {
+        "metric": "MoE-layer tokens/s (decode, whole layer) + achieved HBM GB/s of the expert FFN",
+        "value": round(head["tokens_per_s"], 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": head["steps"],
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.wfmt != "f32" else "f32",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights)",
+        "config": {"workload": "%s decode" % wl.name, "T": args.T, "hidden": wl.H, "experts": wl.E, "top_k": wl.k,
+                   "inter": wl.I, "weights": wl.wfmt, "activations": wl.xdt},
+        "roofline": {"bound": "hbm", "kernel": "ffn_stream_kernel gate/up (weight-streaming grouped GEMM + SwiGLU)",
+                     "achieved": round(head["gu_gbps"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(head["gu_gbps"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_launch_us": round(head["gu_us"], 3),
+                     "algorithmic_bytes_per_launch": int(head["gu_bytes_per_launch"]),
+                     "timed_launches": head["traced"]},
+        "expert_ffn": {"gbps": round(head["ffn_gbps"], 1), "frac": round(head["ffn_gbps"] / HBM_PEAK_GBS, 4),
+                       "gu_us": round(head["gu_us"], 3), "down_us": round(head["down_us"], 3),
+                       "down_gbps": round(head["down_gbps"], 1)},
+        "step_hbm_gbps": round(head["step_gbps"], 1),
+        "sweep": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()
+                   if k in ("T", "tokens_per_s", "ms_per_step", "gu_gbps", "down_gbps", "ffn_gbps", "step_gbps",
+                            "touched_mean")} for r in results.values()],
+    }
+    # the pages' decode cost model T = C + S for this step: S = expert bytes / peak HBM bandwidth
+    S = streaming_time(head["gu_bytes_per_launch"] + step_bytes(wl, args.T, int(round(head["touched_mean"])))["down"],
+                       HBM_PEAK_GBS * 1e9)
+    C = head["ms_per_step"] / 1e3 - S
+    out["cost_model"] = {"S_ms_at_peak": round(S * 1e3, 4), "C_ms_residual": round(C * 1e3, 4)}
+    if args.cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, head["xs_host"][0], min(args.cpu_tokens, args.T))
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="mixtral", choices=["mixtral", "gptoss"])
+    ap.add_argument("--T", type=int, default=64)
+    ap.add_argument("--batches", type=int, default=8, help="distinct input batches the steps rotate through")
+    ap.add_argument("--no-sweep", dest="sweep", action="store_false")
+    ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
+    ap.add_argument("--cpu-tokens", type=int, default=8)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (expert parallelism is a design note "
+              "only); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    out = run(args)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -171,6 +171,14 @@ size_t moe_ffn_workspace(const moe_experts* w, int T, int k, int mode);
 int moe_expert_ffn(const moe_experts* w, const void* x, int xdt, int T, int k, const int32_t* offsets,
                    const int32_t* perm_src, float* y_perm, int mode, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Profiling hook.  While set (on the calling thread), every moe_expert_ffn call records, on its
+ * stream, events[0] before its first kernel, events[1] after the gate/up kernel (before the
+ * down kernel) and events[2] after the down kernel.  `events` points to 3 hipEvent_t passed as
+ * void*; the array is read at each call, so it must stay valid while set.  NULL turns it off.
+ */
+int moe_ffn_trace_events(void* const* events);
+
 /* ------------------------------------------------------------------ combine */
 
 /*

@@ -8,6 +8,9 @@
 namespace moe {
 
 static thread_local char g_err[512] = "";
+static thread_local void* const* g_trace = nullptr;
+
+void* const* trace_events() { return g_trace; }
 
 void set_error(const char* fmt, ...) {
   va_list ap;
@@ -46,6 +49,11 @@ static int check_experts(const moe_experts* w, const char* fn) {
 using namespace moe;
 
 extern "C" const char* moe_last_error(void) { return g_err; }
+
+extern "C" int moe_ffn_trace_events(void* const* events) {
+  g_trace = events;
+  return MOE_OK;
+}
 
 extern "C" int moe_route(const void* x, int xdt, int T, int H, const void* w_router, const float* bias, int E, int k,
                          int32_t* topk_ids, float* topk_w, float* logits, void* stream) {

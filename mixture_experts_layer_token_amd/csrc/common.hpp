@@ -87,6 +87,7 @@ __host__ __device__ inline PackGeom pack_geom(int H, int I, int fmt) {
 }
 
 bool fmt_valid(int fmt);
+void* const* trace_events();  // moe_ffn_trace_events setting of this thread (or nullptr)
 bool dtype_valid(int dt);
 
 // ------------------------------------------------------------ launch helpers (internal)

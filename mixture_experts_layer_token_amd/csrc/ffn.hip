@@ -140,171 +140,229 @@ struct FfnArgs {
 
 // ------------------------------------------------------------------ streaming kernel
 
-// GU = true: strips (2j, 2j+1) of the GU matrix (K = H), epilogue SiLU(g)*u -> h.
-// GU = false: strip j of the down matrix (K = I), epilogue -> y_perm.
-template <int FMT, int MT, int NW, bool GU>
-__global__ __launch_bounds__(NW * 64) void ffn_stream_kernel(FfnArgs args) {
+// Weight loads of one pipeline stage, held in registers until consumed PF stages later.
+// bf16: a stage is one k-step: NSTR fragments of 16 bytes per lane.
+// 4-bit: a stage is one chunk of up to 4 k-steps: NSTR 16-byte code words + their scales.
+template <int FMT, int NSTR>
+struct Stage {
+  u32x4 code[NSTR];
+  unsigned scale[NSTR][FMT == MOE_W_INT4G32 ? 2 : 1];
+};
+
+// GU = true: a unit is the strip pair (2u, 2u+1) of the GU matrix (gate rows, up rows; K = H),
+//            epilogue SiLU(g)*u -> h.
+// GU = false: a unit is strip u of the down matrix (K = I), epilogue -> y_perm.
+// A workgroup owns units [NP*blockIdx.x, +NP) of one row tile; its NW waves split K.
+template <int FMT, int MT, int NW, int NP, int PF, bool GU>
+__global__ __launch_bounds__(NW * 64, (FMT == MOE_W_BF16 ? 3 : 2) * 4 / NW) void ffn_stream_kernel(FfnArgs args) {
   typedef typename Op<FMT>::T OpT;
-  constexpr int NS = GU ? 2 : 1;  // strips per workgroup
+  constexpr int SPU = GU ? 2 : 1;  // strips per unit
+  constexpr int NSTR = NP * SPU;   // strips per workgroup (every wave covers all of them)
   constexpr int MR = 16 * MT;
+  constexpr bool Q4 = FMT != MOE_W_BF16;
+  constexpr int SB = FMT == MOE_W_MXFP4 ? 1 : 2;  // scale bytes
+  constexpr int KPS = Q4 ? 4 : 1;                 // k-steps per stage
   __shared__ RowTile tile;
-  __shared__ f32x4 red[NW > 1 ? NW * MT * NS * 64 : 1];
+  __shared__ f32x4 red[NW > 1 ? NW * NSTR * 64 : 1];
 
   if (!find_row_tile(args.offsets, args.E, MR, blockIdx.y, &tile)) return;
   const int e = tile.e, p0 = tile.p0, rows = tile.rows;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar addressing
   const int K = GU ? args.H : args.I;
   const int N = GU ? args.I : args.H;  // output features of this matrix
-  const int j = blockIdx.x;            // strip (pair) index
+  const int n_units = N / 16;
+  const int u0 = blockIdx.x * NP;
   const int nks = K / 32;
 
   const int slot = args.slot_of_expert ? args.slot_of_expert[e] : e;
   const char* pkg = args.packages + (size_t)slot * args.pkg_stride;
-  const int strip0 = GU ? 2 * j : j;
 
-  // A operand rows of this lane (row m of each M tile), k offset 8*(lane/16)
+  // strip bases (workgroup-uniform); units past the end repeat the last unit, results dropped
+  const char* cbase[NSTR];
+  const char* sbase[NSTR];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int u = min(u0 + p, n_units - 1);
+#pragma unroll
+    for (int t = 0; t < SPU; ++t) {
+      const int strip = GU ? 2 * u + t : u;
+      cbase[p * SPU + t] = pkg + args.region_codes + (size_t)strip * (Q4 ? 8 : 32) * K;
+      sbase[p * SPU + t] = pkg + args.region_scales + (size_t)strip * 16 * nks * SB;
+    }
+  }
+  const unsigned lane16 = (unsigned)lane * 16, lrow = (unsigned)(lane & 15);
+  // activation rows of this lane: row m = lane % 16 of each M tile, k offset 8 * (lane / 16)
   const unsigned short* arow[MT];
   bool aok[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
-    int r = mt * 16 + (lane & 15);
+    const int r = mt * 16 + (lane & 15);
     aok[mt] = r < rows;
     int src = 0;
     if (aok[mt]) src = GU ? args.perm_src[p0 + r] / args.k : p0 + r;
     arow[mt] = args.a + (size_t)src * K + (lane >> 4) * 8;
   }
 
-  f32x4 acc[MT][NS];
+  f32x4 acc[MT][NSTR];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int s = 0; s < NS; ++s) acc[mt][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < NSTR; ++s) acc[mt][s] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if constexpr (FMT == MOE_W_BF16) {
-    const int ks0 = wave * nks / NW, ks1 = (wave + 1) * nks / NW;
-    const char* bp[NS];
+  // this wave's contiguous range of stages (k-steps for bf16, chunks of 4 k-steps for 4-bit)
+  const int n_stages = Q4 ? (nks + 3) / 4 : nks;
+  const int st0 = wave * n_stages / NW, st1 = (wave + 1) * n_stages / NW;
+  const int count = st1 - st0;
+
+  auto load_a = [&](OpT (&dst)[KPS][MT], int st) {
+    const int ns = Q4 ? min(4, nks - 4 * st) : 1;
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
-      bp[s] = pkg + args.region_codes + (size_t)(strip0 + s) * 16 * K * 2 + (size_t)lane * 16;
-#pragma unroll 4
-    for (int ks = ks0; ks < ks1; ++ks) {
-      OpT b[NS];
-#pragma unroll
-      for (int s = 0; s < NS; ++s) b[s] = *(const OpT*)(bp[s] + (size_t)ks * 1024);
+    for (int q = 0; q < KPS; ++q)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        OpT a = OpT{0, 0, 0, 0, 0, 0, 0, 0};
-        if (aok[mt]) a = *(const OpT*)(arow[mt] + ks * 32);
-#pragma unroll
-        for (int s = 0; s < NS; ++s) acc[mt][s] = mfma(a, b[s], acc[mt][s]);
+        OpT v = OpT{0, 0, 0, 0, 0, 0, 0, 0};
+        if (aok[mt] && q < ns) v = *(const OpT*)(arow[mt] + (KPS * st + q) * 32);
+        dst[q][mt] = v;
       }
-    }
-  } else {
-    constexpr int SB = FMT == MOE_W_MXFP4 ? 1 : 2;
-    const int nch = (nks + 3) / 4;
-    const int c0 = wave * nch / NW, c1 = (wave + 1) * nch / NW;
-    const char* cp[NS];
-    const char* sp[NS];
+  };
+  auto load_b = [&](Stage<FMT, NSTR>& S, int st) {
+    if constexpr (!Q4) {
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      cp[s] = pkg + args.region_codes + (size_t)(strip0 + s) * 8 * K;
-      sp[s] = pkg + args.region_scales + (size_t)(strip0 + s) * 16 * nks * SB;
-    }
-    for (int c = c0; c < c1; ++c) {
-      const int ns = min(4, nks - 4 * c);
-      unsigned wq[NS][4];
-      unsigned sq[NS][4];
+      for (int s = 0; s < NSTR; ++s) S.code[s] = *(const u32x4*)(cbase[s] + (size_t)st * 1024 + lane16);
+    } else {
+      const int ns = min(4, nks - 4 * st);
       if (ns == 4) {
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          u32x4 v = *(const u32x4*)(cp[s] + (size_t)c * 1024 + lane * 16);
-          wq[s][0] = v[0], wq[s][1] = v[1], wq[s][2] = v[2], wq[s][3] = v[3];
-          const char* sc = sp[s] + ((size_t)64 * c + (lane & 15) * 4) * SB;
-          if (SB == 1) {
-            unsigned u = *(const unsigned*)sc;
-            sq[s][0] = u & 255, sq[s][1] = (u >> 8) & 255, sq[s][2] = (u >> 16) & 255, sq[s][3] = u >> 24;
+        for (int s = 0; s < NSTR; ++s) {
+          S.code[s] = *(const u32x4*)(cbase[s] + (size_t)st * 1024 + lane16);
+          const char* sc = sbase[s] + ((size_t)st * 64 + lrow * 4) * SB;
+          if constexpr (SB == 1) {
+            S.scale[s][0] = *(const unsigned*)sc;
           } else {
-            uint2 u = *(const uint2*)sc;
-            sq[s][0] = u.x & 0xFFFF, sq[s][1] = u.x >> 16, sq[s][2] = u.y & 0xFFFF, sq[s][3] = u.y >> 16;
+            const uint2 v = *(const uint2*)sc;
+            S.scale[s][0] = v.x, S.scale[s][SB - 1] = v.y;
           }
         }
-      } else {
+      } else {  // the last, partial chunk: ns k-steps, packed 4 * ns bytes per lane
 #pragma unroll
-        for (int s = 0; s < NS; ++s)
-          for (int q = 0; q < 4; ++q) {
-            if (q < ns) {
-              wq[s][q] = *(const unsigned*)(cp[s] + (size_t)c * 1024 + lane * 4 * ns + 4 * q);
-              const char* sc = sp[s] + ((size_t)64 * c + (lane & 15) * ns + q) * SB;
-              sq[s][q] = SB == 1 ? (unsigned)*(const unsigned char*)sc : (unsigned)*(const unsigned short*)sc;
-            } else {
-              wq[s][q] = 0, sq[s][q] = 0;
-            }
+        for (int s = 0; s < NSTR; ++s) {
+          const char* cb = cbase[s] + (size_t)st * 1024 + (size_t)lane * 4 * ns;
+          const char* sb = sbase[s] + ((size_t)st * 64 + lrow * ns) * SB;
+          unsigned c[4] = {0, 0, 0, 0}, sc[4] = {0, 0, 0, 0};
+          for (int q = 0; q < ns; ++q) {
+            c[q] = *(const unsigned*)(cb + 4 * q);
+            sc[q] = SB == 1 ? (unsigned)*(const unsigned char*)(sb + q) : (unsigned)*(const unsigned short*)(sb + 2 * q);
           }
+          S.code[s] = u32x4{c[0], c[1], c[2], c[3]};
+          if constexpr (SB == 1) {
+            S.scale[s][0] = sc[0] | (sc[1] << 8) | (sc[2] << 16) | (sc[3] << 24);
+          } else {
+            S.scale[s][0] = sc[0] | (sc[1] << 16);
+            S.scale[s][SB - 1] = sc[2] | (sc[3] << 16);
+          }
+        }
       }
+    }
+  };
+  auto compute = [&](const Stage<FMT, NSTR>& S, const OpT (&a)[KPS][MT], int st) {
+    if constexpr (!Q4) {
+#pragma unroll
+      for (int s = 0; s < NSTR; ++s) {
+        const OpT b = __builtin_bit_cast(OpT, S.code[s]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[mt][s] = mfma(a[0][mt], b, acc[mt][s]);
+      }
+    } else {
+      // k-steps past the end of a partial last chunk hold zero codes, zero scales and zero
+      // activations, so all 4 k-steps are computed unconditionally
+      (void)st;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        if (q < ns) {
-          const int ks = 4 * c + q;
-          OpT b[NS];
 #pragma unroll
-          for (int s = 0; s < NS; ++s) {
-            if constexpr (FMT == MOE_W_MXFP4)
-              b[s] = dec_mxfp4(wq[s][q], sq[s][q]);
-            else
-              b[s] = dec_int4(wq[s][q], __builtin_bit_cast(_Float16, (unsigned short)sq[s][q]));
+        for (int s = 0; s < NSTR; ++s) {
+          OpT b;
+          if constexpr (FMT == MOE_W_MXFP4) {
+            b = dec_mxfp4(S.code[s][q], (S.scale[s][0] >> (8 * q)) & 255);
+          } else {
+            const unsigned sw = S.scale[s][q >> 1];
+            b = dec_int4(S.code[s][q], __builtin_bit_cast(_Float16, (unsigned short)(sw >> (16 * (q & 1)))));
           }
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            OpT a = OpT{0, 0, 0, 0, 0, 0, 0, 0};
-            if (aok[mt]) a = *(const OpT*)(arow[mt] + ks * 32);
-#pragma unroll
-            for (int s = 0; s < NS; ++s) acc[mt][s] = mfma(a, b[s], acc[mt][s]);
-          }
+          for (int mt = 0; mt < MT; ++mt) acc[mt][s] = mfma(a[q][mt], b, acc[mt][s]);
         }
+      }
+    }
+  };
+
+  // software pipeline: weights PF stages ahead, activations (L2-resident) one stage ahead
+  Stage<FMT, NSTR> ring[PF];
+  OpT a_cur[KPS][MT], a_nxt[KPS][MT];
+#pragma unroll
+  for (int i = 0; i < PF; ++i)
+    if (i < count) load_b(ring[i], st0 + i);
+  if (count > 0) load_a(a_nxt, st0);
+  for (int base = 0; base < count; base += PF) {
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      const int st = base + i;
+      if (st < count) {
+#pragma unroll
+        for (int q = 0; q < KPS; ++q)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) a_cur[q][mt] = a_nxt[q][mt];
+        if (st + 1 < count) load_a(a_nxt, st0 + st + 1);
+        compute(ring[i], a_cur, st0 + st);
+        if (st + PF < count) load_b(ring[i], st0 + st + PF);
       }
     }
   }
 
-  // ---- reduce the NW partial tiles (fixed wave order) and run the epilogue
-  if constexpr (NW > 1) {
+  // ---- sum the NW partial tiles (fixed wave order) one M tile at a time, then the epilogue
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+  for (int mt = 0; mt < MT; ++mt) {
+    if (mt * 16 >= rows) break;  // block-uniform
+    if constexpr (NW > 1) {
+      if (mt) __syncthreads();
 #pragma unroll
-      for (int s = 0; s < NS; ++s) red[((wave * MT + mt) * NS + s) * 64 + lane] = acc[mt][s];
-    __syncthreads();
-  }
-  // each thread finishes (mt, lane') pairs: tid -> lane' = tid % 64, mt = tid / 64 + NW * i
-  for (int idx = threadIdx.x; idx < MT * 64; idx += NW * 64) {
-    const int mt = idx >> 6, ln = idx & 63;
-    f32x4 v[NS];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      if constexpr (NW > 1) {
-        v[s] = red[((0 * MT + mt) * NS + s) * 64 + ln];
-        for (int w = 1; w < NW; ++w) {
-          f32x4 o = red[((w * MT + mt) * NS + s) * 64 + ln];
-          v[s][0] += o[0], v[s][1] += o[1], v[s][2] += o[2], v[s][3] += o[3];
-        }
-      } else {
-        v[s] = acc[mt][s];
-      }
+      for (int s = 0; s < NSTR; ++s) red[(wave * NSTR + s) * 64 + lane] = acc[mt][s];
+      __syncthreads();
     }
-    const int col = j * 16 + (ln & 15);
+    for (int idx = threadIdx.x; idx < NP * 64; idx += NW * 64) {
+      const int p = idx >> 6, ln = idx & 63;
+      const int u = u0 + p;
+      if (u >= n_units) continue;
+      f32x4 v[SPU];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = mt * 16 + (ln >> 4) * 4 + r;
-      if (row >= rows) continue;
-      const size_t p = (size_t)(p0 + row);
-      if constexpr (GU) {
-        float h = silu(v[0][r]) * v[1][r];
-        unsigned short hb;
-        if constexpr (FMT == MOE_W_INT4G32)
-          hb = __builtin_bit_cast(unsigned short, (_Float16)h);
-        else
-          hb = f32_to_bf16_rne(h);
-        ((unsigned short*)args.out)[p * N + col] = hb;
-      } else {
-        ((float*)args.out)[p * N + col] = v[0][r];
+      for (int t = 0; t < SPU; ++t) {
+        const int s = p * SPU + t;
+        if constexpr (NW > 1) {
+          v[t] = red[s * 64 + ln];
+          for (int w = 1; w < NW; ++w) {
+            const f32x4 o = red[(w * NSTR + s) * 64 + ln];
+            v[t][0] += o[0], v[t][1] += o[1], v[t][2] += o[2], v[t][3] += o[3];
+          }
+        } else {
+          v[t] = acc[mt][s];
+        }
+      }
+      const int col = u * 16 + (ln & 15);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = mt * 16 + (ln >> 4) * 4 + r;
+        if (row >= rows) continue;
+        const size_t pr = (size_t)(p0 + row);
+        if constexpr (GU) {
+          const float h = silu(v[0][r]) * v[1][r];
+          unsigned short hb;
+          if constexpr (FMT == MOE_W_INT4G32)
+            hb = __builtin_bit_cast(unsigned short, (_Float16)h);
+          else
+            hb = f32_to_bf16_rne(h);
+          ((unsigned short*)args.out)[pr * N + col] = hb;
+        } else {
+          ((float*)args.out)[pr * N + col] = v[0][r];
+        }
       }
     }
   }
@@ -445,23 +503,46 @@ WsLayout ws_layout(const moe_experts* w, int T, int k, int xdt) {
 
 int pick_mt(int T, int k, int E) {
   double avg = (double)T * k / E;
-  int mt = (int)ceil(1.5 * avg / 16.0);
-  return mt < 1 ? 1 : (mt > 4 ? 4 : mt);
+  return 1.5 * avg > 16.0 ? 2 : 1;
 }
+
+inline void trace(int i, hipStream_t s) {
+  void* const* ev = trace_events();
+  if (ev && ev[i]) (void)hipEventRecord((hipEvent_t)ev[i], s);
+}
+
+// Tile shapes per format and M-tile count: (units per workgroup, waves, pipeline depth) for
+// gate/up and down.  bf16 fragments are 1 KiB per strip and k-step, so a few strips already keep
+// enough bytes in flight; 4-bit fragments are 4x smaller, so a workgroup covers more strips,
+// which also lets one activation fragment feed more weight fragments (less L2 traffic).  The
+// 4-bit shapes stay within 256 VGPRs (2 waves per SIMD).
+template <int FMT, int MT>
+struct Cfg {
+  static constexpr bool Q4 = FMT != MOE_W_BF16;
+  static constexpr int GU_NP = Q4 ? (MT == 1 ? 4 : 2) : 1;
+  static constexpr int GU_NW = 4;
+  static constexpr int GU_PF = Q4 ? 2 : 4;
+  static constexpr int D_NP = Q4 ? (MT == 1 ? 8 : 4) : 2;
+  static constexpr int D_NW = Q4 ? 4 : 8;
+  static constexpr int D_PF = Q4 ? 2 : 4;
+};
 
 template <int FMT, int MT>
 void launch_stream_mt(const FfnArgs& gu, const FfnArgs& dn, int H, int I, int S, hipStream_t s) {
-  hipLaunchKernelGGL((ffn_stream_kernel<FMT, MT, 4, true>), dim3(I / 16, S), dim3(256), 0, s, gu);
-  hipLaunchKernelGGL((ffn_stream_kernel<FMT, MT, 8, false>), dim3(H / 16, S), dim3(512), 0, s, dn);
+  typedef Cfg<FMT, MT> C;
+  const int gx = (I / 16 + C::GU_NP - 1) / C::GU_NP, dx = (H / 16 + C::D_NP - 1) / C::D_NP;
+  hipLaunchKernelGGL((ffn_stream_kernel<FMT, MT, C::GU_NW, C::GU_NP, C::GU_PF, true>), dim3(gx, S),
+                     dim3(64 * C::GU_NW), 0, s, gu);
+  trace(1, s);
+  hipLaunchKernelGGL((ffn_stream_kernel<FMT, MT, C::D_NW, C::D_NP, C::D_PF, false>), dim3(dx, S), dim3(64 * C::D_NW),
+                     0, s, dn);
 }
 
 template <int FMT>
 void launch_stream(int mt, const FfnArgs& gu, const FfnArgs& dn, int H, int I, int S, hipStream_t s) {
   switch (mt) {
     case 1: launch_stream_mt<FMT, 1>(gu, dn, H, I, S, s); break;
-    case 2: launch_stream_mt<FMT, 2>(gu, dn, H, I, S, s); break;
-    case 3: launch_stream_mt<FMT, 3>(gu, dn, H, I, S, s); break;
-    default: launch_stream_mt<FMT, 4>(gu, dn, H, I, S, s); break;
+    default: launch_stream_mt<FMT, 2>(gu, dn, H, I, S, s); break;
   }
 }
 
@@ -496,6 +577,7 @@ int launch_ffn(const moe_experts* w, const void* x, int xdt, int T, int k, const
   FfnArgs dn = gu;
   void* h = wsp + L.h_off;
 
+  trace(0, s);
   if (w->fmt == MOE_W_F32) {
     const int S = (int)((n + (size_t)(n < (size_t)E ? n : E) * 63) / 64);
     gu.a = (const unsigned short*)x;
@@ -506,7 +588,9 @@ int launch_ffn(const moe_experts* w, const void* x, int xdt, int T, int k, const
       hipLaunchKernelGGL((ffn_f32_kernel<float, true>), dim3((I + 3) / 4, S), dim3(256), 0, s, gu);
     else
       hipLaunchKernelGGL((ffn_f32_kernel<unsigned short, true>), dim3((I + 3) / 4, S), dim3(256), 0, s, gu);
+    trace(1, s);
     hipLaunchKernelGGL((ffn_f32_kernel<float, false>), dim3((H + 3) / 4, S), dim3(256), 0, s, dn);
+    trace(2, s);
     MOE_CHECK_LAUNCH("moe_expert_ffn f32 launch");
     return MOE_OK;
   }
@@ -541,6 +625,7 @@ int launch_ffn(const moe_experts* w, const void* x, int xdt, int T, int k, const
     case MOE_W_INT4G32: launch_stream<MOE_W_INT4G32>(mt, gu, dn, H, I, S, s); break;
     default: return fail(MOE_ERR_UNSUPPORTED, "moe_expert_ffn: format %d", w->fmt);
   }
+  trace(2, s);
   MOE_CHECK_LAUNCH("moe_expert_ffn launch");
   return MOE_OK;
 }

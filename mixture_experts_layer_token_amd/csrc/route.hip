@@ -3,9 +3,10 @@
 // expert for every token ("Mixture of experts VRAM: total vs active parameters", section "How
 // current MoE models route each token").
 //
-// bf16 activations: one workgroup per 16 tokens; its 4 waves split the experts into 16-wide
-// MFMA tiles (v_mfma_f32_16x16x32_bf16, fp32 accumulation), the 16 x E logit block goes to
-// LDS, then each wave selects the top-k of 4 tokens with 64-lane shuffle reductions.
+// bf16 activations: one workgroup per 16 tokens; its 8 waves cover the experts in 16-wide MFMA
+// tiles (v_mfma_f32_16x16x32_bf16, fp32 accumulation) and, when there are few tiles, also split
+// the hidden dimension; the 16 x E logit block goes to LDS, then each wave selects the top-k of
+// 2 tokens with 64-lane shuffle reductions.
 // fp32 activations: one workgroup per token, fp32 FMA dot products reduced across the wave.
 #include <math.h>
 
@@ -15,7 +16,6 @@ namespace moe {
 namespace {
 
 constexpr int kRouteTokens = 16;    // tokens per workgroup (MFMA M)
-constexpr int kRouteWaves = 4;
 constexpr int kTilesPerPass = 8;    // 16-expert tiles each wave accumulates per pass over H
 constexpr int kMaxE = 1024;
 
@@ -56,38 +56,51 @@ __device__ void wave_topk(float* lg, int E, int k, int32_t* ids, float* w) {
   }
 }
 
-__global__ __launch_bounds__(256) void route_bf16_kernel(const unsigned short* __restrict__ x,
-                                                         const unsigned short* __restrict__ wg,
-                                                         const float* __restrict__ bias, int T, int H, int E, int k,
-                                                         int32_t* __restrict__ ids, float* __restrict__ w,
-                                                         float* __restrict__ logits) {
-  extern __shared__ float lds[];  // [16][Epad]
+// 8 waves: G groups of expert tiles x R ranges of H (G * R = 8).  Few experts (decode shapes):
+// all waves split H, so every wave has a short run of loads in flight; many experts: waves split
+// the expert tiles.  Partial logits of the R ranges are summed in LDS in fixed order.
+constexpr int kRouteThreads = 512;
+
+__global__ __launch_bounds__(kRouteThreads) void route_bf16_kernel(const unsigned short* __restrict__ x,
+                                                                   const unsigned short* __restrict__ wg,
+                                                                   const float* __restrict__ bias, int T, int H,
+                                                                   int E, int k, int G, int32_t* __restrict__ ids,
+                                                                   float* __restrict__ w,
+                                                                   float* __restrict__ logits) {
+  extern __shared__ float lds[];  // [R][16][Epad]
   const int Epad = ((E + 15) / 16) * 16 + 1;
+  const int R = 8 / G;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int grp = wave % G, rng = wave / G;
   const int t0 = blockIdx.x * kRouteTokens;
   const int m = lane & 15, kq = (lane >> 4) * 8;
   const int n_tiles = (E + 15) / 16;
+  const int nks = H / 32;
+  const int ks0 = rng * nks / R, ks1 = (rng + 1) * nks / R;
   const bool row_ok = t0 + m < T;
   const unsigned short* xrow = x + (size_t)(row_ok ? t0 + m : 0) * H + kq;
+  float* part = lds + (size_t)rng * kRouteTokens * Epad;
 
-  for (int first = wave; first < n_tiles; first += kRouteWaves * kTilesPerPass) {
+  for (int first = grp; first < n_tiles; first += G * kTilesPerPass) {
     f32x4 acc[kTilesPerPass];
     const unsigned short* brow[kTilesPerPass];
     bool bok[kTilesPerPass];
 #pragma unroll
     for (int i = 0; i < kTilesPerPass; ++i) {
       acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-      int nt = first + i * kRouteWaves;
+      int nt = first + i * G;
       int e = nt * 16 + m;
       bok[i] = nt < n_tiles && e < E;
       brow[i] = wg + (size_t)(bok[i] ? e : 0) * H + kq;
     }
-    for (int kk = 0; kk < H; kk += 32) {
+#pragma unroll 4
+    for (int ks = ks0; ks < ks1; ++ks) {
+      const int kk = ks * 32;
       bf16x8 a = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
       if (row_ok) a = *(const bf16x8*)(xrow + kk);
 #pragma unroll
       for (int i = 0; i < kTilesPerPass; ++i) {
-        if (first + i * kRouteWaves < n_tiles) {  // wave-uniform
+        if (first + i * G < n_tiles) {  // wave-uniform
           bf16x8 b = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
           if (bok[i]) b = *(const bf16x8*)(brow[i] + kk);
           acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[i], 0, 0, 0);
@@ -96,25 +109,28 @@ __global__ __launch_bounds__(256) void route_bf16_kernel(const unsigned short* _
     }
 #pragma unroll
     for (int i = 0; i < kTilesPerPass; ++i) {
-      int nt = first + i * kRouteWaves;
+      int nt = first + i * G;
       if (nt >= n_tiles) continue;
       int e = nt * 16 + (lane & 15);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         int row = (lane >> 4) * 4 + r;
-        if (e < E) lds[row * Epad + e] = acc[i][r] + (bias ? bias[e] : 0.f);
+        if (e < E) part[row * Epad + e] = acc[i][r];
       }
     }
   }
   __syncthreads();
-  if (logits) {
-    for (int i = threadIdx.x; i < kRouteTokens * E; i += blockDim.x) {
-      int row = i / E, e = i % E;
-      if (t0 + row < T) logits[(size_t)(t0 + row) * E + e] = lds[row * Epad + e];
-    }
-    __syncthreads();
+  // sum the R partial blocks into block 0 (fixed order), add the bias
+  for (int i = threadIdx.x; i < kRouteTokens * E; i += blockDim.x) {
+    int row = i / E, e = i % E;
+    float v = lds[row * Epad + e];
+    for (int r = 1; r < R; ++r) v += lds[((size_t)r * kRouteTokens + row) * Epad + e];
+    v += bias ? bias[e] : 0.f;
+    lds[row * Epad + e] = v;
+    if (logits && t0 + row < T) logits[(size_t)(t0 + row) * E + e] = v;
   }
-  for (int row = wave; row < kRouteTokens; row += kRouteWaves) {
+  __syncthreads();
+  for (int row = wave; row < kRouteTokens; row += kRouteThreads / 64) {
     int t = t0 + row;
     if (t >= T) break;
     wave_topk(lds + row * Epad, E, k, ids + (size_t)t * k, w + (size_t)t * k);
@@ -151,15 +167,18 @@ int launch_route(const void* x, int xdt, int T, int H, const void* wg, const flo
   if (E > kMaxE) return fail(MOE_ERR_INVALID, "moe_route: E=%d exceeds %d", E, kMaxE);
   if (xdt == MOE_BF16) {
     if (H % 32) return fail(MOE_ERR_UNSUPPORTED, "moe_route: bf16 path needs H %% 32 == 0 (H=%d)", H);
-    int Epad = ((E + 15) / 16) * 16 + 1;
-    size_t lds = (size_t)kRouteTokens * Epad * sizeof(float);
+    const int Epad = ((E + 15) / 16) * 16 + 1;
+    const int n_tiles = (E + 15) / 16;
+    int G = 1;  // expert-tile groups; the other 8 / G waves split H
+    while (G < 8 && (n_tiles + G - 1) / G > kTilesPerPass) G *= 2;
+    const size_t lds = (size_t)(8 / G) * kRouteTokens * Epad * sizeof(float);
     if (lds > 65536) {
       hipError_t e = hipFuncSetAttribute((const void*)route_bf16_kernel,
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess) return hip_fail(e, "moe_route: LDS attribute");
     }
-    hipLaunchKernelGGL(route_bf16_kernel, dim3((T + kRouteTokens - 1) / kRouteTokens), dim3(64 * kRouteWaves), lds,
-                       s, (const unsigned short*)x, (const unsigned short*)wg, bias, T, H, E, k, ids, w, logits);
+    hipLaunchKernelGGL(route_bf16_kernel, dim3((T + kRouteTokens - 1) / kRouteTokens), dim3(kRouteThreads), lds,
+                       s, (const unsigned short*)x, (const unsigned short*)wg, bias, T, H, E, k, G, ids, w, logits);
   } else {
     hipLaunchKernelGGL(route_f32_kernel, dim3(T), dim3(256), (size_t)E * sizeof(float), s, (const float*)x,
                        (const float*)wg, bias, T, H, E, k, ids, w, logits);
