@@ -350,3 +350,28 @@ def test_belady_at_least_lru_large():
     hb, _ = oracle.belady(64, groups)
     hl, _, _ = oracle.lru(64, groups)
     assert hb.sum() >= hl.sum()
+
+
+# ------------------------------------------------------------- cost model (report formula)
+
+def test_cost_model_matches_the_printed_worked_example():
+    """T = C + S, S = B / W: the GLM and Kimi figures of the Galactus cost model."""
+    import json
+    import os
+
+    import bench
+
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "galactus_cost_model.json")))
+    k = g["kimi_streaming"]
+    assert abs(bench.streaming_time(k["B_bytes"], k["W_bytes_per_s"]) - k["S_s_approx"]) < 1e-9
+    r = g["glm_rounded"]
+    cm = bench.cost_model(r["C_s"], r["S_s"])
+    assert abs(cm["T_s"] - r["T_s"]) < 1e-12 and round(cm["tokens_per_s"], 2) == r["tokens_per_s"]
+    m = g["glm_traffic_minus_25pct"]
+    S2 = round(r["S_s"] * 0.75, 3)  # "about 68 ms"
+    assert abs(S2 - m["S_s_approx"]) < 1e-9
+    cm2 = bench.cost_model(r["C_s"], S2)
+    assert abs(cm2["T_s"] - m["T_s_approx"]) < 1e-9 and round(cm2["tokens_per_s"], 2) == m["tokens_per_s"]
+    assert round(cm2["tokens_per_s"] / cm["tokens_per_s"] - 1, 2) == m["gain_approx"]
+    mr = g["measured_reciprocals"]
+    assert round(1000 / mr["kimi_tok_s"]) == mr["kimi_ms"] and round(1000 / mr["glm_tok_s"]) == mr["glm_ms"]
