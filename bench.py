@@ -69,9 +69,6 @@ def measure(layer, xs, steps: int, warmup: int, trace: bool, max_traced: int = 3
     also records events around the gate/up and down kernels (on the launch stream)."""
     import torch
 
-    from mixture_experts_layer_token_amd import _lib
-
-    L = _lib.lib()
     R = len(xs)
     for i in range(warmup):
         layer.forward(xs[i % R])
@@ -88,12 +85,7 @@ def measure(layer, xs, steps: int, warmup: int, trace: bool, max_traced: int = 3
     wall0 = time.perf_counter()
     t0.record()
     for i in range(steps):
-        h = handles.get(i)
-        if h is not None:
-            L.moe_ffn_trace_events(h)
-        layer.forward(xs[i % R])
-        if h is not None:
-            L.moe_ffn_trace_events(None)
+        layer.forward(xs[i % R], trace=handles.get(i))
     t1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -121,9 +113,10 @@ def touched_per_batch(layer, xs, E):
     return out
 
 
-def cpu_baseline(wl, xs_host, min_seconds: float = 10.0):
-    """The oracle on whole batches of the timed workload until about `min_seconds` of host time is
-    spent (routing, touched experts' SwiGLU FFN, combine; expert weights generated untimed)."""
+def cpu_baseline(wl, xs_host, min_seconds: float = 10.0, max_tokens: int | None = None):
+    """The oracle on whole batches of the timed workload (or on the first `max_tokens` tokens of one
+    batch) until about `min_seconds` of host time is spent: routing, touched experts' SwiGLU FFN,
+    shared expert, combine; expert weights generated untimed."""
     import oracle
     from synth import workloads as W
 
@@ -132,6 +125,8 @@ def cpu_baseline(wl, xs_host, min_seconds: float = 10.0):
     tokens, spent, batches = 0, 0.0, 0
     for i in range(64 * len(xs_host)):
         x = xs_host[i % len(xs_host)]
+        if max_tokens is not None:
+            x = np.ascontiguousarray(x[:max_tokens])
         lg = oracle.router_logits(wl.xdt, np.ascontiguousarray(x), wg, bias)
         ids, _ = oracle.topk_gates(lg, wl.k)
         experts = [None] * wl.E
@@ -150,8 +145,8 @@ def cpu_baseline(wl, xs_host, min_seconds: float = 10.0):
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {"value": tokens / spent, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": "%d batch(es) of %d tokens of the timed workload (%d tokens), whole layer in fp64: "
-                      "routing, top-k, touched experts' SwiGLU FFN, combine; %.1f s"
-                      % (batches, xs_host[0].shape[0], tokens, spent)}
+                      "routing, top-k, touched experts' SwiGLU FFN, shared expert, combine; %.1f s"
+                      % (batches, x.shape[0], tokens, spent)}
 
 
 def run(args):
@@ -162,15 +157,20 @@ def run(args):
     from mixture_experts_layer_token_amd.layer import build_layer, to_device_act
 
     wl = W.WORKLOADS[args.workload]
-    Ts = sorted(set([args.T] + (list(wl.Ts) if args.sweep else [])))
+    prefill = args.workload in PREFILL
+    if args.T is None:
+        args.T = wl.Ts[-1] if prefill else 64
+    Ts = sorted(set([args.T] + (list(wl.Ts) if args.sweep and not prefill else [])))
     layer = build_layer(wl, max(Ts))
     results = {}
     for T in Ts:
-        xs_host = [W.activations(wl, T, 0, 1000 + r) for r in range(args.batches)]
+        xs_host = [W.activations(wl, T, 0, 1000 + r) for r in range(args.batches if not prefill else 2)]
         xs = [to_device_act(a, wl.xdt) for a in xs_host]
         touched = touched_per_batch(layer, xs, wl.E)
         steps = args.steps if T == args.T else max(20, args.steps // 4)
-        total_ms, wall, gu_ms, dn_ms, traced = measure(layer, xs, steps, args.warmup, trace=True)
+        if prefill:
+            steps = min(steps, args.prefill_steps)
+        total_ms, wall, gu_ms, dn_ms, traced = measure(layer, xs, steps, min(args.warmup, steps), trace=True)
         b = [step_bytes(wl, T, touched[i % len(xs)]) for i in range(steps)]
         tot_bytes = sum(x["total"] for x in b)
         gu_bytes = sum(b[i]["gu"] for i in traced)  # bytes of the traced launches only
@@ -186,6 +186,8 @@ def run(args):
                           traced=len(traced),
                           steps=steps, wall_s=wall, xs_host=xs_host)
     head = results[args.T]
+    if prefill:
+        return prefill_report(wl, args, head)
     out = {
         "metric": "MoE-layer tokens/s (decode, whole layer) + achieved HBM GB/s of the expert FFN",
         "value": round(head["tokens_per_s"], 2),
@@ -225,13 +227,57 @@ def run(args):
     return out
 
 
+PREFILL = ("kimi",)
+MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 MFMA, published
+
+
+def prefill_report(wl, args, head):
+    """Prefill: the expert FFN is a dense grouped contraction, so the roofline is MFMA throughput."""
+    T, n = args.T, args.T * wl.k
+    gu_flops = 2.0 * n * (2 * wl.I) * wl.H
+    dn_flops = 2.0 * n * wl.H * wl.I
+    sh_flops = 2.0 * T * 3 * wl.H * wl.I if wl.shared else 0.0
+    step_flops = gu_flops + dn_flops + sh_flops + 2.0 * T * wl.E * wl.H
+    gu_tf = gu_flops / (head["gu_us"] * 1e-6) / 1e12
+    dn_tf = dn_flops / (head["down_us"] * 1e-6) / 1e12
+    out = {
+        "metric": "MoE-layer tokens/s (prefill, whole layer incl. shared expert) + MFMA utilisation of the expert FFN",
+        "value": round(head["tokens_per_s"], 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": head["steps"],
+        "warmup": min(args.warmup, head["steps"]),
+        "ms_per_step": round(head["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16" if wl.wfmt == "int4g32" else "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights quantized to %s)" % wl.wfmt,
+        "config": {"workload": "%s" % wl.name, "T": T, "hidden": wl.H, "experts": wl.E, "top_k": wl.k,
+                   "inter": wl.I, "weights": wl.wfmt, "shared_expert": "bf16" if wl.shared else None},
+        "roofline": {"bound": "mfma", "kernel": "routed gate/up grouped GEMM + SwiGLU",
+                     "achieved": round(gu_tf, 1), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gu_tf / MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                     "avg_launch_us": round(head["gu_us"], 1), "flops_per_launch": gu_flops,
+                     "timed_launches": head["traced"]},
+        "expert_ffn": {"gu_us": round(head["gu_us"], 1), "down_us": round(head["down_us"], 1),
+                       "down_tflops": round(dn_tf, 1)},
+        "step_tflops": round(step_flops / (head["ms_per_step"] * 1e-3) / 1e12, 1),
+    }
+    if args.cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, head["xs_host"], args.cpu_seconds, max_tokens=args.cpu_tokens)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="mixtral", choices=["mixtral", "gptoss"])
-    ap.add_argument("--T", type=int, default=64)
+    ap.add_argument("--workload", default="mixtral", choices=["mixtral", "gptoss", "kimi"])
+    ap.add_argument("--T", type=int, default=None, help="tokens per step (default 64 decode, 8192 prefill)")
+    ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--cpu-tokens", type=int, default=16, help="prefill: oracle token sample")
     ap.add_argument("--batches", type=int, default=8, help="distinct input batches the steps rotate through")
     ap.add_argument("--no-sweep", dest="sweep", action="store_false")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")

@@ -65,7 +65,9 @@ class MoeLayer:
         pws = api.moe_permute_workspace(T, k, E)
         self.pws = torch.empty(pws, dtype=torch.uint8, device=d) if pws else None
 
-    def forward(self, x: torch.Tensor, out: torch.Tensor | None = None, mode="auto") -> torch.Tensor:
+    def forward(self, x: torch.Tensor, out: torch.Tensor | None = None, mode="auto", trace=None) -> torch.Tensor:
+        """One layer forward on the current stream.  `trace`: optional ctypes array of 3 HIP events
+        recorded around the routed expert FFN's kernels (moe_ffn_trace_events)."""
         T = x.shape[0]
         if T > self.max_T:
             self._alloc(T)
@@ -74,10 +76,15 @@ class MoeLayer:
             out = torch.empty((T, self.H), dtype=x.dtype, device=x.device)
         ids, w = self.topk_ids[:T], self.topk_w[:T]
         api.moe_route(x, self.w_router, self.bias, k, ids, w)
-        self.route_only_done = True
         api.moe_permute(ids, self.E, self.counts, self.offsets, self.perm_src[:T * k], self.inv_perm[:T * k],
                         self.pws)
-        api.moe_expert_ffn(self.desc, x, k, self.offsets, self.perm_src, self.y_perm, self.ws, mode)
+        if trace is not None:
+            api.lib().moe_ffn_trace_events(trace)
+        try:
+            api.moe_expert_ffn(self.desc, x, k, self.offsets, self.perm_src, self.y_perm, self.ws, mode)
+        finally:
+            if trace is not None:
+                api.lib().moe_ffn_trace_events(None)
         sh = None
         if self.shared is not None:
             if T != self.sh_perm.numel():

@@ -204,10 +204,12 @@ def min_gap(logits: np.ndarray, k: int) -> np.ndarray:
     return np.min(top[:, :-1] - top[:, 1:], axis=1)
 
 
-def rank_gap_inputs(wl, T: int, layer: int = 0, step: int = 0, gap: float = 1e-3, max_attempts: int = 64):
+def rank_gap_inputs(wl, T: int, layer: int = 0, step: int = 0, gap: float = 1e-3, max_attempts: int = 64,
+                    return_logits: bool = False):
     """x [T, H] from the generator, every row redrawn until its top-(k+1) logits differ by >= gap.
 
-    Returns (x, attempts) where attempts[t] is the redraw index row t ended on.
+    Returns (x, attempts) where attempts[t] is the redraw index row t ended on, plus the final
+    fp64 logits [T, E] when return_logits is set.
     """
     from synth import workloads as W
 
@@ -215,12 +217,14 @@ def rank_gap_inputs(wl, T: int, layer: int = 0, step: int = 0, gap: float = 1e-3
     bias = W.router_bias(wl, layer, step)
     attempts = np.zeros(T, dtype=np.int64)
     x = W.activations(wl, T, layer, step)
-    bad = np.nonzero(min_gap(router_logits(wl.xdt, x, wg, bias), wl.k) < gap)[0]
+    logits = router_logits(wl.xdt, x, wg, bias)
+    bad = np.nonzero(min_gap(logits, wl.k) < gap)[0]
     while len(bad):
         attempts[bad] += 1
         if attempts.max() > max_attempts:
             raise RuntimeError("rank-gap redraw did not converge")
         x[bad] = W.activation_rows(wl, layer, step, bad, attempts[bad])
         lg = router_logits(wl.xdt, np.ascontiguousarray(x[bad]), wg, bias)
+        logits[bad] = lg
         bad = bad[min_gap(lg, wl.k) < gap]
-    return x, attempts
+    return (x, attempts, logits) if return_logits else (x, attempts)

@@ -211,3 +211,28 @@ def test_full_size_sampled(name, T):
     sample = np.sort(rng.choice(T, size=min(T, 6), replace=False))
     ref, _, _ = oracle_reference(wl, x, sample)
     assert_output_close(to_f64(out)[sample], ref, wl.xdt, "%s T=%d" % (wl.name, T))
+
+
+def test_kimi_prefill_full_size():
+    """Kimi-K2-shaped INT4 layer + bf16 shared expert at T=8192: routing and permutation of every
+    token bit-exact, layer output of sampled tokens within tolerance."""
+    wl = W.WORKLOADS["kimi"]
+    T = wl.Ts[0]
+    say("kimi full size: inputs")
+    x, _, lg = oracle.rank_gap_inputs(wl, T, return_logits=True)
+    ids_ref, w_ref = oracle.topk_gates(lg, wl.k)
+    say("kimi full size: building the device bank")
+    layer = build_layer(wl, T)
+    say("kimi full size: forward")
+    out = layer.forward(to_device_act(x, wl.xdt))
+    torch.cuda.synchronize()
+    assert np.array_equal(layer.topk_ids.cpu().numpy(), ids_ref)
+    np.testing.assert_allclose(layer.topk_w.cpu().numpy(), w_ref, rtol=GATE_RTOL, atol=GATE_ATOL)
+    c, o, p, i = oracle.permute(ids_ref, wl.E)
+    assert np.array_equal(layer.counts.cpu().numpy(), c)
+    assert np.array_equal(layer.perm_src.cpu().numpy(), p)
+    assert np.array_equal(layer.inv_perm.cpu().numpy(), i)
+    sample = np.array([0, 1, 777, 4095, 4096, 6000, 8190, 8191])
+    say("kimi full size: oracle on", len(sample), "tokens")
+    ref, _, _ = oracle_reference(wl, x, sample)
+    assert_output_close(to_f64(out)[sample], ref, "bf16", "kimi T=8192")
