@@ -21,122 +21,10 @@
 // host never reads the routing back.
 #include <math.h>
 
-#include "common.hpp"
+#include "ffn_common.hpp"
 
 namespace moe {
 namespace {
-
-// ------------------------------------------------------------------ decoders
-
-__device__ __forceinline__ float e8m0_to_f32(unsigned s) {
-  unsigned bits = s == 0 ? 0x00400000u : (s == 255 ? 0x7FC00000u : (s << 23));
-  return __uint_as_float(bits);
-}
-
-// 8 MXFP4 elements (4 bytes, element 2b / 2b+1 in the low / high nibble of byte b) -> bf16
-__device__ __forceinline__ bf16x8 dec_mxfp4(unsigned word, unsigned scale_byte) {
-  float s = e8m0_to_f32(scale_byte);
-  bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, s, 0);
-  bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, s, 1);
-  bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, s, 2);
-  bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, s, 3);
-  return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-}
-
-// 8 INT4 elements (nibble n < 4: element 2n, n >= 4: element 2(n-4)+1, stored as q + 8) -> fp16 q*s
-__device__ __forceinline__ f16x8 dec_int4(unsigned v, _Float16 s) {
-  const f16x2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
-  const f16x2 ss = {s, s};
-  f16x2 r[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    unsigned p = ((v >> (4 * j)) & 0x000F000Fu) | 0x64006400u;
-    f16x2 h = __builtin_bit_cast(f16x2, p);
-    r[j] = (h - bias) * ss;
-  }
-  return f16x8{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
-}
-
-template <int FMT>
-struct Op;  // MFMA operand type per weight format
-template <>
-struct Op<MOE_W_BF16> {
-  typedef bf16x8 T;
-};
-template <>
-struct Op<MOE_W_MXFP4> {
-  typedef bf16x8 T;
-};
-template <>
-struct Op<MOE_W_INT4G32> {
-  typedef f16x8 T;
-};
-
-__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mfma(f16x8 a, f16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-
-// ------------------------------------------------------------------ row tiles
-
-// Row tile `slot` of the grouped rows: experts in id order, each cut into ceil(n_e / mr) tiles.
-// Executed by wave 0; result in shared memory.  Returns false (all threads) when the slot is
-// past the last tile.
-struct RowTile {
-  int e, p0, rows;  // expert, first grouped row, rows in this tile (<= mr)
-};
-
-__device__ bool find_row_tile(const int32_t* __restrict__ offsets, int E, int mr, int slot, RowTile* sh) {
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    const int per = (E + 63) / 64;
-    const int e_begin = lane * per, e_end = min(E, e_begin + per);
-    int local = 0;
-    for (int e = e_begin; e < e_end; ++e) {
-      int c = offsets[e + 1] - offsets[e];
-      local += (c + mr - 1) / mr;
-    }
-    int incl = local;
-    for (int off = 1; off < 64; off <<= 1) {
-      int o = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += o;
-    }
-    int excl = incl - local;
-    bool mine = slot >= excl && slot < incl;
-    if (lane == 63 && slot >= incl) sh->e = -1;
-    if (mine) {
-      int acc = excl;
-      for (int e = e_begin; e < e_end; ++e) {
-        int o0 = offsets[e], c = offsets[e + 1] - o0;
-        int nt = (c + mr - 1) / mr;
-        if (slot < acc + nt) {
-          int t = slot - acc;
-          sh->e = e;
-          sh->p0 = o0 + t * mr;
-          sh->rows = min(mr, c - t * mr);
-          break;
-        }
-        acc += nt;
-      }
-    }
-  }
-  __syncthreads();
-  return sh->e >= 0;
-}
-
-struct FfnArgs {
-  const char* packages;
-  size_t pkg_stride;
-  const int32_t* slot_of_expert;
-  const int32_t* offsets;
-  const int32_t* perm_src;
-  const unsigned short* a;  // GU: activations [T][H] (operand type); down: h [T*k][I]
-  void* out;                // GU: h [T*k][I] (operand type); down: y_perm [T*k][H] fp32
-  int H, I, E, k;
-  size_t region_codes, region_scales;  // byte offsets of this matrix's codes / scales in a package
-};
 
 // ------------------------------------------------------------------ streaming kernel
 
@@ -506,7 +394,7 @@ int pick_mt(int T, int k, int E) {
   return 1.5 * avg > 16.0 ? 2 : 1;
 }
 
-inline void trace(int i, hipStream_t s) {
+void trace(int i, hipStream_t s) {
   void* const* ev = trace_events();
   if (ev && ev[i]) (void)hipEventRecord((hipEvent_t)ev[i], s);
 }
@@ -557,7 +445,6 @@ size_t ffn_workspace(const moe_experts* w, int T, int k, int mode) {
 
 int launch_ffn(const moe_experts* w, const void* x, int xdt, int T, int k, const int32_t* offsets,
                const int32_t* perm_src, float* y_perm, int mode, void* ws, size_t ws_bytes, hipStream_t s) {
-  (void)mode;
   if (T == 0) return MOE_OK;
   const int H = w->H, I = w->I, E = w->E;
   WsLayout L = ws_layout(w, T, k, xdt);
@@ -607,6 +494,10 @@ int launch_ffn(const moe_experts* w, const void* x, int xdt, int T, int k, const
       hipLaunchKernelGGL(cast_act_kernel<false>, dim3(blocks), dim3(256), 0, s, x, xdt, ne, xc);
     a = xc;
   }
+  // variant: weight streaming (decode) unless the average expert has >= 64 rows (or PREFILL is asked)
+  // (the tile kernel addresses activation rows with 32-bit element offsets)
+  const bool tile_ok = (double)((size_t)T > n ? T : n) * (H > I ? H : I) < 2147483648.0;
+  const bool tile = tile_ok && (mode == MOE_FFN_PREFILL || (mode == MOE_FFN_AUTO && (double)n >= 64.0 * E));
   const int mt = pick_mt(T, k, E);
   const int mr = 16 * mt;
   const size_t nz = n < (size_t)E ? n : (size_t)E;
@@ -619,6 +510,13 @@ int launch_ffn(const moe_experts* w, const void* x, int xdt, int T, int k, const
   dn.out = y_perm;
   dn.region_codes = g.d_codes;
   dn.region_scales = g.d_scales;
+  if (tile) {
+    int rc = launch_ffn_tile(w->fmt, gu, dn, H, I, (int)n, E, s, trace);
+    if (rc != MOE_OK) return rc;
+    trace(2, s);
+    MOE_CHECK_LAUNCH("moe_expert_ffn prefill launch");
+    return MOE_OK;
+  }
   switch (w->fmt) {
     case MOE_W_BF16: launch_stream<MOE_W_BF16>(mt, gu, dn, H, I, S, s); break;
     case MOE_W_MXFP4: launch_stream<MOE_W_MXFP4>(mt, gu, dn, H, I, S, s); break;

@@ -1,0 +1,320 @@
+// Prefill variant of the grouped SwiGLU expert FFN: output-stationary MFMA tiles.
+//
+// When many tokens share an expert, one read of its weights serves many rows and the
+// contraction becomes dense ("Understanding MoE Inference Costs on Galactus", section "Prompt
+// processing is a different phase"), so the roofline is MFMA throughput rather than HBM.
+//
+// A workgroup (8 waves as 2 x 4) computes a 192-row x 256-column tile of one expert:
+//  - activation rows (gathered through perm_src for gate/up) are staged through a double
+//    buffer in LDS, one 128-wide (4-bit) or 64-wide (bf16) K block at a time, and read back as
+//    MFMA A operands (row stride padded by 16 bytes against bank conflicts);
+//  - each wave owns 96 rows x 4 strips of 16 columns; its weight fragments come straight from
+//    the package (16 bytes per lane are one MFMA B operand) and are decoded in registers
+//    (MXFP4 -> bf16, INT4 -> fp16, both exact), one K block ahead of their use;
+//  - v_mfma_f32_16x16x32_{bf16,f16}, fp32 accumulation, 24 accumulator tiles per wave;
+//  - gate/up epilogue: SiLU(g) * u on the lane's own (gate, up) pair, rounded once to h;
+//    down epilogue: fp32 y_perm.
+// Work order is XCD-aware: consecutive work items (all column blocks of a row tile, then the
+// next row tile of the same expert) go to the same XCD, so one L2 holds the tile's activations
+// and the expert's weights while they are reused.
+#include "ffn_common.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kTW = 8;       // waves per workgroup: 2 (rows) x 4 (columns)
+constexpr int kTM = 192;     // rows per workgroup tile
+constexpr int kTN = 256;     // columns per workgroup tile
+constexpr int kWMT = 6;      // 16-row MFMA tiles per wave (96 rows)
+constexpr int kWNS = 4;      // 16-column strips per wave
+constexpr int kXCD = 8;      // XCDs of an MI355X; workgroup i is dispatched to XCD i % 8
+
+template <int FMT>
+struct TileCfg {
+  static constexpr int BK = FMT == MOE_W_BF16 ? 64 : 128;   // K per block
+  static constexpr size_t LDS = (size_t)2 * kTM * BK * 2;    // bytes of the A double buffer
+};
+
+template <int FMT, bool GU>
+__global__ __launch_bounds__(kTW * 64, 1) void ffn_tile_kernel(FfnArgs args) {
+  typedef typename Op<FMT>::T OpT;
+  constexpr int BK = TileCfg<FMT>::BK;
+  constexpr int KS = BK / 32;                     // k-steps per block
+  constexpr bool Q4 = FMT != MOE_W_BF16;
+  constexpr int SB = FMT == MOE_W_MXFP4 ? 1 : 2;  // scale bytes
+  constexpr int CPR = BK / 8;                     // 16-byte chunks per staged row
+  constexpr int RPI = 64 / CPR;                   // rows per wave-wide direct-to-LDS load
+  constexpr int IPW = kTM / (kTW * RPI);          // such loads per wave per K block
+  // LDS: [2][kTM rows][CPR chunks of 16 B]; chunk c of row r sits in slot c ^ (r % CPR)
+  extern __shared__ __align__(16) unsigned short lds_a[];
+  __shared__ RowTile tile;
+  __shared__ int sh_total;
+
+  const int K = GU ? args.H : args.I;
+  const int N = GU ? 2 * args.I : args.H;  // columns of this matrix (GU: interleaved gate/up rows)
+  const int n_strips = N / 16;
+  const int ncol = (N + kTN - 1) / kTN;
+  const int nks = K / 32;
+  const int nkb = (K + BK - 1) / BK;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / 4, wn = wave % 4;
+
+  // ---- row tiles of all experts (wave 0), XCD-aware work item, this workgroup's tile
+  int excl = 0, incl = 0, e_begin = 0, e_end = 0;
+  if (tid < 64) {
+    const int per = (args.E + 63) / 64;
+    e_begin = lane * per;
+    e_end = min(args.E, e_begin + per);
+    int local = 0;
+    for (int e = e_begin; e < e_end; ++e) local += (args.offsets[e + 1] - args.offsets[e] + kTM - 1) / kTM;
+    incl = local;
+    for (int off = 1; off < 64; off <<= 1) {
+      int o = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += o;
+    }
+    excl = incl - local;
+    if (lane == 63) sh_total = incl;
+  }
+  __syncthreads();
+  const int total_work = sh_total * ncol;
+  const int per_xcd = (total_work + kXCD - 1) / kXCD;
+  const int w = (int)(blockIdx.x % kXCD) * per_xcd + (int)(blockIdx.x / kXCD);
+  if (w >= total_work || (int)(blockIdx.x / kXCD) >= per_xcd) return;
+  const int slot = w / ncol, col = w % ncol;
+  if (tid < 64 && slot >= excl && slot < incl) {
+    int acc_t = excl;
+    for (int e = e_begin; e < e_end; ++e) {
+      const int o0 = args.offsets[e], c = args.offsets[e + 1] - o0;
+      const int nt = (c + kTM - 1) / kTM;
+      if (slot < acc_t + nt) {
+        const int t = slot - acc_t;
+        tile.e = e;
+        tile.p0 = o0 + t * kTM;
+        tile.rows = min(kTM, c - t * kTM);
+        break;
+      }
+      acc_t += nt;
+    }
+  }
+  __syncthreads();
+  const int e = tile.e, p0 = tile.p0, rows = tile.rows;
+  const int eslot = args.slot_of_expert ? args.slot_of_expert[e] : e;
+  const char* pkg = args.packages + (size_t)eslot * args.pkg_stride;
+
+  // ---- this wave's strips (clamped into range; results of strips past the end are dropped)
+  const char* cbase[kWNS];
+  const char* sbase[kWNS];
+#pragma unroll
+  for (int j = 0; j < kWNS; ++j) {
+    const int s = min(col * 16 + wn * kWNS + j, n_strips - 1);
+    cbase[j] = pkg + args.region_codes + (size_t)s * (Q4 ? 8 : 32) * K;
+    sbase[j] = pkg + args.region_scales + (size_t)s * 16 * nks * SB;
+  }
+
+  // ---- activation staging: direct global -> LDS loads (16 bytes per lane, lane-linear in LDS).
+  // Load i of this wave fills tile rows wave*IPW*RPI + i*RPI + [0, RPI); lane l writes slot l % CPR of
+  // row lane / CPR, so it fetches chunk (l % CPR) ^ (row % CPR) of that row.  Rows past the tile's
+  // end repeat a valid row (their results are dropped); chunks past K repeat the last chunk
+  // (their weights are zero).
+  unsigned aoff[IPW];  // element offset of the lane's source row in args.a
+  unsigned achunk[IPW];
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    const int r = wave * IPW * RPI + i * RPI + lane / CPR;
+    const int rr = r < rows ? r : 0;
+    const int row = GU ? args.perm_src[p0 + rr] / args.k : p0 + rr;
+    aoff[i] = (unsigned)row * (unsigned)K;
+    achunk[i] = (unsigned)((lane % CPR) ^ (r % CPR));
+  }
+  auto load_a = [&](int kb, int buf) {
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const unsigned c = min((unsigned)(kb * CPR) + achunk[i], (unsigned)(K / 8 - 1));
+      const unsigned short* g = args.a + aoff[i] + c * 8;
+      unsigned short* l = lds_a + ((size_t)buf * kTM + wave * IPW * RPI + i * RPI) * BK;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                       (__attribute__((address_space(3))) void*)l, 16, 0, 0);
+    }
+  };
+
+  // ---- weight fragments of one K block for this wave's strips
+  struct BReg {
+    u32x4 v[kWNS][Q4 ? 1 : KS];
+    unsigned sc[kWNS][Q4 ? (SB == 2 ? 2 : 1) : 1];
+  };
+  auto load_b = [&](BReg& B, int kb) {
+    if constexpr (!Q4) {
+#pragma unroll
+      for (int j = 0; j < kWNS; ++j)
+#pragma unroll
+        for (int q = 0; q < KS; ++q) {
+          const int ks = kb * KS + q;
+          u32x4 v = u32x4{0, 0, 0, 0};
+          if (ks < nks) v = *(const u32x4*)(cbase[j] + (size_t)ks * 1024 + lane * 16);
+          B.v[j][q] = v;
+        }
+    } else {
+      const int ns = min(4, nks - 4 * kb);
+      if (ns == 4) {
+#pragma unroll
+        for (int j = 0; j < kWNS; ++j) {
+          B.v[j][0] = *(const u32x4*)(cbase[j] + (size_t)kb * 1024 + lane * 16);
+          const char* sp = sbase[j] + ((size_t)kb * 64 + (lane & 15) * 4) * SB;
+          if constexpr (SB == 1) {
+            B.sc[j][0] = *(const unsigned*)sp;
+          } else {
+            const uint2 v = *(const uint2*)sp;
+            B.sc[j][0] = v.x, B.sc[j][SB - 1] = v.y;
+          }
+        }
+      } else {  // partial last chunk: zero codes, zero scales past its end
+#pragma unroll
+        for (int j = 0; j < kWNS; ++j) {
+          const char* cb = cbase[j] + (size_t)kb * 1024 + (size_t)lane * 4 * ns;
+          const char* sp = sbase[j] + ((size_t)kb * 64 + (lane & 15) * ns) * SB;
+          unsigned c[4] = {0, 0, 0, 0}, s4[4] = {0, 0, 0, 0};
+          for (int q = 0; q < ns; ++q) {
+            c[q] = *(const unsigned*)(cb + 4 * q);
+            s4[q] = SB == 1 ? (unsigned)*(const unsigned char*)(sp + q) : (unsigned)*(const unsigned short*)(sp + 2 * q);
+          }
+          B.v[j][0] = u32x4{c[0], c[1], c[2], c[3]};
+          if constexpr (SB == 1) {
+            B.sc[j][0] = s4[0] | (s4[1] << 8) | (s4[2] << 16) | (s4[3] << 24);
+          } else {
+            B.sc[j][0] = s4[0] | (s4[1] << 16);
+            B.sc[j][SB - 1] = s4[2] | (s4[3] << 16);
+          }
+        }
+      }
+    }
+  };
+
+  f32x4 acc[kWMT][kWNS];
+#pragma unroll
+  for (int mt = 0; mt < kWMT; ++mt)
+#pragma unroll
+    for (int j = 0; j < kWNS; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const BReg& B, int buf) {
+    // A fragment of M tile mt, k-step q: row wm*96 + mt*16 + lane%16, chunk 4q + lane/16
+    const unsigned short* abase = lds_a + ((size_t)buf * kTM + wm * (kWMT * 16) + (lane & 15)) * BK;
+#pragma unroll
+    for (int q = 0; q < KS; ++q) {
+      const int slot = (4 * q + (lane >> 4)) ^ (lane & (CPR - 1));
+      OpT a[kWMT];
+#pragma unroll
+      for (int mt = 0; mt < kWMT; ++mt) a[mt] = *(const OpT*)(abase + mt * 16 * BK + slot * 8);
+#pragma unroll
+      for (int j = 0; j < kWNS; ++j) {
+        OpT b;
+        if constexpr (!Q4) {
+          b = __builtin_bit_cast(OpT, B.v[j][q]);
+        } else if constexpr (FMT == MOE_W_MXFP4) {
+          b = dec_mxfp4(B.v[j][0][q], (B.sc[j][0] >> (8 * q)) & 255);
+        } else {
+          const unsigned sw = B.sc[j][q >> 1];
+          b = dec_int4(B.v[j][0][q], __builtin_bit_cast(_Float16, (unsigned short)(sw >> (16 * (q & 1)))));
+        }
+#pragma unroll
+        for (int mt = 0; mt < kWMT; ++mt) acc[mt][j] = mfma(a[mt], b, acc[mt][j]);
+      }
+    }
+  };
+
+  // ---- K loop: stage block kb+1 (activations to LDS, weights to registers) while block kb runs
+  BReg bc, bn;
+  load_a(0, 0);
+  load_b(bc, 0);
+  __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0): this wave's direct-to-LDS loads have landed
+  __syncthreads();
+  for (int kb = 0; kb < nkb; ++kb) {
+    const bool more = kb + 1 < nkb;
+    if (more) {
+      load_a(kb + 1, (kb + 1) & 1);  // the buffer every wave finished reading before the last barrier
+      load_b(bn, kb + 1);
+    }
+    compute(bc, kb & 1);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    bc = bn;
+  }
+
+  // ---- epilogue
+#pragma unroll
+  for (int mt = 0; mt < kWMT; ++mt) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = wm * (kWMT * 16) + mt * 16 + (lane >> 4) * 4 + r;
+      if (row >= rows) continue;
+      const size_t pr = (size_t)(p0 + row);
+      if constexpr (GU) {
+#pragma unroll
+        for (int j = 0; j < kWNS; j += 2) {
+          const int gs = col * 16 + wn * kWNS + j;  // gate strip 2u, up strip 2u + 1
+          if (gs + 1 >= n_strips) continue;
+          const int f = (gs >> 1) * 16 + (lane & 15);
+          const float hv = silu(acc[mt][j][r]) * acc[mt][j + 1][r];
+          unsigned short hb;
+          if constexpr (FMT == MOE_W_INT4G32)
+            hb = __builtin_bit_cast(unsigned short, (_Float16)hv);
+          else
+            hb = f32_to_bf16_rne(hv);
+          ((unsigned short*)args.out)[pr * args.I + f] = hb;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < kWNS; ++j) {
+          const int s = col * 16 + wn * kWNS + j;
+          if (s >= n_strips) continue;
+          ((float*)args.out)[pr * args.H + s * 16 + (lane & 15)] = acc[mt][j][r];
+        }
+      }
+    }
+  }
+}
+
+template <int FMT, bool GU>
+int launch_one(const FfnArgs& a, int S, int N, hipStream_t s) {
+  static bool attr_set = false;
+  const size_t lds = TileCfg<FMT>::LDS;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)ffn_tile_kernel<FMT, GU>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return hip_fail(e, "moe_expert_ffn: LDS attribute of the prefill kernel");
+    attr_set = true;
+  }
+  const int ncol = (N + kTN - 1) / kTN;
+  const long long total = (long long)S * ncol;
+  const long long per = (total + kXCD - 1) / kXCD;
+  hipLaunchKernelGGL((ffn_tile_kernel<FMT, GU>), dim3((unsigned)(per * kXCD)), dim3(kTW * 64), lds, s, a);
+  return MOE_OK;
+}
+
+}  // namespace
+
+// Row-tile upper bound for n grouped rows over E experts (at most min(E, n) experts are non-empty).
+int tile_rows() { return kTM; }
+
+int launch_ffn_tile(int fmt, const FfnArgs& gu, const FfnArgs& dn, int H, int I, int n, int E, hipStream_t s,
+                    void (*mark)(int, hipStream_t)) {
+  const long long nz = n < E ? n : E;
+  const int S = (int)(((long long)n + nz * (kTM - 1)) / kTM);
+  int rc = MOE_OK;
+  switch (fmt) {
+    case MOE_W_BF16: rc = launch_one<MOE_W_BF16, true>(gu, S, 2 * I, s); break;
+    case MOE_W_MXFP4: rc = launch_one<MOE_W_MXFP4, true>(gu, S, 2 * I, s); break;
+    case MOE_W_INT4G32: rc = launch_one<MOE_W_INT4G32, true>(gu, S, 2 * I, s); break;
+    default: return fail(MOE_ERR_UNSUPPORTED, "moe_expert_ffn: no prefill kernel for format %d", fmt);
+  }
+  if (rc != MOE_OK) return rc;
+  mark(1, s);
+  switch (fmt) {
+    case MOE_W_BF16: rc = launch_one<MOE_W_BF16, false>(dn, S, H, s); break;
+    case MOE_W_MXFP4: rc = launch_one<MOE_W_MXFP4, false>(dn, S, H, s); break;
+    default: rc = launch_one<MOE_W_INT4G32, false>(dn, S, H, s); break;
+  }
+  return rc;
+}
+
+}  // namespace moe

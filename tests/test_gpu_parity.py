@@ -134,12 +134,15 @@ SMALL = [("f32", "f32"), ("f32", "bf16"), ("bf16", "bf16"), ("mxfp4", "bf16"), (
 
 @pytest.mark.parametrize("fmt,xdt", SMALL)
 @pytest.mark.parametrize("T", [1, 3, 40, 130])
-def test_layer_small(fmt, xdt, T):
+@pytest.mark.parametrize("mode", ["auto", "decode", "prefill"])
+def test_layer_small(fmt, xdt, T, mode):
+    if fmt == "f32" and mode != "auto":
+        pytest.skip("fp32 experts have one (VALU) variant")
     wl = small_variant(fmt, xdt)
-    say("layer small", wl.name, "T", T)
+    say("layer small", wl.name, "T", T, "mode", mode)
     x, _ = oracle.rank_gap_inputs(wl, T)
     layer = build_layer(wl, T)
-    out = layer.forward(to_device_act(x, xdt))
+    out = layer.forward(to_device_act(x, xdt), mode=mode)
     torch.cuda.synchronize()
     ref, ids_ref, w_ref = oracle_reference(wl, x, np.arange(T))
     assert np.array_equal(layer.topk_ids[:T].cpu().numpy(), ids_ref)
@@ -186,17 +189,18 @@ def test_shared_expert_small():
 
 # ------------------------------------------------------------------ full-size configurations (sampled tokens)
 
-FULL = [("mixtral", 1), ("mixtral", 8), ("mixtral", 32), ("mixtral", 64), ("gptoss", 1), ("gptoss", 64),
-        ("gptoss", 512)]
+FULL = [("mixtral", 1, "auto"), ("mixtral", 8, "auto"), ("mixtral", 32, "auto"), ("mixtral", 64, "auto"),
+        ("mixtral", 64, "prefill"), ("gptoss", 1, "auto"), ("gptoss", 64, "auto"), ("gptoss", 512, "auto"),
+        ("gptoss", 512, "prefill")]
 
 
-@pytest.mark.parametrize("name,T", FULL)
-def test_full_size_sampled(name, T):
+@pytest.mark.parametrize("name,T,mode", FULL)
+def test_full_size_sampled(name, T, mode):
     wl = W.WORKLOADS[name]
-    say("full size", wl.name, "T", T)
+    say("full size", wl.name, "T", T, "mode", mode)
     x, _ = oracle.rank_gap_inputs(wl, T)
     layer = build_layer(wl, T)
-    out = layer.forward(to_device_act(x, wl.xdt))
+    out = layer.forward(to_device_act(x, wl.xdt), mode=mode)
     torch.cuda.synchronize()
     ids_all = layer.topk_ids[:T].cpu().numpy()
     # routing and permutation of every token
@@ -210,7 +214,7 @@ def test_full_size_sampled(name, T):
     rng = np.random.default_rng(T)
     sample = np.sort(rng.choice(T, size=min(T, 6), replace=False))
     ref, _, _ = oracle_reference(wl, x, sample)
-    assert_output_close(to_f64(out)[sample], ref, wl.xdt, "%s T=%d" % (wl.name, T))
+    assert_output_close(to_f64(out)[sample], ref, wl.xdt, "%s T=%d %s" % (wl.name, T, mode))
 
 
 def test_kimi_prefill_full_size():
