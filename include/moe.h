@@ -147,6 +147,9 @@ typedef struct {
   const void* packages;          /* device: package of logical expert e at packages + slot(e) * pkg_stride */
   size_t pkg_stride;             /* bytes between packages, >= moe_package_bytes, multiple of 256 */
   const int32_t* slot_of_expert; /* device [E] stable logical -> physical slot, or NULL for slot(e) = e */
+  int n_slots;                   /* packages available at `packages` when slot_of_expert is set (>= 1);
+                                    an expert whose slot is outside [0, n_slots) is skipped (its rows of
+                                    y_perm are not written); ignored when slot_of_expert is NULL */
 } moe_experts;
 
 /* Workspace bytes moe_expert_ffn needs for these experts, T tokens and top-k. */

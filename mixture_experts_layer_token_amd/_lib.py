@@ -18,7 +18,7 @@ c_int, c_size_t, vp, i32p, f32p = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
 
 class MoeExperts(ctypes.Structure):
     _fields_ = [("H", c_int), ("I", c_int), ("E", c_int), ("fmt", c_int), ("packages", vp),
-                ("pkg_stride", c_size_t), ("slot_of_expert", vp)]
+                ("pkg_stride", c_size_t), ("slot_of_expert", vp), ("n_slots", c_int)]
 
 
 class MoeCacheDesc(ctypes.Structure):

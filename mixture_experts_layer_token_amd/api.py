@@ -84,12 +84,17 @@ def moe_dequant_expert(package, H, I, fmt, out, stream=None):
     check(lib().moe_dequant_expert(_dp(package), H, I, FMT[fmt], _dp(out), _stream(stream)))
 
 
-def experts_desc(H, I, E, fmt, packages, pkg_stride, slot_of_expert=None) -> MoeExperts:
+def experts_desc(H, I, E, fmt, packages, pkg_stride, slot_of_expert=None, n_slots=None) -> MoeExperts:
+    """`packages`: device tensor of packages, `pkg_stride` bytes apart (its leading dimension is the
+    number of slots when a slot table is given)."""
     d = MoeExperts()
     d.H, d.I, d.E, d.fmt = H, I, E, FMT[fmt]
     d.packages = packages.data_ptr() if packages is not None else None
     d.pkg_stride = pkg_stride
     d.slot_of_expert = slot_of_expert.data_ptr() if slot_of_expert is not None else None
+    if n_slots is None:
+        n_slots = packages.numel() * packages.element_size() // pkg_stride if packages is not None else E
+    d.n_slots = n_slots
     return d
 
 

@@ -101,6 +101,8 @@ extern "C" int moe_expert_ffn(const moe_experts* w, const void* x, int xdt, int 
     return fail(MOE_ERR_INVALID, "moe_expert_ffn: pkg_stride %zu (need >= %zu, multiple of 256)", w->pkg_stride, need);
   if (T > 0 && (!w->packages || !x || !offsets || !perm_src || !y_perm))
     return fail(MOE_ERR_INVALID, "moe_expert_ffn: null pointer");
+  if (w->slot_of_expert && w->n_slots < 1)
+    return fail(MOE_ERR_INVALID, "moe_expert_ffn: n_slots=%d with a slot table", w->n_slots);
   return launch_ffn(w, x, xdt, T, k, offsets, perm_src, y_perm, mode, ws, ws_bytes, (hipStream_t)stream);
 }
 

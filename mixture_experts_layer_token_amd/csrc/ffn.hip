@@ -64,6 +64,7 @@ __global__ __launch_bounds__(NW * 64, (FMT == MOE_W_BF16 ? 3 : 2) * 4 / NW) void
   const int nks = K / 32;
 
   const int slot = args.slot_of_expert ? args.slot_of_expert[e] : e;
+  if ((unsigned)slot >= (unsigned)args.n_slots) return;  // workgroup-uniform: not resident, skip
   const char* pkg = args.packages + (size_t)slot * args.pkg_stride;
 
   // strip bases (workgroup-uniform); units past the end repeat the last unit, results dropped
@@ -267,6 +268,7 @@ __global__ __launch_bounds__(256) void ffn_f32_kernel(FfnArgs args) {
   const int e = tile.e, p0 = tile.p0, rows = tile.rows;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int slot = args.slot_of_expert ? args.slot_of_expert[e] : e;
+  if ((unsigned)slot >= (unsigned)args.n_slots) return;  // workgroup-uniform: not resident, skip
   const float* pkg = (const float*)(args.packages + (size_t)slot * args.pkg_stride);
   const int H = args.H, I = args.I;
   const bool ok = lane < rows;
@@ -458,6 +460,7 @@ int launch_ffn(const moe_experts* w, const void* x, int xdt, int T, int k, const
   gu.packages = (const char*)w->packages;
   gu.pkg_stride = w->pkg_stride;
   gu.slot_of_expert = w->slot_of_expert;
+  gu.n_slots = w->slot_of_expert ? w->n_slots : E;
   gu.offsets = offsets;
   gu.perm_src = perm_src;
   gu.H = H, gu.I = I, gu.E = E, gu.k = k;

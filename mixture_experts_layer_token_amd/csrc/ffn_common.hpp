@@ -112,6 +112,7 @@ struct FfnArgs {
   const char* packages;
   size_t pkg_stride;
   const int32_t* slot_of_expert;
+  int n_slots;  // valid slots are [0, n_slots)
   const int32_t* offsets;
   const int32_t* perm_src;
   const unsigned short* a;  // GU: activations [T][H] (operand type); down: h [T*k][I]

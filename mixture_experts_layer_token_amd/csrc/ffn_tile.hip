@@ -100,6 +100,7 @@ __global__ __launch_bounds__(kTW * 64, 1) void ffn_tile_kernel(FfnArgs args) {
   __syncthreads();
   const int e = tile.e, p0 = tile.p0, rows = tile.rows;
   const int eslot = args.slot_of_expert ? args.slot_of_expert[e] : e;
+  if ((unsigned)eslot >= (unsigned)args.n_slots) return;  // workgroup-uniform: not resident, skip
   const char* pkg = args.packages + (size_t)eslot * args.pkg_stride;
 
   // ---- this wave's strips (clamped into range; results of strips past the end are dropped)

@@ -1,0 +1,164 @@
+"""Decode through an expert bank that lives in page-locked host memory.
+
+Expert weights stay on the host; an HBM pool of `capacity` package slots caches
+the most recently used ones ("What expert offloading actually costs", section
+"Inside expert paging": expert math stays on the GPU, weights stream in on
+demand and are addressed through stable logical slots).  Per layer and step:
+
+  route (compute stream) -> ids to the host -> moe_cache_plan (host LRU) ->
+  moe_cache_fetch (one hipMemcpyAsync per miss + the slot table, copy stream,
+  event) -> the compute stream waits for the event -> permute -> grouped FFN
+  reading packages through the slot table -> combine.
+
+Layers run strictly in order.  A slot evicted by a plan is never in use: the
+host waits for the router of the layer being planned, and every earlier FFN
+precedes that router on the compute stream.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import torch
+
+from . import api
+from .layer import MoeLayer, to_device_act
+
+
+class PinnedBuffer:
+    """Page-locked host memory from hipHostMalloc, viewed as a numpy uint8 array."""
+
+    def __init__(self, nbytes: int):
+        self._hip = ctypes.CDLL("libamdhip64.so")
+        self._hip.hipHostMalloc.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_size_t, ctypes.c_uint]
+        self._hip.hipHostFree.argtypes = [ctypes.c_void_p]
+        p = ctypes.c_void_p()
+        rc = self._hip.hipHostMalloc(ctypes.byref(p), ctypes.c_size_t(nbytes), 0)
+        if rc != 0 or not p.value:
+            raise MemoryError("hipHostMalloc(%d) failed with %d" % (nbytes, rc))
+        self.ptr, self.nbytes = p.value, nbytes
+        self.array = np.ctypeslib.as_array((ctypes.c_uint8 * nbytes).from_address(self.ptr))
+
+    def data_ptr(self) -> int:
+        return self.ptr
+
+    def close(self):
+        if self.ptr:
+            self.array = None
+            self._hip.hipHostFree(ctypes.c_void_p(self.ptr))
+            self.ptr = 0
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class OffloadedModel:
+    """L MoE layers whose experts live in a pinned host bank, cached in an HBM slot pool."""
+
+    def __init__(self, wl, max_T: int, capacity: int | None = None, device="cuda", fill=True):
+        from synth import workloads as W
+
+        self.wl = wl
+        self.L, self.E, self.H, self.I, self.k = wl.layers, wl.E, wl.H, wl.I, wl.k
+        self.pkg_bytes = api.moe_package_bytes(wl.H, wl.I, wl.wfmt)
+        self.stride = (self.pkg_bytes + 255) // 256 * 256
+        self.capacity = capacity or int(wl.cache_frac * wl.layers * wl.E)
+        self.bank = PinnedBuffer(self.L * self.E * self.pkg_bytes)
+        if fill:
+            for l in range(self.L):
+                self.fill(l, list(range(self.E)))
+        self.pool = torch.empty((self.capacity, self.stride), dtype=torch.uint8, device=device)
+        self.cache = api.ExpertCache(self.bank, self.pkg_bytes, self.L, self.E, self.pool, self.stride,
+                                     self.capacity)
+        self.slot_tables = [torch.full((self.E,), -1, dtype=torch.int32, device=device) for _ in range(self.L)]
+        self.wg = [to_device_act(W.router_weights(wl, l), wl.xdt, device) for l in range(self.L)]
+        self.bias_cache = {}
+        self.layers = []
+        for l in range(self.L):
+            lay = MoeLayer(wl.H, wl.I, wl.E, wl.k, wl.wfmt, wl.xdt, self.wg[l], None, self.pool, self.stride,
+                           max_T=max_T, slot_of_expert=self.slot_tables[l], device=device)
+            self.layers.append(lay)
+        self.copy_stream = torch.cuda.Stream(device=device)
+        self.ids_host = torch.empty((max_T, wl.k), dtype=torch.int32, pin_memory=True)
+        self.done = torch.cuda.Event()
+        self.done.record(self.copy_stream)  # creates the HIP event the library records into
+        self.routed = torch.cuda.Event()
+        self.copy_t0 = torch.cuda.Event(enable_timing=True)
+        self.copy_t1 = torch.cuda.Event(enable_timing=True)
+        self.copy_ms = 0.0
+        self.plans = []
+        self.groups = []
+        self.filled = {}
+
+    def reset_cache(self):
+        """Empty the HBM cache (a new planner) and the run records."""
+        self.cache.close()
+        self.cache = api.ExpertCache(self.bank, self.pkg_bytes, self.L, self.E, self.pool, self.stride,
+                                     self.capacity)
+        for t in self.slot_tables:
+            t.fill_(-1)
+        self.plans, self.groups, self.copy_ms = [], [], 0.0
+
+    def fill(self, l: int, experts):
+        """Generate and pack experts of layer l into the host bank."""
+        from .layer import pack_bank
+
+        experts = sorted(experts)
+        for i in range(0, len(experts), 64):
+            ids = experts[i:i + 64]
+            host = pack_bank(self.wl, l, ids, stride=self.pkg_bytes)
+            for j, e in enumerate(ids):
+                o = (l * self.E + e) * self.pkg_bytes
+                self.bank.array[o:o + self.pkg_bytes] = host[j]
+
+    def package(self, l: int, e: int) -> np.ndarray:
+        o = (l * self.E + e) * self.pkg_bytes
+        return self.bank.array[o:o + self.pkg_bytes]
+
+    def bias(self, l: int, step: int):
+        from synth import workloads as W
+
+        epoch = step // self.wl.rerank_every if self.wl.rerank_every else 0
+        key = (l, epoch)
+        if key not in self.bias_cache:
+            b = W.router_bias(self.wl, l, step)
+            self.bias_cache[key] = torch.from_numpy(b).cuda() if b is not None else None
+        return self.bias_cache[key]
+
+    def layer_forward(self, l: int, step: int, x: torch.Tensor, out: torch.Tensor | None = None,
+                      time_copies: bool = False) -> torch.Tensor:
+        lay = self.layers[l]
+        T, k = x.shape[0], self.k
+        if out is None:
+            out = torch.empty((T, self.H), dtype=x.dtype, device=x.device)
+        ids, w = lay.topk_ids[:T], lay.topk_w[:T]
+        api.moe_route(x, self.wg[l], self.bias(l, step), k, ids, w)
+        host_ids = self.ids_host[:T]
+        host_ids.copy_(ids, non_blocking=True)
+        self.routed.record()
+        self.routed.synchronize()  # the router's choice, on the host
+        hid = host_ids.numpy()
+        plan = self.cache.plan(l, hid)
+        self.plans.append((step, l, plan.n_ids, plan.n_hits, plan.n_misses))
+        self.groups.append(set((l * self.E + hid.ravel()).tolist()))
+        if time_copies:
+            self.copy_t0.record(self.copy_stream)
+        self.cache.fetch(plan, self.slot_tables[l], self.copy_stream, self.done)
+        if time_copies:
+            self.copy_t1.record(self.copy_stream)
+        torch.cuda.current_stream().wait_event(self.done)
+        api.moe_permute(ids, self.E, lay.counts, lay.offsets, lay.perm_src[:T * k], lay.inv_perm[:T * k], lay.pws)
+        api.moe_expert_ffn(lay.desc, x, k, lay.offsets, lay.perm_src, lay.y_perm, lay.ws)
+        api.moe_combine(lay.y_perm, w, lay.inv_perm, k, None, out)
+        if time_copies:
+            self.copy_t1.synchronize()
+            self.copy_ms += self.copy_t0.elapsed_time(self.copy_t1)
+        self.last_plan = plan
+        return out
+
+    def close(self):
+        self.cache.close()
+        self.bank.close()
