@@ -149,6 +149,20 @@ def cpu_baseline(wl, xs_host, min_seconds: float = 10.0, max_tokens: int | None 
                       % (batches, x.shape[0], tokens, spent)}
 
 
+def profiled_traffic(name: str):
+    """HBM bytes per launch measured by the profiler for a kernel, if its sources are unchanged since."""
+    import hashlib
+
+    p = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(p):
+        return None
+    rec = json.load(open(p))
+    h = hashlib.sha256()
+    for src in rec["sources"]:
+        h.update(open(os.path.join(ROOT, src), "rb").read())
+    return rec if h.hexdigest() == rec["sources_sha256"] else None
+
+
 def run(args):
     import torch
 
@@ -217,6 +231,10 @@ def run(args):
                    if k in ("T", "tokens_per_s", "ms_per_step", "gu_gbps", "down_gbps", "ffn_gbps", "step_gbps",
                             "touched_mean")} for r in results.values()],
     }
+    if args.workload == "mixtral" and args.T == 64:
+        rec = profiled_traffic("ffn_gu_mixtral_bf16_decode_T64_traffic.json")
+        if rec is not None:
+            out["roofline"]["traffic"] = int(rec["gu_traffic_bytes_per_launch"])
     # the pages' decode cost model T = C + S for this step: S = expert bytes / peak HBM bandwidth
     S = streaming_time(head["gu_bytes_per_launch"] + step_bytes(wl, args.T, int(round(head["touched_mean"])))["down"],
                        HBM_PEAK_GBS * 1e9)
@@ -371,6 +389,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="mixtral", choices=["mixtral", "gptoss", "kimi", "glm"])
     ap.add_argument("--offload-steps", type=int, default=256)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="copy 1 GiB device-to-device before measuring (profiler byte-counter calibration)")
     ap.add_argument("--T", type=int, default=None, help="tokens per step (default 64 decode, 8192 prefill)")
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--cpu-tokens", type=int, default=16, help="prefill: oracle token sample")
@@ -388,6 +408,15 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        # a plain device copy of known size, for calibrating the HBM byte counters of a profiler run
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     out = run_offload(args) if args.workload in OFFLOAD else run(args)
     print(json.dumps(out), flush=True)
 
