@@ -81,11 +81,16 @@ const char* moe_last_error(void);
  *   bias      device [E] fp32, or NULL for none
  *   topk_ids  device [T][k] int32 (out);  topk_w device [T][k] fp32 (out)
  *   logits    device [T][E] fp32 (out), or NULL
+ *   ws        device workspace of ws_bytes >= moe_route_workspace(T, H, E, xdt) bytes (may be NULL if 0)
  * Errors: MOE_ERR_INVALID for null x/w_router/topk_ids/topk_w (when T > 0), E out of
- * 1..1024, k out of 1..min(E,16), H <= 0.
+ * 1..1024, k out of 1..min(E,16), H <= 0; MOE_ERR_WORKSPACE if the workspace is too small.
  */
 int moe_route(const void* x, int xdt, int T, int H, const void* w_router, const float* bias, int E, int k,
-              int32_t* topk_ids, float* topk_w, float* logits, void* stream);
+              int32_t* topk_ids, float* topk_w, float* logits, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes moe_route needs (device; 0 when none).  Small batches (bf16, T <= 256) spread the
+ * router over many workgroups and keep partial logits there. */
+size_t moe_route_workspace(int T, int H, int E, int xdt);
 
 /* ------------------------------------------------------------- permutation */
 

@@ -39,7 +39,8 @@ class MoeCacheStats(ctypes.Structure):
 
 SIGNATURES = {
     "moe_last_error": ([], ctypes.c_char_p),
-    "moe_route": ([vp, c_int, c_int, c_int, vp, f32p, c_int, c_int, i32p, f32p, f32p, vp], c_int),
+    "moe_route": ([vp, c_int, c_int, c_int, vp, f32p, c_int, c_int, i32p, f32p, f32p, vp, c_size_t, vp], c_int),
+    "moe_route_workspace": ([c_int, c_int, c_int, c_int], c_size_t),
     "moe_permute_workspace": ([c_int, c_int, c_int], c_size_t),
     "moe_permute": ([i32p, c_int, c_int, c_int, i32p, i32p, i32p, i32p, vp, c_size_t, vp], c_int),
     "moe_package_bytes": ([c_int, c_int, c_int], c_size_t),

@@ -48,11 +48,19 @@ def _dt(t: torch.Tensor) -> int:
     raise TypeError("activations must be float32 or bfloat16, got %s" % t.dtype)
 
 
-def moe_route(x, w_router, bias, k, topk_ids, topk_w, logits=None, stream=None):
+def moe_route_workspace(T, H, E, xdt) -> int:
+    return int(lib().moe_route_workspace(T, H, E, DT[xdt]))
+
+
+def moe_route(x, w_router, bias, k, topk_ids, topk_w, logits=None, ws=None, stream=None):
+    """`ws`: device workspace of at least moe_route_workspace bytes (allocated here if None)."""
     T, H = x.shape
     E = w_router.shape[0]
+    if ws is None:
+        need = moe_route_workspace(T, H, E, "bf16" if x.dtype == torch.bfloat16 else "f32")
+        ws = torch.empty(need, dtype=torch.uint8, device=x.device) if need else None
     check(lib().moe_route(_dp(x), _dt(x), T, H, _dp(w_router), _dp(bias), E, k, _dp(topk_ids), _dp(topk_w),
-                          _dp(logits), _stream(stream)))
+                          _dp(logits), _dp(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def moe_permute_workspace(T, k, E) -> int:

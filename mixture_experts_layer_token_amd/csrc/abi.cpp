@@ -55,14 +55,20 @@ extern "C" int moe_ffn_trace_events(void* const* events) {
   return MOE_OK;
 }
 
+extern "C" size_t moe_route_workspace(int T, int H, int E, int xdt) {
+  if (T < 0 || H <= 0 || E < 1 || E > 1024 || !dtype_valid(xdt)) return 0;
+  return route_workspace(T, H, E, xdt);
+}
+
 extern "C" int moe_route(const void* x, int xdt, int T, int H, const void* w_router, const float* bias, int E, int k,
-                         int32_t* topk_ids, float* topk_w, float* logits, void* stream) {
+                         int32_t* topk_ids, float* topk_w, float* logits, void* ws, size_t ws_bytes, void* stream) {
   if (!dtype_valid(xdt)) return fail(MOE_ERR_INVALID, "moe_route: bad dtype %d", xdt);
   if (T < 0 || H <= 0) return fail(MOE_ERR_INVALID, "moe_route: T=%d H=%d", T, H);
   if (E < 1 || E > 1024) return fail(MOE_ERR_INVALID, "moe_route: E=%d out of 1..1024", E);
   if (k < 1 || k > E || k > 16) return fail(MOE_ERR_INVALID, "moe_route: k=%d out of 1..min(E,16)", k);
   if (T > 0 && (!x || !w_router || !topk_ids || !topk_w)) return fail(MOE_ERR_INVALID, "moe_route: null pointer");
-  return launch_route(x, xdt, T, H, w_router, bias, E, k, topk_ids, topk_w, logits, (hipStream_t)stream);
+  return launch_route(x, xdt, T, H, w_router, bias, E, k, topk_ids, topk_w, logits, ws, ws_bytes,
+                      (hipStream_t)stream);
 }
 
 extern "C" size_t moe_permute_workspace(int T, int k, int E) {

@@ -91,8 +91,9 @@ void* const* trace_events();  // moe_ffn_trace_events setting of this thread (or
 bool dtype_valid(int dt);
 
 // ------------------------------------------------------------ launch helpers (internal)
+size_t route_workspace(int T, int H, int E, int xdt);
 int launch_route(const void* x, int xdt, int T, int H, const void* wg, const float* bias, int E, int k, int32_t* ids,
-                 float* w, float* logits, hipStream_t s);
+                 float* w, float* logits, void* ws, size_t ws_bytes, hipStream_t s);
 int launch_permute(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_t* offsets, int32_t* perm,
                    int32_t* inv, hipStream_t s);
 int launch_combine(const float* y, const float* w, const int32_t* inv, int T, int k, int H, const float* shared,

@@ -53,7 +53,7 @@ __global__ __launch_bounds__(NW * 64, (FMT == MOE_W_BF16 ? 3 : 2) * 4 / NW) void
   __shared__ RowTile tile;
   __shared__ f32x4 red[NW > 1 ? NW * NSTR * 64 : 1];
 
-  if (!find_row_tile(args.offsets, args.E, MR, blockIdx.y, &tile)) return;
+  if (!find_row_tile(args.offsets, args.E, MR, blockIdx.y, &tile, args.min_rows, args.max_rows)) return;
   const int e = tile.e, p0 = tile.p0, rows = tile.rows;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar addressing
@@ -115,22 +115,25 @@ __global__ __launch_bounds__(NW * 64, (FMT == MOE_W_BF16 ? 3 : 2) * 4 / NW) void
         dst[q][mt] = v;
       }
   };
+  // weights are read once per call: non-temporal loads stream them without displacing cached data
   auto load_b = [&](Stage<FMT, NSTR>& S, int st) {
     if constexpr (!Q4) {
 #pragma unroll
-      for (int s = 0; s < NSTR; ++s) S.code[s] = *(const u32x4*)(cbase[s] + (size_t)st * 1024 + lane16);
+      for (int s = 0; s < NSTR; ++s)
+        S.code[s] = __builtin_nontemporal_load((const u32x4*)(cbase[s] + (size_t)st * 1024 + lane16));
     } else {
       const int ns = min(4, nks - 4 * st);
       if (ns == 4) {
 #pragma unroll
         for (int s = 0; s < NSTR; ++s) {
-          S.code[s] = *(const u32x4*)(cbase[s] + (size_t)st * 1024 + lane16);
+          S.code[s] = __builtin_nontemporal_load((const u32x4*)(cbase[s] + (size_t)st * 1024 + lane16));
           const char* sc = sbase[s] + ((size_t)st * 64 + lrow * 4) * SB;
           if constexpr (SB == 1) {
-            S.scale[s][0] = *(const unsigned*)sc;
+            S.scale[s][0] = __builtin_nontemporal_load((const unsigned*)sc);
           } else {
-            const uint2 v = *(const uint2*)sc;
-            S.scale[s][0] = v.x, S.scale[s][SB - 1] = v.y;
+            typedef __attribute__((__vector_size__(2 * sizeof(unsigned)))) unsigned u32x2;
+            const u32x2 v = __builtin_nontemporal_load((const u32x2*)sc);
+            S.scale[s][0] = v[0], S.scale[s][SB - 1] = v[1];
           }
         }
       } else {  // the last, partial chunk: ns k-steps, packed 4 * ns bytes per lane
@@ -411,29 +414,42 @@ struct Cfg {
   static constexpr bool Q4 = FMT != MOE_W_BF16;
   static constexpr int GU_NP = Q4 ? (MT == 1 ? 4 : 2) : 1;
   static constexpr int GU_NW = 4;
-  static constexpr int GU_PF = Q4 ? 2 : 4;
-  static constexpr int D_NP = Q4 ? (MT == 1 ? 8 : 4) : 2;
+  static constexpr int GU_PF = Q4 ? 2 : 8;
+  static constexpr int D_NP = Q4 ? (MT == 1 ? 8 : 4) : 2 * MT;
   static constexpr int D_NW = Q4 ? 4 : 8;
-  static constexpr int D_PF = Q4 ? 2 : 4;
+  static constexpr int D_PF = Q4 ? 2 : 8;
 };
 
 template <int FMT, int MT>
-void launch_stream_mt(const FfnArgs& gu, const FfnArgs& dn, int H, int I, int S, hipStream_t s) {
+void launch_stream_mt(bool gate_up, const FfnArgs& a, int H, int I, int S, hipStream_t s) {
   typedef Cfg<FMT, MT> C;
-  const int gx = (I / 16 + C::GU_NP - 1) / C::GU_NP, dx = (H / 16 + C::D_NP - 1) / C::D_NP;
-  hipLaunchKernelGGL((ffn_stream_kernel<FMT, MT, C::GU_NW, C::GU_NP, C::GU_PF, true>), dim3(gx, S),
-                     dim3(64 * C::GU_NW), 0, s, gu);
-  trace(1, s);
-  hipLaunchKernelGGL((ffn_stream_kernel<FMT, MT, C::D_NW, C::D_NP, C::D_PF, false>), dim3(dx, S), dim3(64 * C::D_NW),
-                     0, s, dn);
+  if (gate_up) {
+    const int gx = (I / 16 + C::GU_NP - 1) / C::GU_NP;
+    hipLaunchKernelGGL((ffn_stream_kernel<FMT, MT, C::GU_NW, C::GU_NP, C::GU_PF, true>), dim3(gx, S),
+                       dim3(64 * C::GU_NW), 0, s, a);
+  } else {
+    const int dx = (H / 16 + C::D_NP - 1) / C::D_NP;
+    hipLaunchKernelGGL((ffn_stream_kernel<FMT, MT, C::D_NW, C::D_NP, C::D_PF, false>), dim3(dx, S),
+                       dim3(64 * C::D_NW), 0, s, a);
+  }
 }
 
 template <int FMT>
-void launch_stream(int mt, const FfnArgs& gu, const FfnArgs& dn, int H, int I, int S, hipStream_t s) {
+void launch_stream(int mt, bool gate_up, const FfnArgs& a, int H, int I, int S, hipStream_t s) {
   switch (mt) {
-    case 1: launch_stream_mt<FMT, 1>(gu, dn, H, I, S, s); break;
-    default: launch_stream_mt<FMT, 2>(gu, dn, H, I, S, s); break;
+    case 1: launch_stream_mt<FMT, 1>(gate_up, a, H, I, S, s); break;
+    default: launch_stream_mt<FMT, 2>(gate_up, a, H, I, S, s); break;
   }
+}
+
+int launch_stream_fmt(int fmt, int mt, bool gate_up, const FfnArgs& a, int H, int I, int S, hipStream_t s) {
+  switch (fmt) {
+    case MOE_W_BF16: launch_stream<MOE_W_BF16>(mt, gate_up, a, H, I, S, s); break;
+    case MOE_W_MXFP4: launch_stream<MOE_W_MXFP4>(mt, gate_up, a, H, I, S, s); break;
+    case MOE_W_INT4G32: launch_stream<MOE_W_INT4G32>(mt, gate_up, a, H, I, S, s); break;
+    default: return fail(MOE_ERR_UNSUPPORTED, "moe_expert_ffn: format %d", fmt);
+  }
+  return MOE_OK;
 }
 
 }  // namespace
@@ -497,10 +513,24 @@ int launch_ffn(const moe_experts* w, const void* x, int xdt, int T, int k, const
       hipLaunchKernelGGL(cast_act_kernel<false>, dim3(blocks), dim3(256), 0, s, x, xdt, ne, xc);
     a = xc;
   }
-  // variant: weight streaming (decode) unless the average expert has >= 64 rows (or PREFILL is asked)
+  // Variant per expert, decided on the device from its row count: experts with at most kHot rows
+  // go to the weight-streaming kernel, the others to the MFMA tile kernel (one weight read per 192
+  // rows instead of one per 16 * mt rows).  AUTO launches only the variants that can have work; DECODE
+  // and PREFILL force one variant for every expert.
+  const int kHot = 4 * 16 * pick_mt(T, k, E);  // at most 4 streaming row tiles per expert
   // (the tile kernel addresses activation rows with 32-bit element offsets)
   const bool tile_ok = (double)((size_t)T > n ? T : n) * (H > I ? H : I) < 2147483648.0;
-  const bool tile = tile_ok && (mode == MOE_FFN_PREFILL || (mode == MOE_FFN_AUTO && (double)n >= 64.0 * E));
+  bool use_stream = true, use_tile = false;
+  int split = 0x7FFFFFFF;  // streaming kernel: rows <= split; tile kernel: rows > split
+  if (mode == MOE_FFN_PREFILL && tile_ok) {
+    use_stream = false, use_tile = true, split = 0;
+  } else if (mode == MOE_FFN_AUTO && tile_ok) {
+    if ((double)n >= 64.0 * E) {
+      use_stream = false, use_tile = true, split = 0;
+    } else if ((long long)n > kHot) {
+      use_tile = true, split = kHot;
+    }
+  }
   const int mt = pick_mt(T, k, E);
   const int mr = 16 * mt;
   const size_t nz = n < (size_t)E ? n : (size_t)E;
@@ -513,19 +543,18 @@ int launch_ffn(const moe_experts* w, const void* x, int xdt, int T, int k, const
   dn.out = y_perm;
   dn.region_codes = g.d_codes;
   dn.region_scales = g.d_scales;
-  if (tile) {
-    int rc = launch_ffn_tile(w->fmt, gu, dn, H, I, (int)n, E, s, trace);
-    if (rc != MOE_OK) return rc;
-    trace(2, s);
-    MOE_CHECK_LAUNCH("moe_expert_ffn prefill launch");
-    return MOE_OK;
-  }
-  switch (w->fmt) {
-    case MOE_W_BF16: launch_stream<MOE_W_BF16>(mt, gu, dn, H, I, S, s); break;
-    case MOE_W_MXFP4: launch_stream<MOE_W_MXFP4>(mt, gu, dn, H, I, S, s); break;
-    case MOE_W_INT4G32: launch_stream<MOE_W_INT4G32>(mt, gu, dn, H, I, S, s); break;
-    default: return fail(MOE_ERR_UNSUPPORTED, "moe_expert_ffn: format %d", w->fmt);
-  }
+  FfnArgs gu_s = gu, dn_s = dn, gu_t = gu, dn_t = dn;
+  gu_s.min_rows = dn_s.min_rows = 1, gu_s.max_rows = dn_s.max_rows = split;
+  gu_t.min_rows = dn_t.min_rows = split == 0x7FFFFFFF ? split : split + 1;
+  gu_t.max_rows = dn_t.max_rows = 0x7FFFFFFF;
+  int rc = MOE_OK;
+  if (use_stream) rc = launch_stream_fmt(w->fmt, mt, true, gu_s, H, I, S, s);
+  if (rc == MOE_OK && use_tile) rc = launch_ffn_tile_part(w->fmt, true, gu_t, H, I, (int)n, E, s);
+  if (rc != MOE_OK) return rc;
+  trace(1, s);
+  if (use_stream) rc = launch_stream_fmt(w->fmt, mt, false, dn_s, H, I, S, s);
+  if (rc == MOE_OK && use_tile) rc = launch_ffn_tile_part(w->fmt, false, dn_t, H, I, (int)n, E, s);
+  if (rc != MOE_OK) return rc;
   trace(2, s);
   MOE_CHECK_LAUNCH("moe_expert_ffn launch");
   return MOE_OK;

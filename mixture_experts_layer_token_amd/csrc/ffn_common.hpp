@@ -63,14 +63,16 @@ __device__ __forceinline__ f32x4 mfma(f16x8 a, f16x8 b, f32x4 c) {
 
 // ------------------------------------------------------------------ row tiles
 
-// Row tile `slot` of the grouped rows: experts in id order, each cut into ceil(n_e / mr) tiles.
+// Row tile `slot` of the grouped rows: experts in id order (those with lo <= n_e <= hi), each cut
+// into ceil(n_e / mr) tiles.
 // Executed by wave 0; result in shared memory.  Returns false (all threads) when the slot is
 // past the last tile.
 struct RowTile {
   int e, p0, rows;  // expert, first grouped row, rows in this tile (<= mr)
 };
 
-__device__ inline bool find_row_tile(const int32_t* __restrict__ offsets, int E, int mr, int slot, RowTile* sh) {
+__device__ inline bool find_row_tile(const int32_t* __restrict__ offsets, int E, int mr, int slot, RowTile* sh,
+                                     int lo = 0, int hi = 0x7FFFFFFF) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     const int per = (E + 63) / 64;
@@ -78,6 +80,7 @@ __device__ inline bool find_row_tile(const int32_t* __restrict__ offsets, int E,
     int local = 0;
     for (int e = e_begin; e < e_end; ++e) {
       int c = offsets[e + 1] - offsets[e];
+      if (c < lo || c > hi) c = 0;
       local += (c + mr - 1) / mr;
     }
     int incl = local;
@@ -92,6 +95,7 @@ __device__ inline bool find_row_tile(const int32_t* __restrict__ offsets, int E,
       int acc = excl;
       for (int e = e_begin; e < e_end; ++e) {
         int o0 = offsets[e], c = offsets[e + 1] - o0;
+        if (c < lo || c > hi) c = 0;
         int nt = (c + mr - 1) / mr;
         if (slot < acc + nt) {
           int t = slot - acc;
@@ -112,7 +116,8 @@ struct FfnArgs {
   const char* packages;
   size_t pkg_stride;
   const int32_t* slot_of_expert;
-  int n_slots;  // valid slots are [0, n_slots)
+  int n_slots;            // valid slots are [0, n_slots)
+  int min_rows, max_rows;  // experts with a row count outside [min_rows, max_rows] are left to the other variant
   const int32_t* offsets;
   const int32_t* perm_src;
   const unsigned short* a;  // GU: activations [T][H] (operand type); down: h [T*k][I]
@@ -122,8 +127,8 @@ struct FfnArgs {
 };
 
 
-// Prefill (tile) variant: gate/up then down launches; mark(1, s) is called between them.
-int launch_ffn_tile(int fmt, const FfnArgs& gu, const FfnArgs& dn, int H, int I, int n, int E, hipStream_t s,
-                    void (*mark)(int, hipStream_t));
+// Prefill (tile) variant, one matrix: gate/up (with SwiGLU) or down, for the experts whose row
+// count lies in [a.min_rows, a.max_rows].
+int launch_ffn_tile_part(int fmt, bool gate_up, const FfnArgs& a, int H, int I, int n, int E, hipStream_t s);
 
 }  // namespace moe

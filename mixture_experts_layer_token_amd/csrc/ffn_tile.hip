@@ -67,7 +67,11 @@ __global__ __launch_bounds__(kTW * 64, 1) void ffn_tile_kernel(FfnArgs args) {
     e_begin = lane * per;
     e_end = min(args.E, e_begin + per);
     int local = 0;
-    for (int e = e_begin; e < e_end; ++e) local += (args.offsets[e + 1] - args.offsets[e] + kTM - 1) / kTM;
+    for (int e = e_begin; e < e_end; ++e) {
+      int c = args.offsets[e + 1] - args.offsets[e];
+      if (c < args.min_rows || c > args.max_rows) c = 0;
+      local += (c + kTM - 1) / kTM;
+    }
     incl = local;
     for (int off = 1; off < 64; off <<= 1) {
       int o = __shfl_up(incl, off, 64);
@@ -85,7 +89,9 @@ __global__ __launch_bounds__(kTW * 64, 1) void ffn_tile_kernel(FfnArgs args) {
   if (tid < 64 && slot >= excl && slot < incl) {
     int acc_t = excl;
     for (int e = e_begin; e < e_end; ++e) {
-      const int o0 = args.offsets[e], c = args.offsets[e + 1] - o0;
+      const int o0 = args.offsets[e];
+      int c = args.offsets[e + 1] - o0;
+      if (c < args.min_rows || c > args.max_rows) c = 0;
       const int nt = (c + kTM - 1) / kTM;
       if (slot < acc_t + nt) {
         const int t = slot - acc_t;
@@ -294,28 +300,23 @@ int launch_one(const FfnArgs& a, int S, int N, hipStream_t s) {
 
 }  // namespace
 
-// Row-tile upper bound for n grouped rows over E experts (at most min(E, n) experts are non-empty).
-int tile_rows() { return kTM; }
-
-int launch_ffn_tile(int fmt, const FfnArgs& gu, const FfnArgs& dn, int H, int I, int n, int E, hipStream_t s,
-                    void (*mark)(int, hipStream_t)) {
+int launch_ffn_tile_part(int fmt, bool gate_up, const FfnArgs& a, int H, int I, int n, int E, hipStream_t s) {
   const long long nz = n < E ? n : E;
   const int S = (int)(((long long)n + nz * (kTM - 1)) / kTM);
-  int rc = MOE_OK;
-  switch (fmt) {
-    case MOE_W_BF16: rc = launch_one<MOE_W_BF16, true>(gu, S, 2 * I, s); break;
-    case MOE_W_MXFP4: rc = launch_one<MOE_W_MXFP4, true>(gu, S, 2 * I, s); break;
-    case MOE_W_INT4G32: rc = launch_one<MOE_W_INT4G32, true>(gu, S, 2 * I, s); break;
-    default: return fail(MOE_ERR_UNSUPPORTED, "moe_expert_ffn: no prefill kernel for format %d", fmt);
+  if (gate_up) {
+    switch (fmt) {
+      case MOE_W_BF16: return launch_one<MOE_W_BF16, true>(a, S, 2 * I, s);
+      case MOE_W_MXFP4: return launch_one<MOE_W_MXFP4, true>(a, S, 2 * I, s);
+      case MOE_W_INT4G32: return launch_one<MOE_W_INT4G32, true>(a, S, 2 * I, s);
+    }
+  } else {
+    switch (fmt) {
+      case MOE_W_BF16: return launch_one<MOE_W_BF16, false>(a, S, H, s);
+      case MOE_W_MXFP4: return launch_one<MOE_W_MXFP4, false>(a, S, H, s);
+      case MOE_W_INT4G32: return launch_one<MOE_W_INT4G32, false>(a, S, H, s);
+    }
   }
-  if (rc != MOE_OK) return rc;
-  mark(1, s);
-  switch (fmt) {
-    case MOE_W_BF16: rc = launch_one<MOE_W_BF16, false>(dn, S, H, s); break;
-    case MOE_W_MXFP4: rc = launch_one<MOE_W_MXFP4, false>(dn, S, H, s); break;
-    default: rc = launch_one<MOE_W_INT4G32, false>(dn, S, H, s); break;
-  }
-  return rc;
+  return fail(MOE_ERR_UNSUPPORTED, "moe_expert_ffn: no prefill kernel for format %d", fmt);
 }
 
 }  // namespace moe

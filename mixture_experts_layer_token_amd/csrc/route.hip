@@ -18,6 +18,7 @@ namespace {
 constexpr int kRouteTokens = 16;    // tokens per workgroup (MFMA M)
 constexpr int kTilesPerPass = 8;    // 16-expert tiles each wave accumulates per pass over H
 constexpr int kMaxE = 1024;
+constexpr int kSplitMaxT = 256;  // tokens up to which the router is split over workgroups
 
 // (value, id) ordering of the router: larger value first, equal values -> lower id first
 __device__ __forceinline__ bool better(float v, int e, float bv, int be) { return v > bv || (v == bv && e < be); }
@@ -137,6 +138,81 @@ __global__ __launch_bounds__(kRouteThreads) void route_bf16_kernel(const unsigne
   }
 }
 
+// ---- small T: the router's weight read is spread over many workgroups
+//
+// route_partial_kernel: workgroup (expert tile, K range, token tile) computes a 16 x 16 block of
+// partial logits over its K range (its 4 waves split the range, summed in LDS in wave order)
+// and stores it to part[range][t][e].  route_topk_kernel: one wave per token sums the ranges in
+// order, adds the bias and selects the top k.  Both fixed-order: deterministic.
+constexpr int kSplitMinSteps = 16;  // k-steps per K range (4 waves x 4)
+
+__global__ __launch_bounds__(256) void route_partial_kernel(const unsigned short* __restrict__ x,
+                                                            const unsigned short* __restrict__ wg, int T, int H,
+                                                            int E, int KS, float* __restrict__ part) {
+  __shared__ f32x4 red[4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int et = blockIdx.x, r = blockIdx.y, tt = blockIdx.z;
+  const int nks = H / 32;
+  const int ks0 = r * nks / KS, ks1 = (r + 1) * nks / KS;
+  const int w0 = ks0 + wave * (ks1 - ks0) / 4, w1 = ks0 + (wave + 1) * (ks1 - ks0) / 4;
+  const int m = lane & 15, kq = (lane >> 4) * 8;
+  const int t = tt * 16 + m, e = et * 16 + m;
+  const bool tok = t < T, exp = e < E;
+  const unsigned short* xr = x + (size_t)(tok ? t : 0) * H + kq;
+  const unsigned short* wr = wg + (size_t)(exp ? e : 0) * H + kq;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int ks = w0; ks < w1; ++ks) {
+    bf16x8 a = bf16x8{0, 0, 0, 0, 0, 0, 0, 0}, b = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    if (tok) a = *(const bf16x8*)(xr + ks * 32);
+    if (exp) b = *(const bf16x8*)(wr + ks * 32);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+  }
+  red[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0) {
+    f32x4 v = red[0][lane];
+    for (int w = 1; w < 4; ++w) {
+      const f32x4 o = red[w][lane];
+      v[0] += o[0], v[1] += o[1], v[2] += o[2], v[3] += o[3];
+    }
+    const int col = et * 16 + (lane & 15);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = tt * 16 + (lane >> 4) * 4 + q;
+      if (row < T && col < E) part[((size_t)r * T + row) * E + col] = v[q];
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ part, const float* __restrict__ bias,
+                                                         int T, int E, int KS, int k, int32_t* __restrict__ ids,
+                                                         float* __restrict__ w, float* __restrict__ logits) {
+  extern __shared__ float lds[];  // [4][E]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;  // whole wave; no block barrier below
+  float* lg = lds + (size_t)wave * E;
+  for (int e = lane; e < E; e += 64) {
+    float v = part[(size_t)t * E + e];
+    for (int r = 1; r < KS; ++r) v += part[((size_t)r * T + t) * E + e];
+    v += bias ? bias[e] : 0.f;
+    lg[e] = v;
+    if (logits) logits[(size_t)t * E + e] = v;
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  wave_topk(lg, E, k, ids + (size_t)t * k, w + (size_t)t * k);
+}
+
+int route_split_ranges(int T, int H, int E) {
+  const int nks = H / 32;
+  const int tiles = ((E + 15) / 16) * ((T + 15) / 16);
+  int KS = 512 / (tiles > 0 ? tiles : 1);
+  if (KS > nks / kSplitMinSteps) KS = nks / kSplitMinSteps;
+  return KS < 1 ? 1 : KS;
+}
+
 __global__ __launch_bounds__(256) void route_f32_kernel(const float* __restrict__ x, const float* __restrict__ wg,
                                                         const float* __restrict__ bias, int T, int H, int E, int k,
                                                         int32_t* __restrict__ ids, float* __restrict__ w,
@@ -161,10 +237,26 @@ __global__ __launch_bounds__(256) void route_f32_kernel(const float* __restrict_
 
 }  // namespace
 
+size_t route_workspace(int T, int H, int E, int xdt) {
+  if (xdt != MOE_BF16 || T > kSplitMaxT || H % 32) return 0;
+  return (size_t)route_split_ranges(T, H, E) * T * E * sizeof(float);
+}
+
 int launch_route(const void* x, int xdt, int T, int H, const void* wg, const float* bias, int E, int k, int32_t* ids,
-                 float* w, float* logits, hipStream_t s) {
+                 float* w, float* logits, void* ws, size_t ws_bytes, hipStream_t s) {
   if (T == 0) return MOE_OK;
   if (E > kMaxE) return fail(MOE_ERR_INVALID, "moe_route: E=%d exceeds %d", E, kMaxE);
+  if (xdt == MOE_BF16 && H % 32 == 0 && T <= kSplitMaxT) {
+    const size_t need = route_workspace(T, H, E, xdt);
+    if (!ws || ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "moe_route: workspace %zu < %zu", ws_bytes, need);
+    const int KS = route_split_ranges(T, H, E);
+    hipLaunchKernelGGL(route_partial_kernel, dim3((E + 15) / 16, KS, (T + 15) / 16), dim3(256), 0, s,
+                       (const unsigned short*)x, (const unsigned short*)wg, T, H, E, KS, (float*)ws);
+    hipLaunchKernelGGL(route_topk_kernel, dim3((T + 3) / 4), dim3(256), (size_t)4 * E * sizeof(float), s,
+                       (const float*)ws, bias, T, E, KS, k, ids, w, logits);
+    MOE_CHECK_LAUNCH("moe_route launch");
+    return MOE_OK;
+  }
   if (xdt == MOE_BF16) {
     if (H % 32) return fail(MOE_ERR_UNSUPPORTED, "moe_route: bf16 path needs H %% 32 == 0 (H=%d)", H);
     const int Epad = ((E + 15) / 16) * 16 + 1;

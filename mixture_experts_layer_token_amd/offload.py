@@ -135,7 +135,7 @@ class OffloadedModel:
         if out is None:
             out = torch.empty((T, self.H), dtype=x.dtype, device=x.device)
         ids, w = lay.topk_ids[:T], lay.topk_w[:T]
-        api.moe_route(x, self.wg[l], self.bias(l, step), k, ids, w)
+        api.moe_route(x, self.wg[l], self.bias(l, step), k, ids, w, ws=lay.rws)
         host_ids = self.ids_host[:T]
         host_ids.copy_(ids, non_blocking=True)
         self.routed.record()

@@ -24,15 +24,21 @@ def test_every_header_symbol_is_exported():
     assert set(_lib.SIGNATURES) == set(syms)
 
 
+def test_route_workspace_sizes():
+    assert moe.api.moe_route_workspace(8192, 7168, 384, "bf16") == 0  # large batches: one kernel, no workspace
+    assert moe.api.moe_route_workspace(1, 2880, 128, "bf16") > 0
+    assert moe.api.moe_route_workspace(16, 256, 8, "f32") == 0
+
+
 def test_route_validation():
     # no pointer is touched before validation fails
-    assert L.moe_route(None, 1, 4, 64, None, None, 0, 1, None, None, None, None) == INVALID
+    assert L.moe_route(None, 1, 4, 64, None, None, 0, 1, None, None, None, None, 0, None) == INVALID
     assert b"E=0" in L.moe_last_error()
-    assert L.moe_route(None, 1, 4, 64, None, None, 8, 9, None, None, None, None) == INVALID
-    assert L.moe_route(None, 1, 4, 64, None, None, 64, 17, None, None, None, None) == INVALID
-    assert L.moe_route(None, 7, 4, 64, None, None, 8, 2, None, None, None, None) == INVALID
-    assert L.moe_route(None, 1, 4, 64, None, None, 8, 2, None, None, None, None) == INVALID  # null x
-    assert L.moe_route(None, 1, 0, 64, None, None, 8, 2, None, None, None, None) == OK  # T = 0: nothing to do
+    assert L.moe_route(None, 1, 4, 64, None, None, 8, 9, None, None, None, None, 0, None) == INVALID
+    assert L.moe_route(None, 1, 4, 64, None, None, 64, 17, None, None, None, None, 0, None) == INVALID
+    assert L.moe_route(None, 7, 4, 64, None, None, 8, 2, None, None, None, None, 0, None) == INVALID
+    assert L.moe_route(None, 1, 4, 64, None, None, 8, 2, None, None, None, None, 0, None) == INVALID  # null x
+    assert L.moe_route(None, 1, 0, 64, None, None, 8, 2, None, None, None, None, 0, None) == OK  # T = 0: nothing to do
 
 
 def test_permute_and_combine_validation():

@@ -151,6 +151,24 @@ def test_layer_small(fmt, xdt, T, mode):
     assert_output_close(to_f64(out), ref, tol_dt, wl.name)
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "mxfp4", "int4g32"])
+def test_layer_hot_expert_split(fmt):
+    """Skewed routing: a few experts get hundreds of rows (MFMA tile kernel), the rest a handful
+    (streaming kernel), in one call."""
+    wl = small_variant(fmt, zipf_s=3.0, name="hot-" + fmt)
+    T = 300
+    say("hot expert split", wl.name)
+    x, _ = oracle.rank_gap_inputs(wl, T)
+    layer = build_layer(wl, T)
+    out = layer.forward(to_device_act(x, "bf16"))
+    torch.cuda.synchronize()
+    counts = layer.counts.cpu().numpy()
+    assert counts.max() > 128 and 0 < counts[counts > 0].min() <= 128  # both variants have work
+    ref, ids_ref, _ = oracle_reference(wl, x, np.arange(T))
+    assert np.array_equal(layer.topk_ids[:T].cpu().numpy(), ids_ref)
+    assert_output_close(to_f64(out), ref, "bf16", wl.name)
+
+
 def test_tiny_config_full():
     wl = W.WORKLOADS["tiny"]
     T = wl.Ts[0]
