@@ -28,13 +28,19 @@ namespace {
 
 // ------------------------------------------------------------------ streaming kernel
 
+// Read-only zeros: the address of prefetches that fall past a wave's last stage (1 KiB covers one
+// lane-strided 16-byte fragment load and every scale or activation offset of a stage).
+__device__ __attribute__((aligned(1024))) unsigned char g_zero_page[1024];
+
 // Weight loads of one pipeline stage, held in registers until consumed PF stages later.
 // bf16: a stage is one k-step: NSTR fragments of 16 bytes per lane.
 // 4-bit: a stage is one chunk of up to 4 k-steps: NSTR 16-byte code words + their scales.
-template <int FMT, int NSTR>
+// Each stage also carries its activation fragments (KPS k-steps x MT row tiles).
+template <int FMT, int NSTR, int KPS, int MT, typename OpT>
 struct Stage {
   u32x4 code[NSTR];
   unsigned scale[NSTR][FMT == MOE_W_INT4G32 ? 2 : 1];
+  OpT a[KPS][MT];
 };
 
 // GU = true: a unit is the strip pair (2u, 2u+1) of the GU matrix (gate rows, up rows; K = H),
@@ -42,7 +48,9 @@ struct Stage {
 // GU = false: a unit is strip u of the down matrix (K = I), epilogue -> y_perm.
 // A workgroup owns units [NP*blockIdx.x, +NP) of one row tile; its NW waves split K.
 template <int FMT, int MT, int NW, int NP, int PF, bool GU>
-__global__ __launch_bounds__(NW * 64, (FMT == MOE_W_BF16 ? 3 : 2) * 4 / NW) void ffn_stream_kernel(FfnArgs args) {
+// (second bound: minimum waves per SIMD, i.e. the register budget: 3 -> 168 VGPRs, 2 -> 256)
+__global__ __launch_bounds__(NW * 64, FMT == MOE_W_BF16 ? 3 : 2) void ffn_stream_kernel(FfnArgs args) {
+  static_assert(NW >= 1 && NW <= 8, "waves per workgroup");
   typedef typename Op<FMT>::T OpT;
   constexpr int SPU = GU ? 2 : 1;  // strips per unit
   constexpr int NSTR = NP * SPU;   // strips per workgroup (every wave covers all of them)
@@ -81,17 +89,6 @@ __global__ __launch_bounds__(NW * 64, (FMT == MOE_W_BF16 ? 3 : 2) * 4 / NW) void
     }
   }
   const unsigned lane16 = (unsigned)lane * 16, lrow = (unsigned)(lane & 15);
-  // activation rows of this lane: row m = lane % 16 of each M tile, k offset 8 * (lane / 16)
-  const unsigned short* arow[MT];
-  bool aok[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int r = mt * 16 + (lane & 15);
-    aok[mt] = r < rows;
-    int src = 0;
-    if (aok[mt]) src = GU ? args.perm_src[p0 + r] / args.k : p0 + r;
-    arow[mt] = args.a + (size_t)src * K + (lane >> 4) * 8;
-  }
 
   f32x4 acc[MT][NSTR];
 #pragma unroll
@@ -99,76 +96,62 @@ __global__ __launch_bounds__(NW * 64, (FMT == MOE_W_BF16 ? 3 : 2) * 4 / NW) void
 #pragma unroll
     for (int s = 0; s < NSTR; ++s) acc[mt][s] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // this wave's contiguous range of stages (k-steps for bf16, chunks of 4 k-steps for 4-bit)
+  // This wave's contiguous range of stages (k-steps for bf16, chunks of 4 k-steps for 4-bit).
+  // A 4-bit matrix whose K is not a multiple of 128 ends in a partial chunk; the wave holding
+  // it computes the nfull whole stages in the pipelined loop and the partial one after it.
   const int n_stages = Q4 ? (nks + 3) / 4 : nks;
   const int st0 = wave * n_stages / NW, st1 = (wave + 1) * n_stages / NW;
   const int count = st1 - st0;
+  const bool part = Q4 && (nks & 3) != 0 && st1 == n_stages && count > 0;
+  const int nfull = count - (part ? 1 : 0);
 
-  auto load_a = [&](OpT (&dst)[KPS][MT], int st) {
-    const int ns = Q4 ? min(4, nks - 4 * st) : 1;
+  // Every load of the pipelined loop is unconditional (a load skipped on one path would make
+  // the compiler wait for all outstanding loads where the paths join), and a stage's weights and
+  // activations are issued together, PF stages before use, so waiting for one stage never waits
+  // for a younger one.  Prefetches past the last stage read the zero page; activation rows past
+  // the tile repeat the tile's last row (their output rows are never stored).
+  typedef Stage<FMT, NSTR, KPS, MT, OpT> StageT;
+  const unsigned short* arow[MT];
 #pragma unroll
-    for (int q = 0; q < KPS; ++q)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        OpT v = OpT{0, 0, 0, 0, 0, 0, 0, 0};
-        if (aok[mt] && q < ns) v = *(const OpT*)(arow[mt] + (KPS * st + q) * 32);
-        dst[q][mt] = v;
-      }
-  };
+  for (int mt = 0; mt < MT; ++mt) {
+    const int r = min(mt * 16 + (lane & 15), rows - 1);
+    const int src = GU ? args.perm_src[p0 + r] / args.k : p0 + r;
+    arow[mt] = args.a + (size_t)src * K + (lane >> 4) * 8;
+  }
   // weights are read once per call: non-temporal loads stream them without displacing cached data
-  auto load_b = [&](Stage<FMT, NSTR>& S, int st) {
-    if constexpr (!Q4) {
+  auto load = [&](StageT& S, int st, bool valid) {
 #pragma unroll
-      for (int s = 0; s < NSTR; ++s)
-        S.code[s] = __builtin_nontemporal_load((const u32x4*)(cbase[s] + (size_t)st * 1024 + lane16));
-    } else {
-      const int ns = min(4, nks - 4 * st);
-      if (ns == 4) {
-#pragma unroll
-        for (int s = 0; s < NSTR; ++s) {
-          S.code[s] = __builtin_nontemporal_load((const u32x4*)(cbase[s] + (size_t)st * 1024 + lane16));
-          const char* sc = sbase[s] + ((size_t)st * 64 + lrow * 4) * SB;
-          if constexpr (SB == 1) {
-            S.scale[s][0] = __builtin_nontemporal_load((const unsigned*)sc);
-          } else {
-            typedef __attribute__((__vector_size__(2 * sizeof(unsigned)))) unsigned u32x2;
-            const u32x2 v = __builtin_nontemporal_load((const u32x2*)sc);
-            S.scale[s][0] = v[0], S.scale[s][SB - 1] = v[1];
-          }
-        }
-      } else {  // the last, partial chunk: ns k-steps, packed 4 * ns bytes per lane
-#pragma unroll
-        for (int s = 0; s < NSTR; ++s) {
-          const char* cb = cbase[s] + (size_t)st * 1024 + (size_t)lane * 4 * ns;
-          const char* sb = sbase[s] + ((size_t)st * 64 + lrow * ns) * SB;
-          unsigned c[4] = {0, 0, 0, 0}, sc[4] = {0, 0, 0, 0};
-          for (int q = 0; q < ns; ++q) {
-            c[q] = *(const unsigned*)(cb + 4 * q);
-            sc[q] = SB == 1 ? (unsigned)*(const unsigned char*)(sb + q) : (unsigned)*(const unsigned short*)(sb + 2 * q);
-          }
-          S.code[s] = u32x4{c[0], c[1], c[2], c[3]};
-          if constexpr (SB == 1) {
-            S.scale[s][0] = sc[0] | (sc[1] << 8) | (sc[2] << 16) | (sc[3] << 24);
-          } else {
-            S.scale[s][0] = sc[0] | (sc[1] << 16);
-            S.scale[s][SB - 1] = sc[2] | (sc[3] << 16);
-          }
+    for (int s = 0; s < NSTR; ++s) {
+      const char* cb = valid ? cbase[s] + (size_t)st * 1024 : (const char*)g_zero_page;
+      S.code[s] = __builtin_nontemporal_load((const u32x4*)(cb + lane16));
+      if constexpr (Q4) {
+        const char* sc = valid ? sbase[s] + (size_t)st * 64 * SB : (const char*)g_zero_page;
+        sc += lrow * 4 * SB;
+        if constexpr (SB == 1) {
+          S.scale[s][0] = __builtin_nontemporal_load((const unsigned*)sc);
+        } else {
+          typedef __attribute__((__vector_size__(2 * sizeof(unsigned)))) unsigned u32x2;
+          const u32x2 v = __builtin_nontemporal_load((const u32x2*)sc);
+          S.scale[s][0] = v[0], S.scale[s][SB - 1] = v[1];
         }
       }
     }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const unsigned short* ar = valid ? arow[mt] + KPS * st * 32 : (const unsigned short*)g_zero_page;
+#pragma unroll
+      for (int q = 0; q < KPS; ++q) S.a[q][mt] = *(const OpT*)(ar + q * 32);
+    }
   };
-  auto compute = [&](const Stage<FMT, NSTR>& S, const OpT (&a)[KPS][MT], int st) {
+  auto compute = [&](const StageT& S) {
     if constexpr (!Q4) {
 #pragma unroll
       for (int s = 0; s < NSTR; ++s) {
         const OpT b = __builtin_bit_cast(OpT, S.code[s]);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc[mt][s] = mfma(a[0][mt], b, acc[mt][s]);
+        for (int mt = 0; mt < MT; ++mt) acc[mt][s] = mfma(S.a[0][mt], b, acc[mt][s]);
       }
     } else {
-      // k-steps past the end of a partial last chunk hold zero codes, zero scales and zero
-      // activations, so all 4 k-steps are computed unconditionally
-      (void)st;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
 #pragma unroll
@@ -181,35 +164,66 @@ __global__ __launch_bounds__(NW * 64, (FMT == MOE_W_BF16 ? 3 : 2) * 4 / NW) void
             b = dec_int4(S.code[s][q], __builtin_bit_cast(_Float16, (unsigned short)(sw >> (16 * (q & 1)))));
           }
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) acc[mt][s] = mfma(a[q][mt], b, acc[mt][s]);
+          for (int mt = 0; mt < MT; ++mt) acc[mt][s] = mfma(S.a[q][mt], b, acc[mt][s]);
         }
       }
     }
   };
 
-  // software pipeline: weights PF stages ahead, activations (L2-resident) one stage ahead
-  Stage<FMT, NSTR> ring[PF];
-  OpT a_cur[KPS][MT], a_nxt[KPS][MT];
+  // software pipeline: a ring of PF stages in registers (the scheduling barriers keep each
+  // refill right after the compute that frees its registers)
+  StageT ring[PF];
 #pragma unroll
-  for (int i = 0; i < PF; ++i)
-    if (i < count) load_b(ring[i], st0 + i);
-  if (count > 0) load_a(a_nxt, st0);
-  for (int base = 0; base < count; base += PF) {
+  for (int i = 0; i < PF; ++i) load(ring[i], st0 + i, i < nfull);
+  __builtin_amdgcn_sched_barrier(0);
+  int base = 0;
+  for (; base + PF <= nfull; base += PF) {
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
-      const int st = base + i;
-      if (st < count) {
-#pragma unroll
-        for (int q = 0; q < KPS; ++q)
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) a_cur[q][mt] = a_nxt[q][mt];
-        if (st + 1 < count) load_a(a_nxt, st0 + st + 1);
-        compute(ring[i], a_cur, st0 + st);
-        if (st + PF < count) load_b(ring[i], st0 + st + PF);
-      }
+      compute(ring[i]);
+      load(ring[i], st0 + base + i + PF, base + i + PF < nfull);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
-
+  // the last nfull - base (< PF) stages are already in the ring
+#pragma unroll
+  for (int i = 0; i < PF - 1; ++i)
+    if (base + i < nfull) compute(ring[i]);
+  // the partial last chunk: ns k-steps packed 4 * ns bytes per lane; the missing k-steps get
+  // zero codes, zero scales and zero activations, so all 4 k-steps are computed
+  if (part) {
+    const int st = st1 - 1, ns = nks - 4 * st;
+    StageT S;
+#pragma unroll
+    for (int s = 0; s < NSTR; ++s) {
+      const char* cb = cbase[s] + (size_t)st * 1024 + (size_t)lane * 4 * ns;
+      const char* sb = sbase[s] + ((size_t)st * 64 + lrow * ns) * SB;
+      unsigned c[4] = {0, 0, 0, 0}, sc[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (q < ns) {
+          c[q] = *(const unsigned*)(cb + 4 * q);
+          sc[q] = SB == 1 ? (unsigned)*(const unsigned char*)(sb + q) : (unsigned)*(const unsigned short*)(sb + 2 * q);
+        }
+      }
+      S.code[s] = u32x4{c[0], c[1], c[2], c[3]};
+      if constexpr (SB == 1) {
+        S.scale[s][0] = sc[0] | (sc[1] << 8) | (sc[2] << 16) | (sc[3] << 24);
+      } else {
+        S.scale[s][0] = sc[0] | (sc[1] << 16);
+        S.scale[s][SB - 1] = sc[2] | (sc[3] << 16);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < KPS; ++q)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        OpT v = OpT{0, 0, 0, 0, 0, 0, 0, 0};
+        if (q < ns) v = *(const OpT*)(arow[mt] + (KPS * st + q) * 32);
+        S.a[q][mt] = v;
+      }
+    compute(S);
+  }
   // ---- sum the NW partial tiles (fixed wave order) one M tile at a time, then the epilogue
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
@@ -409,20 +423,22 @@ void trace(int i, hipStream_t s) {
 // enough bytes in flight; 4-bit fragments are 4x smaller, so a workgroup covers more strips,
 // which also lets one activation fragment feed more weight fragments (less L2 traffic).  The
 // 4-bit shapes stay within 256 VGPRs (2 waves per SIMD).
-template <int FMT, int MT>
+// NARROW: few experts can be touched (small batches), so the workgroups cover fewer strips and
+// there are enough of them to occupy every CU.
+template <int FMT, int MT, bool NARROW>
 struct Cfg {
   static constexpr bool Q4 = FMT != MOE_W_BF16;
-  static constexpr int GU_NP = Q4 ? (MT == 1 ? 4 : 2) : 1;
+  static constexpr int GU_NP = Q4 ? (NARROW ? 1 : (MT == 1 ? 4 : 2)) : 1;
   static constexpr int GU_NW = 4;
-  static constexpr int GU_PF = Q4 ? 2 : 8;
-  static constexpr int D_NP = Q4 ? (MT == 1 ? 8 : 4) : 2 * MT;
+  static constexpr int GU_PF = Q4 ? 2 : 4;
+  static constexpr int D_NP = Q4 ? (NARROW ? 2 : (MT == 1 ? 8 : 4)) : 2 * MT;
   static constexpr int D_NW = Q4 ? 4 : 8;
-  static constexpr int D_PF = Q4 ? 2 : 8;
+  static constexpr int D_PF = Q4 ? 2 : 4;
 };
 
-template <int FMT, int MT>
-void launch_stream_mt(bool gate_up, const FfnArgs& a, int H, int I, int S, hipStream_t s) {
-  typedef Cfg<FMT, MT> C;
+template <int FMT, int MT, bool NARROW>
+void launch_stream_cfg(bool gate_up, const FfnArgs& a, int H, int I, int S, hipStream_t s) {
+  typedef Cfg<FMT, MT, NARROW> C;
   if (gate_up) {
     const int gx = (I / 16 + C::GU_NP - 1) / C::GU_NP;
     hipLaunchKernelGGL((ffn_stream_kernel<FMT, MT, C::GU_NW, C::GU_NP, C::GU_PF, true>), dim3(gx, S),
@@ -435,18 +451,26 @@ void launch_stream_mt(bool gate_up, const FfnArgs& a, int H, int I, int S, hipSt
 }
 
 template <int FMT>
-void launch_stream(int mt, bool gate_up, const FfnArgs& a, int H, int I, int S, hipStream_t s) {
-  switch (mt) {
-    case 1: launch_stream_mt<FMT, 1>(gate_up, a, H, I, S, s); break;
-    default: launch_stream_mt<FMT, 2>(gate_up, a, H, I, S, s); break;
+void launch_stream(int mt, bool narrow, bool gate_up, const FfnArgs& a, int H, int I, int S, hipStream_t s) {
+  if (mt == 1) {
+    if (narrow)
+      launch_stream_cfg<FMT, 1, true>(gate_up, a, H, I, S, s);
+    else
+      launch_stream_cfg<FMT, 1, false>(gate_up, a, H, I, S, s);
+  } else {
+    if (narrow)
+      launch_stream_cfg<FMT, 2, true>(gate_up, a, H, I, S, s);
+    else
+      launch_stream_cfg<FMT, 2, false>(gate_up, a, H, I, S, s);
   }
 }
 
-int launch_stream_fmt(int fmt, int mt, bool gate_up, const FfnArgs& a, int H, int I, int S, hipStream_t s) {
+int launch_stream_fmt(int fmt, int mt, bool narrow, bool gate_up, const FfnArgs& a, int H, int I, int S,
+                      hipStream_t s) {
   switch (fmt) {
-    case MOE_W_BF16: launch_stream<MOE_W_BF16>(mt, gate_up, a, H, I, S, s); break;
-    case MOE_W_MXFP4: launch_stream<MOE_W_MXFP4>(mt, gate_up, a, H, I, S, s); break;
-    case MOE_W_INT4G32: launch_stream<MOE_W_INT4G32>(mt, gate_up, a, H, I, S, s); break;
+    case MOE_W_BF16: launch_stream<MOE_W_BF16>(mt, false, gate_up, a, H, I, S, s); break;
+    case MOE_W_MXFP4: launch_stream<MOE_W_MXFP4>(mt, narrow, gate_up, a, H, I, S, s); break;
+    case MOE_W_INT4G32: launch_stream<MOE_W_INT4G32>(mt, narrow, gate_up, a, H, I, S, s); break;
     default: return fail(MOE_ERR_UNSUPPORTED, "moe_expert_ffn: format %d", fmt);
   }
   return MOE_OK;
@@ -527,7 +551,7 @@ int launch_ffn(const moe_experts* w, const void* x, int xdt, int T, int k, const
   } else if (mode == MOE_FFN_AUTO && tile_ok) {
     if ((double)n >= 64.0 * E) {
       use_stream = false, use_tile = true, split = 0;
-    } else if ((long long)n > kHot) {
+    } else if (T > kHot) {  // a token picks an expert at most once: no expert exceeds T rows
       use_tile = true, split = kHot;
     }
   }
@@ -547,12 +571,16 @@ int launch_ffn(const moe_experts* w, const void* x, int xdt, int T, int k, const
   gu_s.min_rows = dn_s.min_rows = 1, gu_s.max_rows = dn_s.max_rows = split;
   gu_t.min_rows = dn_t.min_rows = split == 0x7FFFFFFF ? split : split + 1;
   gu_t.max_rows = dn_t.max_rows = 0x7FFFFFFF;
+  // at most min(E, n) experts are touched: with the wide 4-bit shapes that could leave CUs idle
+  const long long wide_wgs = (long long)nz * ((I / 16 + Cfg<MOE_W_MXFP4, 1, false>::GU_NP - 1) /
+                                              Cfg<MOE_W_MXFP4, 1, false>::GU_NP);
+  const bool narrow = wide_wgs < 1024;
   int rc = MOE_OK;
-  if (use_stream) rc = launch_stream_fmt(w->fmt, mt, true, gu_s, H, I, S, s);
+  if (use_stream) rc = launch_stream_fmt(w->fmt, mt, narrow, true, gu_s, H, I, S, s);
   if (rc == MOE_OK && use_tile) rc = launch_ffn_tile_part(w->fmt, true, gu_t, H, I, (int)n, E, s);
   if (rc != MOE_OK) return rc;
   trace(1, s);
-  if (use_stream) rc = launch_stream_fmt(w->fmt, mt, false, dn_s, H, I, S, s);
+  if (use_stream) rc = launch_stream_fmt(w->fmt, mt, narrow, false, dn_s, H, I, S, s);
   if (rc == MOE_OK && use_tile) rc = launch_ffn_tile_part(w->fmt, false, dn_t, H, I, (int)n, E, s);
   if (rc != MOE_OK) return rc;
   trace(2, s);

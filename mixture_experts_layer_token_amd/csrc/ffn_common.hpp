@@ -10,10 +10,9 @@ namespace moe {
 
 // ------------------------------------------------------------------ decoders
 
-__device__ __forceinline__ float e8m0_to_f32(unsigned s) {
-  unsigned bits = s == 0 ? 0x00400000u : (s == 255 ? 0x7FC00000u : (s << 23));
-  return __uint_as_float(bits);
-}
+// The scaled conversions read only the exponent field of their fp32 scale operand, which is
+// exactly an E8M0 byte placed at bit 23 (0 -> 2^-127, 0xFF -> NaN).
+__device__ __forceinline__ float e8m0_to_f32(unsigned s) { return __uint_as_float(s << 23); }
 
 // 8 MXFP4 elements (4 bytes, element 2b / 2b+1 in the low / high nibble of byte b) -> bf16
 __device__ __forceinline__ bf16x8 dec_mxfp4(unsigned word, unsigned scale_byte) {

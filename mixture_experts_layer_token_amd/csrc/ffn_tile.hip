@@ -36,7 +36,8 @@ struct TileCfg {
 };
 
 template <int FMT, bool GU>
-__global__ __launch_bounds__(kTW * 64, 1) void ffn_tile_kernel(FfnArgs args) {
+// (second bound: minimum waves per SIMD: 2 -> 256 VGPRs per wave)
+__global__ __launch_bounds__(kTW * 64, 2) void ffn_tile_kernel(FfnArgs args) {
   typedef typename Op<FMT>::T OpT;
   constexpr int BK = TileCfg<FMT>::BK;
   constexpr int KS = BK / 32;                     // k-steps per block
@@ -181,9 +182,12 @@ __global__ __launch_bounds__(kTW * 64, 1) void ffn_tile_kernel(FfnArgs args) {
           const char* cb = cbase[j] + (size_t)kb * 1024 + (size_t)lane * 4 * ns;
           const char* sp = sbase[j] + ((size_t)kb * 64 + (lane & 15) * ns) * SB;
           unsigned c[4] = {0, 0, 0, 0}, s4[4] = {0, 0, 0, 0};
-          for (int q = 0; q < ns; ++q) {
-            c[q] = *(const unsigned*)(cb + 4 * q);
-            s4[q] = SB == 1 ? (unsigned)*(const unsigned char*)(sp + q) : (unsigned)*(const unsigned short*)(sp + 2 * q);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (q < ns) {
+              c[q] = *(const unsigned*)(cb + 4 * q);
+              s4[q] = SB == 1 ? (unsigned)*(const unsigned char*)(sp + q) : (unsigned)*(const unsigned short*)(sp + 2 * q);
+            }
           }
           B.v[j][0] = u32x4{c[0], c[1], c[2], c[3]};
           if constexpr (SB == 1) {

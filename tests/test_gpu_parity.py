@@ -50,6 +50,49 @@ def test_dequant_bit_exact(fmt, H, I):
     assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
 
 
+def _sweep_scales_int4(n):
+    """bf16 scales that binary16 holds exactly (the packer's domain) and whose products with every
+    code stay finite in binary16 (8 * s <= 65504): 2^-14 .. 2^12 with a spread of 8-bit mantissas,
+    zero and a negative value."""
+    vals = []
+    for ex in range(-14, 13):
+        for m in range(0, 128, 9):
+            vals.append(np.float32(2.0 ** ex * (1 + m / 128.0)))
+    vals += [np.float32(0.0), np.float32(-0.75)]
+    v = np.array(vals, np.float32).view(np.uint32) >> 16
+    return np.resize(v.astype(np.uint16), n)
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "int4g32"])
+def test_dequant_every_code_and_scale(fmt):
+    """All 256 code bytes against every E8M0 exponent whose products stay finite in fp32 (0..252)
+    plus the NaN scale 0xFF, or a sweep of binary16-exact INT4 scales: the in-register decoders
+    the FFN kernels use."""
+    H, I = 256, 320
+    say("dequant sweep", fmt)
+    rng = np.random.default_rng(77)
+    ex = {"w": [], "s": []}
+    for rows, K in ((I, H), (I, H), (H, I)):
+        codes = rng.permutation(np.resize(np.arange(256, dtype=np.uint8), rows * K // 2)).reshape(rows, K // 2)
+        ng = rows * K // 32
+        if fmt == "mxfp4":
+            sc = np.resize(np.append(np.arange(253, dtype=np.uint8), np.uint8(255)), ng)
+        else:
+            sc = _sweep_scales_int4(ng)
+        ex["w"].append(codes)
+        ex["s"].append(rng.permutation(sc).reshape(rows, K // 32))
+    pkg = moe.moe_pack_expert(H, I, fmt, ex)
+    out = torch.empty(3 * H * I, dtype=torch.float32, device="cuda")
+    moe.moe_dequant_expert(torch.from_numpy(pkg).cuda(), H, I, fmt, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    want = np.concatenate([oracle.decode(fmt, ex["w"][m], ex["s"][m], *shp).ravel()
+                           for m, shp in enumerate([(I, H), (I, H), (H, I)])]).astype(np.float32)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), want[~nan].view(np.uint32))
+
+
 # ------------------------------------------------------------------ router
 
 ROUTE_CASES = [
