@@ -28,9 +28,6 @@ namespace {
 
 // ------------------------------------------------------------------ streaming kernel
 
-// Read-only zeros: the address of prefetches that fall past a wave's last stage (1 KiB covers one
-// lane-strided 16-byte fragment load and every scale or activation offset of a stage).
-__device__ __attribute__((aligned(1024))) unsigned char g_zero_page[1024];
 
 // Weight loads of one pipeline stage, held in registers until consumed PF stages later.
 // bf16: a stage is one k-step: NSTR fragments of 16 bytes per lane.

@@ -8,6 +8,21 @@
 
 namespace moe {
 
+// Read-only zeros (one copy per translation unit): the address of prefetches that fall past the
+// last stage or block, so that the loads of a software pipeline stay unconditional.  1 KiB covers
+// one lane-strided 16-byte fragment load and every scale or activation offset of a stage.
+static __device__ __attribute__((aligned(1024))) unsigned char g_zero_page[1024];
+
+// s_waitcnt that waits until at most n vector-memory loads are outstanding (expcnt and lgkmcnt
+// left alone); n < 64
+#define MOE_WAIT_VMCNT(n) \
+  __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+
+// Workgroup barrier that leaves vector-memory loads in flight (__syncthreads' fence would wait
+// for all of them, including direct-to-LDS loads of later pipeline stages).  The memory clobber
+// keeps the compiler from moving memory accesses across it; LDS reads of this wave are complete.
+__device__ __forceinline__ void barrier_keep_loads() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // ------------------------------------------------------------------ decoders
 
 // The scaled conversions read only the exponent field of their fp32 scale operand, which is
@@ -24,14 +39,25 @@ __device__ __forceinline__ bf16x8 dec_mxfp4(unsigned word, unsigned scale_byte) 
   return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
-// 8 INT4 elements (nibble n < 4: element 2n, n >= 4: element 2(n-4)+1, stored as q + 8) -> fp16 q*s
+// A constant the compiler must keep in a VGPR: three-operand instructions (v_and_or_b32) take no
+// literal operand, so constants in registers let (x & mask) | magic be one instruction.
+__device__ __forceinline__ unsigned in_vgpr(unsigned c) {
+  unsigned r;
+  asm("; const in vgpr" : "=v"(r) : "0"(c));
+  return r;
+}
+
+// 8 INT4 elements (nibble n < 4: element 2n, n >= 4: element 2(n-4)+1, stored as q + 8) -> fp16 q*s:
+// the nibble pair becomes 1024 + c in each fp16 half (c = q + 8), minus 1032 gives q, times s;
+// every step is exact in fp16 for s in binary16's normal range.
 __device__ __forceinline__ f16x8 dec_int4(unsigned v, _Float16 s) {
   const f16x2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
   const f16x2 ss = {s, s};
+  const unsigned mask = in_vgpr(0x000F000Fu), magic = in_vgpr(0x64006400u);
   f16x2 r[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    unsigned p = ((v >> (4 * j)) & 0x000F000Fu) | 0x64006400u;
+    unsigned p = ((v >> (4 * j)) & mask) | magic;
     f16x2 h = __builtin_bit_cast(f16x2, p);
     r[j] = (h - bias) * ss;
   }

@@ -5,12 +5,16 @@
 // processing is a different phase"), so the roofline is MFMA throughput rather than HBM.
 //
 // A workgroup (8 waves as 2 x 4) computes a 192-row x 256-column tile of one expert:
-//  - activation rows (gathered through perm_src for gate/up) are staged through a double
-//    buffer in LDS, one 128-wide (4-bit) or 64-wide (bf16) K block at a time, and read back as
-//    MFMA A operands (row stride padded by 16 bytes against bank conflicts);
+//  - activation rows (gathered through perm_src for gate/up) are staged in LDS by direct
+//    global->LDS loads, one K block (64 wide for 4-bit weights, 32 for bf16) per buffer, and
+//    read back as MFMA A operands (16-byte chunks XOR-swizzled per row against bank conflicts);
 //  - each wave owns 96 rows x 4 strips of 16 columns; its weight fragments come straight from
-//    the package (16 bytes per lane are one MFMA B operand) and are decoded in registers
-//    (MXFP4 -> bf16, INT4 -> fp16, both exact), one K block ahead of their use;
+//    the package into registers (16 bytes per lane are one bf16 MFMA B operand; a 4-bit lane
+//    word holds 4 k-steps, a block reads half of it) and are decoded in registers (MXFP4 ->
+//    bf16, INT4 -> fp16, both exact);
+//  - a kD-deep software pipeline: block kb+kD-1's activations and weights are issued while
+//    block kb is computed, every load unconditional and issued in block order, so waiting for
+//    one block never waits for a later one, and the barrier leaves later loads in flight;
 //  - v_mfma_f32_16x16x32_{bf16,f16}, fp32 accumulation, 24 accumulator tiles per wave;
 //  - gate/up epilogue: SiLU(g) * u on the lane's own (gate, up) pair, rounded once to h;
 //    down epilogue: fp32 y_perm.
@@ -28,11 +32,13 @@ constexpr int kTN = 256;     // columns per workgroup tile
 constexpr int kWMT = 6;      // 16-row MFMA tiles per wave (96 rows)
 constexpr int kWNS = 4;      // 16-column strips per wave
 constexpr int kXCD = 8;      // XCDs of an MI355X; workgroup i is dispatched to XCD i % 8
+constexpr int kD = 4;        // pipeline depth: K blocks in flight
 
 template <int FMT>
 struct TileCfg {
-  static constexpr int BK = FMT == MOE_W_BF16 ? 64 : 128;   // K per block
-  static constexpr size_t LDS = (size_t)2 * kTM * BK * 2;    // bytes of the A double buffer
+  static constexpr int BK = FMT == MOE_W_BF16 ? 32 : 64;  // K per block
+  // kD ring buffers plus one that absorbs the loads of blocks past the end
+  static constexpr size_t LDS = (size_t)(kD + 1) * kTM * BK * 2;
 };
 
 template <int FMT, bool GU>
@@ -45,8 +51,9 @@ __global__ __launch_bounds__(kTW * 64, 2) void ffn_tile_kernel(FfnArgs args) {
   constexpr int SB = FMT == MOE_W_MXFP4 ? 1 : 2;  // scale bytes
   constexpr int CPR = BK / 8;                     // 16-byte chunks per staged row
   constexpr int RPI = 64 / CPR;                   // rows per wave-wide direct-to-LDS load
-  constexpr int IPW = kTM / (kTW * RPI);          // such loads per wave per K block
-  // LDS: [2][kTM rows][CPR chunks of 16 B]; chunk c of row r sits in slot c ^ (r % CPR)
+  constexpr int IPW = (kTM + kTW * RPI - 1) / (kTW * RPI);  // such loads per wave per block
+  static_assert(!Q4 || KS == 2, "a 4-bit block is half of a 4-k-step package chunk");
+  // LDS: [kD + 1][kTM rows][CPR chunks of 16 B]; chunk c of row r sits in slot c ^ (r % CPR)
   extern __shared__ __align__(16) unsigned short lds_a[];
   __shared__ RowTile tile;
   __shared__ int sh_total;
@@ -56,7 +63,8 @@ __global__ __launch_bounds__(kTW * 64, 2) void ffn_tile_kernel(FfnArgs args) {
   const int n_strips = N / 16;
   const int ncol = (N + kTN - 1) / kTN;
   const int nks = K / 32;
-  const int nkb = (K + BK - 1) / BK;
+  const int nkb = (nks + KS - 1) / KS;                     // K blocks
+  const int nfb = Q4 ? (nks / 4) * 2 : nks;                // blocks in whole package chunks
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / 4, wn = wave % 4;
@@ -121,15 +129,16 @@ __global__ __launch_bounds__(kTW * 64, 2) void ffn_tile_kernel(FfnArgs args) {
   }
 
   // ---- activation staging: direct global -> LDS loads (16 bytes per lane, lane-linear in LDS).
-  // Load i of this wave fills tile rows wave*IPW*RPI + i*RPI + [0, RPI); lane l writes slot l % CPR of
-  // row lane / CPR, so it fetches chunk (l % CPR) ^ (row % CPR) of that row.  Rows past the tile's
+  // Load i of this wave fills tile rows (wave*IPW + i)*RPI + [0, RPI); lane l writes slot l % CPR
+  // of row l / CPR, so it fetches chunk (l % CPR) ^ (row % CPR) of that row.  Rows past the tile's
   // end repeat a valid row (their results are dropped); chunks past K repeat the last chunk
-  // (their weights are zero).
+  // (their weights are zero); loads whose rows lie past the 192-row tile, and loads of blocks
+  // past the end, go to the spare buffer kD.
   unsigned aoff[IPW];  // element offset of the lane's source row in args.a
   unsigned achunk[IPW];
 #pragma unroll
   for (int i = 0; i < IPW; ++i) {
-    const int r = wave * IPW * RPI + i * RPI + lane / CPR;
+    const int r = (wave * IPW + i) * RPI + lane / CPR;
     const int rr = r < rows ? r : 0;
     const int row = GU ? args.perm_src[p0 + rr] / args.k : p0 + rr;
     aoff[i] = (unsigned)row * (unsigned)K;
@@ -138,66 +147,67 @@ __global__ __launch_bounds__(kTW * 64, 2) void ffn_tile_kernel(FfnArgs args) {
   auto load_a = [&](int kb, int buf) {
 #pragma unroll
     for (int i = 0; i < IPW; ++i) {
+      const int r0 = (wave * IPW + i) * RPI;
       const unsigned c = min((unsigned)(kb * CPR) + achunk[i], (unsigned)(K / 8 - 1));
       const unsigned short* g = args.a + aoff[i] + c * 8;
-      unsigned short* l = lds_a + ((size_t)buf * kTM + wave * IPW * RPI + i * RPI) * BK;
+      const int b = r0 < kTM ? buf : kD;
+      unsigned short* l = lds_a + ((size_t)b * kTM + (r0 < kTM ? r0 : 0)) * BK;
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
                                        (__attribute__((address_space(3))) void*)l, 16, 0, 0);
     }
   };
 
-  // ---- weight fragments of one K block for this wave's strips
+  // ---- weight fragments of one K block for this wave's strips.  bf16: KS fragments of 16 bytes
+  // per strip.  4-bit: half of the lane's 16-byte word of a 4-k-step chunk (8 bytes, 2 k-steps)
+  // and the 2 matching scales.  Blocks past the whole chunks read the zero page (weights 0); the
+  // blocks of a partial last chunk are recomputed after the loop from their packed layout.
   struct BReg {
-    u32x4 v[kWNS][Q4 ? 1 : KS];
-    unsigned sc[kWNS][Q4 ? (SB == 2 ? 2 : 1) : 1];
+    unsigned v[kWNS][Q4 ? 2 : 4 * KS];
+    unsigned sc[kWNS];
   };
-  auto load_b = [&](BReg& B, int kb) {
-    if constexpr (!Q4) {
+  auto load_b = [&](BReg& B, int kb, bool valid) {
 #pragma unroll
-      for (int j = 0; j < kWNS; ++j)
+    for (int j = 0; j < kWNS; ++j) {
+      if constexpr (!Q4) {
 #pragma unroll
         for (int q = 0; q < KS; ++q) {
-          const int ks = kb * KS + q;
-          u32x4 v = u32x4{0, 0, 0, 0};
-          if (ks < nks) v = *(const u32x4*)(cbase[j] + (size_t)ks * 1024 + lane * 16);
-          B.v[j][q] = v;
+          const char* cp = valid ? cbase[j] + (size_t)(kb * KS + q) * 1024 : (const char*)g_zero_page;
+          const u32x4 v = *(const u32x4*)(cp + lane * 16);
+          B.v[j][4 * q] = v[0], B.v[j][4 * q + 1] = v[1], B.v[j][4 * q + 2] = v[2], B.v[j][4 * q + 3] = v[3];
         }
-    } else {
-      const int ns = min(4, nks - 4 * kb);
-      if (ns == 4) {
+      } else {
+        const int c = kb >> 1, h = kb & 1;
+        const char* cp = valid ? cbase[j] + (size_t)c * 1024 + h * 8 : (const char*)g_zero_page;
+        const uint2 v = *(const uint2*)(cp + lane * 16);
+        B.v[j][0] = v.x, B.v[j][1] = v.y;
+        const char* sp = valid ? sbase[j] + ((size_t)c * 64 + 2 * h) * SB : (const char*)g_zero_page;
+        sp += (lane & 15) * 4 * SB;
+        if constexpr (SB == 1)
+          B.sc[j] = *(const unsigned short*)sp;
+        else
+          B.sc[j] = *(const unsigned*)sp;
+      }
+    }
+  };
+  // a block of the partial last chunk: ns k-steps packed 4 * ns bytes per lane; k-steps past
+  // the end get zero codes and zero scales
+  auto load_b_partial = [&](BReg& B, int kb) {
+    const int c = kb >> 1, h = kb & 1, ns = nks - 4 * c;
 #pragma unroll
-        for (int j = 0; j < kWNS; ++j) {
-          B.v[j][0] = *(const u32x4*)(cbase[j] + (size_t)kb * 1024 + lane * 16);
-          const char* sp = sbase[j] + ((size_t)kb * 64 + (lane & 15) * 4) * SB;
-          if constexpr (SB == 1) {
-            B.sc[j][0] = *(const unsigned*)sp;
-          } else {
-            const uint2 v = *(const uint2*)sp;
-            B.sc[j][0] = v.x, B.sc[j][SB - 1] = v.y;
-          }
-        }
-      } else {  // partial last chunk: zero codes, zero scales past its end
+    for (int j = 0; j < kWNS; ++j) {
+      const char* cb = cbase[j] + (size_t)c * 1024 + (size_t)lane * 4 * ns;
+      const char* sp = sbase[j] + ((size_t)c * 64 + (lane & 15) * ns) * SB;
+      unsigned cw[2] = {0, 0}, sw[2] = {0, 0};
 #pragma unroll
-        for (int j = 0; j < kWNS; ++j) {
-          const char* cb = cbase[j] + (size_t)kb * 1024 + (size_t)lane * 4 * ns;
-          const char* sp = sbase[j] + ((size_t)kb * 64 + (lane & 15) * ns) * SB;
-          unsigned c[4] = {0, 0, 0, 0}, s4[4] = {0, 0, 0, 0};
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            if (q < ns) {
-              c[q] = *(const unsigned*)(cb + 4 * q);
-              s4[q] = SB == 1 ? (unsigned)*(const unsigned char*)(sp + q) : (unsigned)*(const unsigned short*)(sp + 2 * q);
-            }
-          }
-          B.v[j][0] = u32x4{c[0], c[1], c[2], c[3]};
-          if constexpr (SB == 1) {
-            B.sc[j][0] = s4[0] | (s4[1] << 8) | (s4[2] << 16) | (s4[3] << 24);
-          } else {
-            B.sc[j][0] = s4[0] | (s4[1] << 16);
-            B.sc[j][SB - 1] = s4[2] | (s4[3] << 16);
-          }
+      for (int q = 0; q < 2; ++q) {
+        const int qq = 2 * h + q;
+        if (qq < ns) {
+          cw[q] = *(const unsigned*)(cb + 4 * qq);
+          sw[q] = SB == 1 ? (unsigned)*(const unsigned char*)(sp + qq) : (unsigned)*(const unsigned short*)(sp + 2 * qq);
         }
       }
+      B.v[j][0] = cw[0], B.v[j][1] = cw[1];
+      B.sc[j] = sw[0] | (sw[1] << (8 * SB));
     }
   };
 
@@ -207,48 +217,90 @@ __global__ __launch_bounds__(kTW * 64, 2) void ffn_tile_kernel(FfnArgs args) {
 #pragma unroll
     for (int j = 0; j < kWNS; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  auto decode = [&](const BReg& B, int j, int q) -> OpT {
+    if constexpr (!Q4)
+      return __builtin_bit_cast(OpT, u32x4{B.v[j][4 * q], B.v[j][4 * q + 1], B.v[j][4 * q + 2], B.v[j][4 * q + 3]});
+    else if constexpr (FMT == MOE_W_MXFP4)
+      return dec_mxfp4(B.v[j][q], (B.sc[j] >> (8 * q)) & 255);
+    else
+      return dec_int4(B.v[j][q], __builtin_bit_cast(_Float16, (unsigned short)(B.sc[j] >> (16 * q))));
+  };
+  // VALU instructions of one strip's decode, spread over the MFMAs of the strip before it
+  constexpr int kDecV = FMT == MOE_W_INT4G32 ? 15 : (FMT == MOE_W_MXFP4 ? 5 : 0);
+  constexpr int kDecPerMfma = (kDecV + kWMT - 1) / kWMT;
   auto compute = [&](const BReg& B, int buf) {
     // A fragment of M tile mt, k-step q: row wm*96 + mt*16 + lane%16, chunk 4q + lane/16
     const unsigned short* abase = lds_a + ((size_t)buf * kTM + wm * (kWMT * 16) + (lane & 15)) * BK;
 #pragma unroll
     for (int q = 0; q < KS; ++q) {
+      // one k-step at a time: keeps the live A fragments to this step's (register budget)
+      if (q) __builtin_amdgcn_sched_barrier(0);
       const int slot = (4 * q + (lane >> 4)) ^ (lane & (CPR - 1));
       OpT a[kWMT];
 #pragma unroll
       for (int mt = 0; mt < kWMT; ++mt) a[mt] = *(const OpT*)(abase + mt * 16 * BK + slot * 8);
+      // strip j's MFMAs run while strip j+1 is decoded into the other operand register
+      OpT b = decode(B, 0, q), bn = b;
 #pragma unroll
       for (int j = 0; j < kWNS; ++j) {
-        OpT b;
-        if constexpr (!Q4) {
-          b = __builtin_bit_cast(OpT, B.v[j][q]);
-        } else if constexpr (FMT == MOE_W_MXFP4) {
-          b = dec_mxfp4(B.v[j][0][q], (B.sc[j][0] >> (8 * q)) & 255);
-        } else {
-          const unsigned sw = B.sc[j][q >> 1];
-          b = dec_int4(B.v[j][0][q], __builtin_bit_cast(_Float16, (unsigned short)(sw >> (16 * (q & 1)))));
-        }
+        if (j + 1 < kWNS) bn = decode(B, j + 1, q);
 #pragma unroll
         for (int mt = 0; mt < kWMT; ++mt) acc[mt][j] = mfma(a[mt], b, acc[mt][j]);
+        b = bn;
+      }
+      if constexpr (Q4) {  // issue order: A reads, strip 0's decode, then MFMA / decode pairs
+        __builtin_amdgcn_sched_group_barrier(0x100, kWMT, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, kDecV, 0);
+#pragma unroll
+        for (int i = 0; i < (kWNS - 1) * kWMT; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, kDecPerMfma, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kWMT, 0);
       }
     }
   };
 
-  // ---- K loop: stage block kb+1 (activations to LDS, weights to registers) while block kb runs
-  BReg bc, bn;
-  load_a(0, 0);
-  load_b(bc, 0);
-  __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0): this wave's direct-to-LDS loads have landed
-  __syncthreads();
-  for (int kb = 0; kb < nkb; ++kb) {
-    const bool more = kb + 1 < nkb;
-    if (more) {
-      load_a(kb + 1, (kb + 1) & 1);  // the buffer every wave finished reading before the last barrier
-      load_b(bn, kb + 1);
+  // ---- K loop: kD blocks in flight.  Block kb issues block kb+kD-1 (activations, then weights)
+  // and computes block kb from LDS buffer kb % kD and register ring entry kb % kD; at its end the
+  // wave waits until only the loads of blocks kb+2 .. kb+kD-1 are outstanding (block kb+1 has
+  // landed), and the barrier publishes block kb+1's buffer to every wave.
+  constexpr int kLoads = IPW + kWNS * (Q4 ? 2 : KS);  // vector loads per block and wave
+  BReg ring[kD];
+#pragma unroll
+  for (int i = 0; i < kD - 1; ++i) {
+    load_a(i, i < nkb ? i : kD);
+    load_b(ring[i], i, i < nfb);
+  }
+  MOE_WAIT_VMCNT((kD - 2) * kLoads);
+  barrier_keep_loads();
+  int kb = 0;
+  for (; kb + kD <= nkb; kb += kD) {
+#pragma unroll
+    for (int i = 0; i < kD; ++i) {
+      const int nb = kb + i + kD - 1;  // block to issue
+      load_a(nb, nb < nkb ? (i + kD - 1) % kD : kD);
+      load_b(ring[(i + kD - 1) % kD], nb, nb < nfb);
+      __builtin_amdgcn_sched_barrier(0);  // issue this block's loads before its compute
+      compute(ring[i], i);
+      MOE_WAIT_VMCNT((kD - 2) * kLoads);  // block kb+i+1 has landed
+      barrier_keep_loads();
     }
-    compute(bc, kb & 1);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    bc = bn;
+  }
+  // the last nkb - kb (< kD) blocks were issued kD-1 blocks ahead
+#pragma unroll
+  for (int i = 0; i < kD - 1; ++i) {
+    if (kb + i < nkb) {
+      compute(ring[i], i);
+      __builtin_amdgcn_s_waitcnt(0);
+      barrier_keep_loads();
+    }
+  }
+  // the blocks of a partial last chunk computed above with zero weights: again with their own
+  for (int pb = nfb; pb < nkb; ++pb) {
+    BReg bp;
+    load_b_partial(bp, pb);
+    compute(bp, pb % kD);
   }
 
   // ---- epilogue
