@@ -64,14 +64,15 @@ def streaming_time(bytes_: float, bandwidth: float) -> float:
 
 # ------------------------------------------------------------------ measurement
 
-def measure(layer, xs, steps: int, warmup: int, trace: bool, max_traced: int = 32):
-    """Time `steps` steps between two events; on up to `max_traced` evenly spaced steps the library
-    also records events around the gate/up and down kernels (on the launch stream)."""
+def measure(layers, xs, outs, steps: int, warmup: int, trace: bool, max_traced: int = 32):
+    """Time `steps` eager steps between two events; step i runs layer instance i % len(layers) on
+    batch i % len(xs).  On up to `max_traced` evenly spaced steps the library also records events
+    around the gate/up and down kernels (on the launch stream)."""
     import torch
 
-    R = len(xs)
+    R, L = len(xs), len(layers)
     for i in range(warmup):
-        layer.forward(xs[i % R])
+        layers[i % L].forward(xs[i % R], outs[i % R])
     stride = max(1, steps // max_traced) if trace else steps + 1
     traced = list(range(0, steps, stride)) if trace else []
     ev = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in traced}
@@ -85,7 +86,7 @@ def measure(layer, xs, steps: int, warmup: int, trace: bool, max_traced: int = 3
     wall0 = time.perf_counter()
     t0.record()
     for i in range(steps):
-        layer.forward(xs[i % R], trace=handles.get(i))
+        layers[i % L].forward(xs[i % R], outs[i % R], trace=handles.get(i))
     t1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -93,6 +94,58 @@ def measure(layer, xs, steps: int, warmup: int, trace: bool, max_traced: int = 3
     gu_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in traced]
     dn_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in traced]
     return total_ms, wall, gu_ms, dn_ms, traced
+
+
+def measure_graph(layers, xs, outs, steps: int, warmup: int):
+    """The same step sequence with every step captured once as a HIP graph (one graph per step of
+    a period of the layer and batch rotation) and replayed: exactly `steps` replays are timed.  The
+    host launch overhead and inter-kernel gaps of the eager loop are gone.  Returns ms per step."""
+    import math
+
+    import torch
+
+    R, L = len(xs), len(layers)
+    period = L * R // math.gcd(L, R)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm every instance up off the capture
+        for i in range(period):
+            layers[i % L].forward(xs[i % R], outs[i % R])
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for i in range(period):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            layers[i % L].forward(xs[i % R], outs[i % R])
+        graphs.append(g)
+    for i in range(warmup):
+        graphs[i % period].replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        graphs[i % period].replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1)
+    del graphs
+    return ms / steps
+
+
+def layer_instances(layer, n: int):
+    """`n` layer instances with the same weights at distinct addresses (the first is `layer`): steps
+    rotate through them so that the expert bytes of one step are not still in the 256 MB
+    last-level cache from an earlier one."""
+    from mixture_experts_layer_token_amd.layer import MoeLayer
+
+    out = [layer]
+    for _ in range(n - 1):
+        out.append(MoeLayer(layer.H, layer.I, layer.E, layer.k, layer.fmt, layer.xdt, layer.w_router, layer.bias,
+                            layer.packages.clone(), layer.pkg_stride, layer.shared, max_T=layer.max_T,
+                            device=layer.device))
+    return out
 
 
 def ctypes_arr(trio):
@@ -176,29 +229,37 @@ def run(args):
         args.T = wl.Ts[-1] if prefill else 64
     Ts = sorted(set([args.T] + (list(wl.Ts) if args.sweep and not prefill else [])))
     layer = build_layer(wl, max(Ts))
+    n_inst = args.layers if args.layers is not None else (1 if prefill else DECODE_INSTANCES.get(wl.name, 8))
+    layers = layer_instances(layer, n_inst)
     results = {}
     for T in Ts:
         xs_host = [W.activations(wl, T, 0, 1000 + r) for r in range(args.batches if not prefill else 2)]
         xs = [to_device_act(a, wl.xdt) for a in xs_host]
+        outs = [torch.empty_like(x) for x in xs]
         touched = touched_per_batch(layer, xs, wl.E)
         steps = args.steps if T == args.T else max(20, args.steps // 4)
         if prefill:
             steps = min(steps, args.prefill_steps)
-        total_ms, wall, gu_ms, dn_ms, traced = measure(layer, xs, steps, min(args.warmup, steps), trace=True)
+        total_ms, wall, gu_ms, dn_ms, traced = measure(layers, xs, outs, steps, min(args.warmup, steps), trace=True)
+        graph_ms = (measure_graph(layers, xs, outs, steps, min(args.warmup, steps))
+                    if args.graph and not prefill else None)
         b = [step_bytes(wl, T, touched[i % len(xs)]) for i in range(steps)]
         tot_bytes = sum(x["total"] for x in b)
         gu_bytes = sum(b[i]["gu"] for i in traced)  # bytes of the traced launches only
         dn_bytes = sum(b[i]["down"] for i in traced)
         ms = total_ms / steps
-        results[T] = dict(T=T, ms_per_step=ms, tokens_per_s=T * steps / (total_ms / 1e3),
+        results[T] = dict(T=T, ms_per_step=graph_ms if graph_ms is not None else ms,
+                          tokens_per_s=T / ((graph_ms if graph_ms is not None else ms) / 1e3),
+                          eager_ms_per_step=ms, eager_tokens_per_s=T * steps / (total_ms / 1e3),
                           gu_us=1e3 * float(np.mean(gu_ms)), down_us=1e3 * float(np.mean(dn_ms)),
                           gu_gbps=gu_bytes / (sum(gu_ms) / 1e3) / 1e9,
                           down_gbps=dn_bytes / (sum(dn_ms) / 1e3) / 1e9,
                           ffn_gbps=(gu_bytes + dn_bytes) / ((sum(gu_ms) + sum(dn_ms)) / 1e3) / 1e9,
-                          step_gbps=tot_bytes / (total_ms / 1e3) / 1e9,
+                          step_gbps=tot_bytes / steps / ((graph_ms if graph_ms is not None else ms) / 1e3) / 1e9,
                           touched_mean=float(np.mean(touched)), gu_bytes_per_launch=gu_bytes / len(traced),
                           traced=len(traced),
-                          steps=steps, wall_s=wall, xs_host=xs_host)
+                          steps=steps, wall_s=wall, xs_host=xs_host,
+                          instances=n_inst)
     head = results[args.T]
     if prefill:
         return prefill_report(wl, args, head)
@@ -216,7 +277,11 @@ def run(args):
         "dtype": "bf16" if wl.wfmt != "f32" else "f32",
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights)",
         "config": {"workload": "%s decode" % wl.name, "T": args.T, "hidden": wl.H, "experts": wl.E, "top_k": wl.k,
-                   "inter": wl.I, "weights": wl.wfmt, "activations": wl.xdt},
+                   "inter": wl.I, "weights": wl.wfmt, "activations": wl.xdt,
+                   "launch": "hipGraph replay" if args.graph else "eager",
+                   "layer_instances": head["instances"], "input_batches": args.batches},
+        "eager": {"ms_per_step": round(head["eager_ms_per_step"], 5),
+                  "tokens_per_s": round(head["eager_tokens_per_s"], 2), "steps": args.steps},
         "roofline": {"bound": "hbm", "kernel": "ffn_stream_kernel gate/up (weight-streaming grouped GEMM + SwiGLU)",
                      "achieved": round(head["gu_gbps"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(head["gu_gbps"] / HBM_PEAK_GBS, 4), "traffic": None,
@@ -228,8 +293,8 @@ def run(args):
                        "down_gbps": round(head["down_gbps"], 1)},
         "step_hbm_gbps": round(head["step_gbps"], 1),
         "sweep": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()
-                   if k in ("T", "tokens_per_s", "ms_per_step", "gu_gbps", "down_gbps", "ffn_gbps", "step_gbps",
-                            "touched_mean")} for r in results.values()],
+                   if k in ("T", "tokens_per_s", "ms_per_step", "eager_ms_per_step", "gu_gbps", "down_gbps",
+                            "ffn_gbps", "step_gbps", "touched_mean")} for r in results.values()],
     }
     if args.workload == "mixtral" and args.T == 64:
         rec = profiled_traffic("ffn_gu_mixtral_bf16_decode_T64_traffic.json")
@@ -246,6 +311,9 @@ def run(args):
 
 
 PREFILL = ("kimi",)
+# decode layer instances per workload: enough that the bytes touched between two visits of one
+# instance exceed the 256 MB last-level cache (gpt-oss touches ~53 MB per step at T = 1)
+DECODE_INSTANCES = {"mixtral": 8, "gptoss": 24}
 OFFLOAD = ("glm",)
 PCIE_PEAK_GBS = 64.0  # PCIe 5.0 x16, one direction (the link figure the pages quote)
 
@@ -395,6 +463,10 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--cpu-tokens", type=int, default=16, help="prefill: oracle token sample")
     ap.add_argument("--batches", type=int, default=8, help="distinct input batches the steps rotate through")
+    ap.add_argument("--layers", type=int, default=None,
+                    help="decode: layer instances (same weights, distinct addresses) the steps rotate through")
+    ap.add_argument("--no-graph", dest="graph", action="store_false",
+                    help="decode: report the eager loop only (default: HIP graph replay, eager beside it)")
     ap.add_argument("--no-sweep", dest="sweep", action="store_false")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)

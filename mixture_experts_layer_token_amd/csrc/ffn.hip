@@ -55,11 +55,11 @@ __global__ __launch_bounds__(NW * 64, FMT == MOE_W_BF16 ? 3 : 2) void ffn_stream
   constexpr bool Q4 = FMT != MOE_W_BF16;
   constexpr int SB = FMT == MOE_W_MXFP4 ? 1 : 2;  // scale bytes
   constexpr int KPS = Q4 ? 4 : 1;                 // k-steps per stage
-  __shared__ RowTile tile;
   __shared__ f32x4 red[NW > 1 ? NW * NSTR * 64 : 1];
 
-  if (!find_row_tile(args.offsets, args.E, MR, blockIdx.y, &tile, args.min_rows, args.max_rows)) return;
-  const int e = tile.e, p0 = tile.p0, rows = tile.rows;
+  const int4 tdesc = args.plan[blockIdx.y];  // uniform: one scalar load
+  if (tdesc.x < 0) return;
+  const int p0 = tdesc.y, rows = tdesc.z, slot = tdesc.w;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar addressing
   const int K = GU ? args.H : args.I;
@@ -68,8 +68,6 @@ __global__ __launch_bounds__(NW * 64, FMT == MOE_W_BF16 ? 3 : 2) void ffn_stream
   const int u0 = blockIdx.x * NP;
   const int nks = K / 32;
 
-  const int slot = args.slot_of_expert ? args.slot_of_expert[e] : e;
-  if ((unsigned)slot >= (unsigned)args.n_slots) return;  // workgroup-uniform: not resident, skip
   const char* pkg = args.packages + (size_t)slot * args.pkg_stride;
 
   // strip bases (workgroup-uniform); units past the end repeat the last unit, results dropped
@@ -108,15 +106,17 @@ __global__ __launch_bounds__(NW * 64, FMT == MOE_W_BF16 ? 3 : 2) void ffn_stream
   // for a younger one.  Prefetches past the last stage read the zero page; activation rows past
   // the tile repeat the tile's last row (their output rows are never stored).
   typedef Stage<FMT, NSTR, KPS, MT, OpT> StageT;
-  const unsigned short* arow[MT];
+  // gate/up rows are gathered through perm_src: its load is issued first, so that its latency
+  // overlaps the first stage's weight loads
+  int srow[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int r = min(mt * 16 + (lane & 15), rows - 1);
-    const int src = GU ? args.perm_src[p0 + r] / args.k : p0 + r;
-    arow[mt] = args.a + (size_t)src * K + (lane >> 4) * 8;
+    srow[mt] = GU ? args.perm_src[p0 + r] : p0 + r;
   }
+  const unsigned short* arow[MT];
   // weights are read once per call: non-temporal loads stream them without displacing cached data
-  auto load = [&](StageT& S, int st, bool valid) {
+  auto load_w = [&](StageT& S, int st, bool valid) {
 #pragma unroll
     for (int s = 0; s < NSTR; ++s) {
       const char* cb = valid ? cbase[s] + (size_t)st * 1024 : (const char*)g_zero_page;
@@ -133,12 +133,18 @@ __global__ __launch_bounds__(NW * 64, FMT == MOE_W_BF16 ? 3 : 2) void ffn_stream
         }
       }
     }
+  };
+  auto load_a = [&](StageT& S, int st, bool valid) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const unsigned short* ar = valid ? arow[mt] + KPS * st * 32 : (const unsigned short*)g_zero_page;
 #pragma unroll
       for (int q = 0; q < KPS; ++q) S.a[q][mt] = *(const OpT*)(ar + q * 32);
     }
+  };
+  auto load = [&](StageT& S, int st, bool valid) {
+    load_w(S, st, valid);
+    load_a(S, st, valid);
   };
   auto compute = [&](const StageT& S) {
     if constexpr (!Q4) {
@@ -170,8 +176,13 @@ __global__ __launch_bounds__(NW * 64, FMT == MOE_W_BF16 ? 3 : 2) void ffn_stream
   // software pipeline: a ring of PF stages in registers (the scheduling barriers keep each
   // refill right after the compute that frees its registers)
   StageT ring[PF];
+  load_w(ring[0], st0, 0 < nfull);
 #pragma unroll
-  for (int i = 0; i < PF; ++i) load(ring[i], st0 + i, i < nfull);
+  for (int mt = 0; mt < MT; ++mt)
+    arow[mt] = args.a + (size_t)(GU ? srow[mt] / args.k : srow[mt]) * K + (lane >> 4) * 8;
+  load_a(ring[0], st0, 0 < nfull);
+#pragma unroll
+  for (int i = 1; i < PF; ++i) load(ring[i], st0 + i, i < nfull);
   __builtin_amdgcn_sched_barrier(0);
   int base = 0;
   for (; base + PF <= nfull; base += PF) {
@@ -269,6 +280,44 @@ __global__ __launch_bounds__(NW * 64, FMT == MOE_W_BF16 ? 3 : 2) void ffn_stream
       }
     }
   }
+}
+
+// ------------------------------------------------------------------ row-tile plan
+
+// One workgroup of 1024 threads, thread e for expert e (E <= 1024): experts whose row count lies
+// in [lo, hi] and whose slot is resident are cut into tiles of mr rows, in expert order;
+// plan[i] = {expert, first grouped row, rows, slot}; entries from the last tile up to n_plan
+// get expert -1.
+__global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ offsets, int E, int mr, int lo,
+                                                    int hi, const int32_t* __restrict__ slot_of_expert,
+                                                    int n_slots, int4* __restrict__ plan, int n_plan) {
+  __shared__ int wsum[16];
+  const int e = threadIdx.x, lane = e & 63, wave = e >> 6;
+  int c = 0, o0 = 0, slot = -1;
+  if (e < E) {
+    o0 = offsets[e];
+    c = offsets[e + 1] - o0;
+    slot = slot_of_expert ? slot_of_expert[e] : e;
+    if (c < lo || c > hi || (unsigned)slot >= (unsigned)n_slots) c = 0;
+  }
+  const int nt = (c + mr - 1) / mr;
+  int incl = nt;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int base = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) {
+    base += w < wave ? wsum[w] : 0;
+    total += wsum[w];
+  }
+  const int excl = base + incl - nt;
+  for (int t = 0; t < nt; ++t) plan[excl + t] = make_int4(e, o0 + t * mr, min(mr, c - t * mr), slot);
+  for (int i = total + (int)threadIdx.x; i < n_plan; i += 1024) plan[i] = make_int4(-1, 0, 0, 0);
 }
 
 // ------------------------------------------------------------------ fp32 experts (VALU)
@@ -388,7 +437,7 @@ __global__ void dequant_f32_kernel(const float* __restrict__ pkg, size_t n, floa
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-  size_t cast_off, cast_bytes, h_off, h_bytes, total;
+  size_t cast_off, cast_bytes, h_off, h_bytes, plan_off, plan_bytes, total;
 };
 
 WsLayout ws_layout(const moe_experts* w, int T, int k, int xdt) {
@@ -401,7 +450,10 @@ WsLayout ws_layout(const moe_experts* w, int T, int k, int xdt) {
   L.cast_bytes = cast ? align256((size_t)T * w->H * 2) : 0;
   L.h_off = L.cast_off + L.cast_bytes;
   L.h_bytes = align256(n * w->I * (f32w ? 4 : 2));
-  L.total = L.h_off + L.h_bytes;
+  // row-tile plan of the streaming kernels: at most n / 16 + min(n, E) tiles
+  L.plan_off = L.h_off + L.h_bytes;
+  L.plan_bytes = f32w ? 0 : align256((n / 16 + (n < (size_t)w->E ? n : (size_t)w->E)) * sizeof(int4));
+  L.total = L.plan_off + L.plan_bytes;
   return L;
 }
 
@@ -422,15 +474,37 @@ void trace(int i, hipStream_t s) {
 // 4-bit shapes stay within 256 VGPRs (2 waves per SIMD).
 // NARROW: few experts can be touched (small batches), so the workgroups cover fewer strips and
 // there are enough of them to occupy every CU.
+// (MOE_CFG_* macros override the defaults when tuning.)
+#ifndef MOE_CFG_Q4_GU_NP
+#define MOE_CFG_Q4_GU_NP 2  // 4-bit gate/up units per workgroup at one M tile (wide)
+#endif
+#ifndef MOE_CFG_Q4_D_NP
+#define MOE_CFG_Q4_D_NP 4
+#endif
+#ifndef MOE_CFG_Q4_NW
+#define MOE_CFG_Q4_NW 2
+#endif
+#ifndef MOE_CFG_Q4_PF
+#define MOE_CFG_Q4_PF 2
+#endif
+#ifndef MOE_CFG_BF16_PF
+#define MOE_CFG_BF16_PF 4
+#endif
+#ifndef MOE_CFG_BF16_GU_NW
+#define MOE_CFG_BF16_GU_NW 4
+#endif
+#ifndef MOE_CFG_BF16_D_NW
+#define MOE_CFG_BF16_D_NW 8
+#endif
 template <int FMT, int MT, bool NARROW>
 struct Cfg {
   static constexpr bool Q4 = FMT != MOE_W_BF16;
-  static constexpr int GU_NP = Q4 ? (NARROW ? 1 : (MT == 1 ? 4 : 2)) : 1;
-  static constexpr int GU_NW = 4;
-  static constexpr int GU_PF = Q4 ? 2 : 4;
-  static constexpr int D_NP = Q4 ? (NARROW ? 2 : (MT == 1 ? 8 : 4)) : 2 * MT;
-  static constexpr int D_NW = Q4 ? 4 : 8;
-  static constexpr int D_PF = Q4 ? 2 : 4;
+  static constexpr int GU_NP = Q4 ? (NARROW ? 1 : (MT == 1 ? MOE_CFG_Q4_GU_NP : 2)) : 1;
+  static constexpr int GU_NW = Q4 ? MOE_CFG_Q4_NW : MOE_CFG_BF16_GU_NW;
+  static constexpr int GU_PF = Q4 ? MOE_CFG_Q4_PF : MOE_CFG_BF16_PF;
+  static constexpr int D_NP = Q4 ? (NARROW ? 2 : (MT == 1 ? MOE_CFG_Q4_D_NP : 4)) : 2 * MT;
+  static constexpr int D_NW = Q4 ? MOE_CFG_Q4_NW : MOE_CFG_BF16_D_NW;
+  static constexpr int D_PF = Q4 ? MOE_CFG_Q4_PF : MOE_CFG_BF16_PF;
 };
 
 template <int FMT, int MT, bool NARROW>
@@ -572,6 +646,12 @@ int launch_ffn(const moe_experts* w, const void* x, int xdt, int T, int k, const
   const long long wide_wgs = (long long)nz * ((I / 16 + Cfg<MOE_W_MXFP4, 1, false>::GU_NP - 1) /
                                               Cfg<MOE_W_MXFP4, 1, false>::GU_NP);
   const bool narrow = wide_wgs < 1024;
+  if (use_stream) {
+    int4* plan = (int4*)(wsp + L.plan_off);
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, offsets, E, mr, 1, split, w->slot_of_expert,
+                       gu.n_slots, plan, S);
+    gu_s.plan = dn_s.plan = plan;
+  }
   int rc = MOE_OK;
   if (use_stream) rc = launch_stream_fmt(w->fmt, mt, narrow, true, gu_s, H, I, S, s);
   if (rc == MOE_OK && use_tile) rc = launch_ffn_tile_part(w->fmt, true, gu_t, H, I, (int)n, E, s);

@@ -194,8 +194,20 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
   if (t >= T) return;  // whole wave; no block barrier below
   float* lg = lds + (size_t)wave * E;
   for (int e = lane; e < E; e += 64) {
-    float v = part[(size_t)t * E + e];
-    for (int r = 1; r < KS; ++r) v += part[((size_t)r * T + t) * E + e];
+    // the ranges' partials are loaded 16 at a time (independent loads in flight together), then
+    // summed in range order
+    float v = 0.f;
+    for (int r0 = 0; r0 < KS; r0 += 16) {
+      float pv[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = r0 + i < KS ? r0 + i : r0;
+        pv[i] = part[((size_t)r * T + t) * E + e];
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (r0 + i < KS) v = (r0 + i == 0) ? pv[i] : v + pv[i];
+    }
     v += bias ? bias[e] : 0.f;
     lg[e] = v;
     if (logits) logits[(size_t)t * E + e] = v;
