@@ -181,9 +181,10 @@ int moe_expert_ffn(const moe_experts* w, const void* x, int xdt, int T, int k, c
 
 /*
  * Profiling hook.  While set (on the calling thread), every moe_expert_ffn call records, on its
- * stream, events[0] before its first kernel, events[1] after the gate/up kernel (before the
- * down kernel) and events[2] after the down kernel.  `events` points to 3 hipEvent_t passed as
- * void*; the array is read at each call, so it must stay valid while set.  NULL turns it off.
+ * stream, events[0] right before the gate/up GEMM kernel(s) (after any activation cast and
+ * row-tile planning), events[1] after the gate/up kernel(s) (before the down kernel(s)) and
+ * events[2] after the down kernel(s).  `events` points to 3 hipEvent_t passed as void*; the
+ * array is read at each call, so it must stay valid while set.  NULL turns it off.
  */
 int moe_ffn_trace_events(void* const* events);
 

@@ -578,8 +578,8 @@ int launch_ffn(const moe_experts* w, const void* x, int xdt, int T, int k, const
   FfnArgs dn = gu;
   void* h = wsp + L.h_off;
 
-  trace(0, s);
   if (w->fmt == MOE_W_F32) {
+    trace(0, s);
     const int S = (int)((n + (size_t)(n < (size_t)E ? n : E) * 63) / 64);
     gu.a = (const unsigned short*)x;
     gu.out = h;
@@ -652,6 +652,7 @@ int launch_ffn(const moe_experts* w, const void* x, int xdt, int T, int k, const
                        gu.n_slots, plan, S);
     gu_s.plan = dn_s.plan = plan;
   }
+  trace(0, s);
   int rc = MOE_OK;
   if (use_stream) rc = launch_stream_fmt(w->fmt, mt, narrow, true, gu_s, H, I, S, s);
   if (rc == MOE_OK && use_tile) rc = launch_ffn_tile_part(w->fmt, true, gu_t, H, I, (int)n, E, s);
