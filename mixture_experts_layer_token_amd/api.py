@@ -68,7 +68,11 @@ def moe_permute_workspace(T, k, E) -> int:
 
 
 def moe_permute(topk_ids, E, counts, offsets, perm_src, inv_perm, ws=None, stream=None):
+    """`ws`: device workspace of at least moe_permute_workspace bytes (allocated here if None)."""
     T, k = topk_ids.shape
+    if ws is None:
+        need = moe_permute_workspace(T, k, E)
+        ws = torch.empty(need, dtype=torch.uint8, device=topk_ids.device) if need else None
     check(lib().moe_permute(_dp(topk_ids), T, k, E, _dp(counts), _dp(offsets), _dp(perm_src), _dp(inv_perm),
                             _dp(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
 

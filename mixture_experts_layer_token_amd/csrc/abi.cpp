@@ -72,20 +72,19 @@ extern "C" int moe_route(const void* x, int xdt, int T, int H, const void* w_rou
 }
 
 extern "C" size_t moe_permute_workspace(int T, int k, int E) {
-  (void)T, (void)k, (void)E;
-  return 0;
+  if (T < 0 || k < 1 || E < 1) return 0;
+  return permute_workspace(T, k, E);
 }
 
 extern "C" int moe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t* counts, int32_t* offsets,
                            int32_t* perm_src, int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
   if (T < 0 || k < 1 || k > 16) return fail(MOE_ERR_INVALID, "moe_permute: T=%d k=%d", T, k);
   if (E < 1 || E > 1024) return fail(MOE_ERR_INVALID, "moe_permute: E=%d out of 1..1024", E);
   if ((long long)T * k > (1LL << 24)) return fail(MOE_ERR_INVALID, "moe_permute: T*k too large");
   if (!counts || !offsets) return fail(MOE_ERR_INVALID, "moe_permute: null counts/offsets");
   if (T > 0 && (!topk_ids || !perm_src || !inv_perm)) return fail(MOE_ERR_INVALID, "moe_permute: null pointer");
   if (ws_bytes < moe_permute_workspace(T, k, E)) return fail(MOE_ERR_WORKSPACE, "moe_permute: workspace too small");
-  return launch_permute(topk_ids, T, k, E, counts, offsets, perm_src, inv_perm, (hipStream_t)stream);
+  return launch_permute(topk_ids, T, k, E, counts, offsets, perm_src, inv_perm, ws, ws_bytes, (hipStream_t)stream);
 }
 
 extern "C" size_t moe_ffn_workspace(const moe_experts* w, int T, int k, int mode) {

@@ -24,12 +24,19 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   }
   __syncthreads();
   for (int c = threadIdx.x * 4; c < H; c += blockDim.x * 4) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      f32x4 v = *(const f32x4*)(y + (size_t)rows[j] * H + c);
-      float g = gates[j];
+    // the k rows' loads are issued together, then summed in slot order
+    f32x4 v[16];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc[q] = fmaf(g, v[q], acc[q]);
+    for (int j = 0; j < 16; ++j)
+      if (j < k) v[j] = *(const f32x4*)(y + (size_t)rows[j] * H + c);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (j < k) {
+        const float g = gates[j];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[q] = fmaf(g, v[j][q], acc[q]);
+      }
     }
     if (shared) {
       f32x4 v = *(const f32x4*)(shared + (size_t)t * H + c);

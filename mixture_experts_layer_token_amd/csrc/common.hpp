@@ -94,8 +94,9 @@ bool dtype_valid(int dt);
 size_t route_workspace(int T, int H, int E, int xdt);
 int launch_route(const void* x, int xdt, int T, int H, const void* wg, const float* bias, int E, int k, int32_t* ids,
                  float* w, float* logits, void* ws, size_t ws_bytes, hipStream_t s);
+size_t permute_workspace(int T, int k, int E);
 int launch_permute(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_t* offsets, int32_t* perm,
-                   int32_t* inv, hipStream_t s);
+                   int32_t* inv, void* ws, size_t ws_bytes, hipStream_t s);
 int launch_combine(const float* y, const float* w, const int32_t* inv, int T, int k, int H, const float* shared,
                    void* out, int odt, hipStream_t s);
 int launch_dequant(const void* pkg, int H, int I, int fmt, float* out, hipStream_t s);

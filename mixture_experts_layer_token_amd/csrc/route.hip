@@ -10,7 +10,7 @@
 // fp32 activations: one workgroup per token, fp32 FMA dot products reduced across the wave.
 #include <math.h>
 
-#include "common.hpp"
+#include "ffn_common.hpp"
 
 namespace moe {
 namespace {
@@ -249,7 +249,46 @@ __global__ __launch_bounds__(256) void route_f32_kernel(const float* __restrict_
 
 }  // namespace
 
+// ---- large T: the logits are a dense [T x H] x [H x E] product, computed by the prefill MFMA
+// tile kernel as a "down" projection of one expert whose package is the router matrix in the
+// fragment layout; then the top-k kernel above with one range.
+
+// Wg [E][H] bf16 row-major -> strips of 16 rows, 1 KiB per 32-wide k-step, lane l's 16 bytes =
+// row 16s + l%16, k 32ks + 8(l/16)..+7 (the bf16 package layout); also writes offsets {0, T}.
+__global__ __launch_bounds__(256) void route_pack_kernel(const unsigned short* __restrict__ wg, int H, int E, int T,
+                                                         unsigned short* __restrict__ packed,
+                                                         int32_t* __restrict__ offsets) {
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx == 0) offsets[0] = 0, offsets[1] = T;
+  const size_t per_row = (size_t)H / 8;
+  if (idx >= (size_t)E * per_row) return;
+  const int r = (int)(idx / per_row), k = (int)(idx % per_row) * 8;
+  const int st = r / 16, rr = r % 16, ks = k / 32, q = (k % 32) / 8, nks = H / 32;
+  const uint4 v = *(const uint4*)(wg + (size_t)r * H + k);
+  *(uint4*)(packed + ((size_t)st * nks + ks) * 512 + (rr + 16 * q) * 8) = v;
+}
+
+struct RouteTileWs {
+  size_t packed_off, logits_off, offsets_off, total;
+};
+
+inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool route_tile_path(int T, int H, int E, int xdt) {
+  return xdt == MOE_BF16 && T > kSplitMaxT && H % 32 == 0 && E % 16 == 0 && (double)T * H < 2147483648.0;
+}
+
+RouteTileWs route_tile_ws(int T, int H, int E) {
+  RouteTileWs L;
+  L.packed_off = 0;
+  L.logits_off = al256((size_t)E * H * 2);
+  L.offsets_off = L.logits_off + al256((size_t)T * E * sizeof(float));
+  L.total = L.offsets_off + 256;
+  return L;
+}
+
 size_t route_workspace(int T, int H, int E, int xdt) {
+  if (route_tile_path(T, H, E, xdt)) return route_tile_ws(T, H, E).total;
   if (xdt != MOE_BF16 || T > kSplitMaxT || H % 32) return 0;
   return (size_t)route_split_ranges(T, H, E) * T * E * sizeof(float);
 }
@@ -258,6 +297,37 @@ int launch_route(const void* x, int xdt, int T, int H, const void* wg, const flo
                  float* w, float* logits, void* ws, size_t ws_bytes, hipStream_t s) {
   if (T == 0) return MOE_OK;
   if (E > kMaxE) return fail(MOE_ERR_INVALID, "moe_route: E=%d exceeds %d", E, kMaxE);
+  if (route_tile_path(T, H, E, xdt)) {
+    const RouteTileWs L = route_tile_ws(T, H, E);
+    if (!ws || ws_bytes < L.total) return fail(MOE_ERR_WORKSPACE, "moe_route: workspace %zu < %zu", ws_bytes, L.total);
+    char* wsp = (char*)ws;
+    unsigned short* packed = (unsigned short*)(wsp + L.packed_off);
+    float* lg = (float*)(wsp + L.logits_off);
+    int32_t* offs = (int32_t*)(wsp + L.offsets_off);
+    const size_t chunks = (size_t)E * H / 8;
+    hipLaunchKernelGGL(route_pack_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, s,
+                       (const unsigned short*)wg, H, E, T, packed, offs);
+    FfnArgs a{};
+    a.packages = (const char*)packed;
+    a.pkg_stride = (size_t)E * H * 2;
+    a.slot_of_expert = nullptr;
+    a.n_slots = 1;
+    a.min_rows = 0, a.max_rows = 0x7FFFFFFF;
+    a.offsets = offs;
+    a.perm_src = nullptr;
+    a.a = (const unsigned short*)x;
+    a.out = lg;
+    a.H = E;  // output columns of the "down" projection
+    a.I = H;  // its contraction
+    a.E = 1, a.k = 1;
+    a.region_codes = 0, a.region_scales = 0;
+    int rc = launch_ffn_tile_part(MOE_W_BF16, false, a, E, H, T, 1, s);
+    if (rc != MOE_OK) return rc;
+    hipLaunchKernelGGL(route_topk_kernel, dim3((T + 3) / 4), dim3(256), (size_t)4 * E * sizeof(float), s,
+                       (const float*)lg, bias, T, E, 1, k, ids, w, logits);
+    MOE_CHECK_LAUNCH("moe_route launch");
+    return MOE_OK;
+  }
   if (xdt == MOE_BF16 && H % 32 == 0 && T <= kSplitMaxT) {
     const size_t need = route_workspace(T, H, E, xdt);
     if (!ws || ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "moe_route: workspace %zu < %zu", ws_bytes, need);

@@ -25,7 +25,9 @@ def test_every_header_symbol_is_exported():
 
 
 def test_route_workspace_sizes():
-    assert moe.api.moe_route_workspace(8192, 7168, 384, "bf16") == 0  # large batches: one kernel, no workspace
+    # large bf16 batches: the router matrix repacked for the MFMA tile kernel + [T][E] fp32 logits
+    assert moe.api.moe_route_workspace(8192, 7168, 384, "bf16") == 384 * 7168 * 2 + 8192 * 384 * 4 + 256
+    assert moe.api.moe_route_workspace(300, 64, 24, "bf16") == 0  # E not a multiple of 16: one kernel
     assert moe.api.moe_route_workspace(1, 2880, 128, "bf16") > 0
     assert moe.api.moe_route_workspace(16, 256, 8, "f32") == 0
 
@@ -39,6 +41,13 @@ def test_route_validation():
     assert L.moe_route(None, 7, 4, 64, None, None, 8, 2, None, None, None, None, 0, None) == INVALID
     assert L.moe_route(None, 1, 4, 64, None, None, 8, 2, None, None, None, None, 0, None) == INVALID  # null x
     assert L.moe_route(None, 1, 0, 64, None, None, 8, 2, None, None, None, None, 0, None) == OK  # T = 0: nothing to do
+
+
+def test_permute_workspace_sizes():
+    assert moe.api.moe_permute_workspace(64, 2, 8) == 0  # one workgroup
+    assert moe.api.moe_permute_workspace(1024, 8, 384) == 0
+    assert moe.api.moe_permute_workspace(8192, 8, 384) == 8 * 32 * 384  # 32 blocks of 2048 indices
+    assert moe.api.moe_permute_workspace(1025, 8, 16) == 8 * 5 * 16
 
 
 def test_permute_and_combine_validation():

@@ -103,6 +103,8 @@ ROUTE_CASES = [
     ("tiny", 16, dict(E=1, k=1, name="e1k1")),
     ("tiny", 16, dict(k=8, name="k-eq-e")),
     ("tiny", 37, dict(E=1024, k=16, H=64, name="e1024", xdt="bf16")),
+    ("tiny", 300, dict(E=24, k=3, name="e24-bf16", xdt="bf16")),  # large T, E not a multiple of 16
+    ("tiny", 700, dict(E=48, k=5, H=96, name="e48-bf16", xdt="bf16")),  # large T, ragged 192-row tile
 ]
 
 
@@ -131,7 +133,7 @@ def test_route_exact(name, T, kw):
 # ------------------------------------------------------------------ permutation
 
 PERM_CASES = [(0, 2, 8), (1, 1, 1), (16, 2, 8), (64, 2, 8), (512, 4, 128), (8192, 8, 384), (100, 16, 1024),
-              (333, 3, 7), (4096, 16, 1024)]
+              (333, 3, 7), (4096, 16, 1024), (1025, 8, 16), (2048, 4, 5)]
 
 
 @pytest.mark.parametrize("T,k,E", PERM_CASES)
