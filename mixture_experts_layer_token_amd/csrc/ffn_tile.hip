@@ -26,10 +26,10 @@
 namespace moe {
 namespace {
 
-constexpr int kTW = 8;       // waves per workgroup: 2 (rows) x 4 (columns)
+constexpr int kTW = 4;       // waves per workgroup, one per SIMD; each owns 64 columns
 constexpr int kTM = 192;     // rows per workgroup tile
 constexpr int kTN = 256;     // columns per workgroup tile
-constexpr int kWMT = 6;      // 16-row MFMA tiles per wave (96 rows)
+constexpr int kWMT = 12;     // 16-row MFMA tiles per wave (all 192 rows)
 constexpr int kWNS = 4;      // 16-column strips per wave
 constexpr int kXCD = 8;      // XCDs of an MI355X; workgroup i is dispatched to XCD i % 8
 constexpr int kD = 4;        // pipeline depth: K blocks in flight
@@ -42,8 +42,8 @@ struct TileCfg {
 };
 
 template <int FMT, bool GU>
-// (second bound: minimum waves per SIMD: 2 -> 256 VGPRs per wave)
-__global__ __launch_bounds__(kTW * 64, 2) void ffn_tile_kernel(FfnArgs args) {
+// one wave per SIMD: the 96 accumulator tiles' 192 registers live in the AGPR half of the file
+__global__ __launch_bounds__(kTW * 64, 1) void ffn_tile_kernel(FfnArgs args) {
   typedef typename Op<FMT>::T OpT;
   constexpr int BK = TileCfg<FMT>::BK;
   constexpr int KS = BK / 32;                     // k-steps per block
@@ -67,7 +67,6 @@ __global__ __launch_bounds__(kTW * 64, 2) void ffn_tile_kernel(FfnArgs args) {
   const int nfb = Q4 ? (nks / 4) * 2 : nks;                // blocks in whole package chunks
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / 4, wn = wave % 4;
 
   // ---- row tiles of all experts (wave 0), XCD-aware work item, this workgroup's tile
   int excl = 0, incl = 0, e_begin = 0, e_end = 0;
@@ -123,7 +122,7 @@ __global__ __launch_bounds__(kTW * 64, 2) void ffn_tile_kernel(FfnArgs args) {
   const char* sbase[kWNS];
 #pragma unroll
   for (int j = 0; j < kWNS; ++j) {
-    const int s = min(col * 16 + wn * kWNS + j, n_strips - 1);
+    const int s = min(col * 16 + wave * kWNS + j, n_strips - 1);
     cbase[j] = pkg + args.region_codes + (size_t)s * (Q4 ? 8 : 32) * K;
     sbase[j] = pkg + args.region_scales + (size_t)s * 16 * nks * SB;
   }
@@ -216,6 +215,9 @@ __global__ __launch_bounds__(kTW * 64, 2) void ffn_tile_kernel(FfnArgs args) {
   for (int mt = 0; mt < kWMT; ++mt)
 #pragma unroll
     for (int j = 0; j < kWNS; ++j) acc[mt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // An (empty) use of an accumulation register: without it the compiler keeps the function to
+  // the 256 architectural VGPRs; with it the 192 accumulator registers go to the AGPRs.
+  asm volatile("" ::: "a0");
 
   auto decode = [&](const BReg& B, int j, int q) -> OpT {
     if constexpr (!Q4)
@@ -225,82 +227,96 @@ __global__ __launch_bounds__(kTW * 64, 2) void ffn_tile_kernel(FfnArgs args) {
     else
       return dec_int4(B.v[j][q], __builtin_bit_cast(_Float16, (unsigned short)(B.sc[j] >> (16 * q))));
   };
-  // VALU instructions of one strip's decode, spread over the MFMAs of the strip before it
-  constexpr int kDecV = FMT == MOE_W_INT4G32 ? 15 : (FMT == MOE_W_MXFP4 ? 5 : 0);
-  constexpr int kDecPerMfma = (kDecV + kWMT - 1) / kWMT;
-  auto compute = [&](const BReg& B, int buf) {
-    // A fragment of M tile mt, k-step q: row wm*96 + mt*16 + lane%16, chunk 4q + lane/16
-    const unsigned short* abase = lds_a + ((size_t)buf * kTM + wm * (kWMT * 16) + (lane & 15)) * BK;
+  // A fragment of M tile mt, k-step q of buffer buf: row mt*16 + lane%16, chunk 4q + lane/16
+  auto read_a = [&](OpT (&a)[kWMT], int buf, int q) {
+    const unsigned short* abase = lds_a + ((size_t)buf * kTM + (lane & 15)) * BK;
+    const int slot = (4 * q + (lane >> 4)) ^ (lane & (CPR - 1));
 #pragma unroll
-    for (int q = 0; q < KS; ++q) {
-      // one k-step at a time: keeps the live A fragments to this step's (register budget)
-      if (q) __builtin_amdgcn_sched_barrier(0);
-      const int slot = (4 * q + (lane >> 4)) ^ (lane & (CPR - 1));
-      OpT a[kWMT];
+    for (int mt = 0; mt < kWMT; ++mt) a[mt] = *(const OpT*)(abase + mt * 16 * BK + slot * 8);
+  };
+  // one k-step: strip j's 12 MFMAs run while strip j+1 is decoded
+  auto mfma_step = [&](const BReg& B, const OpT (&a)[kWMT], int q) {
+    OpT b = decode(B, 0, q), bn = b;
 #pragma unroll
-      for (int mt = 0; mt < kWMT; ++mt) a[mt] = *(const OpT*)(abase + mt * 16 * BK + slot * 8);
-      // strip j's MFMAs run while strip j+1 is decoded into the other operand register
-      OpT b = decode(B, 0, q), bn = b;
+    for (int j = 0; j < kWNS; ++j) {
+      if (j + 1 < kWNS) bn = decode(B, j + 1, q);
 #pragma unroll
-      for (int j = 0; j < kWNS; ++j) {
-        if (j + 1 < kWNS) bn = decode(B, j + 1, q);
-#pragma unroll
-        for (int mt = 0; mt < kWMT; ++mt) acc[mt][j] = mfma(a[mt], b, acc[mt][j]);
-        b = bn;
-      }
-      if constexpr (Q4) {  // issue order: A reads, strip 0's decode, then MFMA / decode pairs
-        __builtin_amdgcn_sched_group_barrier(0x100, kWMT, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, kDecV, 0);
-#pragma unroll
-        for (int i = 0; i < (kWNS - 1) * kWMT; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, kDecPerMfma, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, kWMT, 0);
-      }
+      for (int mt = 0; mt < kWMT; ++mt) acc[mt][j] = mfma(a[mt], b, acc[mt][j]);
+      b = bn;
     }
   };
 
-  // ---- K loop: kD blocks in flight.  Block kb issues block kb+kD-1 (activations, then weights)
-  // and computes block kb from LDS buffer kb % kD and register ring entry kb % kD; at its end the
-  // wave waits until only the loads of blocks kb+2 .. kb+kD-1 are outstanding (block kb+1 has
-  // landed), and the barrier publishes block kb+1's buffer to every wave.
+  // ---- K loop: kD blocks in flight.  At the start of block kb a barrier publishes block kb+1's
+  // LDS buffer (every wave has waited for its own loads of it) and retires block kb-1's buffer,
+  // into which block kb+kD-1 is then loaded (activations, then weights).  The A fragments of the
+  // next k-step are read from LDS while the current k-step's MFMAs run, across block edges too
+  // (the next block is already published), so the matrix cores never wait for LDS.
+  static_assert(kD == 4 && (kD * KS) % 2 == 0, "the loop below is unrolled for four blocks");
   constexpr int kLoads = IPW + kWNS * (Q4 ? 2 : KS);  // vector loads per block and wave
   BReg ring[kD];
+  OpT abuf[2][kWMT];
 #pragma unroll
   for (int i = 0; i < kD - 1; ++i) {
     load_a(i, i < nkb ? i : kD);
     load_b(ring[i], i, i < nfb);
   }
-  MOE_WAIT_VMCNT((kD - 2) * kLoads);
+  MOE_WAIT_VMCNT((kD - 2) * kLoads);  // block 0 has landed
   barrier_keep_loads();
+  read_a(abuf[0], 0, 0);
+  // The prologue's loads complete before the loop (once per workgroup): otherwise the compiler,
+  // merging the loop entry with the loop's back edge, waits for every outstanding load at the
+  // first use of a weight register in each iteration.
+  __builtin_amdgcn_s_waitcnt(0);
   int kb = 0;
   for (; kb + kD <= nkb; kb += kD) {
 #pragma unroll
     for (int i = 0; i < kD; ++i) {
-      const int nb = kb + i + kD - 1;  // block to issue
+      // block kb+i+1 landed (own loads), then every wave: its buffer is published and block
+      // kb+i-1's buffer is free
+      MOE_WAIT_VMCNT((kD - 3) * kLoads);
+      barrier_keep_loads();
+      const int nb = kb + i + kD - 1;  // block to issue, into the buffer of block kb+i-1
       load_a(nb, nb < nkb ? (i + kD - 1) % kD : kD);
       load_b(ring[(i + kD - 1) % kD], nb, nb < nfb);
-      __builtin_amdgcn_sched_barrier(0);  // issue this block's loads before its compute
-      compute(ring[i], i);
-      MOE_WAIT_VMCNT((kD - 2) * kLoads);  // block kb+i+1 has landed
-      barrier_keep_loads();
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int q = 0; q < KS; ++q) {
+        // A of the next k-step (the next block's first when q is the last); the register buffer
+        // alternates per k-step, and kD * KS is even, so every block of the loop starts on 0
+        const int step = i * KS + q;
+        const int nbuf = q + 1 < KS ? i : (i + 1) % kD;
+        read_a(abuf[(step + 1) & 1], nbuf, (q + 1) % KS);
+        mfma_step(ring[i], abuf[step & 1], q);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
-  // the last nkb - kb (< kD) blocks were issued kD-1 blocks ahead
+  // the last nkb - kb (< kD) blocks were issued kD-1 blocks ahead; the A fragments of block
+  // kb's first k-step are in abuf[0]
+  __builtin_amdgcn_s_waitcnt(0);
+  barrier_keep_loads();
 #pragma unroll
   for (int i = 0; i < kD - 1; ++i) {
     if (kb + i < nkb) {
-      compute(ring[i], i);
-      __builtin_amdgcn_s_waitcnt(0);
-      barrier_keep_loads();
+#pragma unroll
+      for (int q = 0; q < KS; ++q) {
+        const int step = i * KS + q;
+        const int nbuf = q + 1 < KS ? i : (i + 1) % kD;
+        read_a(abuf[(step + 1) & 1], nbuf, (q + 1) % KS);
+        mfma_step(ring[i], abuf[step & 1], q);
+      }
     }
   }
   // the blocks of a partial last chunk computed above with zero weights: again with their own
   for (int pb = nfb; pb < nkb; ++pb) {
     BReg bp;
     load_b_partial(bp, pb);
-    compute(bp, pb % kD);
+#pragma unroll
+    for (int q = 0; q < KS; ++q) {
+      OpT a[kWMT];
+      read_a(a, pb % kD, q);
+      mfma_step(bp, a, q);
+    }
   }
 
   // ---- epilogue
@@ -308,13 +324,13 @@ __global__ __launch_bounds__(kTW * 64, 2) void ffn_tile_kernel(FfnArgs args) {
   for (int mt = 0; mt < kWMT; ++mt) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int row = wm * (kWMT * 16) + mt * 16 + (lane >> 4) * 4 + r;
+      const int row = mt * 16 + (lane >> 4) * 4 + r;
       if (row >= rows) continue;
       const size_t pr = (size_t)(p0 + row);
       if constexpr (GU) {
 #pragma unroll
         for (int j = 0; j < kWNS; j += 2) {
-          const int gs = col * 16 + wn * kWNS + j;  // gate strip 2u, up strip 2u + 1
+          const int gs = col * 16 + wave * kWNS + j;  // gate strip 2u, up strip 2u + 1
           if (gs + 1 >= n_strips) continue;
           const int f = (gs >> 1) * 16 + (lane & 15);
           const float hv = silu(acc[mt][j][r]) * acc[mt][j + 1][r];
@@ -328,7 +344,7 @@ __global__ __launch_bounds__(kTW * 64, 2) void ffn_tile_kernel(FfnArgs args) {
       } else {
 #pragma unroll
         for (int j = 0; j < kWNS; ++j) {
-          const int s = col * 16 + wn * kWNS + j;
+          const int s = col * 16 + wave * kWNS + j;
           if (s >= n_strips) continue;
           ((float*)args.out)[pr * args.H + s * 16 + (lane & 15)] = acc[mt][j][r];
         }
