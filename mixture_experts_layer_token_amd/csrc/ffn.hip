@@ -468,10 +468,11 @@ void trace(int i, hipStream_t s) {
 }
 
 // Tile shapes per format and M-tile count: (units per workgroup, waves, pipeline depth) for
-// gate/up and down.  bf16 fragments are 1 KiB per strip and k-step, so a few strips already keep
-// enough bytes in flight; 4-bit fragments are 4x smaller, so a workgroup covers more strips,
-// which also lets one activation fragment feed more weight fragments (less L2 traffic).  The
-// 4-bit shapes stay within 256 VGPRs (2 waves per SIMD).
+// gate/up and down, chosen by measurement on MI355X.  bf16 fragments are 1 KiB per strip and
+// k-step, so a few strips already keep enough bytes in flight; at two M tiles a workgroup covers
+// two units, so one activation fragment feeds twice the weight bytes (L2 traffic of the
+// activations stays half the weight traffic).  4-bit fragments are 4x smaller; the 4-bit shapes
+// stay within 256 VGPRs (2 waves per SIMD).
 // NARROW: few experts can be touched (small batches), so the workgroups cover fewer strips and
 // there are enough of them to occupy every CU.
 // (MOE_CFG_* macros override the defaults when tuning.)
@@ -487,8 +488,11 @@ void trace(int i, hipStream_t s) {
 #ifndef MOE_CFG_Q4_PF
 #define MOE_CFG_Q4_PF 2
 #endif
-#ifndef MOE_CFG_BF16_PF
-#define MOE_CFG_BF16_PF 4
+#ifndef MOE_CFG_BF16_GU_PF
+#define MOE_CFG_BF16_GU_PF 2
+#endif
+#ifndef MOE_CFG_BF16_D_PF
+#define MOE_CFG_BF16_D_PF 4
 #endif
 #ifndef MOE_CFG_BF16_GU_NW
 #define MOE_CFG_BF16_GU_NW 4
@@ -496,15 +500,18 @@ void trace(int i, hipStream_t s) {
 #ifndef MOE_CFG_BF16_D_NW
 #define MOE_CFG_BF16_D_NW 8
 #endif
+#ifndef MOE_CFG_BF16_GU_NP2
+#define MOE_CFG_BF16_GU_NP2 2  // bf16 gate/up units per workgroup at two M tiles
+#endif
 template <int FMT, int MT, bool NARROW>
 struct Cfg {
   static constexpr bool Q4 = FMT != MOE_W_BF16;
-  static constexpr int GU_NP = Q4 ? (NARROW ? 1 : (MT == 1 ? MOE_CFG_Q4_GU_NP : 2)) : 1;
+  static constexpr int GU_NP = Q4 ? (NARROW ? 1 : (MT == 1 ? MOE_CFG_Q4_GU_NP : 2)) : (MT == 1 ? 1 : MOE_CFG_BF16_GU_NP2);
   static constexpr int GU_NW = Q4 ? MOE_CFG_Q4_NW : MOE_CFG_BF16_GU_NW;
-  static constexpr int GU_PF = Q4 ? MOE_CFG_Q4_PF : MOE_CFG_BF16_PF;
+  static constexpr int GU_PF = Q4 ? MOE_CFG_Q4_PF : MOE_CFG_BF16_GU_PF;
   static constexpr int D_NP = Q4 ? (NARROW ? 2 : (MT == 1 ? MOE_CFG_Q4_D_NP : 4)) : 2 * MT;
   static constexpr int D_NW = Q4 ? MOE_CFG_Q4_NW : MOE_CFG_BF16_D_NW;
-  static constexpr int D_PF = Q4 ? MOE_CFG_Q4_PF : MOE_CFG_BF16_PF;
+  static constexpr int D_PF = Q4 ? MOE_CFG_Q4_PF : MOE_CFG_BF16_D_PF;
 };
 
 template <int FMT, int MT, bool NARROW>
