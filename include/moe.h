@@ -88,8 +88,8 @@ const char* moe_last_error(void);
 int moe_route(const void* x, int xdt, int T, int H, const void* w_router, const float* bias, int E, int k,
               int32_t* topk_ids, float* topk_w, float* logits, void* ws, size_t ws_bytes, void* stream);
 
-/* Workspace bytes moe_route needs (device, 256-byte aligned; 0 when none).  Small batches (bf16,
- * T <= 256) spread the router over many workgroups and keep partial logits there; large bf16
+/* Workspace bytes moe_route needs (device, 256-byte aligned; 0 when none).  bf16 batches with
+ * T*E <= 2^20 spread the router over many workgroups and keep partial logits there; larger bf16
  * batches with E a multiple of 16 keep the router matrix repacked into MFMA fragments
  * (E*H*2 bytes) and the [T][E] fp32 logits there. */
 size_t moe_route_workspace(int T, int H, int E, int xdt);

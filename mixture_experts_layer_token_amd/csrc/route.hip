@@ -18,7 +18,10 @@ namespace {
 constexpr int kRouteTokens = 16;    // tokens per workgroup (MFMA M)
 constexpr int kTilesPerPass = 8;    // 16-expert tiles each wave accumulates per pass over H
 constexpr int kMaxE = 1024;
-constexpr int kSplitMaxT = 256;  // tokens up to which the router is split over workgroups
+// The router is split over workgroups (16 x 16 logit tiles, K ranges) while T * E <= kSplitMaxTE:
+// each workgroup re-reads its 16 rows of x and of Wg from L2, which is cheap until the product
+// is large; larger batches use the MFMA tile kernel (one read per 192 x 256 tile).
+constexpr long long kSplitMaxTE = 1 << 20;
 
 // (value, id) ordering of the router: larger value first, equal values -> lower id first
 __device__ __forceinline__ bool better(float v, int e, float bv, int be) { return v > bv || (v == bv && e < be); }
@@ -274,8 +277,13 @@ struct RouteTileWs {
 
 inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+bool route_split_path(int T, int H, int E, int xdt) {
+  return xdt == MOE_BF16 && H % 32 == 0 && (long long)T * E <= kSplitMaxTE;
+}
+
 bool route_tile_path(int T, int H, int E, int xdt) {
-  return xdt == MOE_BF16 && T > kSplitMaxT && H % 32 == 0 && E % 16 == 0 && (double)T * H < 2147483648.0;
+  return xdt == MOE_BF16 && !route_split_path(T, H, E, xdt) && H % 32 == 0 && E % 16 == 0 &&
+         (double)T * H < 2147483648.0;
 }
 
 RouteTileWs route_tile_ws(int T, int H, int E) {
@@ -289,7 +297,7 @@ RouteTileWs route_tile_ws(int T, int H, int E) {
 
 size_t route_workspace(int T, int H, int E, int xdt) {
   if (route_tile_path(T, H, E, xdt)) return route_tile_ws(T, H, E).total;
-  if (xdt != MOE_BF16 || T > kSplitMaxT || H % 32) return 0;
+  if (!route_split_path(T, H, E, xdt)) return 0;
   return (size_t)route_split_ranges(T, H, E) * T * E * sizeof(float);
 }
 
@@ -328,7 +336,7 @@ int launch_route(const void* x, int xdt, int T, int H, const void* wg, const flo
     MOE_CHECK_LAUNCH("moe_route launch");
     return MOE_OK;
   }
-  if (xdt == MOE_BF16 && H % 32 == 0 && T <= kSplitMaxT) {
+  if (route_split_path(T, H, E, xdt)) {
     const size_t need = route_workspace(T, H, E, xdt);
     if (!ws || ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "moe_route: workspace %zu < %zu", ws_bytes, need);
     const int KS = route_split_ranges(T, H, E);

@@ -65,8 +65,7 @@ class MoeLayer:
         pws = api.moe_permute_workspace(T, k, E)
         self.pws = torch.empty(pws, dtype=torch.uint8, device=d) if pws else None
         # every batch size up to T may be routed with this buffer
-        # (above 256 tokens the need grows with T, so T itself bounds it)
-        rws = max(api.moe_route_workspace(t, H, E, self.xdt) for t in list(range(1, min(T, 256) + 1)) + [T])
+        rws = max(api.moe_route_workspace(t, H, E, self.xdt) for t in range(1, T + 1))
         self.rws = torch.empty(max(rws, 256), dtype=torch.uint8, device=d)
 
     def forward(self, x: torch.Tensor, out: torch.Tensor | None = None, mode="auto", trace=None) -> torch.Tensor:
