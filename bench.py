@@ -315,6 +315,35 @@ PREFILL = ("kimi",)
 # instance exceed the 256 MB last-level cache (gpt-oss touches ~53 MB per step at T = 1)
 DECODE_INSTANCES = {"mixtral": 8, "gptoss": 24}
 OFFLOAD = ("glm",)
+# cache policies the offload run compares (the last one is the reported value): the plain LRU, and
+# use counts halved every 32 lookup groups (4 steps of the 8 layers)
+POLICIES = (("lru", 0), ("lfu_decay", 32))
+
+
+def belady_hits(capacity: int, groups) -> int:
+    """Hits of Belady's MIN over the same lookup groups (upper bound for any policy): a miss with a
+    full cache evicts the resident key whose next use lies farthest ahead."""
+    nxt = [dict() for _ in groups]  # per group: key -> index of its next group
+    later = {}
+    for g in range(len(groups) - 1, -1, -1):
+        for key in groups[g]:
+            nxt[g][key] = later.get(key, 1 << 60)
+        for key in groups[g]:
+            later[key] = g
+    resident, nu, hits = set(), {}, 0
+    for g, grp in enumerate(groups):
+        cur = set(grp)
+        for key in sorted(cur):
+            if key in resident:
+                hits += 1
+            else:
+                if len(resident) >= capacity:
+                    victim = max((k for k in resident if k not in cur), key=lambda k: (nu[k], k))
+                    resident.discard(victim)
+                resident.add(key)
+        for key in cur:
+            nu[key] = nxt[g][key]
+    return hits
 PCIE_PEAK_GBS = 64.0  # PCIe 5.0 x16, one direction (the link figure the pages quote)
 
 
@@ -332,7 +361,7 @@ def run_offload(args):
     steps = min(args.offload_steps, wl.steps)
     Ts = [args.T] if args.T else [16, 1]
     model = OffloadedModel(wl, max(Ts), fill=False)
-    runs = {}
+    runs, belady = {}, {}
     for T in Ts:
         xs = {(l, s): to_device_act(W.activations(wl, T, l, s), wl.xdt) for s in range(steps) for l in range(wl.layers)}
         # route every (step, layer) once to know which experts the run touches; only those packages are
@@ -346,43 +375,46 @@ def run_offload(args):
         for l in range(wl.layers):
             model.fill(l, touched[l] - model.filled.get(l, set()))
             model.filled[l] = model.filled.get(l, set()) | touched[l]
-        model.reset_cache()
         out = torch.empty((T, wl.H), dtype=torch.bfloat16, device="cuda")
+        model.reset_cache()
         for l in range(wl.layers):  # warm the kernels through the full path (the cache is reset below)
             model.layer_forward(l, 0, xs[(l, 0)], out)
-        model.reset_cache()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for s in range(steps):
-            for l in range(wl.layers):
-                model.layer_forward(l, s, xs[(l, s)], out, time_copies=True)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        st = model.cache.stats()
-        plans = model.plans
-        seen, cold = set(), 0
-        per_epoch = {}
-        for (s, l, n, h, m) in plans:
-            ep = s // wl.rerank_every
-            a = per_epoch.setdefault(ep, [0, 0])
-            a[0] += h
-            a[1] += n
-        # compulsory misses: first lookup of each (layer, expert) key
-        for (s, l, n, h, m), grp in zip(plans, model.groups):
-            for key in grp:
-                if key not in seen:
-                    seen.add(key)
-                    cold += 1
-        runs[T] = {"T": T, "steps": steps, "layers": wl.layers, "wall_s": wall,
-                   "tokens_per_s": T * steps / wall,
-                   "hit_rate": st["hits"] / max(1, st["lookups"]),
-                   "hit_rate_cold_excluded": st["hits"] / max(1, st["lookups"] - cold),
-                   "hit_rate_per_epoch": [round(v[0] / max(1, v[1]), 4) for _, v in sorted(per_epoch.items())],
-                   "lookups": st["lookups"], "misses": st["misses"], "bytes_fetched": st["bytes_fetched"],
-                   "copy_busy_s": model.copy_ms / 1e3,
-                   "link_gbps_busy": st["bytes_fetched"] / max(1e-9, model.copy_ms / 1e3) / 1e9,
-                   "link_gbps_wall": st["bytes_fetched"] / wall / 1e9}
-    head = runs[Ts[0]]
+        for policy, period in POLICIES:
+            model.reset_cache(policy, period)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for s in range(steps):
+                for l in range(wl.layers):
+                    model.layer_forward(l, s, xs[(l, s)], out, time_copies=True)
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
+            st = model.cache.stats()
+            plans = model.plans
+            seen, cold = set(), 0
+            per_epoch = {}
+            for (s, l, n, h, m) in plans:
+                ep = s // wl.rerank_every
+                a = per_epoch.setdefault(ep, [0, 0])
+                a[0] += h
+                a[1] += n
+            # compulsory misses: first lookup of each (layer, expert) key
+            for (s, l, n, h, m), grp in zip(plans, model.groups):
+                for key in grp:
+                    if key not in seen:
+                        seen.add(key)
+                        cold += 1
+            runs[(T, policy)] = {
+                "T": T, "policy": policy if policy == "lru" else "%s/%d" % (policy, period), "steps": steps,
+                "layers": wl.layers, "wall_s": wall, "tokens_per_s": T * steps / wall,
+                "hit_rate": st["hits"] / max(1, st["lookups"]),
+                "hit_rate_cold_excluded": st["hits"] / max(1, st["lookups"] - cold),
+                "hit_rate_per_epoch": [round(v[0] / max(1, v[1]), 4) for _, v in sorted(per_epoch.items())],
+                "hit_rate_belady": belady.setdefault(T, belady_hits(model.capacity, model.groups)) / max(1, st["lookups"]),
+                "lookups": st["lookups"], "misses": st["misses"], "bytes_fetched": st["bytes_fetched"],
+                "copy_busy_s": model.copy_ms / 1e3,
+                "link_gbps_busy": st["bytes_fetched"] / max(1e-9, model.copy_ms / 1e3) / 1e9,
+                "link_gbps_wall": st["bytes_fetched"] / wall / 1e9}
+    head = runs[(Ts[0], POLICIES[-1][0])]
     out = {
         "metric": "MoE-layer tokens/s (offloaded expert bank, decode) + expert-cache hit rate + link GB/s",
         "value": round(head["tokens_per_s"], 2),
@@ -398,7 +430,7 @@ def run_offload(args):
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights quantized to int4g32)",
         "config": {"workload": wl.name, "T": Ts[0], "layers": wl.layers, "hidden": wl.H, "experts": wl.E,
                    "top_k": wl.k, "inter": wl.I, "cache_slots": model.capacity,
-                   "bank_bytes": wl.layers * wl.E * model.pkg_bytes},
+                   "cache_policy": head["policy"], "bank_bytes": wl.layers * wl.E * model.pkg_bytes},
         "roofline": {"bound": "link", "kernel": "hipMemcpyAsync host bank -> HBM slots (copy stream)",
                      "achieved": round(head["link_gbps_busy"], 2), "peak": PCIE_PEAK_GBS, "unit": "GB/s",
                      "frac": round(head["link_gbps_busy"] / PCIE_PEAK_GBS, 4), "traffic": None},

@@ -214,10 +214,16 @@ int moe_combine(const float* y_perm, const float* topk_w, const int32_t* inv_per
  * offloading actually costs", "Inside expert paging": stable logical slots over moving
  * physical residency; theflow.svmpsp.dev related-abstracts list: an LRU cache serves
  * most expert lookups).  Keys are (layer, expert); one global pool of `capacity` slots.
- * Policy: least recently used.  Lookups come in groups (one layer of one step); duplicate
- * ids in a group count once; a distinct id found resident is a hit; every id of the group
- * gets the group's tick; a miss evicts the resident key not in the current group with the
- * smallest (tick, layer*E + expert).  The cache starts empty.
+ * Lookups come in groups (one layer of one step; group g = the g-th moe_cache_plan call,
+ * from 0); duplicate ids in a group count once; a distinct id found resident is a hit;
+ * every id of the group gets tick g.  The cache starts empty.  A miss evicts a resident key
+ * not in the current group:
+ *   MOE_CACHE_LRU (0): the one with the smallest (tick, layer*E + expert);
+ *   MOE_CACHE_LFU_DECAY (1): every key carries a use count; at the start of group g, when
+ *     decay_period > 0, g > 0 and g % decay_period == 0, every count is halved (integer
+ *     shift); then every key of the group gains 1024; the victim is the one with the
+ *     smallest (count, tick, layer*E + expert).  Under a skewed, slowly drifting expert
+ *     popularity this keeps the popular experts resident through bursts of one-off lookups.
  *
  * The cache object keeps the two pointers of its descriptor (it does not own them) and is
  * host-side state with a single owner (not thread-safe).
@@ -231,7 +237,11 @@ typedef struct {
   void* device_pool;     /* device: capacity slots, slot_stride bytes apart */
   size_t slot_stride;    /* >= pkg_bytes, multiple of 256 */
   int capacity;          /* number of slots (1 .. L*E) */
+  int policy;            /* MOE_CACHE_LRU or MOE_CACHE_LFU_DECAY */
+  int decay_period;      /* LFU_DECAY: groups between halvings of the counts (0: never) */
 } moe_cache_desc;
+
+enum { MOE_CACHE_LRU = 0, MOE_CACHE_LFU_DECAY = 1 };
 
 typedef struct {
   int layer;
@@ -256,7 +266,7 @@ int moe_cache_create(const moe_cache_desc* desc, moe_cache_t** out);
 
 /*
  * Host only, synchronous: look up the n expert ids host_ids[0..n) of `layer` (the ids a
- * router chose, already copied to the host), update LRU state and fill *plan.
+ * router chose, already copied to the host), update the policy state and fill *plan.
  * Errors: MOE_ERR_INVALID (bad layer, id outside [0, E), n < 0), MOE_ERR_CAPACITY if the
  * group has more distinct ids than the cache has slots (state is then unchanged).
  */

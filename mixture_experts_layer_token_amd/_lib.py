@@ -23,7 +23,7 @@ class MoeExperts(ctypes.Structure):
 
 class MoeCacheDesc(ctypes.Structure):
     _fields_ = [("host_bank", vp), ("pkg_bytes", c_size_t), ("L", c_int), ("E", c_int), ("device_pool", vp),
-                ("slot_stride", c_size_t), ("capacity", c_int)]
+                ("slot_stride", c_size_t), ("capacity", c_int), ("policy", c_int), ("decay_period", c_int)]
 
 
 class MoeCachePlan(ctypes.Structure):

@@ -17,6 +17,7 @@ from ._lib import MoeCacheDesc, MoeCachePlan, MoeCacheStats, MoeExperts, check, 
 FMT = {"f32": 0, "bf16": 1, "mxfp4": 2, "int4g32": 3}
 DT = {"f32": 0, "bf16": 1}
 MODE = {"auto": 0, "decode": 1, "prefill": 2}
+POLICY = {"lru": 0, "lfu_decay": 1}
 TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 
@@ -130,12 +131,14 @@ def moe_combine(y_perm, topk_w, inv_perm, k, shared_y, out, stream=None):
 class ExpertCache:
     """Owner of a moe_cache_t.  `bank` (pinned host tensor) and `pool` (device tensor) must outlive it."""
 
-    def __init__(self, bank, pkg_bytes, L, E, pool, slot_stride, capacity):
+    def __init__(self, bank, pkg_bytes, L, E, pool, slot_stride, capacity, policy="lru", decay_period=0):
         d = MoeCacheDesc()
         d.host_bank = bank.data_ptr() if bank is not None else None
         d.pkg_bytes, d.L, d.E = pkg_bytes, L, E
         d.device_pool = pool.data_ptr() if pool is not None else None
         d.slot_stride, d.capacity = slot_stride, capacity
+        d.policy = POLICY[policy]
+        d.decay_period = decay_period
         self._keep = (bank, pool)
         h = ctypes.c_void_p()
         check(lib().moe_cache_create(ctypes.byref(d), ctypes.byref(h)))

@@ -10,6 +10,7 @@
 // hipMemcpyAsync from the page-locked bank plus one small copy of the slot table.
 #include <algorithm>
 #include <set>
+#include <tuple>
 #include <utility>
 #include <vector>
 
@@ -22,6 +23,8 @@ struct moe_cache {
   std::vector<int64_t> last;                 // key -> tick of last use
   std::vector<int32_t> key_of_slot;          // slot -> key, -1 if free
   std::set<std::pair<int64_t, int32_t>> lru;  // (tick, key) of resident keys
+  std::vector<int64_t> count;                 // key -> use count (LFU_DECAY)
+  std::set<std::tuple<int64_t, int64_t, int32_t>> lfu;  // (count, tick, key) of resident keys
   std::set<int32_t> free_slots;
   moe_cache_stats_t st{};
 };
@@ -35,6 +38,9 @@ extern "C" int moe_cache_create(const moe_cache_desc* desc, moe_cache_t** out) {
   if (d.capacity < 1 || (int64_t)d.capacity > (int64_t)d.L * d.E)
     return fail(MOE_ERR_INVALID, "moe_cache_create: capacity %d out of 1..L*E", d.capacity);
   if (d.pkg_bytes == 0) return fail(MOE_ERR_INVALID, "moe_cache_create: pkg_bytes 0");
+  if (d.policy != MOE_CACHE_LRU && d.policy != MOE_CACHE_LFU_DECAY)
+    return fail(MOE_ERR_INVALID, "moe_cache_create: policy %d", d.policy);
+  if (d.decay_period < 0) return fail(MOE_ERR_INVALID, "moe_cache_create: decay_period %d", d.decay_period);
   // host_bank == NULL and device_pool == NULL: planning-only cache (moe_cache_fetch refuses it)
   if ((d.host_bank == nullptr) != (d.device_pool == nullptr))
     return fail(MOE_ERR_INVALID, "moe_cache_create: host_bank and device_pool must both be set (or both NULL)");
@@ -52,6 +58,7 @@ extern "C" int moe_cache_create(const moe_cache_desc* desc, moe_cache_t** out) {
   c->d = d;
   c->slot_of.assign((size_t)d.L * d.E, -1);
   c->last.assign((size_t)d.L * d.E, -1);
+  c->count.assign((size_t)d.L * d.E, 0);
   c->key_of_slot.assign(d.capacity, -1);
   for (int s = 0; s < d.capacity; ++s) c->free_slots.insert(s);
   *out = c;
@@ -73,9 +80,21 @@ extern "C" int moe_cache_plan(moe_cache_t* c, int layer, const int32_t* host_ids
 
   const int64_t g = c->tick++;
   const int32_t kbase = layer * E;
+  const bool lfu = c->d.policy == MOE_CACHE_LFU_DECAY;
   auto in_group = [&](int32_t key) {
     return key >= kbase && key < kbase + E && std::binary_search(ids.begin(), ids.end(), key - kbase);
   };
+  if (lfu) {
+    // decay, then this group's uses; the resident order is rebuilt (halving can create ties)
+    if (c->d.decay_period > 0 && g > 0 && g % c->d.decay_period == 0)
+      for (int64_t& v : c->count) v >>= 1;
+    for (int32_t id : ids) c->count[kbase + id] += 1024;
+    c->lfu.clear();
+    for (int s = 0; s < c->d.capacity; ++s) {
+      const int32_t key = c->key_of_slot[s];
+      if (key >= 0) c->lfu.insert({c->count[key], c->last[key], key});
+    }
+  }
   plan->layer = layer;
   plan->n_ids = (int)ids.size();
   plan->n_hits = plan->n_misses = 0;
@@ -83,20 +102,33 @@ extern "C" int moe_cache_plan(moe_cache_t* c, int layer, const int32_t* host_ids
     const int32_t key = kbase + id;
     if (c->slot_of[key] >= 0) {
       plan->n_hits++;
-      c->lru.erase({c->last[key], key});
+      if (lfu)
+        c->lfu.erase({c->count[key], c->last[key], key});
+      else
+        c->lru.erase({c->last[key], key});
     } else {
       int32_t slot;
       if (!c->free_slots.empty()) {
         slot = *c->free_slots.begin();
         c->free_slots.erase(c->free_slots.begin());
       } else {
-        auto it = c->lru.begin();
-        while (it != c->lru.end() && in_group(it->second)) ++it;
-        // cannot be end(): distinct ids <= capacity and every slot is taken
-        const int32_t victim = it->second;
+        // the first resident key not in the group (cannot run out: distinct ids <= capacity
+        // and every slot is taken)
+        int32_t victim;
+        if (lfu) {
+          auto it = c->lfu.begin();
+          while (it != c->lfu.end() && in_group(std::get<2>(*it))) ++it;
+          victim = std::get<2>(*it);
+          c->lfu.erase(it);
+        } else {
+          auto it = c->lru.begin();
+          while (it != c->lru.end() && in_group(it->second)) ++it;
+          victim = it->second;
+          c->lru.erase(it);
+        }
         slot = c->slot_of[victim];
         c->slot_of[victim] = -1;
-        c->lru.erase(it);
+        c->key_of_slot[slot] = -1;
         c->st.evictions++;
       }
       c->slot_of[key] = slot;
@@ -106,7 +138,10 @@ extern "C" int moe_cache_plan(moe_cache_t* c, int layer, const int32_t* host_ids
       plan->n_misses++;
     }
     c->last[key] = g;
-    c->lru.insert({g, key});
+    if (lfu)
+      c->lfu.insert({c->count[key], g, key});
+    else
+      c->lru.insert({g, key});
   }
   for (int e = 0; e < E; ++e) plan->slot_of_expert[e] = c->slot_of[kbase + e];
   c->st.lookups += plan->n_ids;

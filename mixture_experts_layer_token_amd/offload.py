@@ -58,7 +58,8 @@ class PinnedBuffer:
 class OffloadedModel:
     """L MoE layers whose experts live in a pinned host bank, cached in an HBM slot pool."""
 
-    def __init__(self, wl, max_T: int, capacity: int | None = None, device="cuda", fill=True):
+    def __init__(self, wl, max_T: int, capacity: int | None = None, device="cuda", fill=True, policy="lru",
+                 decay_period=0):
         from synth import workloads as W
 
         self.wl = wl
@@ -71,8 +72,9 @@ class OffloadedModel:
             for l in range(self.L):
                 self.fill(l, list(range(self.E)))
         self.pool = torch.empty((self.capacity, self.stride), dtype=torch.uint8, device=device)
+        self.policy, self.decay_period = policy, decay_period
         self.cache = api.ExpertCache(self.bank, self.pkg_bytes, self.L, self.E, self.pool, self.stride,
-                                     self.capacity)
+                                     self.capacity, policy, decay_period)
         self.slot_tables = [torch.full((self.E,), -1, dtype=torch.int32, device=device) for _ in range(self.L)]
         self.wg = [to_device_act(W.router_weights(wl, l), wl.xdt, device) for l in range(self.L)]
         self.bias_cache = {}
@@ -93,11 +95,15 @@ class OffloadedModel:
         self.groups = []
         self.filled = {}
 
-    def reset_cache(self):
-        """Empty the HBM cache (a new planner) and the run records."""
+    def reset_cache(self, policy=None, decay_period=None):
+        """Empty the HBM cache (a new planner, optionally with another policy) and the run records."""
+        if policy is not None:
+            self.policy = policy
+        if decay_period is not None:
+            self.decay_period = decay_period
         self.cache.close()
         self.cache = api.ExpertCache(self.bank, self.pkg_bytes, self.L, self.E, self.pool, self.stride,
-                                     self.capacity)
+                                     self.capacity, self.policy, self.decay_period)
         for t in self.slot_tables:
             t.fill_(-1)
         self.plans, self.groups, self.copy_ms = [], [], 0.0

@@ -57,6 +57,8 @@ def lib():
         L.oracle_moe_layer.restype = i32
         L.oracle_lru.argtypes = [i64, i64, vp, vp, vp, vp, vp, vp]
         L.oracle_lru.restype = i32
+        L.oracle_lfu_decay.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, vp]
+        L.oracle_lfu_decay.restype = i32
         L.oracle_belady.argtypes = [i64, i64, vp, vp, vp, vp]
         L.oracle_belady.restype = i32
         for f in ("oracle_decode", "oracle_decode_act", "oracle_router_logits", "oracle_topk_gates",
@@ -178,6 +180,22 @@ def lru(capacity: int, groups):
     victims = np.zeros(max(len(keys), 1), np.int64)
     nv = np.zeros(G, np.int64)
     rc = lib().oracle_lru(capacity, G, _p(off), _p(keys), _p(hits), _p(misses), _p(victims), _p(nv))
+    if rc != 0:
+        raise ValueError("a group holds more distinct keys than the capacity")
+    vo = np.concatenate([[0], np.cumsum(nv)])
+    return hits, misses, [victims[vo[g]:vo[g + 1]].copy() for g in range(G)]
+
+
+def lfu_decay(capacity: int, period: int, groups):
+    """Use counts with decay (+1024 per group a key appears in, halved every `period` groups);
+    victim = smallest (count, last use, key) not in the group -> (hits[g], misses[g], victims)."""
+    off, keys = _groups(groups)
+    G = len(groups)
+    hits = np.zeros(G, np.int64)
+    misses = np.zeros(G, np.int64)
+    victims = np.zeros(max(len(keys), 1), np.int64)
+    nv = np.zeros(G, np.int64)
+    rc = lib().oracle_lfu_decay(capacity, period, G, _p(off), _p(keys), _p(hits), _p(misses), _p(victims), _p(nv))
     if rc != 0:
         raise ValueError("a group holds more distinct keys than the capacity")
     vo = np.concatenate([[0], np.cumsum(nv)])

@@ -376,6 +376,71 @@ int oracle_lru(int64_t capacity, int64_t n_groups, const int64_t* group_off, con
 }
 
 /*
+ * Frequency with decay, over the same groups: every key carries a use count.  At the start
+ * of group g (g > 0, period > 0, g multiple of period) every count is halved (integer
+ * shift); then each distinct key of the group gains 1024.  A miss with a full cache evicts
+ * the resident key not in the current group with the smallest count, then the oldest last
+ * use, then the smallest key.  Keys of a group are visited in ascending order; a key's last
+ * use becomes g when it is visited.  Outputs as oracle_lru.
+ */
+int oracle_lfu_decay(int64_t capacity, int64_t period, int64_t n_groups, const int64_t* group_off,
+                     const int64_t* keys, int64_t* hits, int64_t* misses, int64_t* victims, int64_t* n_victims) {
+  int64_t max_key = 0;
+  for (int64_t i = 0; i < group_off[n_groups]; ++i)
+    if (keys[i] > max_key) max_key = keys[i];
+  int64_t nk = max_key + 1;
+  int64_t* last = (int64_t*)malloc(sizeof(int64_t) * (size_t)nk);     /* last use, -1 = never */
+  int64_t* count = (int64_t*)malloc(sizeof(int64_t) * (size_t)nk);
+  char* res = (char*)malloc((size_t)nk);                                 /* resident? */
+  int64_t* in_group = (int64_t*)malloc(sizeof(int64_t) * (size_t)nk);
+  for (int64_t i = 0; i < nk; ++i) last[i] = -1, count[i] = 0, res[i] = 0, in_group[i] = -1;
+  int64_t resident = 0, nv = 0, rc = 0;
+  for (int64_t g = 0; g < n_groups && rc == 0; ++g) {
+    int64_t distinct = 0;
+    for (int64_t i = group_off[g]; i < group_off[g + 1]; ++i)
+      if (in_group[keys[i]] != g) in_group[keys[i]] = g, distinct++;
+    if (distinct > capacity) {
+      rc = -1;
+      break;
+    }
+    if (period > 0 && g > 0 && g % period == 0)
+      for (int64_t k = 0; k < nk; ++k) count[k] /= 2; /* counts are non-negative: a shift */
+    for (int64_t k = 0; k < nk; ++k)
+      if (in_group[k] == g) count[k] += 1024;
+    hits[g] = misses[g] = n_victims[g] = 0;
+    for (int64_t key = 0; key < nk; ++key) {
+      if (in_group[key] != g) continue;
+      if (res[key]) {
+        hits[g]++;
+      } else {
+        misses[g]++;
+        if (resident == capacity) {
+          int64_t best = -1;
+          for (int64_t c = 0; c < nk; ++c) {
+            if (!res[c] || in_group[c] == g) continue;
+            if (best < 0 || count[c] < count[best] || (count[c] == count[best] && last[c] < last[best]) ||
+                (count[c] == count[best] && last[c] == last[best] && c < best))
+              best = c;
+          }
+          res[best] = 0;
+          resident--;
+          victims[nv++] = best;
+          n_victims[g]++;
+        }
+        res[key] = 1;
+        resident++;
+      }
+      last[key] = g;
+    }
+  }
+  free(last);
+  free(count);
+  free(res);
+  free(in_group);
+  return (int)rc;
+}
+
+/*
  * Belady's MIN on the same groups: on a miss with a full cache, evict the
  * resident key (not in the current group) whose next use lies farthest ahead
  * (never = infinitely far; ties: smallest key).  Gives the largest hit count

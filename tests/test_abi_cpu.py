@@ -118,14 +118,15 @@ def test_pack_rejects_int4_scale_outside_binary16():
 
 # ------------------------------------------------------------------ cache planner (host only)
 
-def _planner(cap, L_, E):
-    return ExpertCache(None, 1 << 20, L_, E, None, 0, cap)
+def _planner(cap, L_, E, policy="lru", period=0):
+    return ExpertCache(None, 1 << 20, L_, E, None, 0, cap, policy, period)
 
 
-def test_cache_planner_matches_oracle_lru():
+@pytest.mark.parametrize("policy,period", [("lru", 0), ("lfu_decay", 32), ("lfu_decay", 0), ("lfu_decay", 1)])
+def test_cache_planner_matches_oracle(policy, period):
     L_, E, cap, steps = 4, 64, 64, 120
     rng = np.random.default_rng(11)
-    c = _planner(cap, L_, E)
+    c = _planner(cap, L_, E, policy, period)
     groups, plans = [], []
     p = 1.0 / np.arange(1, E + 1) ** 1.2
     p /= p.sum()
@@ -134,12 +135,22 @@ def test_cache_planner_matches_oracle_lru():
             ids = rng.choice(E, size=16, p=p)
             groups.append((layer * E + ids).tolist())
             plans.append(c.plan(layer, ids))
-    h, m, v = oracle.lru(cap, groups)
+    if policy == "lru":
+        h, m, v = oracle.lru(cap, groups)
+    else:
+        h, m, v = oracle.lfu_decay(cap, period, groups)
     assert [pl.n_hits for pl in plans] == list(h)
     assert [pl.n_misses for pl in plans] == list(m)
     st = c.stats()
     assert st["hits"] == h.sum() and st["misses"] == m.sum() and st["evictions"] == sum(len(a) for a in v)
     assert st["bytes_fetched"] == m.sum() * (1 << 20)
+
+
+def test_cache_rejects_unknown_policy():
+    d = _lib.MoeCacheDesc()
+    d.pkg_bytes, d.L, d.E, d.capacity, d.policy = 1024, 1, 8, 4, 7
+    h = ctypes.c_void_p()
+    assert L.moe_cache_create(ctypes.byref(d), ctypes.byref(h)) == INVALID
 
 
 def test_cache_plan_slot_table_is_injective_and_consistent():

@@ -23,13 +23,13 @@ def _gpu():
     moe.lib()
 
 
-def run_and_check(wl, T, steps, check_steps, fill_all=True, capacity=None):
+def run_and_check(wl, T, steps, check_steps, fill_all=True, capacity=None, policy="lru", period=0):
     xs = {}
     for s in range(steps):
         for l in range(wl.layers):
             x, _ = oracle.rank_gap_inputs(wl, T, layer=l, step=s)
             xs[(l, s)] = x
-    model = OffloadedModel(wl, T, capacity=capacity, fill=fill_all)
+    model = OffloadedModel(wl, T, capacity=capacity, fill=fill_all, policy=policy, decay_period=period)
     if not fill_all:  # only the experts some step routes to (the others are never fetched)
         touched = {l: set() for l in range(wl.layers)}
         for (l, s), x in xs.items():
@@ -55,8 +55,11 @@ def run_and_check(wl, T, steps, check_steps, fill_all=True, capacity=None):
                 got_bytes = model.pool[torch.tensor(slots, device="cuda")][:, :model.pkg_bytes].cpu().numpy()
                 for i, e in enumerate(mine):
                     assert np.array_equal(got_bytes[i], model.package(l, e)), (l, s, e)
-    # cache decisions: identical to the oracle's LRU
-    h, m, v = oracle.lru(model.capacity, groups)
+    # cache decisions: identical to the oracle's policy
+    if policy == "lru":
+        h, m, v = oracle.lru(model.capacity, groups)
+    else:
+        h, m, v = oracle.lfu_decay(model.capacity, period, groups)
     got = [(p[3], p[4]) for p in model.plans]
     assert got == list(zip(h.tolist(), m.tolist()))
     st = model.cache.stats()
@@ -64,7 +67,7 @@ def run_and_check(wl, T, steps, check_steps, fill_all=True, capacity=None):
     assert st["bytes_fetched"] == m.sum() * model.pkg_bytes
     hb, _ = oracle.belady(model.capacity, groups)
     assert hb.sum() >= h.sum()
-    say("  lru hits %d / %d lookups (belady %d)" % (h.sum(), h.sum() + m.sum(), hb.sum()))
+    say("  %s hits %d / %d lookups (belady %d)" % (policy, h.sum(), h.sum() + m.sum(), hb.sum()))
     # outputs of the checked steps
     for (l, s), got_out in outs.items():
         experts = [None] * wl.E
@@ -83,6 +86,13 @@ def test_offload_small_all_steps():
                     zipf_s=1.2, layers=3, steps=24, rerank_every=8, cache_frac=0.25)
     say("offload small")
     run_and_check(wl, 5, wl.steps, set(range(wl.steps)))
+
+
+def test_offload_small_frequency_policy():
+    wl = W.Workload(name="offload-lfu", H=224, E=16, k=4, I=352, wfmt="int4g32", xdt="bf16", Ts=(5,), seed=608,
+                    zipf_s=1.2, layers=3, steps=24, rerank_every=8, cache_frac=0.25)
+    say("offload small, lfu-decay")
+    run_and_check(wl, 5, wl.steps, {0, 11, 23}, policy="lfu_decay", period=6)
 
 
 def test_offload_small_tight_capacity():

@@ -345,11 +345,44 @@ def test_belady_is_optimal_on_tiny_inputs(seed):
     assert hb.sum() >= hl.sum() and (hb + mb == hl + ml).all()
 
 
+@pytest.mark.parametrize("cap,space,seed", [(4, 12, 0), (16, 64, 1), (33, 256, 2)])
+def test_lfu_decay_with_period_one_is_lru_on_single_key_groups(cap, space, seed):
+    """Halving every group makes the most recent use dominate every count (a use one group ago
+    outweighs all older uses together), so with one key per group (no ties in last use) the
+    eviction order is exactly least-recently-used."""
+    groups = [[int(k)] for k in np.concatenate(_zipf_groups(600, 1, space, seed))]
+    h, m, v = oracle.lfu_decay(cap, 1, groups)
+    h2, m2, v2 = lru_ordered_dict(cap, groups)
+    assert list(h) == h2 and list(m) == m2
+    assert [list(a) for a in v] == v2
+
+
+def test_lfu_decay_keeps_a_hot_set_that_lru_loses():
+    """Without decay, keys used again and again outrank one-off keys: four hot keys come back
+    every third group, two bursts of six new keys come between.  With 12 slots LRU evicts the
+    hot keys every time (the 12 keys of the two bursts are all more recent); frequency keeps
+    them resident once their counts exceed a one-off key's."""
+    hot = list(range(4))
+    groups, nxt = [], 100
+    for g in range(90):
+        if g % 3 == 0:
+            groups.append(list(hot))
+        else:
+            groups.append(list(range(nxt, nxt + 6)))
+            nxt += 6
+    hl, ml, _ = oracle.lfu_decay(12, 0, groups)
+    hr, mr, _ = oracle.lru(12, groups)
+    assert all(hl[g] == 4 for g in range(9, 90, 3))
+    assert all(hr[g] == 0 for g in range(3, 90, 3))
+    assert (hl + ml == hr + mr).all()
+
+
 def test_belady_at_least_lru_large():
     groups = _zipf_groups(400, 16, 512, 7)
     hb, _ = oracle.belady(64, groups)
     hl, _, _ = oracle.lru(64, groups)
-    assert hb.sum() >= hl.sum()
+    hf, _, _ = oracle.lfu_decay(64, 32, groups)
+    assert hb.sum() >= hl.sum() and hb.sum() >= hf.sum()
 
 
 # ------------------------------------------------------------- cost model (report formula)
