@@ -18,6 +18,7 @@ typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 f16x2;
 typedef __attribute__((__vector_size__(2 * sizeof(short)))) short bf16x2;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(4 * sizeof(unsigned)))) unsigned u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(unsigned)))) unsigned u32x2;
 
 constexpr int kWave = 64;
 

@@ -1,0 +1,8 @@
+// Prefill tile kernel for mxfp4 weights, down matrix (one kernel per file: they compile in parallel).
+#include "ffn_tile.hpp"
+
+namespace moe {
+int launch_tile_mxfp4_down(const FfnArgs& a, int H, int I, int n, int E, hipStream_t s) {
+  return tile_launch<MOE_W_MXFP4, false>(a, H, I, n, E, s);
+}
+}  // namespace moe
