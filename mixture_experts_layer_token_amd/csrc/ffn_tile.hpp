@@ -47,8 +47,7 @@ constexpr int kD = 4;     // pipeline depth: K blocks in flight
 template <int FMT>
 struct TileCfg {
   static constexpr int BK = FMT == MOE_W_BF16 ? 32 : 64;  // K per block
-  // kD ring buffers plus one that absorbs the loads of blocks past the end
-  static constexpr size_t LDS = (size_t)(kD + 1) * kTM * BK * 2;
+  static constexpr size_t LDS = (size_t)kD * kTM * BK * 2;  // kD ring buffers
 };
 
 // In-place MFMA on an accumulator held in AGPRs, written as inline assembly: with the compiler's
@@ -106,7 +105,6 @@ struct TileCtx {
   int lane, wave, p0, rows, col;
   const char* cbase[kWNS];  // code base of each of the wave's strips
   const char* sbase[kWNS];  // scale base of each strip
-  gptr zpage;               // the zero page (weights of blocks in a partial last chunk)
 };
 
 // One row tile of NMT 16-row MFMA tiles (rows <= 16 * NMT).
@@ -131,18 +129,16 @@ __device__ __forceinline__ void tile_body(const FfnArgs& args, const TileCtx& c,
 
   // ---- activation staging: lane l writes slot l % CPR of row l / CPR of its load's rows, so it
   // fetches chunk (l % CPR) ^ (row % CPR) of that row.  Rows past the tile's end repeat row 0
-  // (their results are dropped); chunks past K repeat the last chunk (their weights are zero);
-  // loads of blocks past the end go to the spare buffer kD.
-  unsigned aoff[IPW];  // element offset of the lane's source row in args.a
-  unsigned achunk[IPW];
-#pragma unroll
-  for (int i = 0; i < IPW; ++i) {
+  // (their results are dropped).
+  auto a_row = [&](int i) {  // source row of the lane in activation load i
     const int r = (i * kTW + wave) * RPI + lane / CPR;
     const int rr = r < c.rows ? r : 0;
-    const int row = GU ? args.perm_src[c.p0 + rr] / args.k : c.p0 + rr;
-    aoff[i] = (unsigned)row * (unsigned)K;
-    achunk[i] = (unsigned)((lane % CPR) ^ (r % CPR));
-  }
+    return GU ? args.perm_src[c.p0 + rr] / args.k : c.p0 + rr;
+  };
+  auto a_chunk = [&](int i) { return (unsigned)((lane % CPR) ^ (((i * kTW + wave) * RPI + lane / CPR) % CPR)); };
+  unsigned avoff[IPW];  // byte offset of the lane's chunk of block 0 (block kb adds kb * BK * 2)
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) avoff[i] = ((unsigned)a_row(i) * (unsigned)K + a_chunk(i) * 8) * 2;
 
   // weight registers of one K block.  bf16: KS fragments of 16 bytes per strip.  4-bit: half of
   // the lane's 16-byte word of a 4-k-step chunk (8 bytes, 2 k-steps) and the 2 matching scales.
@@ -150,43 +146,41 @@ __device__ __forceinline__ void tile_body(const FfnArgs& args, const TileCtx& c,
     unsigned v[kWNS][Q4 ? 2 : 4 * KS];
     unsigned sc[kWNS];
   };
-  // load L of a block's load list (the IPW activation loads, then the weight loads).  Blocks past
-  // the whole package chunks read the zero page (weights 0); the blocks of a partial last chunk
-  // are recomputed after the loop from their packed layout.
-  auto load_one = [&](int L, BReg& B, int kb, int buf, bool valid) {
+  // load L of block kb's load list (the IPW activation loads, then the weight loads), kb < nfb:
+  // a uniform base plus a 32-bit per-lane offset, so every load is one instruction on a scalar
+  // base, and the offsets of one block are shared by all strips
+  auto load_one = [&](int L, BReg& B, int kb, int buf) {
     if (L < IPW) {
       const int i = L;
       const int r0 = (i * kTW + wave) * RPI;
-      const unsigned ch = min((unsigned)(kb * CPR) + achunk[i], (unsigned)(K / 8 - 1));
-      const unsigned short* g = args.a + aoff[i] + ch * 8;
+      gptr g = (gptr)args.a + (size_t)kb * (BK * 2) + avoff[i];
       unsigned short* l = lds_a + ((size_t)buf * kTM + r0) * BK;
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
                                        (__attribute__((address_space(3))) void*)l, 16, 0, 0);
     } else if constexpr (!Q4) {
       const int j = (L - IPW) / KS, q = (L - IPW) % KS;
-      gptr cp = valid ? (gptr)(c.cbase[j] + (size_t)(kb * KS + q) * 1024) : c.zpage;
-      const u32x4 v = *(const __attribute__((address_space(1))) u32x4*)(cp + lane * 16);
+      const unsigned off = (unsigned)(kb * KS + q) * 1024u + (unsigned)lane * 16u;
+      const u32x4 v = *(const __attribute__((address_space(1))) u32x4*)((gptr)c.cbase[j] + off);
       B.v[j][4 * q] = v[0], B.v[j][4 * q + 1] = v[1], B.v[j][4 * q + 2] = v[2], B.v[j][4 * q + 3] = v[3];
     } else {
       const int j = (L - IPW) / 2, part = (L - IPW) % 2;
-      const int ch = kb >> 1, h = kb & 1;
+      const unsigned ch = (unsigned)kb >> 1, h = (unsigned)kb & 1;
       if (part == 0) {
-        gptr cp = valid ? (gptr)(c.cbase[j] + (size_t)ch * 1024 + h * 8) : c.zpage;
-        const u32x2 v = *(const __attribute__((address_space(1))) u32x2*)(cp + lane * 16);
+        const unsigned off = ch * 1024u + h * 8u + (unsigned)lane * 16u;
+        const u32x2 v = *(const __attribute__((address_space(1))) u32x2*)((gptr)c.cbase[j] + off);
         B.v[j][0] = v[0], B.v[j][1] = v[1];
       } else {
-        gptr sp = valid ? (gptr)(c.sbase[j] + ((size_t)ch * 64 + 2 * h) * SB) : c.zpage;
-        sp += (lane & 15) * 4 * SB;
+        const unsigned off = (ch * 64u + 2u * h) * SB + ((unsigned)lane & 15) * 4u * SB;
         if constexpr (SB == 1)
-          B.sc[j] = *(const __attribute__((address_space(1))) unsigned short*)sp;
+          B.sc[j] = *(const __attribute__((address_space(1))) unsigned short*)((gptr)c.sbase[j] + off);
         else
-          B.sc[j] = *(const __attribute__((address_space(1))) unsigned*)sp;
+          B.sc[j] = *(const __attribute__((address_space(1))) unsigned*)((gptr)c.sbase[j] + off);
       }
     }
   };
-  auto load_block = [&](BReg& B, int kb, int buf, bool valid) {
+  auto load_block = [&](BReg& B, int kb, int buf) {
 #pragma unroll
-    for (int L = 0; L < kLoads; ++L) load_one(L, B, kb, buf, valid);
+    for (int L = 0; L < kLoads; ++L) load_one(L, B, kb, buf);
   };
   // a block of the partial last chunk: ns k-steps packed 4 * ns bytes per lane; k-steps past
   // the end get zero codes and zero scales
@@ -249,12 +243,17 @@ __device__ __forceinline__ void tile_body(const FfnArgs& args, const TileCtx& c,
       const unsigned v = B.v[j][q];
       auto sub = [&](unsigned w) { return __builtin_bit_cast(unsigned, __builtin_bit_cast(f16x2, w) - bias); };
       auto mul = [&](unsigned w) { return __builtin_bit_cast(unsigned, __builtin_bit_cast(f16x2, w) * ss); };
+      // Two dependency chains, one instruction of each per sub-step, the longer chain first: an
+      // instruction never follows its producer with only MFMA code in between (the compiler
+      // would insert a wait state there: it cannot see that the assembly is not a vector op).
+      //   chain a (pairs 1, 3): shift, and-or, subtract, multiply, then the same for pair 3
+      //   chain b (pairs 0, 2): and-or, subtract, multiply, then shift, and-or, subtract, multiply
       switch (st) {
-        case 0: t[0] = pin((v & mask) | magic); t[1] = pin(v >> 4); break;
+        case 0: t[1] = pin(v >> 4); t[0] = pin((v & mask) | magic); break;
         case 1: t[1] = pin((t[1] & mask) | magic); t[0] = pin(sub(t[0])); break;
         case 2: t[1] = pin(sub(t[1])); out[0] = pin(mul(t[0])); break;
         case 3: out[1] = pin(mul(t[1])); t[2] = pin(v >> 8); break;
-        case 4: t[2] = pin((t[2] & mask) | magic); t[3] = pin(v >> 12); break;
+        case 4: t[3] = pin(v >> 12); t[2] = pin((t[2] & mask) | magic); break;
         case 5: t[3] = pin((t[3] & mask) | magic); t[2] = pin(sub(t[2])); break;
         case 6: t[3] = pin(sub(t[3])); out[2] = pin(mul(t[2])); break;
         default: out[3] = pin(mul(t[3])); break;
@@ -283,115 +282,137 @@ __device__ __forceinline__ void tile_body(const FfnArgs& args, const TileCtx& c,
     }
   };
 
-  // ---- K loop: kD blocks in flight.  At the start of block kb a barrier publishes block kb+1's
-  // LDS buffer (every wave has waited for its own loads of it) and retires block kb-1's buffer,
-  // into which block kb+kD-1 is then loaded.  The A fragments of the next k-step are read from
-  // LDS while the current k-step's MFMAs run, across block edges too (the next block is already
-  // published); so is the operand of the next strip, the next k-step's first strip included.
+  // ---- K loop over the blocks of whole package chunks: kD blocks in flight.  At the start of
+  // block kb a barrier publishes block kb+1's LDS buffer (every wave has waited for its own loads
+  // of it) and retires block kb-1's buffer, into which block kb+kD-1 is then loaded.  The A
+  // fragments of the next k-step are read from LDS while the current k-step's MFMAs run, across
+  // block edges too (the next block is already published); so is the operand of the next strip,
+  // the next k-step's first strip included.
   static_assert(kD == 4 && (kD * KS) % 2 == 0, "the loop below is unrolled for four blocks");
-  BReg ring[kD];
-  OpT abuf[2][NMT];
-#pragma unroll
-  for (int i = 0; i < kD - 1; ++i) load_block(ring[i], i, i < nkb ? i : kD, i < nfb);
-  MOE_WAIT_VMCNT((kD - 2) * kLoads);  // block 0 has landed
-  barrier_keep_loads();
-  read_a(abuf[0], 0, 0);
-  // The prologue's loads complete before the loop (once per row tile): otherwise the compiler,
-  // merging the loop entry with the loop's back edge, waits for every outstanding load at the
-  // first use of a weight register in each iteration.
-  __builtin_amdgcn_s_waitcnt(0);
-  u32x4 b0 = __builtin_bit_cast(u32x4, decode(ring[0], 0, 0));  // operand of the next strip
   int kb = 0;
-  for (; kb + kD <= nkb; kb += kD) {
-    static_for<kD>([&](auto ic) {
-      constexpr int i = ic;
-      // block kb+i+1 landed (own loads), then every wave: its buffer is published and block
-      // kb+i-1's buffer is free
-      MOE_WAIT_VMCNT((kD - 3) * kLoads);
-      barrier_keep_loads();
+  if (nfb > 0) {  // (uniform)
+    BReg ring[kD];
+    OpT abuf[2][NMT];
+    // blocks in order (the waits count loads in issue order, so no load of a later block may be
+    // scheduled before one of an earlier block)
+#pragma unroll
+    for (int i = 0; i < kD - 1; ++i) {
+      load_block(ring[i], min(i, nfb - 1), i);
       __builtin_amdgcn_sched_barrier(0);
-      const int nb = kb + i + kD - 1;  // block to issue, into the buffer of block kb+i-1
-      const int lbuf = nb < nkb ? (i + kD - 1) % kD : kD;
-      const bool lvalid = nb < nfb;
-      BReg& lring = ring[(i + kD - 1) % kD];
-      static_for<KS>([&](auto qc) {
-        constexpr int q = qc;
-        // A of the next k-step (the next block's first when q is the last); the register buffer
-        // alternates per k-step, and kD * KS is even, so every block of the loop starts on 0
-        constexpr int step = i * KS + q;
-        constexpr int nbuf = q + 1 < KS ? i : (i + 1) % kD;
-        constexpr int nq = (q + 1) % KS;
-        OpT(&acur)[NMT] = abuf[step & 1];
-        OpT(&anx)[NMT] = abuf[(step + 1) & 1];
-        u32x4 b = b0, bn = b0;
-        unsigned dt[4];
-        static_for<kWNS>([&](auto jc) {
-          constexpr int j = jc;
-          if constexpr (!Q4) b = __builtin_bit_cast(u32x4, decode(ring[i], j, q));
-          static_for<NMT>([&](auto mtc) {
-            constexpr int mt = mtc;
-            constexpr int r = j * NMT + mt;
-            mfma_acc<Q4 && mt == 0>(acc[mt][j], acur[mt], __builtin_bit_cast(OpT, b));
-            // the next strip's operand: 8 sub-steps over this strip's MFMAs, done before its last
-            if constexpr (Q4) {
-              constexpr int T = NMT > 1 ? NMT - 1 : 1;
-              constexpr int lo = spread_lo(mt, 8, T), hi = mt < T ? spread_hi(mt, 8, T) : lo;
-              static_for<hi - lo>([&](auto sc) {
-                constexpr int st = lo + sc;
-                if constexpr (j + 1 < kWNS) decode_sub(ring[i], j + 1, q, st, bn, dt);
-                else decode_sub(ring[nbuf], 0, nq, st, bn, dt);
-              });
-            }
-            // the next k-step's A fragments, over the first three quarters of this k-step
-            {
-              constexpr int T = 3 * R / 4 > 0 ? 3 * R / 4 : 1;
-              constexpr int lo = spread_lo(r, NMT, T), hi = r < T ? spread_hi(r, NMT, T) : lo;
-              static_for<hi - lo>([&](auto mc) {
-                constexpr int m = lo + mc;
-                read_a_one(anx[m], nbuf, nq, m);
-              });
-            }
-            // block nb's loads, over the MFMAs of the whole block
-            {
-              constexpr int s0 = q * R + r;
-              constexpr int lo = spread_lo(s0, kLoads, KS * R), hi = spread_hi(s0, kLoads, KS * R);
-              static_for<hi - lo>([&](auto Lc) { load_one(lo + Lc, lring, nb, lbuf, lvalid); });
-            }
-            __builtin_amdgcn_sched_barrier(0);
+    }
+    MOE_WAIT_VMCNT((kD - 2) * kLoads);  // block 0 has landed
+    barrier_keep_loads();
+    read_a(abuf[0], 0, 0);
+    // The prologue's loads complete before the loop (once per row tile): otherwise the compiler,
+    // merging the loop entry with the loop's back edge, waits for every outstanding load at the
+    // first use of a weight register in each iteration.
+    __builtin_amdgcn_s_waitcnt(0);
+    u32x4 b0 = __builtin_bit_cast(u32x4, decode(ring[0], 0, 0));  // operand of the next strip
+    for (; kb + kD <= nfb; kb += kD) {
+      static_for<kD>([&](auto ic) {
+        constexpr int i = ic;
+        // block kb+i+1 landed (own loads), then every wave: its buffer is published and block
+        // kb+i-1's buffer is free
+        MOE_WAIT_VMCNT((kD - 3) * kLoads);
+        barrier_keep_loads();
+        __builtin_amdgcn_sched_barrier(0);
+        // block to issue, into the buffer of block kb+i-1; past the end, the last block again
+        // (its buffer and registers are not read any more)
+        const int nb = min(kb + i + kD - 1, nfb - 1);
+        constexpr int lbuf = (i + kD - 1) % kD;
+        BReg& lring = ring[(i + kD - 1) % kD];
+        static_for<KS>([&](auto qc) {
+          constexpr int q = qc;
+          // A of the next k-step (the next block's first when q is the last); the register buffer
+          // alternates per k-step, and kD * KS is even, so every block of the loop starts on 0
+          constexpr int step = i * KS + q;
+          constexpr int nbuf = q + 1 < KS ? i : (i + 1) % kD;
+          constexpr int nq = (q + 1) % KS;
+          OpT(&acur)[NMT] = abuf[step & 1];
+          OpT(&anx)[NMT] = abuf[(step + 1) & 1];
+          u32x4 b = b0, bn = b0;
+          unsigned dt[4];
+          static_for<kWNS>([&](auto jc) {
+            constexpr int j = jc;
+            if constexpr (!Q4) b = __builtin_bit_cast(u32x4, decode(ring[i], j, q));
+            static_for<NMT>([&](auto mtc) {
+              constexpr int mt = mtc;
+              constexpr int r = j * NMT + mt;
+              mfma_acc<Q4 && mt == 0>(acc[mt][j], acur[mt], __builtin_bit_cast(OpT, b));
+              // the next strip's operand: 8 sub-steps over this strip's MFMAs, done before its last
+              if constexpr (Q4) {
+                constexpr int T = NMT > 1 ? NMT - 1 : 1;
+                constexpr int lo = spread_lo(mt, 8, T), hi = mt < T ? spread_hi(mt, 8, T) : lo;
+                static_for<hi - lo>([&](auto sc) {
+                  constexpr int st = lo + sc;
+                  if constexpr (j + 1 < kWNS) decode_sub(ring[i], j + 1, q, st, bn, dt);
+                  else decode_sub(ring[nbuf], 0, nq, st, bn, dt);
+                });
+              }
+              // the next k-step's A fragments, over the first three quarters of this k-step
+              {
+                constexpr int T = 3 * R / 4 > 0 ? 3 * R / 4 : 1;
+                constexpr int lo = spread_lo(r, NMT, T), hi = r < T ? spread_hi(r, NMT, T) : lo;
+                static_for<hi - lo>([&](auto mc) {
+                  constexpr int m = lo + mc;
+                  read_a_one(anx[m], nbuf, nq, m);
+                });
+              }
+              // block nb's loads, over the MFMAs of the whole block
+              {
+                constexpr int s0 = q * R + r;
+                constexpr int lo = spread_lo(s0, kLoads, KS * R), hi = spread_hi(s0, kLoads, KS * R);
+                static_for<hi - lo>([&](auto Lc) { load_one(lo + Lc, lring, nb, lbuf); });
+              }
+              __builtin_amdgcn_sched_barrier(0);
+            });
+            if constexpr (Q4) b = bn;
           });
-          if constexpr (Q4) b = bn;
+          if constexpr (Q4) b0 = b;
         });
-        if constexpr (Q4) b0 = b;
       });
-    });
-    // leaving the MFMA code (the loop's exit may copy accumulators between registers)
-    acc_hazard_guard();
-  }
-  // the last nkb - kb (< kD) blocks were issued kD-1 blocks ahead; the A fragments of block
-  // kb's first k-step are in abuf[0]
-  __builtin_amdgcn_s_waitcnt(0);
-  barrier_keep_loads();
-#pragma unroll
-  for (int i = 0; i < kD - 1; ++i) {
-    if (kb + i < nkb) {
-#pragma unroll
-      for (int q = 0; q < KS; ++q) {
-        const int step = i * KS + q;
-        const int nbuf = q + 1 < KS ? i : (i + 1) % kD;
-        read_a(abuf[(step + 1) & 1], nbuf, (q + 1) % KS);
-        mfma_step(ring[i], abuf[step & 1], q);
-      }
+      // leaving the MFMA code (the loop's exit may copy accumulators between registers)
       acc_hazard_guard();
     }
+    // the last nfb - kb (< kD) blocks were issued kD-1 blocks ahead; the A fragments of block
+    // kb's first k-step are in abuf[0]
+    __builtin_amdgcn_s_waitcnt(0);
+    barrier_keep_loads();
+#pragma unroll
+    for (int i = 0; i < kD - 1; ++i) {
+      if (kb + i < nfb) {
+#pragma unroll
+        for (int q = 0; q < KS; ++q) {
+          const int step = i * KS + q;
+          const int nbuf = q + 1 < KS ? i : (i + 1) % kD;
+          read_a(abuf[(step + 1) & 1], nbuf, (q + 1) % KS);
+          mfma_step(ring[i], abuf[step & 1], q);
+        }
+        acc_hazard_guard();
+      }
+    }
   }
-  // the blocks of a partial last chunk computed above with zero weights: again with their own
+  // ---- the blocks of a partial last chunk (4-bit weights, K/32 not a multiple of 4): staged
+  // alone in buffer 0, chunks past K repeating the last chunk (their weights are zero)
   for (int pb = nfb; pb < nkb; ++pb) {
+    __builtin_amdgcn_s_waitcnt(0);
+    barrier_keep_loads();  // every wave is done with buffer 0
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int r0 = (i * kTW + wave) * RPI;
+      const unsigned ch = min((unsigned)(pb * CPR) + a_chunk(i), (unsigned)(K / 8 - 1));
+      gptr g = (gptr)args.a + ((size_t)a_row(i) * K + ch * 8) * 2;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                       (__attribute__((address_space(3))) void*)(lds_a + (size_t)r0 * BK), 16, 0, 0);
+    }
     BReg bp;
     load_b_partial(bp, pb);
+    __builtin_amdgcn_s_waitcnt(0);
+    barrier_keep_loads();
 #pragma unroll
     for (int q = 0; q < KS; ++q) {
       OpT a[NMT];
-      read_a(a, pb % kD, q);
+      read_a(a, 0, q);
       mfma_step(bp, a, q);
     }
     acc_hazard_guard();
@@ -520,10 +541,6 @@ __global__ __launch_bounds__(kTW * 64, 1) void ffn_tile_kernel(FfnArgs args) {
     c.cbase[j] = pkg + args.region_codes + (size_t)s * (Q4 ? 8 : 32) * c.K;
     c.sbase[j] = pkg + args.region_scales + (size_t)s * 16 * c.nks * SB;
   }
-  // the zero page's address, computed once and opaque to the compiler (rematerialising it inside
-  // the K loop costs a scalar load there, whose wait also waits for every outstanding LDS read)
-  c.zpage = (gptr)g_zero_page;
-  asm volatile("" : "+s"(c.zpage));
 
   switch ((c.rows + 15) / 16) {
     case 1: tile_body<FMT, GU, 1>(args, c, lds_a); break;
@@ -553,6 +570,12 @@ int tile_launch(const FfnArgs& a, int H, int I, int n, int E, hipStream_t s) {
     if (e != hipSuccess) return hip_fail(e, "moe_expert_ffn: LDS attribute of the prefill kernel");
     attr_set = true;
   }
+  // activation offsets are 32-bit byte offsets: the A matrix (x for gate/up, h for down) must
+  // stay under 4 GiB
+  const long long a_rows = GU ? (a.k > 0 ? n / a.k : 0) : n;
+  if (a_rows * (long long)(GU ? H : I) * 2 >= (1LL << 32))
+    return fail(MOE_ERR_UNSUPPORTED, "moe_expert_ffn: prefill activations of %lld x %d elements exceed 4 GiB", a_rows,
+                GU ? H : I);
   const long long nz = n < E ? n : E;
   const long long S = ((long long)n + nz * (kTM - 1)) / kTM;
   const int N = GU ? 2 * I : H;
