@@ -42,12 +42,20 @@ constexpr int kTN = 256;  // columns per workgroup tile
 constexpr int kMT = 12;   // 16-row MFMA tiles of a full row tile
 constexpr int kWNS = 4;   // 16-column strips per wave
 constexpr int kXCD = 8;   // XCDs of an MI355X; workgroup i is dispatched to XCD i % 8
-constexpr int kD = 4;     // pipeline depth: K blocks in flight
-
+#ifndef MOE_CFG_TILE_D_BF16
+#define MOE_CFG_TILE_D_BF16 4
+#endif
+#ifndef MOE_CFG_TILE_D_Q4
+#define MOE_CFG_TILE_D_Q4 4
+#endif
 template <int FMT>
 struct TileCfg {
   static constexpr int BK = FMT == MOE_W_BF16 ? 32 : 64;  // K per block
-  static constexpr size_t LDS = (size_t)kD * kTM * BK * 2;  // kD ring buffers
+  // pipeline depth kD: K blocks in flight (4 covers the load latency: 5 measured no faster for
+  // 4-bit weights and costs 12 more registers); even kD * BK / 32 keeps the register buffers of
+  // A fragments in step across loop iterations
+  static constexpr int D = FMT == MOE_W_BF16 ? MOE_CFG_TILE_D_BF16 : MOE_CFG_TILE_D_Q4;
+  static constexpr size_t LDS = (size_t)D * kTM * BK * 2;  // kD ring buffers
 };
 
 // In-place MFMA on an accumulator held in AGPRs, written as inline assembly: with the compiler's
@@ -122,6 +130,7 @@ __device__ __forceinline__ void tile_body(const FfnArgs& args, const TileCtx& c,
   constexpr int NBL = Q4 ? 2 : KS;                // weight loads per strip and block
   constexpr int kLoads = IPW + kWNS * NBL;        // vector loads per block and wave
   constexpr int R = NMT * kWNS;                   // MFMAs per k-step and wave
+  constexpr int kD = TileCfg<FMT>::D;             // pipeline depth
   static_assert(!Q4 || KS == 2, "a 4-bit block is half of a 4-k-step package chunk");
   static_assert(IPW * kTW * RPI <= kTM, "activation loads stay inside the tile buffer");
   const int K = c.K, lane = c.lane, wave = c.wave;
@@ -288,7 +297,7 @@ __device__ __forceinline__ void tile_body(const FfnArgs& args, const TileCtx& c,
   // fragments of the next k-step are read from LDS while the current k-step's MFMAs run, across
   // block edges too (the next block is already published); so is the operand of the next strip,
   // the next k-step's first strip included.
-  static_assert(kD == 4 && (kD * KS) % 2 == 0, "the loop below is unrolled for four blocks");
+  static_assert(kD >= 3 && (kD * KS) % 2 == 0, "pipeline depth");
   int kb = 0;
   if (nfb > 0) {  // (uniform)
     BReg ring[kD];
