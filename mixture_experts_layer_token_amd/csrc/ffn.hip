@@ -43,7 +43,10 @@ struct Stage {
 // GU = true: a unit is the strip pair (2u, 2u+1) of the GU matrix (gate rows, up rows; K = H),
 //            epilogue SiLU(g)*u -> h.
 // GU = false: a unit is strip u of the down matrix (K = I), epilogue -> y_perm.
-// A workgroup owns units [NP*blockIdx.x, +NP) of one row tile; its NW waves split K.
+// A workgroup owns NP units of one row tile; its NW waves split K.  Work items (row tile, unit
+// group) are ordered expert by expert, unit group by unit group, the row tiles of one expert
+// consecutive, and dealt to the XCDs in contiguous ranges (workgroup i runs on XCD i % 8): the row
+// tiles of an expert read the same weights at the same time on one XCD, one HBM read and L2 hits.
 template <int FMT, int MT, int NW, int NP, int PF, bool GU>
 // (second bound: minimum waves per SIMD, i.e. the register budget: 3 -> 168 VGPRs, 2 -> 256)
 __global__ __launch_bounds__(NW * 64, FMT == MOE_W_BF16 ? 3 : 2) void ffn_stream_kernel(FfnArgs args) {
@@ -57,15 +60,24 @@ __global__ __launch_bounds__(NW * 64, FMT == MOE_W_BF16 ? 3 : 2) void ffn_stream
   constexpr int KPS = Q4 ? 4 : 1;                 // k-steps per stage
   __shared__ f32x4 red[NW > 1 ? NW * NSTR * 64 : 1];
 
-  const int4 tdesc = args.plan[blockIdx.y];  // uniform: one scalar load
-  if (tdesc.x < 0) return;
-  const int p0 = tdesc.y, rows = tdesc.z, slot = tdesc.w;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar addressing
   const int K = GU ? args.H : args.I;
   const int N = GU ? args.I : args.H;  // output features of this matrix
   const int n_units = N / 16;
-  const int u0 = blockIdx.x * NP;
+  const int gx = (n_units + NP - 1) / NP;  // unit groups
+  // work item (uniform: scalar loads).  plan[0].x = row tiles; plan[1 + t] = {first tile of the
+  // expert, its first grouped row, its rows, its slot} for every tile t of that expert
+  const int n_items = args.plan[0].x * gx;
+  const int per_xcd = (n_items + 7) / 8;
+  const int j = (int)blockIdx.x / 8, item = (int)(blockIdx.x % 8) * per_xcd + j;
+  if (j >= per_xcd || item >= n_items) return;
+  const int4 td = args.plan[1 + item / gx];
+  const int nt = (td.z + MR - 1) / MR;
+  const int local = item - gx * td.x;
+  const int t = local % nt;
+  const int p0 = td.y + t * MR, rows = min(MR, td.z - t * MR), slot = td.w;
+  const int u0 = (local / nt) * NP;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar addressing
   const int nks = K / 32;
 
   const char* pkg = args.packages + (size_t)slot * args.pkg_stride;
@@ -286,11 +298,11 @@ __global__ __launch_bounds__(NW * 64, FMT == MOE_W_BF16 ? 3 : 2) void ffn_stream
 
 // One workgroup of 1024 threads, thread e for expert e (E <= 1024): experts whose row count lies
 // in [lo, hi] and whose slot is resident are cut into tiles of mr rows, in expert order;
-// plan[i] = {expert, first grouped row, rows, slot}; entries from the last tile up to n_plan
-// get expert -1.
+// plan[0] = {number of tiles}, plan[1 + i] = {first tile of its expert, the expert's first grouped
+// row, the expert's rows, its slot} for every tile i.
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ offsets, int E, int mr, int lo,
                                                     int hi, const int32_t* __restrict__ slot_of_expert,
-                                                    int n_slots, int4* __restrict__ plan, int n_plan) {
+                                                    int n_slots, int4* __restrict__ plan) {
   __shared__ int wsum[16];
   const int e = threadIdx.x, lane = e & 63, wave = e >> 6;
   int c = 0, o0 = 0, slot = -1;
@@ -316,8 +328,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
     total += wsum[w];
   }
   const int excl = base + incl - nt;
-  for (int t = 0; t < nt; ++t) plan[excl + t] = make_int4(e, o0 + t * mr, min(mr, c - t * mr), slot);
-  for (int i = total + (int)threadIdx.x; i < n_plan; i += 1024) plan[i] = make_int4(-1, 0, 0, 0);
+  for (int t = 0; t < nt; ++t) plan[1 + excl + t] = make_int4(excl, o0, c, slot);
+  if (e == 0) plan[0] = make_int4(total, 0, 0, 0);
 }
 
 // ------------------------------------------------------------------ fp32 experts (VALU)
@@ -452,7 +464,7 @@ WsLayout ws_layout(const moe_experts* w, int T, int k, int xdt) {
   L.h_bytes = align256(n * w->I * (f32w ? 4 : 2));
   // row-tile plan of the streaming kernels: at most n / 16 + min(n, E) tiles
   L.plan_off = L.h_off + L.h_bytes;
-  L.plan_bytes = f32w ? 0 : align256((n / 16 + (n < (size_t)w->E ? n : (size_t)w->E)) * sizeof(int4));
+  L.plan_bytes = f32w ? 0 : align256((1 + n / 16 + (n < (size_t)w->E ? n : (size_t)w->E)) * sizeof(int4));
   L.total = L.plan_off + L.plan_bytes;
   return L;
 }
@@ -516,14 +528,16 @@ struct Cfg {
 
 template <int FMT, int MT, bool NARROW>
 void launch_stream_cfg(bool gate_up, const FfnArgs& a, int H, int I, int S, hipStream_t s) {
+  // one workgroup per (unit group, row tile) at most, rounded up to whole rounds of the 8 XCDs
+  auto grid8 = [](int g, int S) { return (unsigned)(((long long)g * S + 7) / 8 * 8); };
   typedef Cfg<FMT, MT, NARROW> C;
   if (gate_up) {
     const int gx = (I / 16 + C::GU_NP - 1) / C::GU_NP;
-    hipLaunchKernelGGL((ffn_stream_kernel<FMT, MT, C::GU_NW, C::GU_NP, C::GU_PF, true>), dim3(gx, S),
+    hipLaunchKernelGGL((ffn_stream_kernel<FMT, MT, C::GU_NW, C::GU_NP, C::GU_PF, true>), dim3(grid8(gx, S)),
                        dim3(64 * C::GU_NW), 0, s, a);
   } else {
     const int dx = (H / 16 + C::D_NP - 1) / C::D_NP;
-    hipLaunchKernelGGL((ffn_stream_kernel<FMT, MT, C::D_NW, C::D_NP, C::D_PF, false>), dim3(dx, S),
+    hipLaunchKernelGGL((ffn_stream_kernel<FMT, MT, C::D_NW, C::D_NP, C::D_PF, false>), dim3(grid8(dx, S)),
                        dim3(64 * C::D_NW), 0, s, a);
   }
 }
@@ -656,7 +670,7 @@ int launch_ffn(const moe_experts* w, const void* x, int xdt, int T, int k, const
   if (use_stream) {
     int4* plan = (int4*)(wsp + L.plan_off);
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, offsets, E, mr, 1, split, w->slot_of_expert,
-                       gu.n_slots, plan, S);
+                       gu.n_slots, plan);
     gu_s.plan = dn_s.plan = plan;
   }
   trace(0, s);

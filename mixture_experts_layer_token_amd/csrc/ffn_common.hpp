@@ -149,8 +149,9 @@ struct FfnArgs {
   void* out;                // GU: h [T*k][I] (operand type); down: y_perm [T*k][H] fp32
   int H, I, E, k;
   size_t region_codes, region_scales;  // byte offsets of this matrix's codes / scales in a package
-  // streaming variant: row tile blockIdx.y is plan[blockIdx.y] = {expert, first row, rows, slot}
-  // (expert -1: no tile), written by the plan kernel from offsets and the slot table
+  // streaming variant: plan[0].x = row tiles; plan[1 + t] = {first tile of the expert of tile t,
+  // the expert's first grouped row, its rows, its slot}, written by the plan kernel from the
+  // offsets and the slot table
   const int4* plan;
 };
 
