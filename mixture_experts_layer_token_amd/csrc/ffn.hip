@@ -294,6 +294,245 @@ __global__ __launch_bounds__(NW * 64, FMT == MOE_W_BF16 ? 3 : 2) void ffn_stream
   }
 }
 
+// ------------------------------------------------------------------ 4-bit streaming, shared activations
+
+// 4-bit weights carry as many activation bytes per stage as weight bytes (16 rows x 2 B per k
+// against 4 strips x 16 rows x 0.5 B per k), and every unit group of a row tile loads them again.
+// This variant shares them: a workgroup's NW waves each own NPW units over the whole
+// contraction (no cross-wave sum), and a stage's activation fragments (4 k-steps x MT row tiles,
+// 1 KiB each in lane order) are loaded once per workgroup straight into LDS, NA / NW fragments by
+// each wave, and read back by every wave.  Stage st lives in LDS buffer st % (PF + 1): the loads
+// of stage st + PF, issued after stage st's barrier, go to the buffer of stage st - 1, which every
+// wave has finished reading once it reached that barrier.
+template <int FMT, int MT, int NW, int NPW, int PF, bool GU>
+__global__ __launch_bounds__(NW * 64, 2) void ffn_stream_sa_kernel(FfnArgs args) {
+  typedef typename Op<FMT>::T OpT;
+  constexpr int SPU = GU ? 2 : 1;  // strips per unit
+  constexpr int NSTR = NPW * SPU;  // strips per wave
+  constexpr int MR = 16 * MT;
+  constexpr int SB = FMT == MOE_W_MXFP4 ? 1 : 2;  // scale bytes
+  constexpr int KPS = 4;                          // k-steps per stage
+  constexpr int NA = KPS * MT;                    // activation fragments per stage
+  static_assert(FMT != MOE_W_BF16 && NW == KPS, "4-bit weights; wave q loads k-step q's fragments");
+  constexpr int NAW = MT;        // activation loads per wave and stage
+  constexpr int NBUF = PF + 1;   // LDS stage buffers
+  constexpr int L = 2 * NSTR + NAW;  // vector loads per wave and stage
+  __shared__ __align__(16) unsigned char a_lds[NBUF * NA * 1024];
+
+  const int K = GU ? args.H : args.I;
+  const int N = GU ? args.I : args.H;  // output features of this matrix
+  const int n_units = N / 16;
+  constexpr int UPW = NW * NPW;        // units per workgroup
+  const int gx = (n_units + UPW - 1) / UPW;
+  // work item, as in ffn_stream_kernel
+  const int n_items = args.plan[0].x * gx;
+  const int per_xcd = (n_items + 7) / 8;
+  const int j = (int)blockIdx.x / 8, item = (int)(blockIdx.x % 8) * per_xcd + j;
+  if (j >= per_xcd || item >= n_items) return;
+  const int4 td = args.plan[1 + item / gx];
+  const int nt = (td.z + MR - 1) / MR;
+  const int local = item - gx * td.x;
+  const int t = local % nt;
+  const int p0 = td.y + t * MR, rows = min(MR, td.z - t * MR), slot = td.w;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int u0 = (local / nt) * UPW + wave * NPW;
+  const int nks = K / 32;
+  const char* pkg = args.packages + (size_t)slot * args.pkg_stride;
+
+  const char* cbase[NSTR];
+  const char* sbase[NSTR];
+#pragma unroll
+  for (int p = 0; p < NPW; ++p) {
+    const int u = min(u0 + p, n_units - 1);
+#pragma unroll
+    for (int s = 0; s < SPU; ++s) {
+      const int strip = GU ? 2 * u + s : u;
+      cbase[p * SPU + s] = pkg + args.region_codes + (size_t)strip * 8 * K;
+      sbase[p * SPU + s] = pkg + args.region_scales + (size_t)strip * 16 * nks * SB;
+    }
+  }
+  const unsigned lane16 = (unsigned)lane * 16, lrow = (unsigned)(lane & 15);
+  // the zero page's address, computed once (rematerialised inside the loop it costs a scalar
+  // load there, whose wait also waits for the LDS reads)
+  typedef const __attribute__((address_space(1))) char* gptr;
+  gptr zpage = (gptr)g_zero_page;
+  asm volatile("" : "+s"(zpage));
+  // this lane's activation row of every M tile (rows past the tile repeat its last row)
+  const unsigned short* arow[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int r = min(mt * 16 + (lane & 15), rows - 1);
+    const int srow = GU ? args.perm_src[p0 + r] / args.k : p0 + r;
+    arow[mt] = args.a + (size_t)srow * K + (lane >> 4) * 8;
+  }
+
+  f32x4 acc[MT][NSTR];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int s = 0; s < NSTR; ++s) acc[mt][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nfull = nks / 4;                // whole stages
+  const bool part = (nks & 3) != 0;         // one partial stage after them
+  struct WStage {
+    u32x4 code[NSTR];
+    unsigned scale[NSTR][SB];
+  };
+  // every load unconditional: past the whole stages they read the zero page
+  auto load_w = [&](WStage& S, int st, bool valid) {
+#pragma unroll
+    for (int s = 0; s < NSTR; ++s) {
+      gptr cb = valid ? (gptr)(cbase[s] + (size_t)st * 1024) : zpage;
+      S.code[s] = __builtin_nontemporal_load((const __attribute__((address_space(1))) u32x4*)(cb + lane16));
+      gptr sc = valid ? (gptr)(sbase[s] + (size_t)st * 64 * SB) : zpage;
+      sc += lrow * 4 * SB;
+      if constexpr (SB == 1) {
+        S.scale[s][0] = __builtin_nontemporal_load((const __attribute__((address_space(1))) unsigned*)sc);
+      } else {
+        const u32x2 v = __builtin_nontemporal_load((const __attribute__((address_space(1))) u32x2*)sc);
+        S.scale[s][0] = v[0], S.scale[s][1] = v[1];
+      }
+    }
+  };
+  // this wave's share of stage st's activation fragments: wave q loads fragments f = q * MT + mt
+  // (k-step q of every M tile), 16 bytes per lane in lane order, straight into the stage's LDS
+  // buffer
+  auto load_a = [&](int st, bool valid) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int q = wave, f = q * MT + mt;
+      gptr g = valid ? (gptr)(arow[mt] + (KPS * st + q) * 32) : zpage + lane16;
+      unsigned char* l = a_lds + ((size_t)(st % NBUF) * NA + f) * 1024;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                       (__attribute__((address_space(3))) void*)l, 16, 0, 0);
+    }
+  };
+  auto compute = [&](const WStage& S, const OpT (&a)[KPS][MT]) {
+#pragma unroll
+    for (int q = 0; q < KPS; ++q) {
+#pragma unroll
+      for (int s = 0; s < NSTR; ++s) {
+        OpT b;
+        if constexpr (FMT == MOE_W_MXFP4) {
+          b = dec_mxfp4(S.code[s][q], (S.scale[s][0] >> (8 * q)) & 255);
+        } else {
+          const unsigned sw = S.scale[s][q >> 1];
+          b = dec_int4(S.code[s][q], __builtin_bit_cast(_Float16, (unsigned short)(sw >> (16 * (q & 1)))));
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[mt][s] = mfma(a[q][mt], b, acc[mt][s]);
+      }
+    }
+  };
+  auto read_a = [&](OpT (&a)[KPS][MT], int st) {
+    const unsigned char* l = a_lds + (size_t)(st % NBUF) * NA * 1024 + lane16;
+#pragma unroll
+    for (int q = 0; q < KPS; ++q)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) a[q][mt] = *(const OpT*)(l + (q * MT + mt) * 1024);
+  };
+
+  WStage ring[PF];
+  // stages in order (the waits count this wave's loads in issue order)
+#pragma unroll
+  for (int i = 0; i < PF; ++i) {
+    load_w(ring[i], i, i < nfull);
+    load_a(i, i < nfull);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  int base = 0;
+  for (; base + PF <= nfull; base += PF) {
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      const int st = base + i;
+      MOE_WAIT_VMCNT((PF - 1) * L);  // this wave's loads of stage st have landed
+      barrier_keep_loads();          // every wave's: stage st is in LDS, stage st - 1 is read
+      __builtin_amdgcn_sched_barrier(0);
+      OpT a[KPS][MT];
+      read_a(a, st);
+      compute(ring[i], a);
+      load_w(ring[i], st + PF, st + PF < nfull);
+      load_a(st + PF, st + PF < nfull);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // the last nfull - base (< PF) stages are already loaded
+  __builtin_amdgcn_s_waitcnt(0);
+  barrier_keep_loads();
+#pragma unroll
+  for (int i = 0; i < PF - 1; ++i) {
+    if (base + i < nfull) {
+      OpT a[KPS][MT];
+      read_a(a, base + i);
+      compute(ring[i], a);
+    }
+  }
+  // the partial last chunk: ns k-steps packed 4 * ns bytes per lane; the missing k-steps get
+  // zero codes, zero scales and zero activations
+  if (part) {
+    const int st = nfull, ns = nks - 4 * st;
+    WStage S;
+#pragma unroll
+    for (int s = 0; s < NSTR; ++s) {
+      const char* cb = cbase[s] + (size_t)st * 1024 + (size_t)lane * 4 * ns;
+      const char* sb = sbase[s] + ((size_t)st * 64 + lrow * ns) * SB;
+      unsigned c[4] = {0, 0, 0, 0}, sc[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (q < ns) {
+          c[q] = *(const unsigned*)(cb + 4 * q);
+          sc[q] = SB == 1 ? (unsigned)*(const unsigned char*)(sb + q) : (unsigned)*(const unsigned short*)(sb + 2 * q);
+        }
+      }
+      S.code[s] = u32x4{c[0], c[1], c[2], c[3]};
+      if constexpr (SB == 1) {
+        S.scale[s][0] = sc[0] | (sc[1] << 8) | (sc[2] << 16) | (sc[3] << 24);
+      } else {
+        S.scale[s][0] = sc[0] | (sc[1] << 16);
+        S.scale[s][1] = sc[2] | (sc[3] << 16);
+      }
+    }
+    OpT a[KPS][MT];
+#pragma unroll
+    for (int q = 0; q < KPS; ++q)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        OpT v = OpT{0, 0, 0, 0, 0, 0, 0, 0};
+        if (q < ns) v = *(const OpT*)(arow[mt] + (KPS * st + q) * 32);
+        a[q][mt] = v;
+      }
+    compute(S, a);
+  }
+  // ---- epilogue: this wave's strips
+#pragma unroll
+  for (int p = 0; p < NPW; ++p) {
+    const int u = u0 + p;
+    if (u >= n_units) continue;
+    const int col = u * 16 + (lane & 15);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = mt * 16 + (lane >> 4) * 4 + r;
+        if (row >= rows) continue;
+        const size_t pr = (size_t)(p0 + row);
+        if constexpr (GU) {
+          const float h = silu(acc[mt][p * 2][r]) * acc[mt][p * 2 + 1][r];
+          unsigned short hb;
+          if constexpr (FMT == MOE_W_INT4G32)
+            hb = __builtin_bit_cast(unsigned short, (_Float16)h);
+          else
+            hb = f32_to_bf16_rne(h);
+          ((unsigned short*)args.out)[pr * N + col] = hb;
+        } else {
+          ((float*)args.out)[pr * N + col] = acc[mt][p][r];
+        }
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ row-tile plan
 
 // One workgroup of 1024 threads, thread e for expert e (E <= 1024): experts whose row count lies
@@ -531,6 +770,21 @@ void launch_stream_cfg(bool gate_up, const FfnArgs& a, int H, int I, int S, hipS
   // one workgroup per (unit group, row tile) at most, rounded up to whole rounds of the 8 XCDs
   auto grid8 = [](int g, int S) { return (unsigned)(((long long)g * S + 7) / 8 * 8); };
   typedef Cfg<FMT, MT, NARROW> C;
+  if constexpr (FMT != MOE_W_BF16 && !NARROW) {
+    // 4-bit weights, many experts touched: shared activations (4 waves, each 1 gate/up unit or
+    // 2 down strips, over the whole contraction)
+    constexpr int NW = 4, GU_NPW = 1, D_NPW = 2, PF = 2;
+    if (gate_up) {
+      const int gx = (I / 16 + NW * GU_NPW - 1) / (NW * GU_NPW);
+      hipLaunchKernelGGL((ffn_stream_sa_kernel<FMT, MT, NW, GU_NPW, PF, true>), dim3(grid8(gx, S)), dim3(64 * NW), 0,
+                         s, a);
+    } else {
+      const int dx = (H / 16 + NW * D_NPW - 1) / (NW * D_NPW);
+      hipLaunchKernelGGL((ffn_stream_sa_kernel<FMT, MT, NW, D_NPW, PF, false>), dim3(grid8(dx, S)), dim3(64 * NW), 0,
+                         s, a);
+    }
+    return;
+  }
   if (gate_up) {
     const int gx = (I / 16 + C::GU_NP - 1) / C::GU_NP;
     hipLaunchKernelGGL((ffn_stream_kernel<FMT, MT, C::GU_NW, C::GU_NP, C::GU_PF, true>), dim3(grid8(gx, S)),
