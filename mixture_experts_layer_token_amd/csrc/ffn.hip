@@ -754,6 +754,15 @@ void trace(int i, hipStream_t s) {
 #ifndef MOE_CFG_BF16_GU_NP2
 #define MOE_CFG_BF16_GU_NP2 2  // bf16 gate/up units per workgroup at two M tiles
 #endif
+#ifndef MOE_CFG_Q4S_GU_NPW
+#define MOE_CFG_Q4S_GU_NPW 1  // shared-activation 4-bit kernel: gate/up units per wave
+#endif
+#ifndef MOE_CFG_Q4S_D_NPW
+#define MOE_CFG_Q4S_D_NPW 4  // down strips per wave
+#endif
+#ifndef MOE_CFG_Q4S_PF
+#define MOE_CFG_Q4S_PF 3
+#endif
 template <int FMT, int MT, bool NARROW>
 struct Cfg {
   static constexpr bool Q4 = FMT != MOE_W_BF16;
@@ -771,9 +780,9 @@ void launch_stream_cfg(bool gate_up, const FfnArgs& a, int H, int I, int S, hipS
   auto grid8 = [](int g, int S) { return (unsigned)(((long long)g * S + 7) / 8 * 8); };
   typedef Cfg<FMT, MT, NARROW> C;
   if constexpr (FMT != MOE_W_BF16 && !NARROW) {
-    // 4-bit weights, many experts touched: shared activations (4 waves, each 1 gate/up unit or
-    // 2 down strips, over the whole contraction)
-    constexpr int NW = 4, GU_NPW = 1, D_NPW = 2, PF = 2;
+    // 4-bit weights, many experts touched: shared activations (4 waves, each with its gate/up
+    // units or down strips over the whole contraction)
+    constexpr int NW = 4, GU_NPW = MOE_CFG_Q4S_GU_NPW, D_NPW = MOE_CFG_Q4S_D_NPW, PF = MOE_CFG_Q4S_PF;
     if (gate_up) {
       const int gx = (I / 16 + NW * GU_NPW - 1) / (NW * GU_NPW);
       hipLaunchKernelGGL((ffn_stream_sa_kernel<FMT, MT, NW, GU_NPW, PF, true>), dim3(grid8(gx, S)), dim3(64 * NW), 0,
