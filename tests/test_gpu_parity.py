@@ -214,6 +214,23 @@ def test_layer_hot_expert_split(fmt):
     assert_output_close(to_f64(out), ref, "bf16", wl.name)
 
 
+@pytest.mark.parametrize("fmt", ["mxfp4", "int4g32"])
+@pytest.mark.parametrize("T", [64, 200])
+def test_layer_many_experts_4bit(fmt, T):
+    """Many experts touched (E = 128, top-8) at small H and I with ragged 4-bit chunks: the streaming
+    kernel with activations shared through LDS, at one (T = 64) and two (T = 200) M tiles."""
+    wl = small_variant(fmt, E=128, k=8, name="wide-" + fmt)
+    say("many experts", wl.name, "T", T)
+    x, _ = oracle.rank_gap_inputs(wl, T)
+    layer = build_layer(wl, T)
+    out = layer.forward(to_device_act(x, "bf16"), mode="decode")
+    torch.cuda.synchronize()
+    assert (layer.counts.cpu().numpy() > 0).sum() > 64  # wide: most experts have rows
+    ref, ids_ref, _ = oracle_reference(wl, x, np.arange(T))
+    assert np.array_equal(layer.topk_ids[:T].cpu().numpy(), ids_ref)
+    assert_output_close(to_f64(out), ref, "bf16", wl.name)
+
+
 def test_tiny_config_full():
     wl = W.WORKLOADS["tiny"]
     T = wl.Ts[0]
