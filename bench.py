@@ -379,8 +379,11 @@ def run_offload(args):
         model.reset_cache()
         for l in range(wl.layers):  # warm the kernels through the full path (the cache is reset below)
             model.layer_forward(l, 0, xs[(l, 0)], out)
-        for policy, period in POLICIES:
-            model.reset_cache(policy, period)
+        # every policy with the FFN of the hits overlapping the copies, and the reported policy once
+        # without the overlap
+        variants = [(p, d, True) for p, d in POLICIES] + ([(*POLICIES[-1], False)] if T == Ts[0] else [])
+        for policy, period, overlap in variants:
+            model.reset_cache(policy, period, overlap)
             torch.cuda.synchronize()
             t0 = time.perf_counter()
             for s in range(steps):
@@ -403,8 +406,9 @@ def run_offload(args):
                     if key not in seen:
                         seen.add(key)
                         cold += 1
-            runs[(T, policy)] = {
+            runs[(T, policy, overlap)] = {
                 "T": T, "policy": policy if policy == "lru" else "%s/%d" % (policy, period), "steps": steps,
+                "ffn_of_hits_during_copies": overlap,
                 "layers": wl.layers, "wall_s": wall, "tokens_per_s": T * steps / wall,
                 "hit_rate": st["hits"] / max(1, st["lookups"]),
                 "hit_rate_cold_excluded": st["hits"] / max(1, st["lookups"] - cold),
@@ -414,7 +418,7 @@ def run_offload(args):
                 "copy_busy_s": model.copy_ms / 1e3,
                 "link_gbps_busy": st["bytes_fetched"] / max(1e-9, model.copy_ms / 1e3) / 1e9,
                 "link_gbps_wall": st["bytes_fetched"] / wall / 1e9}
-    head = runs[(Ts[0], POLICIES[-1][0])]
+    head = runs[(Ts[0], POLICIES[-1][0], True)]
     out = {
         "metric": "MoE-layer tokens/s (offloaded expert bank, decode) + expert-cache hit rate + link GB/s",
         "value": round(head["tokens_per_s"], 2),
@@ -430,7 +434,8 @@ def run_offload(args):
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights quantized to int4g32)",
         "config": {"workload": wl.name, "T": Ts[0], "layers": wl.layers, "hidden": wl.H, "experts": wl.E,
                    "top_k": wl.k, "inter": wl.I, "cache_slots": model.capacity,
-                   "cache_policy": head["policy"], "bank_bytes": wl.layers * wl.E * model.pkg_bytes},
+                   "cache_policy": head["policy"], "ffn_of_hits_during_copies": True,
+                   "bank_bytes": wl.layers * wl.E * model.pkg_bytes},
         "roofline": {"bound": "link", "kernel": "hipMemcpyAsync host bank -> HBM slots (copy stream)",
                      "achieved": round(head["link_gbps_busy"], 2), "peak": PCIE_PEAK_GBS, "unit": "GB/s",
                      "frac": round(head["link_gbps_busy"] / PCIE_PEAK_GBS, 4), "traffic": None},

@@ -5,10 +5,14 @@ the most recently used ones ("What expert offloading actually costs", section
 "Inside expert paging": expert math stays on the GPU, weights stream in on
 demand and are addressed through stable logical slots).  Per layer and step:
 
-  route (compute stream) -> ids to the host -> moe_cache_plan (host LRU) ->
+  route (compute stream) -> ids to the host -> moe_cache_plan (host policy) ->
   moe_cache_fetch (one hipMemcpyAsync per miss + the slot table, copy stream,
-  event) -> the compute stream waits for the event -> permute -> grouped FFN
-  reading packages through the slot table -> combine.
+  event) -> permute -> grouped FFN over the experts that were already resident
+  (their slots only; the misses' entries are -1) -> the compute stream waits for
+  the event -> grouped FFN over the fetched experts -> combine.
+
+The FFN of the hits runs while the misses stream in (with `overlap=False` the
+whole FFN waits for the copies).
 
 Layers run strictly in order.  A slot evicted by a plan is never in use: the
 host waits for the router of the layer being planned, and every earlier FFN
@@ -59,7 +63,7 @@ class OffloadedModel:
     """L MoE layers whose experts live in a pinned host bank, cached in an HBM slot pool."""
 
     def __init__(self, wl, max_T: int, capacity: int | None = None, device="cuda", fill=True, policy="lru",
-                 decay_period=0):
+                 decay_period=0, overlap=True):
         from synth import workloads as W
 
         self.wl = wl
@@ -76,6 +80,15 @@ class OffloadedModel:
         self.cache = api.ExpertCache(self.bank, self.pkg_bytes, self.L, self.E, self.pool, self.stride,
                                      self.capacity, policy, decay_period)
         self.slot_tables = [torch.full((self.E,), -1, dtype=torch.int32, device=device) for _ in range(self.L)]
+        # slot tables of the two FFN passes (hits only, misses only), staged from pinned host memory;
+        # a layer's staging buffers are rewritten only after its previous copies ran (the host waits
+        # for that layer's router first)
+        self.overlap = overlap
+        i32 = dict(dtype=torch.int32)
+        self.pass_dev = [[torch.full((self.E,), -1, device=device, **i32) for _ in range(2)] for _ in range(self.L)]
+        self.pass_host = [[torch.full((self.E,), -1, pin_memory=True, **i32) for _ in range(2)] for _ in range(self.L)]
+        self.pass_desc = [[api.experts_desc(wl.H, wl.I, wl.E, wl.wfmt, self.pool, self.stride, t, self.capacity)
+                           for t in pd] for pd in self.pass_dev]
         self.wg = [to_device_act(W.router_weights(wl, l), wl.xdt, device) for l in range(self.L)]
         self.bias_cache = {}
         self.layers = []
@@ -95,8 +108,10 @@ class OffloadedModel:
         self.groups = []
         self.filled = {}
 
-    def reset_cache(self, policy=None, decay_period=None):
+    def reset_cache(self, policy=None, decay_period=None, overlap=None):
         """Empty the HBM cache (a new planner, optionally with another policy) and the run records."""
+        if overlap is not None:
+            self.overlap = overlap
         if policy is not None:
             self.policy = policy
         if decay_period is not None:
@@ -150,14 +165,31 @@ class OffloadedModel:
         plan = self.cache.plan(l, hid)
         self.plans.append((step, l, plan.n_ids, plan.n_hits, plan.n_misses))
         self.groups.append(set((l * self.E + hid.ravel()).tolist()))
+        split = self.overlap and plan.n_hits > 0 and plan.n_misses > 0
+        if split:
+            table = np.ctypeslib.as_array(plan.slot_of_expert)[:self.E]
+            miss = np.ctypeslib.as_array(plan.miss_ids)[:plan.n_misses]
+            hit_t, miss_t = (h.numpy() for h in self.pass_host[l])
+            hit_t[:] = table
+            hit_t[miss] = -1
+            miss_t[:] = -1
+            miss_t[miss] = table[miss]
+            for dev, host in zip(self.pass_dev[l], self.pass_host[l]):
+                dev.copy_(host, non_blocking=True)
         if time_copies:
             self.copy_t0.record(self.copy_stream)
         self.cache.fetch(plan, self.slot_tables[l], self.copy_stream, self.done)
         if time_copies:
             self.copy_t1.record(self.copy_stream)
-        torch.cuda.current_stream().wait_event(self.done)
-        api.moe_permute(ids, self.E, lay.counts, lay.offsets, lay.perm_src[:T * k], lay.inv_perm[:T * k], lay.pws)
-        api.moe_expert_ffn(lay.desc, x, k, lay.offsets, lay.perm_src, lay.y_perm, lay.ws)
+        if split:
+            api.moe_permute(ids, self.E, lay.counts, lay.offsets, lay.perm_src[:T * k], lay.inv_perm[:T * k], lay.pws)
+            api.moe_expert_ffn(self.pass_desc[l][0], x, k, lay.offsets, lay.perm_src, lay.y_perm, lay.ws)
+            torch.cuda.current_stream().wait_event(self.done)
+            api.moe_expert_ffn(self.pass_desc[l][1], x, k, lay.offsets, lay.perm_src, lay.y_perm, lay.ws)
+        else:
+            torch.cuda.current_stream().wait_event(self.done)
+            api.moe_permute(ids, self.E, lay.counts, lay.offsets, lay.perm_src[:T * k], lay.inv_perm[:T * k], lay.pws)
+            api.moe_expert_ffn(lay.desc, x, k, lay.offsets, lay.perm_src, lay.y_perm, lay.ws)
         api.moe_combine(lay.y_perm, w, lay.inv_perm, k, None, out)
         if time_copies:
             self.copy_t1.synchronize()

@@ -23,13 +23,14 @@ def _gpu():
     moe.lib()
 
 
-def run_and_check(wl, T, steps, check_steps, fill_all=True, capacity=None, policy="lru", period=0):
+def run_and_check(wl, T, steps, check_steps, fill_all=True, capacity=None, policy="lru", period=0, overlap=True):
     xs = {}
     for s in range(steps):
         for l in range(wl.layers):
             x, _ = oracle.rank_gap_inputs(wl, T, layer=l, step=s)
             xs[(l, s)] = x
-    model = OffloadedModel(wl, T, capacity=capacity, fill=fill_all, policy=policy, decay_period=period)
+    model = OffloadedModel(wl, T, capacity=capacity, fill=fill_all, policy=policy, decay_period=period,
+                           overlap=overlap)
     if not fill_all:  # only the experts some step routes to (the others are never fetched)
         touched = {l: set() for l in range(wl.layers)}
         for (l, s), x in xs.items():
@@ -81,11 +82,14 @@ def run_and_check(wl, T, steps, check_steps, fill_all=True, capacity=None, polic
     model.close()
 
 
-def test_offload_small_all_steps():
+@pytest.mark.parametrize("overlap", [True, False])
+def test_offload_small_all_steps(overlap):
+    """Every step checked; the FFN of the hits during the copies (two passes over the slot
+    tables), or the whole FFN after them."""
     wl = W.Workload(name="offload-small", H=224, E=16, k=4, I=352, wfmt="int4g32", xdt="bf16", Ts=(5,), seed=606,
                     zipf_s=1.2, layers=3, steps=24, rerank_every=8, cache_frac=0.25)
-    say("offload small")
-    run_and_check(wl, 5, wl.steps, set(range(wl.steps)))
+    say("offload small, overlap", overlap)
+    run_and_check(wl, 5, wl.steps, set(range(wl.steps)), overlap=overlap)
 
 
 def test_offload_small_frequency_policy():
