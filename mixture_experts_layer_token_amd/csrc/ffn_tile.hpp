@@ -347,7 +347,9 @@ __device__ __forceinline__ void tile_body(const FfnArgs& args, const TileCtx& c,
             static_for<NMT>([&](auto mtc) {
               constexpr int mt = mtc;
               constexpr int r = j * NMT + mt;
-              mfma_acc<Q4 && mt == 0>(acc[mt][j], acur[mt], __builtin_bit_cast(OpT, b));
+              // the first MFMA of a strip reads the operand decoded during the previous strip; with
+              // at least 10 M tiles the decode ends two MFMAs before the strip does (no wait states)
+              mfma_acc<Q4 && mt == 0 && NMT < 10>(acc[mt][j], acur[mt], __builtin_bit_cast(OpT, b));
               // the next strip's operand: 8 sub-steps over this strip's MFMAs, done before its last
               if constexpr (Q4) {
                 constexpr int T = NMT > 1 ? NMT - 1 : 1;
