@@ -23,7 +23,8 @@
 //    between consecutive MFMAs sits at most a step or two of other work (the decode of the next
 //    strip's operand, an A-fragment read for the next k-step, one load of the block kD-1 ahead);
 //  - gate/up epilogue: SiLU(g) * u on the lane's own (gate, up) pair, rounded once to h;
-//    down epilogue: fp32 y_perm.
+//    down epilogue: fp32 y_perm; both staged through LDS per 16-row tile, so that the stores
+//    are 16 bytes of one row per lane rather than 4 bytes of a column.
 // Work order is XCD-aware: consecutive work items (all column blocks of a row tile, then the
 // next row tile of the same expert) go to the same XCD, so one L2 holds the tile's activations
 // and the expert's weights while they are reused.
@@ -48,6 +49,11 @@ constexpr int kXCD = 8;   // XCDs of an MI355X; workgroup i is dispatched to XCD
 #ifndef MOE_CFG_TILE_D_Q4
 #define MOE_CFG_TILE_D_Q4 4
 #endif
+// Epilogue staging, one area per wave: 16 rows x 64 fp32 (down) or 16 rows x 32 h values (gate/up),
+// row pitches padded so that the column-wise writes of a wave hit distinct banks.
+constexpr int kEpiPitchY = 68;  // floats
+constexpr int kEpiPitchH = 40;  // 16-bit values
+constexpr int kEpiBytes = 16 * kEpiPitchY * 4;
 template <int FMT>
 struct TileCfg {
   static constexpr int BK = FMT == MOE_W_BF16 ? 32 : 64;  // K per block
@@ -55,7 +61,7 @@ struct TileCfg {
   // 4-bit weights and costs 12 more registers); even kD * BK / 32 keeps the register buffers of
   // A fragments in step across loop iterations
   static constexpr int D = FMT == MOE_W_BF16 ? MOE_CFG_TILE_D_BF16 : MOE_CFG_TILE_D_Q4;
-  static constexpr size_t LDS = (size_t)D * kTM * BK * 2;  // kD ring buffers
+  static constexpr size_t LDS = (size_t)D * kTM * BK * 2 + kTW * kEpiBytes;  // kD ring buffers, epilogue
 };
 
 // In-place MFMA on an accumulator held in AGPRs, written as inline assembly: with the compiler's
@@ -436,35 +442,54 @@ __device__ __forceinline__ void tile_body(const FfnArgs& args, const TileCtx& c,
   for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
     for (int j = 0; j < kWNS; ++j) asm volatile("" : "+a"(acc[mt][j]));
+  // The lane holds 4 consecutive rows of one column of each MFMA tile; every 16-row tile passes
+  // through the wave's own LDS area (no barrier: a wave's LDS accesses complete in order), so
+  // each lane stores 16 contiguous bytes of one row.  Down: 16 x 64 fp32, read back as 4 rows of
+  // 256 bytes per store; gate/up: 16 x 32 h values, read back as 16 rows of 64 bytes.
+  const int g = lane >> 4, cl = lane & 15;
+  char* const ep = (char*)(lds_a + (size_t)kD * kTM * BK) + (size_t)wave * kEpiBytes;
+  if constexpr (GU) {
+    // h columns of the wave: strip pair u = (col*16 + wave*4 + 2p) / 2 -> columns 16u + [0, 16)
+    const int hc = (c.col * 8 + wave * 2) * 16 + (lane & 3) * 8;  // this lane's 8 stored columns
+    const bool col_ok = hc < args.I;
 #pragma unroll
-  for (int mt = 0; mt < NMT; ++mt) {
+    for (int mt = 0; mt < NMT; ++mt) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = mt * 16 + (lane >> 4) * 4 + r;
-      if (row >= c.rows) continue;
-      const size_t pr = (size_t)(c.p0 + row);
-      if constexpr (GU) {
+      for (int p = 0; p < 2; ++p)
 #pragma unroll
-        for (int j = 0; j < kWNS; j += 2) {
-          const int gs = c.col * 16 + wave * kWNS + j;  // gate strip 2u, up strip 2u + 1
-          if (gs + 1 >= c.n_strips) continue;
-          const int f = (gs >> 1) * 16 + (lane & 15);
-          const float hv = silu(acc[mt][j][r]) * acc[mt][j + 1][r];
+        for (int r = 0; r < 4; ++r) {
+          const float hv = silu(acc[mt][2 * p][r]) * acc[mt][2 * p + 1][r];
           unsigned short hb;
           if constexpr (FMT == MOE_W_INT4G32)
             hb = __builtin_bit_cast(unsigned short, (_Float16)hv);
           else
             hb = f32_to_bf16_rne(hv);
-          ((unsigned short*)args.out)[pr * args.I + f] = hb;
+          *(unsigned short*)(ep + ((4 * g + r) * kEpiPitchH + 16 * p + cl) * 2) = hb;
         }
-      } else {
+      const int R = lane >> 2;
+      const u32x4 v = *(const u32x4*)(ep + (R * kEpiPitchH + (lane & 3) * 8) * 2);
+      __builtin_amdgcn_sched_barrier(0);
+      if (col_ok && mt * 16 + R < c.rows)
+        *(__attribute__((address_space(1))) u32x4*)((unsigned short*)args.out + (size_t)(c.p0 + mt * 16 + R) * args.I + hc) = v;
+    }
+  } else {
+    const int yc = c.col * (kWNS * kTW * 16) + wave * (kWNS * 16) + cl * 4;  // this lane's 4 columns
+    const bool col_ok = yc < c.N;
 #pragma unroll
-        for (int j = 0; j < kWNS; ++j) {
-          const int s = c.col * 16 + wave * kWNS + j;
-          if (s >= c.n_strips) continue;
-          ((float*)args.out)[pr * args.H + s * 16 + (lane & 15)] = acc[mt][j][r];
-        }
-      }
+    for (int mt = 0; mt < NMT; ++mt) {
+#pragma unroll
+      for (int j = 0; j < kWNS; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) *(float*)(ep + ((4 * g + r) * kEpiPitchY + 16 * j + cl) * 4) = acc[mt][j][r];
+      f32x4 v[4];  // all four reads in flight before the first store
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = *(const f32x4*)(ep + ((4 * q + g) * kEpiPitchY + cl * 4) * 4);
+      __builtin_amdgcn_sched_barrier(0);
+      float* const yrow = (float*)args.out + (size_t)(c.p0 + mt * 16 + g) * args.H + yc;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (col_ok && mt * 16 + 4 * q + g < c.rows)
+          *(__attribute__((address_space(1))) f32x4*)(yrow + (size_t)(4 * q) * args.H) = v[q];
     }
   }
 }
