@@ -91,7 +91,7 @@ int moe_route(const void* x, int xdt, int T, int H, const void* w_router, const 
 /* Workspace bytes moe_route needs (device, 256-byte aligned; 0 when none).  bf16 batches with
  * T*E <= 2^20 spread the router over many workgroups and keep partial logits there; larger bf16
  * batches with E a multiple of 16 keep the router matrix repacked into MFMA fragments
- * (E*H*2 bytes) and the [T][E] fp32 logits there. */
+ * (E*H*2 bytes), the [T][E] fp32 logits and the row-tile plan of the MFMA kernel there. */
 size_t moe_route_workspace(int T, int H, int E, int xdt);
 
 /* ------------------------------------------------------------- permutation */
@@ -163,7 +163,9 @@ typedef struct {
                                     y_perm are not written); ignored when slot_of_expert is NULL */
 } moe_experts;
 
-/* Workspace bytes moe_expert_ffn needs for these experts, T tokens and top-k. */
+/* Workspace bytes moe_expert_ffn needs for these experts, T tokens and top-k: the activations
+ * cast to the MFMA operand type when they differ from it, h [T*k][I], and the row-tile plans
+ * (with the work counters of the persistent prefill kernels). */
 size_t moe_ffn_workspace(const moe_experts* w, int T, int k, int mode);
 
 /*

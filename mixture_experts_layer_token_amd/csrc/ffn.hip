@@ -536,14 +536,17 @@ __global__ __launch_bounds__(NW * 64, 2) void ffn_stream_sa_kernel(FfnArgs args)
 // ------------------------------------------------------------------ row-tile plan
 
 // One workgroup of 1024 threads, thread e for expert e (E <= 1024): experts whose row count lies
-// in [lo, hi] and whose slot is resident are cut into tiles of mr rows, in expert order;
+// in [lo, hi] and whose slot is resident are cut into ceil(rows / mr) tiles, in expert order;
 // plan[0] = {number of tiles}, plan[1 + i] = {first tile of its expert, the expert's first grouped
-// row, the expert's rows, its slot} for every tile i.
+// row, the expert's rows, its slot} for every tile i.  Also zeroes zero[0, nzero) (the work
+// counters of the tile kernels that read this plan).
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ offsets, int E, int mr, int lo,
                                                     int hi, const int32_t* __restrict__ slot_of_expert,
-                                                    int n_slots, int4* __restrict__ plan) {
+                                                    int n_slots, int4* __restrict__ plan, int* __restrict__ zero,
+                                                    int nzero) {
   __shared__ int wsum[16];
   const int e = threadIdx.x, lane = e & 63, wave = e >> 6;
+  if (e < nzero) zero[e] = 0;
   int c = 0, o0 = 0, slot = -1;
   if (e < E) {
     o0 = offsets[e];
@@ -688,7 +691,7 @@ __global__ void dequant_f32_kernel(const float* __restrict__ pkg, size_t n, floa
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-  size_t cast_off, cast_bytes, h_off, h_bytes, plan_off, plan_bytes, total;
+  size_t cast_off, cast_bytes, h_off, h_bytes, plan_off, plan_bytes, tplan_off, tplan_bytes, total;
 };
 
 WsLayout ws_layout(const moe_experts* w, int T, int k, int xdt) {
@@ -704,7 +707,11 @@ WsLayout ws_layout(const moe_experts* w, int T, int k, int xdt) {
   // row-tile plan of the streaming kernels: at most n / 16 + min(n, E) tiles
   L.plan_off = L.h_off + L.h_bytes;
   L.plan_bytes = f32w ? 0 : align256((1 + n / 16 + (n < (size_t)w->E ? n : (size_t)w->E)) * sizeof(int4));
-  L.total = L.plan_off + L.plan_bytes;
+  // row-tile plan of the tile kernels (at most n / 192 + min(n, E) tiles), then their work
+  // counters (8 for gate/up, 8 for down)
+  L.tplan_off = L.plan_off + L.plan_bytes;
+  L.tplan_bytes = f32w ? 0 : align256((1 + n / 192 + (n < (size_t)w->E ? n : (size_t)w->E)) * sizeof(int4)) + 256;
+  L.total = L.tplan_off + L.tplan_bytes;
   return L;
 }
 
@@ -933,8 +940,17 @@ int launch_ffn(const moe_experts* w, const void* x, int xdt, int T, int k, const
   if (use_stream) {
     int4* plan = (int4*)(wsp + L.plan_off);
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, offsets, E, mr, 1, split, w->slot_of_expert,
-                       gu.n_slots, plan);
+                       gu.n_slots, plan, (int*)nullptr, 0);
     gu_s.plan = dn_s.plan = plan;
+  }
+  if (use_tile) {
+    int4* tplan = (int4*)(wsp + L.tplan_off);
+    int* counters = (int*)(wsp + L.tplan_off + L.tplan_bytes - 256);
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, offsets, E, 192, gu_t.min_rows, 0x7FFFFFFF,
+                       w->slot_of_expert, gu.n_slots, tplan, counters, 16);
+    gu_t.plan = dn_t.plan = tplan;
+    gu_t.tcount = counters;
+    dn_t.tcount = counters + 8;
   }
   trace(0, s);
   int rc = MOE_OK;

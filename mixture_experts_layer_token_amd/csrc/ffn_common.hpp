@@ -149,10 +149,11 @@ struct FfnArgs {
   void* out;                // GU: h [T*k][I] (operand type); down: y_perm [T*k][H] fp32
   int H, I, E, k;
   size_t region_codes, region_scales;  // byte offsets of this matrix's codes / scales in a package
-  // streaming variant: plan[0].x = row tiles; plan[1 + t] = {first tile of the expert of tile t,
-  // the expert's first grouped row, its rows, its slot}, written by the plan kernel from the
-  // offsets and the slot table
+  // row tiles (16 * mt rows for the streaming variant, 192 for the tile variant): plan[0].x =
+  // tiles; plan[1 + t] = {first tile of the expert of tile t, the expert's first grouped row, its
+  // rows, its slot}, written by the plan kernel from the offsets and the slot table
   const int4* plan;
+  int* tcount;  // tile variant: [8] work counters, one per XCD range, zeroed by the plan kernel
 };
 
 

@@ -62,6 +62,23 @@ struct TileCfg {
   // A fragments in step across loop iterations
   static constexpr int D = FMT == MOE_W_BF16 ? MOE_CFG_TILE_D_BF16 : MOE_CFG_TILE_D_Q4;
   static constexpr size_t LDS = (size_t)D * kTM * BK * 2 + kTW * kEpiBytes;  // kD ring buffers, epilogue
+  static constexpr int CPR = BK / 8;    // 16-byte chunks per staged row
+  static constexpr int RPI = 64 / CPR;  // rows per wave-wide direct-to-LDS load
+  // activation loads per wave and block of a full 192-row tile: load i of wave w fills rows
+  // (i*kTW + w)*RPI + [0, RPI)
+  static constexpr int IPW_MAX = (kTM + kTW * RPI - 1) / (kTW * RPI);
+  static constexpr bool Q4 = FMT != MOE_W_BF16;
+  static constexpr int KS = BK / 32;         // k-steps per block
+  static constexpr int NBL = Q4 ? 2 : KS;    // weight loads per strip and block
+  static constexpr int SB = FMT == MOE_W_MXFP4 ? 1 : 2;  // scale bytes
+};
+
+// weight registers of one K block.  bf16: KS fragments of 16 bytes per strip.  4-bit: half of
+// the lane's 16-byte word of a 4-k-step chunk (8 bytes, 2 k-steps) and the 2 matching scales.
+template <int FMT>
+struct TileB {
+  unsigned v[kWNS][TileCfg<FMT>::Q4 ? 2 : 4 * TileCfg<FMT>::KS];
+  unsigned sc[kWNS];
 };
 
 // In-place MFMA on an accumulator held in AGPRs, written as inline assembly: with the compiler's
@@ -116,15 +133,179 @@ typedef const __attribute__((address_space(1))) char* gptr;
 // What every row-tile body needs: the work item and the matrix it multiplies.
 struct TileCtx {
   int K, N, n_strips, nks, nkb, nfb;
-  int lane, wave, p0, rows, col;
+  int lane, wave, p0, rows, col, slot;
+};
+
+// Weight bases of the wave's strips, computed per tile from c.slot and c.col (pointers carried
+// across the persistent loop would be kept in vector registers).
+struct TileBases {
   const char* cbase[kWNS];  // code base of each of the wave's strips
   const char* sbase[kWNS];  // scale base of each strip
 };
 
-// One row tile of NMT 16-row MFMA tiles (rows <= 16 * NMT).
+// Work item w (row tile w / ncol, column tile w % ncol) from the tile plan: plan[1 + t] = {first
+// tile of the expert, the expert's first grouped row, its rows, its slot}; an expert with n rows
+// has ceil(n / 192) tiles, tile i covering rows [i*n/nt, (i+1)*n/nt).  w is uniform.
+// Integer division has no scalar instruction: the quotients (and the plan entry, a vector load
+// once the kernel has stored anything) are moved back to scalar registers, or everything derived
+// from them would stay in vector registers across the persistent loop.
+template <int FMT>
+__device__ __forceinline__ void tile_set_item(const FfnArgs& args, TileCtx& c, int w, int ncol) {
+  const int t = __builtin_amdgcn_readfirstlane(w / ncol);
+  c.col = w - t * ncol;
+  const int4 d = args.plan[1 + t];
+  const int first = __builtin_amdgcn_readfirstlane(d.x), row0 = __builtin_amdgcn_readfirstlane(d.y);
+  const int n = __builtin_amdgcn_readfirstlane(d.z), slot = __builtin_amdgcn_readfirstlane(d.w);
+  const int nt = __builtin_amdgcn_readfirstlane((n + kTM - 1) / kTM), i = t - first;
+  const int r0 = __builtin_amdgcn_readfirstlane((int)((long long)i * n / nt));
+  const int r1 = __builtin_amdgcn_readfirstlane((int)((long long)(i + 1) * n / nt));
+  c.p0 = row0 + r0;
+  c.rows = r1 - r0;
+  c.slot = slot;
+}
+template <int FMT>
+__device__ __forceinline__ TileBases tile_bases(const FfnArgs& args, const TileCtx& c) {
+  TileBases b;
+  const char* pkg = args.packages + (size_t)c.slot * args.pkg_stride;
+  // this wave's strips (clamped into range; results of strips past the end are dropped)
+#pragma unroll
+  for (int j = 0; j < kWNS; ++j) {
+    const int s = min(c.col * 16 + c.wave * kWNS + j, c.n_strips - 1);
+    b.cbase[j] = pkg + args.region_codes + (size_t)s * (TileCfg<FMT>::Q4 ? 8 : 32) * c.K;
+    b.sbase[j] = pkg + args.region_scales + (size_t)s * 16 * c.nks * TileCfg<FMT>::SB;
+  }
+  return b;
+}
+
+// Activation staging: lane l writes slot l % CPR of row l / CPR of its load's rows, so it fetches
+// chunk (l % CPR) ^ (row % CPR) of that row.  Rows past the tile's end repeat row 0 (their
+// results are dropped).  Source row of the lane in activation load i:
+template <int FMT, bool GU>
+__device__ __forceinline__ int tile_a_row(const FfnArgs& args, const TileCtx& c, int i) {
+  constexpr int CPR = TileCfg<FMT>::CPR, RPI = TileCfg<FMT>::RPI;
+  const int r = (i * kTW + c.wave) * RPI + c.lane / CPR;
+  const int rr = r < c.rows ? r : 0;
+  return GU ? args.perm_src[c.p0 + rr] / args.k : c.p0 + rr;
+}
+template <int FMT>
+__device__ __forceinline__ unsigned tile_a_chunk(const TileCtx& c, int i) {
+  constexpr int CPR = TileCfg<FMT>::CPR, RPI = TileCfg<FMT>::RPI;
+  return (unsigned)((c.lane % CPR) ^ (((i * kTW + c.wave) * RPI + c.lane / CPR) % CPR));
+}
+
+// Activation load i of block kb (kb < nfb) into LDS buffer buf: a uniform base plus the lane's
+// 32-bit offset of block 0 (block kb adds kb * BK * 2 bytes).
+template <int FMT>
+__device__ __forceinline__ void tile_load_a(const FfnArgs& args, const TileCtx& c, unsigned short* lds_a,
+                                            unsigned avoff, int i, int kb, int buf) {
+  constexpr int BK = TileCfg<FMT>::BK, RPI = TileCfg<FMT>::RPI;
+  const int r0 = (i * kTW + c.wave) * RPI;
+  gptr g = (gptr)args.a + (size_t)kb * (BK * 2) + avoff;
+  unsigned short* l = lds_a + ((size_t)buf * kTM + r0) * BK;
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                   (__attribute__((address_space(3))) void*)l, 16, 0, 0);
+}
+
+// Weight load L (< kWNS * NBL) of block kb (kb < nfb): one instruction on a scalar base, the
+// per-lane offsets shared by all strips.
+template <int FMT>
+__device__ __forceinline__ void tile_load_b(const TileCtx& c, const TileBases& tb, TileB<FMT>& B, int L, int kb) {
+  constexpr int KS = TileCfg<FMT>::KS, SB = TileCfg<FMT>::SB;
+  const unsigned lane = (unsigned)c.lane;
+  if constexpr (!TileCfg<FMT>::Q4) {
+    const int j = L / KS, q = L % KS;
+    const unsigned off = (unsigned)(kb * KS + q) * 1024u + lane * 16u;
+    const u32x4 v = *(const __attribute__((address_space(1))) u32x4*)((gptr)tb.cbase[j] + off);
+    B.v[j][4 * q] = v[0], B.v[j][4 * q + 1] = v[1], B.v[j][4 * q + 2] = v[2], B.v[j][4 * q + 3] = v[3];
+  } else {
+    const int j = L / 2, part = L % 2;
+    const unsigned ch = (unsigned)kb >> 1, h = (unsigned)kb & 1;
+    if (part == 0) {
+      const unsigned off = ch * 1024u + h * 8u + lane * 16u;
+      const u32x2 v = *(const __attribute__((address_space(1))) u32x2*)((gptr)tb.cbase[j] + off);
+      B.v[j][0] = v[0], B.v[j][1] = v[1];
+    } else {
+      const unsigned off = (ch * 64u + 2u * h) * SB + (lane & 15) * 4u * SB;
+      if constexpr (SB == 1)
+        B.sc[j] = *(const __attribute__((address_space(1))) unsigned short*)((gptr)tb.sbase[j] + off);
+      else
+        B.sc[j] = *(const __attribute__((address_space(1))) unsigned*)((gptr)tb.sbase[j] + off);
+    }
+  }
+}
+
+// The prologue of tile c: its first kD-1 blocks (all of them when nfb < kD-1, the last one
+// repeated), with the activation offsets of all IPW_MAX loads.  It is issued before the tile's own
+// body runs: at the end of the previous tile of the workgroup, while that tile's results are
+// written.  Part b (the source rows of the activation loads, through perm_src for gate/up, and
+// the weights) needs only the ring registers free; part a (the activations, into LDS buffers
+// 0 .. kD-2) needs every wave done with those buffers.
+template <int FMT, bool GU>
+__device__ __forceinline__ void tile_prologue_b(const FfnArgs& args, const TileCtx& c,
+                                                TileB<FMT> (&ring)[TileCfg<FMT>::D],
+                                                int (&rows)[TileCfg<FMT>::IPW_MAX]) {
+  constexpr int kD = TileCfg<FMT>::D, IPW = TileCfg<FMT>::IPW_MAX, NB = kWNS * TileCfg<FMT>::NBL;
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) rows[i] = tile_a_row<FMT, GU>(args, c, i);
+  __builtin_amdgcn_sched_barrier(0);
+  if (c.nfb > 0) {
+    const TileBases tb = tile_bases<FMT>(args, c);
+#pragma unroll
+    for (int i = 0; i < kD - 1; ++i)
+#pragma unroll
+      for (int L = 0; L < NB; ++L) tile_load_b<FMT>(c, tb, ring[i], L, min(i, c.nfb - 1));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+}
+template <int FMT>
+__device__ __forceinline__ void tile_prologue_a(const FfnArgs& args, const TileCtx& c, unsigned short* lds_a,
+                                                unsigned (&avoff)[TileCfg<FMT>::IPW_MAX],
+                                                const int (&rows)[TileCfg<FMT>::IPW_MAX]) {
+  constexpr int kD = TileCfg<FMT>::D, IPW = TileCfg<FMT>::IPW_MAX;
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) avoff[i] = ((unsigned)rows[i] * (unsigned)c.K + tile_a_chunk<FMT>(c, i) * 8) * 2;
+  if (c.nfb > 0) {
+#pragma unroll
+    for (int i = 0; i < kD - 1; ++i)
+#pragma unroll
+      for (int L = 0; L < IPW; ++L) tile_load_a<FMT>(args, c, lds_a, avoff[L], L, min(i, c.nfb - 1), i);
+  }
+}
+
+// Dynamic work distribution over a persistent grid.  The work items are dealt in contiguous
+// ranges of `per` to the 8 XCDs (workgroup i runs on XCD i % 8), so that the column tiles of a
+// row tile (consecutive items) run on one XCD and share its L2; each range has a counter, and a
+// workgroup takes the next item of its own XCD's range, then of the others' once that is drained.
+// Only thread 0 holds the state; an atomic is issued one tile ahead and resolved at the start of
+// the next tile, after that tile's loads were waited for anyway.
+struct TileSched {
+  int* cnt;  // [kXCD] items taken from each range
+  int per, total;
+  int xs, tried, pend;  // range being drained, ranges tried, raw result of the last atomic
+};
+__device__ __forceinline__ int sched_resolve(TileSched& s) {
+  for (;;) {
+    if (s.tried >= kXCD) return -1;
+    if (s.pend < min(s.per, s.total - s.xs * s.per)) return s.xs * s.per + s.pend;
+    if (++s.tried >= kXCD) return -1;  // every range drained
+    s.xs = (s.xs + 1) % kXCD;
+    s.pend = atomicAdd(&s.cnt[s.xs], 1);
+  }
+}
+__device__ __forceinline__ void sched_issue(TileSched& s) {
+  if (s.tried < kXCD) s.pend = atomicAdd(&s.cnt[s.xs], 1);
+}
+
+// One row tile of NMT 16-row MFMA tiles (rows <= 16 * NMT), whose first kD-1 blocks are in
+// flight (tile_prologue_b and _a).  Before its results are written, the next work item of the workgroup
+// is fetched and its prologue issued; c becomes that item (c.rows = 0: none).
 template <int FMT, bool GU, int NMT>
-__device__ __forceinline__ void tile_body(const FfnArgs& args, const TileCtx& c, unsigned short* lds_a) {
+__device__ __forceinline__ void tile_body(const FfnArgs& args, TileCtx& c, unsigned short* lds_a,
+                                          TileB<FMT> (&ring)[TileCfg<FMT>::D],
+                                          unsigned (&avoff)[TileCfg<FMT>::IPW_MAX], TileSched& sch, int ncol,
+                                          int* sh_item) {
   typedef typename Op<FMT>::T OpT;
+  typedef TileB<FMT> BReg;
   constexpr int BK = TileCfg<FMT>::BK;
   constexpr int KS = BK / 32;                     // k-steps per block
   constexpr bool Q4 = FMT != MOE_W_BF16;
@@ -138,64 +319,19 @@ __device__ __forceinline__ void tile_body(const FfnArgs& args, const TileCtx& c,
   constexpr int R = NMT * kWNS;                   // MFMAs per k-step and wave
   constexpr int kD = TileCfg<FMT>::D;             // pipeline depth
   static_assert(!Q4 || KS == 2, "a 4-bit block is half of a 4-k-step package chunk");
-  static_assert(IPW * kTW * RPI <= kTM, "activation loads stay inside the tile buffer");
+  static_assert(IPW <= TileCfg<FMT>::IPW_MAX, "activation loads stay inside the tile buffer");
   const int K = c.K, lane = c.lane, wave = c.wave;
   const int nkb = c.nkb, nfb = c.nfb, nks = c.nks;
 
-  // ---- activation staging: lane l writes slot l % CPR of row l / CPR of its load's rows, so it
-  // fetches chunk (l % CPR) ^ (row % CPR) of that row.  Rows past the tile's end repeat row 0
-  // (their results are dropped).
-  auto a_row = [&](int i) {  // source row of the lane in activation load i
-    const int r = (i * kTW + wave) * RPI + lane / CPR;
-    const int rr = r < c.rows ? r : 0;
-    return GU ? args.perm_src[c.p0 + rr] / args.k : c.p0 + rr;
-  };
-  auto a_chunk = [&](int i) { return (unsigned)((lane % CPR) ^ (((i * kTW + wave) * RPI + lane / CPR) % CPR)); };
-  unsigned avoff[IPW];  // byte offset of the lane's chunk of block 0 (block kb adds kb * BK * 2)
-#pragma unroll
-  for (int i = 0; i < IPW; ++i) avoff[i] = ((unsigned)a_row(i) * (unsigned)K + a_chunk(i) * 8) * 2;
-
-  // weight registers of one K block.  bf16: KS fragments of 16 bytes per strip.  4-bit: half of
-  // the lane's 16-byte word of a 4-k-step chunk (8 bytes, 2 k-steps) and the 2 matching scales.
-  struct BReg {
-    unsigned v[kWNS][Q4 ? 2 : 4 * KS];
-    unsigned sc[kWNS];
-  };
-  // load L of block kb's load list (the IPW activation loads, then the weight loads), kb < nfb:
-  // a uniform base plus a 32-bit per-lane offset, so every load is one instruction on a scalar
-  // base, and the offsets of one block are shared by all strips
+  const TileBases tb = tile_bases<FMT>(args, c);
+  auto a_row = [&](int i) { return tile_a_row<FMT, GU>(args, c, i); };
+  auto a_chunk = [&](int i) { return tile_a_chunk<FMT>(c, i); };
+  // load L of block kb's load list (the IPW activation loads, then the weight loads), kb < nfb
   auto load_one = [&](int L, BReg& B, int kb, int buf) {
-    if (L < IPW) {
-      const int i = L;
-      const int r0 = (i * kTW + wave) * RPI;
-      gptr g = (gptr)args.a + (size_t)kb * (BK * 2) + avoff[i];
-      unsigned short* l = lds_a + ((size_t)buf * kTM + r0) * BK;
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                       (__attribute__((address_space(3))) void*)l, 16, 0, 0);
-    } else if constexpr (!Q4) {
-      const int j = (L - IPW) / KS, q = (L - IPW) % KS;
-      const unsigned off = (unsigned)(kb * KS + q) * 1024u + (unsigned)lane * 16u;
-      const u32x4 v = *(const __attribute__((address_space(1))) u32x4*)((gptr)c.cbase[j] + off);
-      B.v[j][4 * q] = v[0], B.v[j][4 * q + 1] = v[1], B.v[j][4 * q + 2] = v[2], B.v[j][4 * q + 3] = v[3];
-    } else {
-      const int j = (L - IPW) / 2, part = (L - IPW) % 2;
-      const unsigned ch = (unsigned)kb >> 1, h = (unsigned)kb & 1;
-      if (part == 0) {
-        const unsigned off = ch * 1024u + h * 8u + (unsigned)lane * 16u;
-        const u32x2 v = *(const __attribute__((address_space(1))) u32x2*)((gptr)c.cbase[j] + off);
-        B.v[j][0] = v[0], B.v[j][1] = v[1];
-      } else {
-        const unsigned off = (ch * 64u + 2u * h) * SB + ((unsigned)lane & 15) * 4u * SB;
-        if constexpr (SB == 1)
-          B.sc[j] = *(const __attribute__((address_space(1))) unsigned short*)((gptr)c.sbase[j] + off);
-        else
-          B.sc[j] = *(const __attribute__((address_space(1))) unsigned*)((gptr)c.sbase[j] + off);
-      }
-    }
-  };
-  auto load_block = [&](BReg& B, int kb, int buf) {
-#pragma unroll
-    for (int L = 0; L < kLoads; ++L) load_one(L, B, kb, buf);
+    if (L < IPW)
+      tile_load_a<FMT>(args, c, lds_a, avoff[L], L, kb, buf);
+    else
+      tile_load_b<FMT>(c, tb, B, L - IPW, kb);
   };
   // a block of the partial last chunk: ns k-steps packed 4 * ns bytes per lane; k-steps past
   // the end get zero codes and zero scales
@@ -203,15 +339,20 @@ __device__ __forceinline__ void tile_body(const FfnArgs& args, const TileCtx& c,
     const int ch = kb >> 1, h = kb & 1, ns = nks - 4 * ch;
 #pragma unroll
     for (int j = 0; j < kWNS; ++j) {
-      const char* cb = c.cbase[j] + (size_t)ch * 1024 + (size_t)lane * 4 * ns;
-      const char* sp = c.sbase[j] + ((size_t)ch * 64 + (lane & 15) * ns) * SB;
+      // (scalar base plus 32-bit lane offset, as in the whole blocks: a vector use of the bases would
+      // move them to vector registers for the whole kernel)
+      const unsigned coff = (unsigned)ch * 1024u + (unsigned)lane * 4u * (unsigned)ns;
+      const unsigned soff = ((unsigned)ch * 64u + (unsigned)(lane & 15) * (unsigned)ns) * SB;
       unsigned cw[2] = {0, 0}, sw[2] = {0, 0};
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const int qq = 2 * h + q;
         if (qq < ns) {
-          cw[q] = *(const unsigned*)(cb + 4 * qq);
-          sw[q] = SB == 1 ? (unsigned)*(const unsigned char*)(sp + qq) : (unsigned)*(const unsigned short*)(sp + 2 * qq);
+          cw[q] = *(const __attribute__((address_space(1))) unsigned*)((gptr)tb.cbase[j] + (coff + 4u * qq));
+          if constexpr (SB == 1)
+            sw[q] = *(const __attribute__((address_space(1))) unsigned char*)((gptr)tb.sbase[j] + (soff + qq));
+          else
+            sw[q] = *(const __attribute__((address_space(1))) unsigned short*)((gptr)tb.sbase[j] + (soff + 2u * qq));
         }
       }
       B.v[j][0] = cw[0], B.v[j][1] = cw[1];
@@ -304,24 +445,17 @@ __device__ __forceinline__ void tile_body(const FfnArgs& args, const TileCtx& c,
   // block edges too (the next block is already published); so is the operand of the next strip,
   // the next k-step's first strip included.
   static_assert(kD >= 3 && (kD * KS) % 2 == 0, "pipeline depth");
+  // The prologue's loads (and the previous tile's stores, and thread 0's work fetch) complete
+  // before the loop: the loop's waits count its own loads only.  Thread 0 resolves the next work
+  // item; the barrier publishes it with the first kD-1 blocks.
+  __builtin_amdgcn_s_waitcnt(0);
+  if (threadIdx.x == 0) *sh_item = sched_resolve(sch);
+  barrier_keep_loads();
+  const int next = __builtin_amdgcn_readfirstlane(*sh_item);
   int kb = 0;
   if (nfb > 0) {  // (uniform)
-    BReg ring[kD];
     OpT abuf[2][NMT];
-    // blocks in order (the waits count loads in issue order, so no load of a later block may be
-    // scheduled before one of an earlier block)
-#pragma unroll
-    for (int i = 0; i < kD - 1; ++i) {
-      load_block(ring[i], min(i, nfb - 1), i);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    MOE_WAIT_VMCNT((kD - 2) * kLoads);  // block 0 has landed
-    barrier_keep_loads();
     read_a(abuf[0], 0, 0);
-    // The prologue's loads complete before the loop (once per row tile): otherwise the compiler,
-    // merging the loop entry with the loop's back edge, waits for every outstanding load at the
-    // first use of a weight register in each iteration.
-    __builtin_amdgcn_s_waitcnt(0);
     u32x4 b0 = __builtin_bit_cast(u32x4, decode(ring[0], 0, 0));  // operand of the next strip
     for (; kb + kD <= nfb; kb += kD) {
       static_for<kD>([&](auto ic) {
@@ -435,6 +569,24 @@ __device__ __forceinline__ void tile_body(const FfnArgs& args, const TileCtx& c,
     acc_hazard_guard();
   }
 
+  // ---- the next work item: its first kD-1 blocks are issued now and land while this tile's
+  // results are written; the weights at once (the ring registers are free), the activations once
+  // every wave is done with the LDS buffers (the barrier)
+  acc_hazard_guard();
+  const int p0 = c.p0, rows = c.rows, col = c.col;
+  int nrows[TileCfg<FMT>::IPW_MAX];
+  if (next >= 0) {
+    tile_set_item<FMT>(args, c, next, ncol);
+    tile_prologue_b<FMT, GU>(args, c, ring, nrows);
+  }
+  barrier_keep_loads();
+  if (next >= 0) {
+    tile_prologue_a<FMT>(args, c, lds_a, avoff, nrows);
+    if (threadIdx.x == 0) sched_issue(sch);
+  } else {
+    c.rows = 0;
+  }
+
   // ---- epilogue: the wait states of the last MFMAs' results, then every accumulator passes an
   // empty asm after them, so no read of it can be scheduled before the wait
   acc_hazard_guard();
@@ -450,7 +602,7 @@ __device__ __forceinline__ void tile_body(const FfnArgs& args, const TileCtx& c,
   char* const ep = (char*)(lds_a + (size_t)kD * kTM * BK) + (size_t)wave * kEpiBytes;
   if constexpr (GU) {
     // h columns of the wave: strip pair u = (col*16 + wave*4 + 2p) / 2 -> columns 16u + [0, 16)
-    const int hc = (c.col * 8 + wave * 2) * 16 + (lane & 3) * 8;  // this lane's 8 stored columns
+    const int hc = (col * 8 + wave * 2) * 16 + (lane & 3) * 8;  // this lane's 8 stored columns
     const bool col_ok = hc < args.I;
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) {
@@ -469,11 +621,11 @@ __device__ __forceinline__ void tile_body(const FfnArgs& args, const TileCtx& c,
       const int R = lane >> 2;
       const u32x4 v = *(const u32x4*)(ep + (R * kEpiPitchH + (lane & 3) * 8) * 2);
       __builtin_amdgcn_sched_barrier(0);
-      if (col_ok && mt * 16 + R < c.rows)
-        *(__attribute__((address_space(1))) u32x4*)((unsigned short*)args.out + (size_t)(c.p0 + mt * 16 + R) * args.I + hc) = v;
+      if (col_ok && mt * 16 + R < rows)
+        *(__attribute__((address_space(1))) u32x4*)((unsigned short*)args.out + (size_t)(p0 + mt * 16 + R) * args.I + hc) = v;
     }
   } else {
-    const int yc = c.col * (kWNS * kTW * 16) + wave * (kWNS * 16) + cl * 4;  // this lane's 4 columns
+    const int yc = col * (kWNS * kTW * 16) + wave * (kWNS * 16) + cl * 4;  // this lane's 4 columns
     const bool col_ok = yc < c.N;
 #pragma unroll
     for (int mt = 0; mt < NMT; ++mt) {
@@ -485,21 +637,22 @@ __device__ __forceinline__ void tile_body(const FfnArgs& args, const TileCtx& c,
 #pragma unroll
       for (int q = 0; q < 4; ++q) v[q] = *(const f32x4*)(ep + ((4 * q + g) * kEpiPitchY + cl * 4) * 4);
       __builtin_amdgcn_sched_barrier(0);
-      float* const yrow = (float*)args.out + (size_t)(c.p0 + mt * 16 + g) * args.H + yc;
+      float* const yrow = (float*)args.out + (size_t)(p0 + mt * 16 + g) * args.H + yc;
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        if (col_ok && mt * 16 + 4 * q + g < c.rows)
+        if (col_ok && mt * 16 + 4 * q + g < rows)
           *(__attribute__((address_space(1))) f32x4*)(yrow + (size_t)(4 * q) * args.H) = v[q];
     }
   }
 }
 
 template <int FMT, bool GU>
-// one wave per SIMD: the accumulators (up to 192 registers) live in the AGPR half of the file
+// one wave per SIMD: the accumulators (up to 192 registers) live in the AGPR half of the file.
+// Persistent: one workgroup per CU takes work items until every XCD's range is drained.
 __global__ __launch_bounds__(kTW * 64, 1) void ffn_tile_kernel(FfnArgs args) {
   extern __shared__ __align__(16) unsigned short lds_a[];
-  __shared__ RowTile tile;
-  __shared__ int sh_total;
+  __shared__ int sh_item;
+  constexpr int kD = TileCfg<FMT>::D;
 
   TileCtx c;
   c.K = GU ? args.H : args.I;
@@ -514,88 +667,64 @@ __global__ __launch_bounds__(kTW * 64, 1) void ffn_tile_kernel(FfnArgs args) {
   c.lane = tid & 63;
   c.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // ---- row tiles of all experts (wave 0), XCD-aware work item, this workgroup's tile.  An
-  // expert with n rows has ceil(n / 192) tiles; tile t covers rows [t*n/nt, (t+1)*n/nt).
-  int excl = 0, incl = 0, e_begin = 0, e_end = 0;
-  if (tid < 64) {
-    const int per = (args.E + 63) / 64;
-    e_begin = c.lane * per;
-    e_end = min(args.E, e_begin + per);
-    int local = 0;
-    for (int e = e_begin; e < e_end; ++e) {
-      int n = args.offsets[e + 1] - args.offsets[e];
-      if (n < args.min_rows || n > args.max_rows) n = 0;
-      local += (n + kTM - 1) / kTM;
-    }
-    incl = local;
-    for (int off = 1; off < 64; off <<= 1) {
-      int o = __shfl_up(incl, off, 64);
-      if (c.lane >= off) incl += o;
-    }
-    excl = incl - local;
-    if (c.lane == 63) sh_total = incl;
+  TileSched sch;
+  sch.cnt = args.tcount;
+  sch.total = args.plan[0].x * ncol;
+  sch.per = (sch.total + kXCD - 1) / kXCD;
+  sch.xs = (int)(blockIdx.x % kXCD), sch.tried = 0, sch.pend = 0;
+  if (tid == 0) {
+    sch.pend = atomicAdd(&sch.cnt[sch.xs], 1);
+    sh_item = sched_resolve(sch);
+    sched_issue(sch);
   }
   __syncthreads();
-  const int total_work = sh_total * ncol;
-  const int per_xcd = (total_work + kXCD - 1) / kXCD;
-  const int w = (int)(blockIdx.x % kXCD) * per_xcd + (int)(blockIdx.x / kXCD);
-  if (w >= total_work || (int)(blockIdx.x / kXCD) >= per_xcd) return;
-  const int slot = w / ncol;
-  c.col = w % ncol;
-  if (tid < 64 && slot >= excl && slot < incl) {
-    int acc_t = excl;
-    for (int e = e_begin; e < e_end; ++e) {
-      const int o0 = args.offsets[e];
-      int n = args.offsets[e + 1] - o0;
-      if (n < args.min_rows || n > args.max_rows) n = 0;
-      const int nt = (n + kTM - 1) / kTM;
-      if (slot < acc_t + nt) {
-        const int t = slot - acc_t;
-        const int r0 = (int)((long long)t * n / nt), r1 = (int)((long long)(t + 1) * n / nt);
-        tile.e = e;
-        tile.p0 = o0 + r0;
-        tile.rows = r1 - r0;
-        break;
-      }
-      acc_t += nt;
+  const int first = __builtin_amdgcn_readfirstlane(sh_item);
+  __syncthreads();  // every wave has read sh_item before thread 0 writes the next one
+  if (first < 0) return;
+
+  TileB<FMT> ring[kD];
+  unsigned avoff[TileCfg<FMT>::IPW_MAX];
+  tile_set_item<FMT>(args, c, first, ncol);
+  {
+    int rows[TileCfg<FMT>::IPW_MAX];
+    tile_prologue_b<FMT, GU>(args, c, ring, rows);
+    tile_prologue_a<FMT>(args, c, lds_a, avoff, rows);
+  }
+  do {
+    switch ((c.rows + 15) / 16) {
+      case 1: tile_body<FMT, GU, 1>(args, c, lds_a, ring, avoff, sch, ncol, &sh_item); break;
+      case 2: tile_body<FMT, GU, 2>(args, c, lds_a, ring, avoff, sch, ncol, &sh_item); break;
+      case 3: tile_body<FMT, GU, 3>(args, c, lds_a, ring, avoff, sch, ncol, &sh_item); break;
+      case 4: tile_body<FMT, GU, 4>(args, c, lds_a, ring, avoff, sch, ncol, &sh_item); break;
+      case 5: tile_body<FMT, GU, 5>(args, c, lds_a, ring, avoff, sch, ncol, &sh_item); break;
+      case 6: tile_body<FMT, GU, 6>(args, c, lds_a, ring, avoff, sch, ncol, &sh_item); break;
+      case 7: tile_body<FMT, GU, 7>(args, c, lds_a, ring, avoff, sch, ncol, &sh_item); break;
+      case 8: tile_body<FMT, GU, 8>(args, c, lds_a, ring, avoff, sch, ncol, &sh_item); break;
+      case 9: tile_body<FMT, GU, 9>(args, c, lds_a, ring, avoff, sch, ncol, &sh_item); break;
+      case 10: tile_body<FMT, GU, 10>(args, c, lds_a, ring, avoff, sch, ncol, &sh_item); break;
+      case 11: tile_body<FMT, GU, 11>(args, c, lds_a, ring, avoff, sch, ncol, &sh_item); break;
+      default: tile_body<FMT, GU, kMT>(args, c, lds_a, ring, avoff, sch, ncol, &sh_item); break;
     }
-  }
-  __syncthreads();
-  const int e = tile.e;
-  c.p0 = tile.p0;
-  c.rows = tile.rows;
-  const int eslot = args.slot_of_expert ? args.slot_of_expert[e] : e;
-  if ((unsigned)eslot >= (unsigned)args.n_slots) return;  // workgroup-uniform: not resident, skip
-  const char* pkg = args.packages + (size_t)eslot * args.pkg_stride;
-
-  // this wave's strips (clamped into range; results of strips past the end are dropped)
-  constexpr bool Q4 = FMT != MOE_W_BF16;
-  constexpr int SB = FMT == MOE_W_MXFP4 ? 1 : 2;
-#pragma unroll
-  for (int j = 0; j < kWNS; ++j) {
-    const int s = min(c.col * 16 + c.wave * kWNS + j, c.n_strips - 1);
-    c.cbase[j] = pkg + args.region_codes + (size_t)s * (Q4 ? 8 : 32) * c.K;
-    c.sbase[j] = pkg + args.region_scales + (size_t)s * 16 * c.nks * SB;
-  }
-
-  switch ((c.rows + 15) / 16) {
-    case 1: tile_body<FMT, GU, 1>(args, c, lds_a); break;
-    case 2: tile_body<FMT, GU, 2>(args, c, lds_a); break;
-    case 3: tile_body<FMT, GU, 3>(args, c, lds_a); break;
-    case 4: tile_body<FMT, GU, 4>(args, c, lds_a); break;
-    case 5: tile_body<FMT, GU, 5>(args, c, lds_a); break;
-    case 6: tile_body<FMT, GU, 6>(args, c, lds_a); break;
-    case 7: tile_body<FMT, GU, 7>(args, c, lds_a); break;
-    case 8: tile_body<FMT, GU, 8>(args, c, lds_a); break;
-    case 9: tile_body<FMT, GU, 9>(args, c, lds_a); break;
-    case 10: tile_body<FMT, GU, 10>(args, c, lds_a); break;
-    case 11: tile_body<FMT, GU, 11>(args, c, lds_a); break;
-    default: tile_body<FMT, GU, kMT>(args, c, lds_a); break;
-  }
+  } while (c.rows > 0);
 }
 
-// Launch of one (format, matrix) kernel over the routed rows: S row tiles at most (each expert
-// with n_e rows has ceil(n_e / 192) of them), times the column tiles of the matrix.
+// compute units of the current device (cached per device)
+inline int cu_count() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+// Launch of one (format, matrix) kernel over the row tiles of a.plan (written on the stream by
+// the plan kernel, which also zeroes the work counters a.tcount): at most S row tiles (each expert
+// with n_e rows has ceil(n_e / 192) of them) times the column tiles of the matrix, taken by a
+// persistent grid of one workgroup per CU (a multiple of 8, so every XCD has the same number).
 template <int FMT, bool GU>
 int tile_launch(const FfnArgs& a, int H, int I, int n, int E, hipStream_t s) {
   static bool attr_set = false;
@@ -618,7 +747,9 @@ int tile_launch(const FfnArgs& a, int H, int I, int n, int E, hipStream_t s) {
   const int ncol = (N + kTN - 1) / kTN;
   const long long total = S * ncol;
   const long long per = (total + kXCD - 1) / kXCD;
-  hipLaunchKernelGGL((ffn_tile_kernel<FMT, GU>), dim3((unsigned)(per * kXCD)), dim3(kTW * 64), lds, s, a);
+  const long long resident = cu_count() / kXCD;  // workgroups per XCD at one per CU
+  const long long grid = kXCD * (per < resident ? per : (resident > 0 ? resident : 1));
+  hipLaunchKernelGGL((ffn_tile_kernel<FMT, GU>), dim3((unsigned)grid), dim3(kTW * 64), lds, s, a);
   return MOE_OK;
 }
 

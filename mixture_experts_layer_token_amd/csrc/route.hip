@@ -260,9 +260,15 @@ __global__ __launch_bounds__(256) void route_f32_kernel(const float* __restrict_
 // row 16s + l%16, k 32ks + 8(l/16)..+7 (the bf16 package layout); also writes offsets {0, T}.
 __global__ __launch_bounds__(256) void route_pack_kernel(const unsigned short* __restrict__ wg, int H, int E, int T,
                                                          unsigned short* __restrict__ packed,
-                                                         int32_t* __restrict__ offsets) {
+                                                         int32_t* __restrict__ offsets, int4* __restrict__ plan,
+                                                         int* __restrict__ counters) {
   const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx == 0) offsets[0] = 0, offsets[1] = T;
+  // the tile plan of the one "expert" (T rows in 192-row tiles) and zeroed work counters
+  const int nt = (T + 191) / 192;
+  if (idx == 0) plan[0] = make_int4(nt, 0, 0, 0);
+  if (idx < (size_t)nt) plan[1 + idx] = make_int4(0, 0, T, 0);
+  if (idx < 8) counters[idx] = 0;
   const size_t per_row = (size_t)H / 8;
   if (idx >= (size_t)E * per_row) return;
   const int r = (int)(idx / per_row), k = (int)(idx % per_row) * 8;
@@ -272,7 +278,7 @@ __global__ __launch_bounds__(256) void route_pack_kernel(const unsigned short* _
 }
 
 struct RouteTileWs {
-  size_t packed_off, logits_off, offsets_off, total;
+  size_t packed_off, logits_off, offsets_off, plan_off, count_off, total;
 };
 
 inline size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -291,7 +297,9 @@ RouteTileWs route_tile_ws(int T, int H, int E) {
   L.packed_off = 0;
   L.logits_off = al256((size_t)E * H * 2);
   L.offsets_off = L.logits_off + al256((size_t)T * E * sizeof(float));
-  L.total = L.offsets_off + 256;
+  L.plan_off = L.offsets_off + 256;
+  L.count_off = L.plan_off + al256((size_t)(1 + (T + 191) / 192) * 16);
+  L.total = L.count_off + 256;
   return L;
 }
 
@@ -312,9 +320,12 @@ int launch_route(const void* x, int xdt, int T, int H, const void* wg, const flo
     unsigned short* packed = (unsigned short*)(wsp + L.packed_off);
     float* lg = (float*)(wsp + L.logits_off);
     int32_t* offs = (int32_t*)(wsp + L.offsets_off);
-    const size_t chunks = (size_t)E * H / 8;
-    hipLaunchKernelGGL(route_pack_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, s,
-                       (const unsigned short*)wg, H, E, T, packed, offs);
+    int4* plan = (int4*)(wsp + L.plan_off);
+    int* counters = (int*)(wsp + L.count_off);
+    const size_t chunks = (size_t)E * H / 8, nt = (size_t)(T + 191) / 192;
+    const size_t threads = chunks > nt + 8 ? chunks : nt + 8;
+    hipLaunchKernelGGL(route_pack_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+                       (const unsigned short*)wg, H, E, T, packed, offs, plan, counters);
     FfnArgs a{};
     a.packages = (const char*)packed;
     a.pkg_stride = (size_t)E * H * 2;
@@ -329,6 +340,8 @@ int launch_route(const void* x, int xdt, int T, int H, const void* wg, const flo
     a.I = H;  // its contraction
     a.E = 1, a.k = 1;
     a.region_codes = 0, a.region_scales = 0;
+    a.plan = plan;
+    a.tcount = counters;
     int rc = launch_ffn_tile_part(MOE_W_BF16, false, a, E, H, T, 1, s);
     if (rc != MOE_OK) return rc;
     hipLaunchKernelGGL(route_topk_kernel, dim3((T + 3) / 4), dim3(256), (size_t)4 * E * sizeof(float), s,
