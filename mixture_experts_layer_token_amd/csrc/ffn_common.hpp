@@ -153,9 +153,48 @@ struct FfnArgs {
   // tiles; plan[1 + t] = {first tile of the expert of tile t, the expert's first grouped row, its
   // rows, its slot}, written by the plan kernel from the offsets and the slot table
   const int4* plan;
-  int* tcount;  // tile variant: [8] work counters, one per XCD range, zeroed by the plan kernel
+  int* tcount;  // [8] work counters of the persistent kernels, one per XCD range, zeroed by the plan kernel
 };
 
+
+constexpr int kXcds = 8;  // XCDs of an MI355X; workgroup i is dispatched to XCD i % 8
+
+// Dynamic work distribution over a persistent grid.  The work items are dealt in contiguous
+// ranges of `per` to the 8 XCDs (workgroup i runs on XCD i % 8), so that consecutive items (the
+// column tiles or unit groups of one row tile) run on one XCD and share its L2; each range has a
+// counter (zeroed by the plan kernel), and a workgroup takes the next item of its own XCD's range,
+// then of the others' once that is drained.  Only thread 0 holds the state; an atomic is issued
+// one item ahead and resolved at the start of the next item, after it has long returned.
+struct WorkSched {
+  int* cnt;  // [kXcds] items taken from each range
+  int per, total;
+  int xs, tried, pend;  // range being drained, ranges tried, raw result of the last atomic
+};
+__device__ __forceinline__ int sched_resolve(WorkSched& s) {
+  for (;;) {
+    if (s.tried >= kXcds) return -1;
+    if (s.pend < min(s.per, s.total - s.xs * s.per)) return s.xs * s.per + s.pend;
+    if (++s.tried >= kXcds) return -1;  // every range drained
+    s.xs = (s.xs + 1) % kXcds;
+    s.pend = atomicAdd(&s.cnt[s.xs], 1);
+  }
+}
+__device__ __forceinline__ void sched_issue(WorkSched& s) {
+  if (s.tried < kXcds) s.pend = atomicAdd(&s.cnt[s.xs], 1);
+}
+
+// compute units of the current device (cached per device)
+inline int cu_count() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
 
 // Prefill (tile) variant, one matrix: gate/up (with SwiGLU) or down, for the experts whose row
 // count lies in [a.min_rows, a.max_rows].

@@ -42,7 +42,6 @@ constexpr int kTM = 192;  // rows per workgroup tile (at most)
 constexpr int kTN = 256;  // columns per workgroup tile
 constexpr int kMT = 12;   // 16-row MFMA tiles of a full row tile
 constexpr int kWNS = 4;   // 16-column strips per wave
-constexpr int kXCD = 8;   // XCDs of an MI355X; workgroup i is dispatched to XCD i % 8
 #ifndef MOE_CFG_TILE_D_BF16
 #define MOE_CFG_TILE_D_BF16 4
 #endif
@@ -272,29 +271,6 @@ __device__ __forceinline__ void tile_prologue_a(const FfnArgs& args, const TileC
   }
 }
 
-// Dynamic work distribution over a persistent grid.  The work items are dealt in contiguous
-// ranges of `per` to the 8 XCDs (workgroup i runs on XCD i % 8), so that the column tiles of a
-// row tile (consecutive items) run on one XCD and share its L2; each range has a counter, and a
-// workgroup takes the next item of its own XCD's range, then of the others' once that is drained.
-// Only thread 0 holds the state; an atomic is issued one tile ahead and resolved at the start of
-// the next tile, after that tile's loads were waited for anyway.
-struct TileSched {
-  int* cnt;  // [kXCD] items taken from each range
-  int per, total;
-  int xs, tried, pend;  // range being drained, ranges tried, raw result of the last atomic
-};
-__device__ __forceinline__ int sched_resolve(TileSched& s) {
-  for (;;) {
-    if (s.tried >= kXCD) return -1;
-    if (s.pend < min(s.per, s.total - s.xs * s.per)) return s.xs * s.per + s.pend;
-    if (++s.tried >= kXCD) return -1;  // every range drained
-    s.xs = (s.xs + 1) % kXCD;
-    s.pend = atomicAdd(&s.cnt[s.xs], 1);
-  }
-}
-__device__ __forceinline__ void sched_issue(TileSched& s) {
-  if (s.tried < kXCD) s.pend = atomicAdd(&s.cnt[s.xs], 1);
-}
 
 // One row tile of NMT 16-row MFMA tiles (rows <= 16 * NMT), whose first kD-1 blocks are in
 // flight (tile_prologue_b and _a).  Before its results are written, the next work item of the workgroup
@@ -302,7 +278,7 @@ __device__ __forceinline__ void sched_issue(TileSched& s) {
 template <int FMT, bool GU, int NMT>
 __device__ __forceinline__ void tile_body(const FfnArgs& args, TileCtx& c, unsigned short* lds_a,
                                           TileB<FMT> (&ring)[TileCfg<FMT>::D],
-                                          unsigned (&avoff)[TileCfg<FMT>::IPW_MAX], TileSched& sch, int ncol,
+                                          unsigned (&avoff)[TileCfg<FMT>::IPW_MAX], WorkSched& sch, int ncol,
                                           int* sh_item) {
   typedef typename Op<FMT>::T OpT;
   typedef TileB<FMT> BReg;
@@ -667,11 +643,11 @@ __global__ __launch_bounds__(kTW * 64, 1) void ffn_tile_kernel(FfnArgs args) {
   c.lane = tid & 63;
   c.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  TileSched sch;
+  WorkSched sch;
   sch.cnt = args.tcount;
   sch.total = args.plan[0].x * ncol;
-  sch.per = (sch.total + kXCD - 1) / kXCD;
-  sch.xs = (int)(blockIdx.x % kXCD), sch.tried = 0, sch.pend = 0;
+  sch.per = (sch.total + kXcds - 1) / kXcds;
+  sch.xs = (int)(blockIdx.x % kXcds), sch.tried = 0, sch.pend = 0;
   if (tid == 0) {
     sch.pend = atomicAdd(&sch.cnt[sch.xs], 1);
     sh_item = sched_resolve(sch);
@@ -708,19 +684,6 @@ __global__ __launch_bounds__(kTW * 64, 1) void ffn_tile_kernel(FfnArgs args) {
   } while (c.rows > 0);
 }
 
-// compute units of the current device (cached per device)
-inline int cu_count() {
-  static int cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cache[dev] = n;
-  }
-  return cache[dev];
-}
-
 // Launch of one (format, matrix) kernel over the row tiles of a.plan (written on the stream by
 // the plan kernel, which also zeroes the work counters a.tcount): at most S row tiles (each expert
 // with n_e rows has ceil(n_e / 192) of them) times the column tiles of the matrix, taken by a
@@ -746,9 +709,9 @@ int tile_launch(const FfnArgs& a, int H, int I, int n, int E, hipStream_t s) {
   const int N = GU ? 2 * I : H;
   const int ncol = (N + kTN - 1) / kTN;
   const long long total = S * ncol;
-  const long long per = (total + kXCD - 1) / kXCD;
-  const long long resident = cu_count() / kXCD;  // workgroups per XCD at one per CU
-  const long long grid = kXCD * (per < resident ? per : (resident > 0 ? resident : 1));
+  const long long per = (total + kXcds - 1) / kXcds;
+  const long long resident = cu_count() / kXcds;  // workgroups per XCD at one per CU
+  const long long grid = kXcds * (per < resident ? per : (resident > 0 ? resident : 1));
   hipLaunchKernelGGL((ffn_tile_kernel<FMT, GU>), dim3((unsigned)grid), dim3(kTW * 64), lds, s, a);
   return MOE_OK;
 }
