@@ -196,6 +196,28 @@ def test_layer_small(fmt, xdt, T, mode):
     assert_output_close(to_f64(out), ref, tol_dt, wl.name)
 
 
+@pytest.mark.parametrize("fmt,xdt", [("f32", "f32"), ("bf16", "bf16"), ("mxfp4", "bf16"), ("int4g32", "bf16")])
+@pytest.mark.parametrize("mode", ["auto", "decode", "prefill"])
+def test_layer_empty_batch_then_batch(fmt, xdt, mode):
+    """T = 0: every call of the path succeeds and does nothing; the same layer then computes a
+    ragged batch correctly (the workspaces and plans of the empty call leave nothing behind)."""
+    if fmt == "f32" and mode != "auto":
+        pytest.skip("fp32 experts have one (VALU) variant")
+    wl = small_variant(fmt, xdt)
+    say("layer empty batch", wl.name, "mode", mode)
+    layer = build_layer(wl, 8)
+    x0 = np.zeros((0, wl.H), np.float32 if xdt == "f32" else np.uint16)
+    out0 = layer.forward(to_device_act(x0, xdt), mode=mode)
+    torch.cuda.synchronize()
+    assert tuple(out0.shape) == (0, wl.H)
+    x, _ = oracle.rank_gap_inputs(wl, 5)
+    out = layer.forward(to_device_act(x, xdt), mode=mode)
+    torch.cuda.synchronize()
+    ref, ids_ref, _ = oracle_reference(wl, x, np.arange(5))
+    assert np.array_equal(layer.topk_ids[:5].cpu().numpy(), ids_ref)
+    assert_output_close(to_f64(out), ref, "f32" if fmt == "f32" else "bf16", wl.name)
+
+
 @pytest.mark.parametrize("fmt", ["bf16", "mxfp4", "int4g32"])
 def test_layer_hot_expert_split(fmt):
     """Skewed routing: a few experts get hundreds of rows (MFMA tile kernel), the rest a handful
