@@ -259,15 +259,17 @@ __global__ __launch_bounds__(256) void route_f32_kernel(const float* __restrict_
 // Wg [E][H] bf16 row-major -> strips of 16 rows, 1 KiB per 32-wide k-step, lane l's 16 bytes =
 // row 16s + l%16, k 32ks + 8(l/16)..+7 (the bf16 package layout); also writes offsets {0, T}.
 __global__ __launch_bounds__(256) void route_pack_kernel(const unsigned short* __restrict__ wg, int H, int E, int T,
-                                                         unsigned short* __restrict__ packed,
+                                                         int rt, unsigned short* __restrict__ packed,
                                                          int32_t* __restrict__ offsets, int4* __restrict__ plan,
                                                          int* __restrict__ counters) {
   const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx == 0) offsets[0] = 0, offsets[1] = T;
-  // the tile plan of the one "expert" (T rows in 192-row tiles) and zeroed work counters
-  const int nt = (T + 191) / 192;
+  // The tile plan: the T rows in tiles of rt rows, each described as an "expert" of its own (one
+  // tile, first row t*rt), so that the few columns (E) still give enough work items to fill the
+  // GPU; and zeroed work counters.
+  const int nt = (T + rt - 1) / rt;
   if (idx == 0) plan[0] = make_int4(nt, 0, 0, 0);
-  if (idx < (size_t)nt) plan[1 + idx] = make_int4(0, 0, T, 0);
+  if (idx < (size_t)nt) plan[1 + idx] = make_int4((int)idx, (int)idx * rt, min(rt, T - (int)idx * rt), 0);
   if (idx < 8) counters[idx] = 0;
   const size_t per_row = (size_t)H / 8;
   if (idx >= (size_t)E * per_row) return;
@@ -298,7 +300,7 @@ RouteTileWs route_tile_ws(int T, int H, int E) {
   L.logits_off = al256((size_t)E * H * 2);
   L.offsets_off = L.logits_off + al256((size_t)T * E * sizeof(float));
   L.plan_off = L.offsets_off + 256;
-  L.count_off = L.plan_off + al256((size_t)(1 + (T + 191) / 192) * 16);
+  L.count_off = L.plan_off + al256((size_t)(1 + (T + 15) / 16) * 16);  // tiles of >= 16 rows
   L.total = L.count_off + 256;
   return L;
 }
@@ -322,10 +324,15 @@ int launch_route(const void* x, int xdt, int T, int H, const void* wg, const flo
     int32_t* offs = (int32_t*)(wsp + L.offsets_off);
     int4* plan = (int4*)(wsp + L.plan_off);
     int* counters = (int*)(wsp + L.count_off);
-    const size_t chunks = (size_t)E * H / 8, nt = (size_t)(T + 191) / 192;
+    // row tile height: about one work item (row tile x 256 columns) per CU, 32 to 192 rows (every
+    // row tile reads the whole router matrix again, from L2)
+    const long long ncol = (E + 255) / 256;
+    int rt = (int)((long long)T * ncol / cu_count()) / 16 * 16;
+    rt = rt < 32 ? 32 : (rt > 192 ? 192 : rt);
+    const size_t chunks = (size_t)E * H / 8, nt = (size_t)(T + rt - 1) / rt;
     const size_t threads = chunks > nt + 8 ? chunks : nt + 8;
     hipLaunchKernelGGL(route_pack_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
-                       (const unsigned short*)wg, H, E, T, packed, offs, plan, counters);
+                       (const unsigned short*)wg, H, E, T, rt, packed, offs, plan, counters);
     FfnArgs a{};
     a.packages = (const char*)packed;
     a.pkg_stride = (size_t)E * H * 2;
@@ -342,7 +349,8 @@ int launch_route(const void* x, int xdt, int T, int H, const void* wg, const flo
     a.region_codes = 0, a.region_scales = 0;
     a.plan = plan;
     a.tcount = counters;
-    int rc = launch_ffn_tile_part(MOE_W_BF16, false, a, E, H, T, 1, s);
+    // (the launch bounds the row tiles by "experts" = the nt chunks of at most rt rows)
+    int rc = launch_ffn_tile_part(MOE_W_BF16, false, a, E, H, T, (int)nt, s);
     if (rc != MOE_OK) return rc;
     hipLaunchKernelGGL(route_topk_kernel, dim3((T + 3) / 4), dim3(256), (size_t)4 * E * sizeof(float), s,
                        (const float*)lg, bias, T, E, 1, k, ids, w, logits);

@@ -26,8 +26,8 @@ def test_every_header_symbol_is_exported():
 
 def test_route_workspace_sizes():
     # large bf16 batches: the router matrix repacked for the MFMA tile kernel + [T][E] fp32 logits
-    # + offsets + the tile kernel's plan (1 + ceil(T / 192) entries of 16 bytes) + its work counters
-    plan = (1 + (8192 + 191) // 192) * 16
+    # + offsets + the tile kernel's plan (at most 1 + ceil(T / 16) entries of 16 bytes) + its work counters
+    plan = (1 + (8192 + 15) // 16) * 16
     assert moe.api.moe_route_workspace(8192, 7168, 384, "bf16") == (384 * 7168 * 2 + 8192 * 384 * 4 + 256
                                                                      + (plan + 255) // 256 * 256 + 256)
     # T * E <= 2^20: split over workgroups, KS ranges of partial logits (here KS = 1)

@@ -105,6 +105,8 @@ ROUTE_CASES = [
     ("tiny", 37, dict(E=1024, k=16, H=64, name="e1024", xdt="bf16")),
     ("tiny", 300, dict(E=24, k=3, name="e24-bf16", xdt="bf16")),  # large T, E not a multiple of 16
     ("tiny", 700, dict(E=48, k=5, H=96, name="e48-bf16", xdt="bf16")),  # large T, ragged 192-row tile
+    # T * E > 2^20: the MFMA tile kernel in short row tiles (the last one ragged), two column tiles
+    ("tiny", 3000, dict(E=400, k=6, H=96, name="e400-bf16-tile", xdt="bf16")),
 ]
 
 
