@@ -25,9 +25,11 @@
 //  - gate/up epilogue: SiLU(g) * u on the lane's own (gate, up) pair, rounded once to h;
 //    down epilogue: fp32 y_perm; both staged through LDS per 16-row tile, so that the stores
 //    are 16 bytes of one row per lane rather than 4 bytes of a column.
-// Work order is XCD-aware: consecutive work items (all column blocks of a row tile, then the
-// next row tile of the same expert) go to the same XCD, so one L2 holds the tile's activations
-// and the expert's weights while they are reused.
+// The grid is persistent (one workgroup per CU) and work items are taken dynamically, XCD-aware:
+// consecutive items (all column blocks of a row tile, then the next row tile of the same expert)
+// belong to the same XCD's range, so one L2 holds the tile's activations and the expert's weights
+// while they are reused; a workgroup moves on to other XCDs' ranges once its own is drained.  The
+// next item's first blocks are loaded while the current item's results are written.
 #pragma once
 
 #include <utility>
