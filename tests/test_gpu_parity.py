@@ -295,7 +295,7 @@ def test_shared_expert_small():
 
 FULL = [("mixtral", 1, "auto"), ("mixtral", 8, "auto"), ("mixtral", 32, "auto"), ("mixtral", 64, "auto"),
         ("mixtral", 64, "prefill"), ("gptoss", 1, "auto"), ("gptoss", 64, "auto"), ("gptoss", 512, "auto"),
-        ("gptoss", 512, "prefill")]
+        ("gptoss", 512, "prefill"), ("gptoss", 1024, "auto")]  # 1024: hot experts on the tile kernel
 
 
 @pytest.mark.parametrize("name,T,mode", FULL)
