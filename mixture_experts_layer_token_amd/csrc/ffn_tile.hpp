@@ -22,9 +22,9 @@
 //  - one wave per SIMD issues every instruction itself, so the K loop is laid out by hand:
 //    between consecutive MFMAs sits at most a step or two of other work (the decode of the next
 //    strip's operand, an A-fragment read for the next k-step, one load of the block kD-1 ahead);
-//  - gate/up epilogue: SiLU(g) * u on the lane's own (gate, up) pair, rounded once to h;
-//    down epilogue: fp32 y_perm; both staged through LDS per 16-row tile, so that the stores
-//    are 16 bytes of one row per lane rather than 4 bytes of a column.
+//  - the weights are the MFMA's first operand, so a lane's results are 4 consecutive output
+//    features of one row; gate/up epilogue: SiLU(g) * u on the lane's own (gate, up) pairs,
+//    rounded once to h, 8 bytes per store; down epilogue: fp32 y_perm, 16 bytes per store.
 // The grid is persistent (one workgroup per CU) and work items are taken dynamically, XCD-aware:
 // consecutive items (all column blocks of a row tile, then the next row tile of the same expert)
 // belong to the same XCD's range, so one L2 holds the tile's activations and the expert's weights
@@ -50,11 +50,6 @@ constexpr int kWNS = 4;   // 16-column strips per wave
 #ifndef MOE_CFG_TILE_D_Q4
 #define MOE_CFG_TILE_D_Q4 4
 #endif
-// Epilogue staging, one area per wave: 16 rows x 64 fp32 (down) or 16 rows x 32 h values (gate/up),
-// row pitches padded so that the column-wise writes of a wave hit distinct banks.
-constexpr int kEpiPitchY = 68;  // floats
-constexpr int kEpiPitchH = 40;  // 16-bit values
-constexpr int kEpiBytes = 16 * kEpiPitchY * 4;
 template <int FMT>
 struct TileCfg {
   static constexpr int BK = FMT == MOE_W_BF16 ? 32 : 64;  // K per block
@@ -62,7 +57,7 @@ struct TileCfg {
   // 4-bit weights and costs 12 more registers); even kD * BK / 32 keeps the register buffers of
   // A fragments in step across loop iterations
   static constexpr int D = FMT == MOE_W_BF16 ? MOE_CFG_TILE_D_BF16 : MOE_CFG_TILE_D_Q4;
-  static constexpr size_t LDS = (size_t)D * kTM * BK * 2 + kTW * kEpiBytes;  // kD ring buffers, epilogue
+  static constexpr size_t LDS = (size_t)D * kTM * BK * 2;  // kD ring buffers
   static constexpr int CPR = BK / 8;    // 16-byte chunks per staged row
   static constexpr int RPI = 64 / CPR;  // rows per wave-wide direct-to-LDS load
   // activation loads per wave and block of a full 192-row tile: load i of wave w fills rows
@@ -90,19 +85,22 @@ struct TileB {
 // operands written several instructions earlier or by loads (covered by s_waitcnt).
 // acc_hazard_guard() covers the MFMA result latency; it ends every stretch of MFMA code, before
 // the compiler may read or copy an accumulator.
+// The weights are the first operand (the rows of the 16 x 16 result are output features) and the
+// activations the second (its columns are grouped rows), so a lane's 4 results are 4 consecutive
+// output features of one row: 16 contiguous bytes of y_perm (8 of h), stored as they are.
 template <bool WAIT>
 __device__ __forceinline__ void mfma_acc(f32x4& acc, const bf16x8& a, const bf16x8& b) {
   if constexpr (WAIT)
-    asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_bf16 %0, %2, %1, %0" : "+a"(acc) : "v"(a), "v"(b));
   else
-    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %2, %1, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 template <bool WAIT>
 __device__ __forceinline__ void mfma_acc(f32x4& acc, const f16x8& a, const f16x8& b) {
   if constexpr (WAIT)
-    asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    asm volatile("s_nop 1\n\tv_mfma_f32_16x16x32_f16 %0, %2, %1, %0" : "+a"(acc) : "v"(a), "v"(b));
   else
-    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    asm volatile("v_mfma_f32_16x16x32_f16 %0, %2, %1, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void acc_hazard_guard() { asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory"); }
 
@@ -572,54 +570,38 @@ __device__ __forceinline__ void tile_body(const FfnArgs& args, TileCtx& c, unsig
   for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
     for (int j = 0; j < kWNS; ++j) asm volatile("" : "+a"(acc[mt][j]));
-  // The lane holds 4 consecutive rows of one column of each MFMA tile; every 16-row tile passes
-  // through the wave's own LDS area (no barrier: a wave's LDS accesses complete in order), so
-  // each lane stores 16 contiguous bytes of one row.  Down: 16 x 64 fp32, read back as 4 rows of
-  // 256 bytes per store; gate/up: 16 x 32 h values, read back as 16 rows of 64 bytes.
-  const int g = lane >> 4, cl = lane & 15;
-  char* const ep = (char*)(lds_a + (size_t)kD * kTM * BK) + (size_t)wave * kEpiBytes;
-  if constexpr (GU) {
-    // h columns of the wave: strip pair u = (col*16 + wave*4 + 2p) / 2 -> columns 16u + [0, 16)
-    const int hc = (col * 8 + wave * 2) * 16 + (lane & 3) * 8;  // this lane's 8 stored columns
-    const bool col_ok = hc < args.I;
+  // The lane holds 4 consecutive output features (columns) of row mt*16 + lane % 16 of each MFMA
+  // tile: down stores them as 16 bytes, gate/up turns its (gate, up) strip pairs into 4 h values
+  // (8 bytes) each.
+  const int m_lane = lane & 15, q4 = (lane >> 4) * 4;
 #pragma unroll
-    for (int mt = 0; mt < NMT; ++mt) {
+  for (int mt = 0; mt < NMT; ++mt) {
+    const int m = mt * 16 + m_lane;
+    const bool row_ok = m < rows;
+    if constexpr (GU) {
 #pragma unroll
-      for (int p = 0; p < 2; ++p)
+      for (int p = 0; p < 2; ++p) {
+        const int hc = (col * 8 + wave * 2 + p) * 16 + q4;  // h columns of strip pair col*8 + wave*2 + p
+        unsigned short hv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float hv = silu(acc[mt][2 * p][r]) * acc[mt][2 * p + 1][r];
-          unsigned short hb;
+          const float h = silu(acc[mt][2 * p][r]) * acc[mt][2 * p + 1][r];
           if constexpr (FMT == MOE_W_INT4G32)
-            hb = __builtin_bit_cast(unsigned short, (_Float16)hv);
+            hv[r] = __builtin_bit_cast(unsigned short, (_Float16)h);
           else
-            hb = f32_to_bf16_rne(hv);
-          *(unsigned short*)(ep + ((4 * g + r) * kEpiPitchH + 16 * p + cl) * 2) = hb;
+            hv[r] = f32_to_bf16_rne(h);
         }
-      const int R = lane >> 2;
-      const u32x4 v = *(const u32x4*)(ep + (R * kEpiPitchH + (lane & 3) * 8) * 2);
-      __builtin_amdgcn_sched_barrier(0);
-      if (col_ok && mt * 16 + R < rows)
-        *(__attribute__((address_space(1))) u32x4*)((unsigned short*)args.out + (size_t)(p0 + mt * 16 + R) * args.I + hc) = v;
-    }
-  } else {
-    const int yc = col * (kWNS * kTW * 16) + wave * (kWNS * 16) + cl * 4;  // this lane's 4 columns
-    const bool col_ok = yc < c.N;
+        const u32x2 pk = {(unsigned)hv[0] | ((unsigned)hv[1] << 16), (unsigned)hv[2] | ((unsigned)hv[3] << 16)};
+        if (row_ok && hc < args.I)
+          *(__attribute__((address_space(1))) u32x2*)((unsigned short*)args.out + (size_t)(p0 + m) * args.I + hc) = pk;
+      }
+    } else {
 #pragma unroll
-    for (int mt = 0; mt < NMT; ++mt) {
-#pragma unroll
-      for (int j = 0; j < kWNS; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) *(float*)(ep + ((4 * g + r) * kEpiPitchY + 16 * j + cl) * 4) = acc[mt][j][r];
-      f32x4 v[4];  // all four reads in flight before the first store
-#pragma unroll
-      for (int q = 0; q < 4; ++q) v[q] = *(const f32x4*)(ep + ((4 * q + g) * kEpiPitchY + cl * 4) * 4);
-      __builtin_amdgcn_sched_barrier(0);
-      float* const yrow = (float*)args.out + (size_t)(p0 + mt * 16 + g) * args.H + yc;
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (col_ok && mt * 16 + 4 * q + g < rows)
-          *(__attribute__((address_space(1))) f32x4*)(yrow + (size_t)(4 * q) * args.H) = v[q];
+      for (int j = 0; j < kWNS; ++j) {
+        const int n = col * (kWNS * kTW * 16) + wave * (kWNS * 16) + j * 16 + q4;
+        if (row_ok && n < c.N)
+          *(__attribute__((address_space(1))) f32x4*)((float*)args.out + (size_t)(p0 + m) * args.H + n) = acc[mt][j];
+      }
     }
   }
 }
