@@ -238,6 +238,24 @@ def test_layer_hot_expert_split(fmt):
     assert_output_close(to_f64(out), ref, "bf16", wl.name)
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "mxfp4", "int4g32"])
+@pytest.mark.parametrize("mode", ["auto", "prefill"])
+def test_layer_max_experts_and_top_k(fmt, mode):
+    """The largest routing the boundary accepts: E = 1024 experts, top-16, on narrow experts, so
+    that every kernel sees 1024 row groups (most of them empty) and the combine sums 16 rows."""
+    wl = small_variant(fmt, E=1024, k=16, H=64, I=96, name="maxek-" + fmt)
+    T = 48
+    say("layer E=1024 k=16", wl.name, "mode", mode)
+    x, _ = oracle.rank_gap_inputs(wl, T)
+    layer = build_layer(wl, T)
+    out = layer.forward(to_device_act(x, "bf16"), mode=mode)
+    torch.cuda.synchronize()
+    ref, ids_ref, w_ref = oracle_reference(wl, x, np.arange(T))
+    assert np.array_equal(layer.topk_ids[:T].cpu().numpy(), ids_ref)
+    np.testing.assert_allclose(layer.topk_w[:T].cpu().numpy(), w_ref, rtol=GATE_RTOL, atol=GATE_ATOL)
+    assert_output_close(to_f64(out), ref, "bf16", wl.name)
+
+
 @pytest.mark.parametrize("fmt", ["mxfp4", "int4g32"])
 @pytest.mark.parametrize("T", [64, 200])
 def test_layer_many_experts_4bit(fmt, T):
