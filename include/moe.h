@@ -165,7 +165,8 @@ typedef struct {
 
 /* Workspace bytes moe_expert_ffn needs for these experts, T tokens and top-k: the activations
  * cast to the MFMA operand type when they differ from it, h [T*k][I], and the row-tile plans
- * (with the work counters of the persistent prefill kernels). */
+ * (with the work counters of the persistent prefill kernels).  A workspace serves one call at a
+ * time: calls in flight together (on different streams) need workspaces of their own. */
 size_t moe_ffn_workspace(const moe_experts* w, int T, int k, int mode);
 
 /*
