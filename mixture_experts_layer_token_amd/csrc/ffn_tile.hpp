@@ -674,13 +674,15 @@ __global__ __launch_bounds__(kTW * 64, 1) void ffn_tile_kernel(FfnArgs args) {
 // persistent grid of one workgroup per CU (a multiple of 8, so every XCD has the same number).
 template <int FMT, bool GU>
 int tile_launch(const FfnArgs& a, int H, int I, int n, int E, hipStream_t s) {
-  static bool attr_set = false;
+  static bool attr_set[64];  // per device
   const size_t lds = TileCfg<FMT>::LDS;
-  if (!attr_set) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (!attr_set[dev]) {
     hipError_t e = hipFuncSetAttribute((const void*)ffn_tile_kernel<FMT, GU>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return hip_fail(e, "moe_expert_ffn: LDS attribute of the prefill kernel");
-    attr_set = true;
+    attr_set[dev] = true;
   }
   // activation offsets are 32-bit byte offsets: the A matrix (x for gate/up, h for down) must
   // stay under 4 GiB
