@@ -733,10 +733,10 @@ WsLayout ws_layout(const moe_experts* w, int T, int k, int xdt) {
   // row-tile plan of the streaming kernels: at most n / 16 + min(n, E) tiles
   L.plan_off = L.h_off + L.h_bytes;
   L.plan_bytes = f32w ? 0 : align256((1 + n / 16 + (n < (size_t)w->E ? n : (size_t)w->E)) * sizeof(int4));
-  // row-tile plan of the tile kernels (at most n / 192 + min(n, E) tiles), then their work
+  // row-tile plan of the tile kernels (at most n / kTileRows + min(n, E) tiles), then their work
   // counters (8 for gate/up, 8 for down)
   L.tplan_off = L.plan_off + L.plan_bytes;
-  L.tplan_bytes = f32w ? 0 : align256((1 + n / 192 + (n < (size_t)w->E ? n : (size_t)w->E)) * sizeof(int4)) + 256;
+  L.tplan_bytes = f32w ? 0 : align256((1 + n / kTileRows + (n < (size_t)w->E ? n : (size_t)w->E)) * sizeof(int4)) + 256;
   L.total = L.tplan_off + L.tplan_bytes;
   return L;
 }
@@ -990,7 +990,7 @@ int launch_ffn(const moe_experts* w, const void* x, int xdt, int T, int k, const
   if (use_tile) {
     int4* tplan = (int4*)(wsp + L.tplan_off);
     int* counters = (int*)(wsp + L.tplan_off + L.tplan_bytes - 256);
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, offsets, E, 192, gu_t.min_rows, 0x7FFFFFFF,
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, offsets, E, kTileRows, gu_t.min_rows, 0x7FFFFFFF,
                        w->slot_of_expert, gu.n_slots, tplan, counters, 16);
     gu_t.plan = dn_t.plan = tplan;
     gu_t.tcount = counters;

@@ -158,6 +158,9 @@ struct FfnArgs {
 
 
 constexpr int kXcds = 8;  // XCDs of an MI355X; workgroup i is dispatched to XCD i % 8
+// Rows of a tile of the prefill (MFMA tile) kernel at most: its plans cut an expert with n rows
+// into ceil(n / kTileRows) tiles that split the rows evenly.
+constexpr int kTileRows = 192;
 
 // Dynamic work distribution over a persistent grid.  The work items are dealt in contiguous
 // ranges of `per` to the 8 XCDs (workgroup i runs on XCD i % 8), so that consecutive items (the

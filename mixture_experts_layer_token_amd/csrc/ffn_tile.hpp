@@ -40,9 +40,10 @@ namespace moe {
 namespace {
 
 constexpr int kTW = 4;    // waves per workgroup, one per SIMD; each owns 64 columns
-constexpr int kTM = 192;  // rows per workgroup tile (at most)
+constexpr int kTM = kTileRows;  // rows per workgroup tile (at most)
 constexpr int kTN = 256;  // columns per workgroup tile
-constexpr int kMT = 12;   // 16-row MFMA tiles of a full row tile
+constexpr int kMT = kTM / 16;  // 16-row MFMA tiles of a full row tile
+constexpr int kWGPerCU = kTM <= 96 ? 2 : 1;  // resident workgroups per CU (register file)
 constexpr int kWNS = 4;   // 16-column strips per wave
 #ifndef MOE_CFG_TILE_D_BF16
 #define MOE_CFG_TILE_D_BF16 4
@@ -57,12 +58,15 @@ struct TileCfg {
   // 4-bit weights and costs 12 more registers); even kD * BK / 32 keeps the register buffers of
   // A fragments in step across loop iterations
   static constexpr int D = FMT == MOE_W_BF16 ? MOE_CFG_TILE_D_BF16 : MOE_CFG_TILE_D_Q4;
-  static constexpr size_t LDS = (size_t)D * kTM * BK * 2;  // kD ring buffers
   static constexpr int CPR = BK / 8;    // 16-byte chunks per staged row
   static constexpr int RPI = 64 / CPR;  // rows per wave-wide direct-to-LDS load
-  // activation loads per wave and block of a full 192-row tile: load i of wave w fills rows
+  // activation loads per wave and block of a full tile: load i of wave w fills rows
   // (i*kTW + w)*RPI + [0, RPI)
   static constexpr int IPW_MAX = (kTM + kTW * RPI - 1) / (kTW * RPI);
+  // rows of an LDS block buffer: every load of a full tile lands inside (rows past the tile's
+  // own are filled too, and never read)
+  static constexpr int ROWS = IPW_MAX * kTW * RPI;
+  static constexpr size_t LDS = (size_t)D * ROWS * BK * 2;  // kD ring buffers
   static constexpr bool Q4 = FMT != MOE_W_BF16;
   static constexpr int KS = BK / 32;         // k-steps per block
   static constexpr int NBL = Q4 ? 2 : KS;    // weight loads per strip and block
@@ -200,7 +204,7 @@ __device__ __forceinline__ void tile_load_a(const FfnArgs& args, const TileCtx& 
   constexpr int BK = TileCfg<FMT>::BK, RPI = TileCfg<FMT>::RPI;
   const int r0 = (i * kTW + c.wave) * RPI;
   gptr g = (gptr)args.a + (size_t)kb * (BK * 2) + avoff;
-  unsigned short* l = lds_a + ((size_t)buf * kTM + r0) * BK;
+  unsigned short* l = lds_a + ((size_t)buf * TileCfg<FMT>::ROWS + r0) * BK;
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
                                    (__attribute__((address_space(3))) void*)l, 16, 0, 0);
 }
@@ -394,7 +398,7 @@ __device__ __forceinline__ void tile_body(const FfnArgs& args, TileCtx& c, unsig
   };
   // A fragment of M tile mt, k-step q of buffer buf: row mt*16 + lane%16, chunk 4q + lane/16
   auto read_a_one = [&](OpT& dst, int buf, int q, int mt) {
-    const unsigned short* abase = lds_a + ((size_t)buf * kTM + (lane & 15)) * BK;
+    const unsigned short* abase = lds_a + ((size_t)buf * TileCfg<FMT>::ROWS + (lane & 15)) * BK;
     const int slot = (4 * q + (lane >> 4)) ^ (lane & (CPR - 1));
     dst = *(const OpT*)(abase + mt * 16 * BK + slot * 8);
   };
@@ -609,7 +613,7 @@ __device__ __forceinline__ void tile_body(const FfnArgs& args, TileCtx& c, unsig
 template <int FMT, bool GU>
 // one wave per SIMD: the accumulators (up to 192 registers) live in the AGPR half of the file.
 // Persistent: one workgroup per CU takes work items until every XCD's range is drained.
-__global__ __launch_bounds__(kTW * 64, 1) void ffn_tile_kernel(FfnArgs args) {
+__global__ __launch_bounds__(kTW * 64, kWGPerCU) void ffn_tile_kernel(FfnArgs args) {
   extern __shared__ __align__(16) unsigned short lds_a[];
   __shared__ int sh_item;
   constexpr int kD = TileCfg<FMT>::D;
@@ -651,20 +655,12 @@ __global__ __launch_bounds__(kTW * 64, 1) void ffn_tile_kernel(FfnArgs args) {
     tile_prologue_a<FMT>(args, c, lds_a, avoff, rows);
   }
   do {
-    switch ((c.rows + 15) / 16) {
-      case 1: tile_body<FMT, GU, 1>(args, c, lds_a, ring, avoff, sch, ncol, &sh_item); break;
-      case 2: tile_body<FMT, GU, 2>(args, c, lds_a, ring, avoff, sch, ncol, &sh_item); break;
-      case 3: tile_body<FMT, GU, 3>(args, c, lds_a, ring, avoff, sch, ncol, &sh_item); break;
-      case 4: tile_body<FMT, GU, 4>(args, c, lds_a, ring, avoff, sch, ncol, &sh_item); break;
-      case 5: tile_body<FMT, GU, 5>(args, c, lds_a, ring, avoff, sch, ncol, &sh_item); break;
-      case 6: tile_body<FMT, GU, 6>(args, c, lds_a, ring, avoff, sch, ncol, &sh_item); break;
-      case 7: tile_body<FMT, GU, 7>(args, c, lds_a, ring, avoff, sch, ncol, &sh_item); break;
-      case 8: tile_body<FMT, GU, 8>(args, c, lds_a, ring, avoff, sch, ncol, &sh_item); break;
-      case 9: tile_body<FMT, GU, 9>(args, c, lds_a, ring, avoff, sch, ncol, &sh_item); break;
-      case 10: tile_body<FMT, GU, 10>(args, c, lds_a, ring, avoff, sch, ncol, &sh_item); break;
-      case 11: tile_body<FMT, GU, 11>(args, c, lds_a, ring, avoff, sch, ncol, &sh_item); break;
-      default: tile_body<FMT, GU, kMT>(args, c, lds_a, ring, avoff, sch, ncol, &sh_item); break;
-    }
+    // the variant with NMT = ceil(rows / 16) MFMA row tiles
+    const int nmt = (c.rows + 15) / 16;
+    static_for<kMT>([&](auto ic) {
+      constexpr int m = ic + 1;
+      if (nmt == m || (m == kMT && nmt > kMT)) tile_body<FMT, GU, m>(args, c, lds_a, ring, avoff, sch, ncol, &sh_item);
+    });
   } while (c.rows > 0);
 }
 
@@ -696,7 +692,7 @@ int tile_launch(const FfnArgs& a, int H, int I, int n, int E, hipStream_t s) {
   const int ncol = (N + kTN - 1) / kTN;
   const long long total = S * ncol;
   const long long per = (total + kXcds - 1) / kXcds;
-  const long long resident = cu_count() / kXcds;  // workgroups per XCD at one per CU
+  const long long resident = (long long)kWGPerCU * cu_count() / kXcds;  // resident workgroups per XCD
   const long long grid = kXcds * (per < resident ? per : (resident > 0 ? resident : 1));
   hipLaunchKernelGGL((ffn_tile_kernel<FMT, GU>), dim3((unsigned)grid), dim3(kTW * 64), lds, s, a);
   return MOE_OK;

@@ -324,11 +324,11 @@ int launch_route(const void* x, int xdt, int T, int H, const void* wg, const flo
     int32_t* offs = (int32_t*)(wsp + L.offsets_off);
     int4* plan = (int4*)(wsp + L.plan_off);
     int* counters = (int*)(wsp + L.count_off);
-    // row tile height: about one work item (row tile x 256 columns) per CU, 32 to 192 rows (every
+    // row tile height: about one work item (row tile x 256 columns) per CU, 32 to kTileRows rows (every
     // row tile reads the whole router matrix again, from L2)
     const long long ncol = (E + 255) / 256;
     int rt = (int)((long long)T * ncol / cu_count()) / 16 * 16;
-    rt = rt < 32 ? 32 : (rt > 192 ? 192 : rt);
+    rt = rt < 32 ? 32 : (rt > kTileRows ? kTileRows : rt);
     const size_t chunks = (size_t)E * H / 8, nt = (size_t)(T + rt - 1) / rt;
     const size_t threads = chunks > nt + 8 ? chunks : nt + 8;
     hipLaunchKernelGGL(route_pack_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
