@@ -55,8 +55,9 @@ template <int FMT>
 struct TileCfg {
   static constexpr int BK = FMT == MOE_W_BF16 ? 32 : 64;  // K per block
   // pipeline depth kD: K blocks in flight (4 covers the load latency: 5 measured no faster for
-  // 4-bit weights and costs 12 more registers); even kD * BK / 32 keeps the register buffers of
-  // A fragments in step across loop iterations
+  // 4-bit weights and costs 12 more registers, 3 measured 14% slower on the INT4 gate/up of the
+  // Kimi-shaped layer); even kD * BK / 32 keeps the register buffers of A fragments in step
+  // across loop iterations
   static constexpr int D = FMT == MOE_W_BF16 ? MOE_CFG_TILE_D_BF16 : MOE_CFG_TILE_D_Q4;
   static constexpr int CPR = BK / 8;    // 16-byte chunks per staged row
   static constexpr int RPI = 64 / CPR;  // rows per wave-wide direct-to-LDS load
