@@ -955,7 +955,11 @@ int launch_ffn(const moe_experts* w, const void* x, int xdt, int T, int k, const
     // few tiles to fill the GPU (gpt-oss-shaped MXFP4, 128 experts, top-4: T = 256 / 512 / 1024,
     // 223 vs 294, 317 vs 368, 488 vs 469 us per layer step)
     const double min_avg_rows = w->fmt == MOE_W_BF16 ? 0.0 : 24.0;
-    if ((double)n >= 64.0 * E) {
+    // bf16 experts from 28 rows per expert on average: the tile kernel for every expert (a second
+    // streaming row tile re-reads a whole expert from HBM; Mixtral-shaped, 8 experts, top-2:
+    // T = 96 / 128, streaming 531 / 693 us, tile kernel 568 / 576 us per layer step)
+    const double tile_all_rows = w->fmt == MOE_W_BF16 ? 28.0 : 64.0;
+    if ((double)n >= tile_all_rows * E) {
       use_stream = false, use_tile = true, split = 0;
     } else if (T > kHot && (double)n >= min_avg_rows * E) {  // (no expert has more than T rows)
       use_tile = true, split = kHot;
