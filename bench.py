@@ -509,8 +509,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (expert parallelism is a design note "
-              "only); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (expert parallelism is described, "
+              "not implemented); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
 
