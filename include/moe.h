@@ -82,6 +82,10 @@ const char* moe_last_error(void);
  *   topk_ids  device [T][k] int32 (out);  topk_w device [T][k] fp32 (out)
  *   logits    device [T][E] fp32 (out), or NULL
  *   ws        device workspace of ws_bytes >= moe_route_workspace(T, H, E, xdt) bytes (may be NULL if 0)
+ * Logits that are not finite: +inf and -inf order as numbers, NaN below -inf; a token always gets
+ * k distinct ids in [0, E) (a token whose logits are all NaN gets ids 0..k-1), and a NaN among its
+ * chosen logits (or infinities of both signs) makes that token's gate weights NaN; other tokens
+ * are not affected.
  * Errors: MOE_ERR_INVALID for null x/w_router/topk_ids/topk_w (when T > 0), E out of
  * 1..1024, k out of 1..min(E,16), H <= 0; MOE_ERR_WORKSPACE if the workspace is too small.
  */
@@ -106,14 +110,17 @@ size_t moe_permute_workspace(int T, int k, int E);
 /*
  * Group the T*k (token, slot) pairs by expert, stably:
  *   counts[e]   number of pairs routed to e                      device [E] int32 (out)
- *   offsets[e]  exclusive prefix sum of counts, offsets[E] = T*k device [E+1] int32 (out)
+ *   offsets[e]  exclusive prefix sum of counts; offsets[E] = the number of pairs placed
+ *               (T*k when every id is valid)                      device [E+1] int32 (out)
  *   perm_src[p] flat index t*k+j of the p-th pair in expert-major order, ascending
- *               flat index inside an expert                       device [T*k] int32 (out)
- *   inv_perm[i] position p of flat index i (perm_src[inv_perm[i]] == i) device [T*k] int32 (out)
- *   topk_ids    device [T][k] int32, every id in [0, E)
+ *               flat index inside an expert, p < offsets[E]       device [T*k] int32 (out)
+ *   inv_perm[i] position p of flat index i (perm_src[inv_perm[i]] == i), or -1 for a
+ *               dropped pair                                      device [T*k] int32 (out)
+ *   topk_ids    device [T][k] int32
+ * A pair whose id lies outside [0, E) is dropped: not counted, not placed, inv_perm -1 (the
+ * combine then skips it).  moe_route never produces such ids.
  * Errors: MOE_ERR_INVALID for null pointers (T > 0), E out of 1..1024, k < 1,
  * T*k > 1<<24; MOE_ERR_WORKSPACE if ws_bytes < moe_permute_workspace(T, k, E).
- * Ids outside [0, E) are a caller error with undefined (but memory-safe) results.
  */
 int moe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t* counts, int32_t* offsets, int32_t* perm_src,
                 int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream);
@@ -203,7 +210,8 @@ int moe_ffn_trace_events(void* const* events);
  * Weighted combine back to token order:
  *   out[t] = sum_{j<k} topk_w[t][j] * y_perm[inv_perm[t*k+j]]  (+ shared_y[t])
  * fp32 sum in slot order j = 0..k-1, then the shared expert's output with weight 1,
- * then one rounding (nearest-even) to odt.  Deterministic: no atomics.
+ * then one rounding (nearest-even) to odt.  Deterministic: no atomics.  A pair with
+ * inv_perm -1 (dropped by moe_permute) contributes nothing.
  *   y_perm device [T*k][H] fp32; topk_w device [T][k] fp32; inv_perm device [T*k] int32
  *   shared_y device [T][H] fp32 or NULL; out device [T][H] of type odt (out)
  */

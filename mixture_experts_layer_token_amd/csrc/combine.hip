@@ -42,14 +42,19 @@ __global__ __launch_bounds__(512) void combine_kernel(const float* __restrict__ 
     // the k rows' loads are issued together, then summed in slot order
     f32x4 v[K];
 #pragma unroll
-    for (int j = 0; j < K; ++j) v[j] = ld_stream((const f32x4*)(y + (size_t)rows[j] * H + c));
+    for (int j = 0; j < K; ++j) {
+      // a pair the permutation dropped (inv_perm -1: its expert id was outside [0, E)) adds nothing
+      v[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (rows[j] >= 0) v[j] = ld_stream((const f32x4*)(y + (size_t)rows[j] * H + c));
+    }
     f32x4 sv = {0.f, 0.f, 0.f, 0.f};
     if (shared) sv = ld_stream((const f32x4*)(shared + (size_t)t * H + c));
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < K; ++j)
+      if (rows[j] >= 0)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc[q] = fmaf(gates[j], v[j][q], acc[q]);
+        for (int q = 0; q < 4; ++q) acc[q] = fmaf(gates[j], v[j][q], acc[q]);
     if (shared)
 #pragma unroll
       for (int q = 0; q < 4; ++q) acc[q] += sv[q];

@@ -60,7 +60,13 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t* __
     offsets[tid] = excl;
     cursor[tid] = excl;
   }
-  if (tid == 0) offsets[E] = n;
+  // the end of the last expert's range is the number of pairs placed (pairs with an id outside
+  // [0, E) are dropped), so no range covers an unwritten entry
+  if (tid == 0) {
+    int total = 0;
+    for (int w = 0; w < 16; ++w) total += wsum[w];
+    offsets[E] = total;
+  }
   __syncthreads();
 
   scatter_range(ids, 0, n, E, cursor, perm, inv);
@@ -88,6 +94,7 @@ __device__ void scatter_range(const int32_t* __restrict__ ids, int i0, int i1, i
     if (e < 0) peers = 0;
     const int rank = __popcll(peers & below);
     const int total = __popcll(peers);
+    if (valid && e < 0) inv[i] = -1;  // a dropped pair: its combine term is skipped
     for (int w = 0; w < 16; ++w) {
       if (wave == w && e >= 0) {
         // every lane of the wave reads cursor[e] (one LDS instruction) before the last peer
@@ -148,7 +155,11 @@ __global__ __launch_bounds__(kPermThreads) void perm_scan_kernel(const int32_t* 
       run += bcnt[(size_t)b * E + tid];
     }
   }
-  if (tid == 0) offsets[E] = n;
+  if (tid == 0) {  // pairs placed (ids outside [0, E) are dropped)
+    int total = 0;
+    for (int w = 0; w < 16; ++w) total += wsum[w];
+    offsets[E] = total;
+  }
 }
 
 // (3) block b scatters its indices in order, starting expert e at bbase[b][e]

@@ -23,32 +23,52 @@ constexpr int kMaxE = 1024;
 // is large; larger batches use the MFMA tile kernel (one read per 192 x 256 tile).
 constexpr long long kSplitMaxTE = 1 << 20;
 
-// (value, id) ordering of the router: larger value first, equal values -> lower id first
-__device__ __forceinline__ bool better(float v, int e, float bv, int be) { return v > bv || (v == bv && e < be); }
+// The selection compares unsigned keys that order the logits totally: a larger logit has a larger
+// key (-0 counts as +0), every NaN has key 1, below -inf, and a chosen entry has key 0, below
+// everything.  So a token whose logits hold NaN or infinities still gets k distinct ids in [0, E)
+// (finite and infinite logits first, NaN ones last, equal keys -> lower id), and only its own gate
+// weights carry the NaN.
+__device__ __forceinline__ unsigned logit_key(float v) {
+  if (v != v) return 1u;
+  unsigned u = __float_as_uint(v);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_logit(unsigned key) {
+  if (key == 1u) return __uint_as_float(0x7FC00000u);
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
 
-// top-k of one token's E logits in LDS row `lg`; executed by one full wave.  Chosen entries are
-// overwritten with -inf in LDS.  Lane j keeps the j-th choice and writes ids[j], w[j].
+// top-k of one token's E logits in LDS row `lg`; executed by one full wave.  The row is turned into
+// keys in place (logit_key), chosen entries get key 0.  Lane j keeps the j-th choice and writes
+// ids[j], w[j].
 __device__ void wave_topk(float* lg, int E, int k, int32_t* ids, float* w) {
   const int lane = threadIdx.x & 63;
-  float my_v = -INFINITY;
+  unsigned* key = (unsigned*)lg;
+  for (int e = lane; e < E; e += 64) key[e] = logit_key(lg[e]);
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  unsigned my_key = 0;
   int my_e = 0;
   for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int be = 0x7FFFFFFF;
+    // (key, E - 1 - id) as one 64-bit value: its maximum is the largest key, then the lowest id;
+    // an unchosen entry (key >= 1) always exists because k <= E
+    unsigned long long best = 0;
     for (int e = lane; e < E; e += 64) {
-      float v = lg[e];
-      if (better(v, e, bv, be)) bv = v, be = e;
+      const unsigned long long c = ((unsigned long long)key[e] << 32) | (unsigned)(E - 1 - e);
+      best = c > best ? c : best;
     }
     for (int off = 32; off > 0; off >>= 1) {
-      float ov = __shfl_xor(bv, off, 64);
-      int oe = __shfl_xor(be, off, 64);
-      if (better(ov, oe, bv, be)) bv = ov, be = oe;
+      const unsigned long long o = __shfl_xor(best, off, 64);
+      best = o > best ? o : best;
     }
-    if (lane == j) my_v = bv, my_e = be;
-    if (lane == 0) lg[be] = -INFINITY;
+    const int be = E - 1 - (int)(unsigned)(best & 0xFFFFFFFFull);
+    if (lane == j) my_key = (unsigned)(best >> 32), my_e = be;
+    if (lane == 0) key[be] = 0u;
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   }
+  const float my_v = key_logit(my_key);
   // softmax over the k chosen logits (max = the first choice)
   const float v0 = __shfl(my_v, 0, 64);
   float p = lane < k ? expf(my_v - v0) : 0.f;

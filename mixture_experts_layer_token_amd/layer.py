@@ -103,8 +103,10 @@ def _workers():
     return min(16, os.cpu_count() or 1)
 
 
-def pack_bank(wl, layer: int, experts, fmt: str | None = None, stride: int | None = None) -> np.ndarray:
-    """Host [len(experts), stride] uint8 bank of packed experts of one layer (parallel over experts)."""
+def pack_bank(wl, layer: int, experts, fmt: str | None = None, stride: int | None = None,
+              weights=None) -> np.ndarray:
+    """Host [len(experts), stride] uint8 bank of packed experts of one layer (parallel over experts).
+    `weights`: optional mapping expert -> logical weights already generated (else generated here)."""
     from synth import workloads as W
 
     fmt = fmt or wl.wfmt
@@ -114,7 +116,7 @@ def pack_bank(wl, layer: int, experts, fmt: str | None = None, stride: int | Non
 
     def one(i):
         e = experts[i]
-        ex = W.expert_weights(wl, layer, e)
+        ex = weights[e] if weights is not None else W.expert_weights(wl, layer, e)
         api.moe_pack_expert(wl.H, wl.I, fmt, ex, bank[i, :nb])
 
     with cf.ThreadPoolExecutor(max_workers=_workers()) as pool:
@@ -122,8 +124,9 @@ def pack_bank(wl, layer: int, experts, fmt: str | None = None, stride: int | Non
     return bank
 
 
-def build_layer(wl, max_T: int, layer: int = 0, step: int = 0, device="cuda") -> MoeLayer:
-    """Device layer for workload `wl` (layer index `layer`; router bias of `step`'s popularity epoch)."""
+def build_layer(wl, max_T: int, layer: int = 0, step: int = 0, device="cuda", weights=None) -> MoeLayer:
+    """Device layer for workload `wl` (layer index `layer`; router bias of `step`'s popularity epoch).
+    `weights`: optional mapping expert -> logical weights already generated."""
     from synth import workloads as W
 
     nb = api.moe_package_bytes(wl.H, wl.I, wl.wfmt)
@@ -132,7 +135,7 @@ def build_layer(wl, max_T: int, layer: int = 0, step: int = 0, device="cuda") ->
     chunk = max(1, min(wl.E, (1 << 30) // stride))  # pack ~1 GiB at a time on the host
     for e0 in range(0, wl.E, chunk):
         ids = list(range(e0, min(wl.E, e0 + chunk)))
-        host = pack_bank(wl, layer, ids, stride=stride)
+        host = pack_bank(wl, layer, ids, stride=stride, weights=weights)
         packages[e0:e0 + len(ids)].copy_(torch.from_numpy(host))
     wg = to_device_act(W.router_weights(wl, layer), wl.xdt, device)
     b = W.router_bias(wl, layer, step)

@@ -50,8 +50,9 @@ def to_f64(t) -> np.ndarray:
     return t.detach().to("cpu", torch.float32).numpy().astype(np.float64)
 
 
-def oracle_reference(wl, x: np.ndarray, sample, layer: int = 0, step: int = 0):
-    """(out [n, H], ids [n, k], w [n, k]) of the oracle for the sampled tokens, generating only touched experts."""
+def oracle_reference(wl, x: np.ndarray, sample, layer: int = 0, step: int = 0, weights=None):
+    """(out [n, H], ids [n, k], w [n, k]) of the oracle for the sampled tokens, generating only touched experts
+    (or taking them from `weights`, a mapping expert -> logical weights)."""
     wg = W.router_weights(wl, layer)
     bias = W.router_bias(wl, layer, step)
     sample = np.asarray(sample, dtype=np.int64)
@@ -61,7 +62,7 @@ def oracle_reference(wl, x: np.ndarray, sample, layer: int = 0, step: int = 0):
     touched = sorted(set(ids.ravel().tolist()))
     experts = [None] * wl.E
     for e in touched:
-        experts[e] = W.expert_weights(wl, layer, e)
+        experts[e] = weights[e] if weights is not None else W.expert_weights(wl, layer, e)
     shared = W.shared_weights(wl, layer)
     out, ids2, w = oracle.moe_layer(wl.xdt, x, wg, bias, wl.k, wl.I, experts, shared, wl.I if shared else 0,
                                     sample=sample)

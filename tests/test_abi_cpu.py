@@ -74,7 +74,13 @@ def test_ffn_validation():
     assert L.moe_expert_ffn(ctypes.byref(d2), None, 1, 4, 2, None, None, None, 0, None, 0, None) == UNSUPPORTED
     d3 = moe.experts_desc(4096, 14336, 0, "bf16", None, 1 << 30)
     assert L.moe_expert_ffn(ctypes.byref(d3), None, 1, 4, 2, None, None, None, 0, None, 0, None) == INVALID
-    assert L.moe_ffn_workspace(ref, 64, 2, 0) > 0 or True
+    # workspace of bf16 experts, T = 64, k = 2 (128 pairs): the activation cast sized for fp32 input
+    # (64 x 4096 bf16), h (128 x 14336 bf16), the streaming row-tile plan (1 + 128 / 16 + min(128, 8)
+    # int4 entries) and the tile plan (1 + 0 + 8 entries) plus its 256 bytes of work counters, each
+    # region rounded up to 256 bytes
+    al = lambda b: (b + 255) // 256 * 256
+    want = al(64 * 4096 * 2) + al(128 * 14336 * 2) + al((1 + 8 + 8) * 16) + al((1 + 0 + 8) * 16) + 256
+    assert L.moe_ffn_workspace(ref, 64, 2, 0) == want
 
 
 @pytest.mark.parametrize("fmt,H,I,want", [("bf16", 4096, 14336, 352321536), ("mxfp4", 2880, 2880, 13219200),
@@ -147,6 +153,24 @@ def test_cache_planner_matches_oracle(policy, period):
     st = c.stats()
     assert st["hits"] == h.sum() and st["misses"] == m.sum() and st["evictions"] == sum(len(a) for a in v)
     assert st["bytes_fetched"] == m.sum() * (1 << 20)
+
+
+def test_cache_planner_hand_worked_decay_order():
+    """The planner on the hand-worked sequence that fixes when counts are halved (the halving at a
+    decay group comes before that group's own increments; see the oracle pins)."""
+    from test_oracle_pins import LFU_HAND_GROUPS, LFU_HAND_HITS
+
+    c = _planner(2, 1, 4, "lfu_decay", 2)
+    hits, victims = [], []
+    prev = {}
+    for grp in LFU_HAND_GROUPS:
+        pl = c.plan(0, np.array(grp))
+        hits.append(pl.n_hits)
+        now = {e: pl.slot_of_expert[e] for e in range(4) if pl.slot_of_expert[e] >= 0}
+        victims.append(sorted(set(prev) - set(now)))
+        prev = now
+    assert hits == LFU_HAND_HITS
+    assert victims == [[], [], [0], [1], [2], [0], []]
 
 
 def test_cache_rejects_unknown_policy():

@@ -156,3 +156,48 @@ def test_slots_outside_the_pool_are_skipped(mode):
         else:
             ref = oracle.ffn(ex[e], wl.H, wl.I, xd[rows])
             assert_output_close(got.astype(np.float64), ref, "bf16", "slot guard expert %d" % e)
+
+
+@pytest.mark.parametrize("T", [1, 16])
+def test_glm_full_run_planner_vs_oracle(T):
+    """The whole lookup sequence of the GLM-shaped offload run (256 steps x 8 layers, the activations
+    the offload bench routes, no rank-gap redraw): routed on the GPU, planned by the library's
+    planner under both policies the bench reports, and compared group by group with the oracle's
+    LRU and frequency-with-decay simulations (hits, misses) and the Belady bound."""
+    from mixture_experts_layer_token_amd import api
+    from mixture_experts_layer_token_amd.api import ExpertCache
+
+    wl = W.WORKLOADS["glm"]
+    say("glm planner, T", T)
+    ids = torch.empty((T, wl.k), dtype=torch.int32, device="cuda")
+    gw = torch.empty((T, wl.k), dtype=torch.float32, device="cuda")
+    wg = [to_device_act(W.router_weights(wl, l), wl.xdt) for l in range(wl.layers)]
+    bias = {}
+    groups = []
+    for s in range(wl.steps):
+        for l in range(wl.layers):
+            ep = s // wl.rerank_every
+            if (l, ep) not in bias:
+                bias[(l, ep)] = torch.from_numpy(W.router_bias(wl, l, s)).cuda()
+            x = to_device_act(W.activations(wl, T, l, s), wl.xdt)
+            api.moe_route(x, wg[l], bias[(l, ep)], wl.k, ids, gw)
+            got = ids.cpu().numpy()
+            assert got.min() >= 0 and got.max() < wl.E
+            assert all(len(set(r.tolist())) == wl.k for r in got)
+            groups.append((l * wl.E + got.ravel()).tolist())
+    cap = int(wl.cache_frac * wl.layers * wl.E)
+    for policy, period in (("lru", 0), ("lfu_decay", 32)):
+        c = ExpertCache(None, 1 << 20, wl.layers, wl.E, None, 0, cap, policy, period)
+        plans = [c.plan(g % wl.layers, np.array(grp, dtype=np.int64) - (g % wl.layers) * wl.E)
+                 for g, grp in enumerate(groups)]
+        if policy == "lru":
+            h, m, _ = oracle.lru(cap, groups)
+        else:
+            h, m, _ = oracle.lfu_decay(cap, period, groups)
+        assert [p.n_hits for p in plans] == h.tolist()
+        assert [p.n_misses for p in plans] == m.tolist()
+        hb, _ = oracle.belady(cap, groups)
+        assert hb.sum() >= h.sum()
+        say("  %s: hit rate %.4f (belady %.4f) over %d lookups" % (policy, h.sum() / (h.sum() + m.sum()),
+                                                                  hb.sum() / (h.sum() + m.sum()), h.sum() + m.sum()))
+        c.close()

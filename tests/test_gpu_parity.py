@@ -107,6 +107,8 @@ ROUTE_CASES = [
     ("tiny", 700, dict(E=48, k=5, H=96, name="e48-bf16", xdt="bf16")),  # large T, ragged 192-row tile
     # T * E > 2^20: the MFMA tile kernel in short row tiles (the last one ragged), two column tiles
     ("tiny", 3000, dict(E=400, k=6, H=96, name="e400-bf16-tile", xdt="bf16")),
+    # T * E > 2^20 with E not a multiple of 16: the one-kernel bf16 router (16 tokens per workgroup)
+    ("tiny", 50000, dict(E=24, k=3, H=96, name="e24-bf16-onekernel", xdt="bf16")),
 ]
 
 
@@ -130,6 +132,72 @@ def test_route_exact(name, T, kw):
     assert np.array_equal(ids.cpu().numpy(), ids_ref)
     np.testing.assert_allclose(w.cpu().numpy(), w_ref, rtol=GATE_RTOL, atol=GATE_ATOL)
     np.testing.assert_allclose(logits.cpu().numpy(), lg, rtol=1e-4, atol=1e-4 * np.abs(lg).max())
+
+
+# router inputs that are not finite: the ids stay distinct and in [0, E) on every router path
+ROUTE_NAN_CASES = [
+    ("tiny", 16, {}),                                                       # fp32, one workgroup per token
+    ("tiny", 300, dict(E=24, k=3, name="nan-split", xdt="bf16")),           # split over workgroups
+    ("tiny", 50000, dict(E=24, k=3, H=96, name="nan-onekernel", xdt="bf16")),  # one-kernel bf16 router
+    ("tiny", 3000, dict(E=400, k=6, H=96, name="nan-tile", xdt="bf16")),    # MFMA tile kernel
+]
+
+
+def _poison(x, xdt, rows):
+    """x with row rows[0] all NaN, row rows[1] holding one +inf and row rows[2] one NaN element."""
+    x = x.copy()
+    nan, inf = (np.float32(np.nan), np.float32(np.inf)) if xdt == "f32" else (np.uint16(0x7FC0), np.uint16(0x7F80))
+    x[rows[0], :] = nan
+    x[rows[1], 5] = inf
+    x[rows[2], 3] = nan
+    return x
+
+
+@pytest.mark.parametrize("name,T,kw", ROUTE_NAN_CASES, ids=[c[2].get("name", c[0]) for c in ROUTE_NAN_CASES])
+def test_route_nonfinite_rows(name, T, kw):
+    """A token whose logits are NaN or infinite gets k distinct ids in [0, E) (infinite and finite
+    logits first, NaN last, equal keys to the lower id: an all-NaN row takes ids 0..k-1); every other
+    token's routing is unchanged."""
+    wl = W.WORKLOADS[name].with_(**kw)
+    say("route non-finite rows", wl.name, "T", T)
+    x, _ = oracle.rank_gap_inputs(wl, T)
+    bad = [1, T // 2, T - 1]
+    xp = _poison(x, wl.xdt, bad)
+    wg, bias = W.router_weights(wl), W.router_bias(wl)
+    ids_ref, _ = oracle.topk_gates(oracle.router_logits(wl.xdt, x, wg, bias), wl.k)
+    ids = torch.empty((T, wl.k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, wl.k), dtype=torch.float32, device="cuda")
+    bd = torch.from_numpy(bias).cuda() if bias is not None else None
+    moe.moe_route(to_device_act(xp, wl.xdt), to_device_act(wg, wl.xdt), bd, wl.k, ids, w)
+    torch.cuda.synchronize()
+    got = ids.cpu().numpy()
+    assert got.min() >= 0 and got.max() < wl.E
+    assert all(len(set(r.tolist())) == wl.k for r in got)
+    assert got[bad[0]].tolist() == list(range(wl.k))
+    good = np.setdiff1d(np.arange(T), bad)
+    assert np.array_equal(got[good], ids_ref[good])
+    assert np.isnan(w.cpu().numpy()[bad[0]]).all()
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "mxfp4", "int4g32"])
+@pytest.mark.parametrize("mode", ["auto", "prefill"])
+def test_layer_nonfinite_token_leaves_others_exact(fmt, mode):
+    """One all-NaN token and one token with an infinite element go through the whole layer: every
+    other token's routing and output match the oracle."""
+    wl = small_variant(fmt)
+    T = 40
+    say("layer non-finite tokens", wl.name, mode)
+    x, _ = oracle.rank_gap_inputs(wl, T)
+    bad = [3, 20, 37]
+    layer = build_layer(wl, T)
+    out = layer.forward(to_device_act(_poison(x, wl.xdt, bad), wl.xdt), mode=mode)
+    torch.cuda.synchronize()
+    ids = layer.topk_ids[:T].cpu().numpy()
+    assert ids.min() >= 0 and ids.max() < wl.E
+    good = np.setdiff1d(np.arange(T), bad)
+    ref, ids_ref, _ = oracle_reference(wl, x, good)
+    assert np.array_equal(ids[good], ids_ref)
+    assert_output_close(to_f64(out)[good], ref, "bf16", wl.name + " finite tokens")
 
 
 # ------------------------------------------------------------------ permutation
@@ -335,23 +403,46 @@ def test_full_size_sampled(name, T, mode):
     c, o, p, i = oracle.permute(ids_ref, wl.E)
     assert np.array_equal(layer.offsets.cpu().numpy(), o)
     assert np.array_equal(layer.perm_src[:T * wl.k].cpu().numpy(), p)
-    # outputs of sampled tokens
-    rng = np.random.default_rng(T)
-    sample = np.sort(rng.choice(T, size=min(T, 6), replace=False))
+    # outputs of up to 64 tokens: every token of a small batch, else rows of every row tile of the
+    # hottest experts plus random tokens
+    sample = np.arange(T) if T <= 64 else kimi_sample(c, o, p, wl.k, T, n_total=64, seed=T)
     ref, _, _ = oracle_reference(wl, x, sample)
     assert_output_close(to_f64(out)[sample], ref, wl.xdt, "%s T=%d %s" % (wl.name, T, mode))
 
 
+def kimi_sample(counts, offsets, perm_src, k, T, n_total=256, hottest=3, seed=8192):
+    """Tokens to check at full size: for each of the `hottest` experts, the first, middle and last row
+    of each of its 192-row tiles (the tile kernel splits an expert's n rows evenly over ceil(n / 192)
+    tiles), topped up with seeded random tokens to n_total."""
+    pick = set()
+    for e in np.argsort(-counts, kind="stable")[:hottest]:
+        n = int(counts[e])
+        nt = (n + 191) // 192
+        for i in range(nt):
+            r0, r1 = i * n // nt, (i + 1) * n // nt
+            for r in (r0, (r0 + r1) // 2, r1 - 1):
+                pick.add(int(perm_src[offsets[e] + r]) // k)
+    rng = np.random.default_rng(seed)
+    rest = rng.permutation(np.setdiff1d(np.arange(T), sorted(pick)))
+    return np.sort(np.concatenate([sorted(pick), rest[:max(0, n_total - len(pick))]]).astype(np.int64))
+
+
 def test_kimi_prefill_full_size():
     """Kimi-K2-shaped INT4 layer + bf16 shared expert at T=8192: routing and permutation of every
-    token bit-exact, layer output of sampled tokens within tolerance."""
+    token bit-exact; the layer output of 256 tokens (every row tile of the three hottest experts
+    among them) within tolerance."""
+    import concurrent.futures as cf
+
     wl = W.WORKLOADS["kimi"]
     T = wl.Ts[0]
     say("kimi full size: inputs")
     x, _, lg = oracle.rank_gap_inputs(wl, T, return_logits=True)
     ids_ref, w_ref = oracle.topk_gates(lg, wl.k)
+    say("kimi full size: expert weights")
+    with cf.ThreadPoolExecutor(max_workers=4) as pool:
+        weights = dict(zip(range(wl.E), pool.map(lambda e: W.expert_weights(wl, 0, e), range(wl.E))))
     say("kimi full size: building the device bank")
-    layer = build_layer(wl, T)
+    layer = build_layer(wl, T, weights=weights)
     say("kimi full size: forward")
     out = layer.forward(to_device_act(x, wl.xdt))
     torch.cuda.synchronize()
@@ -361,7 +452,8 @@ def test_kimi_prefill_full_size():
     assert np.array_equal(layer.counts.cpu().numpy(), c)
     assert np.array_equal(layer.perm_src.cpu().numpy(), p)
     assert np.array_equal(layer.inv_perm.cpu().numpy(), i)
-    sample = np.array([0, 1, 777, 4095, 4096, 6000, 8190, 8191])
+    sample = kimi_sample(c, o, p, wl.k, T)
+    assert len(sample) >= 256
     say("kimi full size: oracle on", len(sample), "tokens")
-    ref, _, _ = oracle_reference(wl, x, sample)
+    ref, _, _ = oracle_reference(wl, x, sample, weights=weights)
     assert_output_close(to_f64(out)[sample], ref, "bf16", "kimi T=8192")

@@ -377,6 +377,31 @@ def test_lfu_decay_keeps_a_hot_set_that_lru_loses():
     assert (hl + ml == hr + mr).all()
 
 
+# A hand-worked sequence that fixes when the counts are halved: at the start of a decay group,
+# before that group's keys gain their 1024.  Capacity 2, period 2, keys a=0 b=1 c=2 d=3, one key
+# per group: [a] [b] [c] [a] [d] [b] [d].  Counts (before each group's lookups) and the victim
+# chosen by the smallest (count, last use, key) among resident keys not in the group:
+#   g0 a=1024                                   miss
+#   g1 b=1024                                   miss
+#   g2 halve: a=512 b=512;   c=1024             miss, a (512, last 0) < b (512, last 1): evict a
+#   g3 a=512+1024=1536                          miss, b (512) < c (1024): evict b
+#   g4 halve: a=768 b=256 c=512; d=1024         miss, c (512) < a (768): evict c
+#   g5 b=256+1024=1280                          miss, a (768) < d (1024): evict a
+#   g6 halve: a=384 b=640 c=256 d=512; d=1536   d resident: hit
+# Halving after the group's own increment would give d (1024 + 0) / 2 = 512 at g4 and evict d at g5
+# (then miss at g6); no decay at all would also evict d at g5 (a=2048 > d=1024).
+LFU_HAND_GROUPS = [[0], [1], [2], [0], [3], [1], [3]]
+LFU_HAND_HITS = [0, 0, 0, 0, 0, 0, 1]
+LFU_HAND_VICTIMS = [[], [], [0], [1], [2], [0], []]
+
+
+def test_lfu_decay_hand_worked_order_of_halving():
+    h, m, v = oracle.lfu_decay(2, 2, LFU_HAND_GROUPS)
+    assert list(h) == LFU_HAND_HITS
+    assert list(m) == [1 - x for x in LFU_HAND_HITS]
+    assert [list(a) for a in v] == LFU_HAND_VICTIMS
+
+
 def test_belady_at_least_lru_large():
     groups = _zipf_groups(400, 16, 512, 7)
     hb, _ = oracle.belady(64, groups)
