@@ -166,40 +166,76 @@ def touched_per_batch(layer, xs, E):
     return out
 
 
-def cpu_baseline(wl, xs_host, min_seconds: float = 10.0, max_tokens: int | None = None):
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _omp_threads(n: int | None):
+    """Set the OpenMP thread count of this process (the oracle's parallel loops); returns the previous one."""
+    import ctypes
+
+    try:
+        gomp = ctypes.CDLL("libgomp.so.1")
+    except OSError:
+        return None
+    prev = gomp.omp_get_max_threads()
+    if n is not None:
+        gomp.omp_set_num_threads(n)
+    return prev
+
+
+def cpu_baseline(wl, xs_host, min_seconds: float = 10.0, max_tokens: int | None = None,
+                 one_core_seconds: float = 3.0, one_core_tokens: int = 4):
     """The oracle on whole batches of the timed workload (or on the first `max_tokens` tokens of one
     batch) until about `min_seconds` of host time is spent: routing, touched experts' SwiGLU FFN,
-    shared expert, combine; expert weights generated untimed."""
+    shared expert, combine; expert weights generated untimed.  Then the same on one core, on the
+    first `one_core_tokens` tokens of the batches, for about `one_core_seconds`."""
     import oracle
     from synth import workloads as W
 
     wg, bias = W.router_weights(wl), W.router_bias(wl)
     cache = {}
-    tokens, spent, batches = 0, 0.0, 0
-    for i in range(64 * len(xs_host)):
-        x = xs_host[i % len(xs_host)]
-        if max_tokens is not None:
-            x = np.ascontiguousarray(x[:max_tokens])
-        lg = oracle.router_logits(wl.xdt, np.ascontiguousarray(x), wg, bias)
-        ids, _ = oracle.topk_gates(lg, wl.k)
-        experts = [None] * wl.E
-        for e in sorted(set(ids.ravel().tolist())):
-            if e not in cache:
-                cache[e] = W.expert_weights(wl, 0, e)
-            experts[e] = cache[e]
-        shared = W.shared_weights(wl)
-        t = time.perf_counter()
-        oracle.moe_layer(wl.xdt, x, wg, bias, wl.k, wl.I, experts, shared, wl.I if shared else 0)
-        spent += time.perf_counter() - t
-        tokens += x.shape[0]
-        batches += 1
-        if spent >= min_seconds:
-            break
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    shared = W.shared_weights(wl)
+
+    def timed(budget, cap):
+        tokens, spent, batches = 0, 0.0, 0
+        for i in range(64 * len(xs_host)):
+            x = xs_host[i % len(xs_host)]
+            if cap is not None:
+                x = np.ascontiguousarray(x[:cap])
+            lg = oracle.router_logits(wl.xdt, np.ascontiguousarray(x), wg, bias)
+            ids, _ = oracle.topk_gates(lg, wl.k)
+            experts = [None] * wl.E
+            for e in sorted(set(ids.ravel().tolist())):
+                if e not in cache:
+                    cache[e] = W.expert_weights(wl, 0, e)
+                experts[e] = cache[e]
+            t = time.perf_counter()
+            oracle.moe_layer(wl.xdt, x, wg, bias, wl.k, wl.I, experts, shared, wl.I if shared else 0)
+            spent += time.perf_counter() - t
+            tokens += x.shape[0]
+            batches += 1
+            if spent >= budget:
+                break
+        return tokens, spent, batches, x.shape[0]
+
+    threads = _omp_threads(None) or int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    tokens, spent, batches, bt = timed(min_seconds, max_tokens)
+    prev = _omp_threads(1)
+    t1, s1, _, _ = timed(one_core_seconds, min(one_core_tokens, max_tokens or one_core_tokens))
+    _omp_threads(prev)
     return {"value": tokens / spent, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "one_core": {"value": t1 / s1, "unit": "tokens/s", "cores": 1, "tokens": t1, "seconds": round(s1, 2)},
+            "cpu_model": cpu_model(),
             "sample": "%d batch(es) of %d tokens of the timed workload (%d tokens), whole layer in fp64: "
                       "routing, top-k, touched experts' SwiGLU FFN, shared expert, combine; %.1f s"
-                      % (batches, x.shape[0], tokens, spent)}
+                      % (batches, bt, tokens, spent)}
 
 
 def profiled_traffic(name: str):
@@ -318,6 +354,9 @@ OFFLOAD = ("glm",)
 # cache policies the offload run compares (the last one is the reported value): the plain LRU, and
 # use counts halved every 32 lookup groups (4 steps of the 8 layers)
 POLICIES = (("lru", 0), ("lfu_decay", 32))
+# prefetch heuristics the offload run compares: none, the next layer's experts of its previous step, its most
+# used experts so far
+PREFETCH = (None, "last", "popular")
 
 
 def belady_hits(capacity: int, groups) -> int:
@@ -347,8 +386,19 @@ def belady_hits(capacity: int, groups) -> int:
 PCIE_PEAK_GBS = 64.0  # PCIe 5.0 x16, one direction (the link figure the pages quote)
 
 
+def static_pins(model, groups_by_layer, per_layer: int):
+    """Static pin: each layer's `per_layer` most used experts over a calibration window of lookups."""
+    pins = {}
+    for l, groups in groups_by_layer.items():
+        cnt = np.zeros(model.E, np.int64)
+        for g in groups:
+            cnt[np.unique(g)] += 1
+        pins[l] = np.sort(np.argsort(-cnt, kind="stable")[:per_layer])
+    return pins
+
+
 def run_offload(args):
-    """256 decode steps through 8 layers whose experts live in pinned host memory (LRU cache in HBM)."""
+    """256 decode steps through 8 layers whose experts live in pinned host memory (HBM cache)."""
     import torch
 
     from synth import workloads as W
@@ -367,23 +417,30 @@ def run_offload(args):
         # route every (step, layer) once to know which experts the run touches; only those packages are
         # generated into the bank (the others are never fetched); the timed run routes again itself
         touched = {l: set() for l in range(wl.layers)}
+        calib = {l: [] for l in range(wl.layers)}  # lookups of the first epoch: the static pin's profile
         ids = torch.empty((T, wl.k), dtype=torch.int32, device="cuda")
         gw = torch.empty((T, wl.k), dtype=torch.float32, device="cuda")
         for (l, s), x in xs.items():
             api.moe_route(x, model.wg[l], model.bias(l, s), wl.k, ids, gw)
-            touched[l] |= set(ids.cpu().numpy().ravel().tolist())
+            got = ids.cpu().numpy().ravel()
+            touched[l] |= set(got.tolist())
+            if s < wl.rerank_every:
+                calib[l].append(got)
         for l in range(wl.layers):
             model.fill(l, touched[l] - model.filled.get(l, set()))
             model.filled[l] = model.filled.get(l, set()) | touched[l]
         out = torch.empty((T, wl.H), dtype=torch.bfloat16, device="cuda")
-        model.reset_cache()
+        model.reset_cache(prefetch=None)
         for l in range(wl.layers):  # warm the kernels through the full path (the cache is reset below)
             model.layer_forward(l, 0, xs[(l, 0)], out)
-        # every policy with the FFN of the hits overlapping the copies, and the reported policy once
-        # without the overlap
-        variants = [(p, d, True) for p, d in POLICIES] + ([(*POLICIES[-1], False)] if T == Ts[0] else [])
-        for policy, period, overlap in variants:
-            model.reset_cache(policy, period, overlap)
+        # half the slots pinned (the layers' most used experts over the first popularity epoch), LRU on the rest
+        pins = static_pins(model, calib, model.capacity // 2 // wl.layers)
+        variants = [(p, d, True, pf, None) for p, d in POLICIES for pf in PREFETCH]
+        variants += [("lru", 0, True, None, pins)]
+        if T == Ts[0]:  # the reported policy without the FFN/copy overlap
+            variants.append((*POLICIES[-1], False, None, None))
+        for policy, period, overlap, pf, pin in variants:
+            model.reset_cache(policy, period, overlap, prefetch=pf, pins=pin)
             torch.cuda.synchronize()
             t0 = time.perf_counter()
             for s in range(steps):
@@ -391,6 +448,7 @@ def run_offload(args):
                     model.layer_forward(l, s, xs[(l, s)], out, time_copies=True)
             torch.cuda.synchronize()
             wall = time.perf_counter() - t0
+            copy_s = model.copy_seconds()
             st = model.cache.stats()
             plans = model.plans
             seen, cold = set(), 0
@@ -406,8 +464,11 @@ def run_offload(args):
                     if key not in seen:
                         seen.add(key)
                         cold += 1
-            runs[(T, policy, overlap)] = {
-                "T": T, "policy": policy if policy == "lru" else "%s/%d" % (policy, period), "steps": steps,
+            name = policy if policy == "lru" else "%s/%d" % (policy, period)
+            if pin is not None:
+                name = "static-pin(%d/layer)+%s" % (len(pin[0]), name)
+            runs[(T, name, overlap, pf)] = {
+                "T": T, "policy": name, "prefetch": pf or "none", "steps": steps,
                 "ffn_of_hits_during_copies": overlap,
                 "layers": wl.layers, "wall_s": wall, "tokens_per_s": T * steps / wall,
                 "hit_rate": st["hits"] / max(1, st["lookups"]),
@@ -415,10 +476,12 @@ def run_offload(args):
                 "hit_rate_per_epoch": [round(v[0] / max(1, v[1]), 4) for _, v in sorted(per_epoch.items())],
                 "hit_rate_belady": belady.setdefault(T, belady_hits(model.capacity, model.groups)) / max(1, st["lookups"]),
                 "lookups": st["lookups"], "misses": st["misses"], "bytes_fetched": st["bytes_fetched"],
-                "copy_busy_s": model.copy_ms / 1e3,
-                "link_gbps_busy": st["bytes_fetched"] / max(1e-9, model.copy_ms / 1e3) / 1e9,
+                "prefetch_fetches": st["prefetch_fetches"], "prefetch_hits": st["prefetch_hits"],
+                "copy_busy_s": copy_s,
+                "link_gbps_busy": st["bytes_fetched"] / max(1e-9, copy_s) / 1e9,
                 "link_gbps_wall": st["bytes_fetched"] / wall / 1e9}
-    head = runs[(Ts[0], POLICIES[-1][0], True)]
+    head = max((r for r in runs.values() if r["T"] == Ts[0] and r["ffn_of_hits_during_copies"]),
+               key=lambda r: r["tokens_per_s"])
     out = {
         "metric": "MoE-layer tokens/s (offloaded expert bank, decode) + expert-cache hit rate + link GB/s",
         "value": round(head["tokens_per_s"], 2),
@@ -434,7 +497,8 @@ def run_offload(args):
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights quantized to int4g32)",
         "config": {"workload": wl.name, "T": Ts[0], "layers": wl.layers, "hidden": wl.H, "experts": wl.E,
                    "top_k": wl.k, "inter": wl.I, "cache_slots": model.capacity,
-                   "cache_policy": head["policy"], "ffn_of_hits_during_copies": True,
+                   "cache_policy": head["policy"], "prefetch": head["prefetch"], "ffn_of_hits_during_copies": True,
+                   "reported": "the fastest policy / prefetch combination at this T",
                    "bank_bytes": wl.layers * wl.E * model.pkg_bytes},
         "roofline": {"bound": "link", "kernel": "hipMemcpyAsync host bank -> HBM slots (copy stream)",
                      "achieved": round(head["link_gbps_busy"], 2), "peak": PCIE_PEAK_GBS, "unit": "GB/s",
@@ -444,6 +508,75 @@ def run_offload(args):
     model.close()
     return out
 
+
+
+SPEC_ACCEPT = (0.5, 0.7, 0.9)  # per-position draft acceptance rates the report is given for
+
+
+def expected_accepted(T: int, alpha: float) -> float:
+    """Accepted tokens per verification block of T = depth + 1 positions when each draft position is
+    accepted with probability alpha until the first rejection, plus the target's own token:
+    1 + alpha + ... + alpha^(T-1)."""
+    return sum(alpha ** i for i in range(T))
+
+
+def run_spec(args):
+    """Speculative verification: one request's block of T = depth + 1 positions through the GLM-shaped
+    INT4 layer resident in HBM, T = 1 (ordinary decode) to 4.  Grouping by expert reads each expert
+    of the block once (the union); a position-by-position pass would read k experts per position.
+    Reported per T: time per block, distinct experts, expert bytes per block with and without reuse,
+    and per accepted token at the acceptance rates SPEC_ACCEPT."""
+    import torch
+
+    from synth import workloads as W
+
+    from mixture_experts_layer_token_amd import api
+    from mixture_experts_layer_token_amd.layer import build_layer, to_device_act
+
+    wl = W.WORKLOADS["glm"].with_(name="glm-spec-int4", layers=1, steps=1, rerank_every=0)
+    pkg = api.moe_package_bytes(wl.H, wl.I, wl.wfmt)
+    layer = build_layer(wl, 4)
+    layers = layer_instances(layer, args.layers or 4)  # (4 x 3.4 GB: a step's experts are not in the MALL)
+    rows = []
+    for T in (1, 2, 3, 4):
+        xs_host = [W.activations(wl, T, 0, 2000 + r) for r in range(args.batches)]
+        xs = [to_device_act(a, wl.xdt) for a in xs_host]
+        outs = [torch.empty_like(x) for x in xs]
+        touched = touched_per_batch(layer, xs, wl.E)
+        steps = args.steps
+        total_ms, _, gu_ms, dn_ms, _ = measure(layers, xs, outs, steps, min(args.warmup, steps), trace=True)
+        graph_ms = measure_graph(layers, xs, outs, steps, min(args.warmup, steps))
+        union = float(np.mean(touched))
+        row = {"T": T, "depth": T - 1, "ms_per_block": round(graph_ms, 5),
+               "eager_ms_per_block": round(total_ms / steps, 5), "ffn_us": round(1e3 * float(np.mean(gu_ms) + np.mean(dn_ms)), 2),
+               "distinct_experts": union, "expert_bytes_union": int(union * pkg),
+               "expert_bytes_no_reuse": T * wl.k * pkg,
+               "hbm_gbps_experts": round(union * pkg / (graph_ms * 1e-3) / 1e9, 1), "per_accept_rate": []}
+        for a in SPEC_ACCEPT:
+            acc = expected_accepted(T, a)
+            row["per_accept_rate"].append({
+                "alpha": a, "accepted_per_block": round(acc, 4),
+                "expert_bytes_per_accepted": int(union * pkg / acc),
+                "expert_bytes_per_accepted_no_reuse": int(T * wl.k * pkg / acc),
+                "accepted_tokens_per_s": round(acc / (graph_ms * 1e-3), 1)})
+        rows.append(row)
+    base = rows[0]["ms_per_block"]
+    head = rows[-1]
+    best = next(r for r in head["per_accept_rate"] if r["alpha"] == 0.7)
+    return {
+        "metric": "MoE-layer accepted tokens/s of speculative verification (block of depth + 1 positions) "
+                  "+ expert bytes per accepted token",
+        "value": best["accepted_tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": head["ms_per_block"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp16",
+        "data": "synthetic (one request's positions routed independently; N(0,1) activations, N(0,0.02) weights "
+                "quantized to int4g32; per-position acceptance rate assumed, not measured)",
+        "config": {"workload": wl.name, "T": 4, "depth": 3, "hidden": wl.H, "experts": wl.E, "top_k": wl.k,
+                   "inter": wl.I, "alpha_reported": 0.7, "launch": "hipGraph replay",
+                   "layer_instances": len(layers), "input_batches": args.batches},
+        "blocks": rows,
+        "block_vs_decode_time": [round(r["ms_per_block"] / base, 3) for r in rows],
+    }
 
 
 MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 / fp16 MFMA, published
@@ -492,7 +625,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="mixtral", choices=["mixtral", "gptoss", "kimi", "glm"])
+    ap.add_argument("--workload", default="mixtral", choices=["mixtral", "gptoss", "kimi", "glm", "spec"])
     ap.add_argument("--offload-steps", type=int, default=256)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="copy 1 GiB device-to-device before measuring (profiler byte-counter calibration)")
@@ -506,6 +639,8 @@ def main():
                     help="decode: report the eager loop only (default: HIP graph replay, eager beside it)")
     ap.add_argument("--no-sweep", dest="sweep", action="store_false")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
+    ap.add_argument("--no-prefill", dest="prefill", action="store_false",
+                    help="default (Mixtral decode) run: leave out the Kimi-shaped prefill leg")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -526,8 +661,31 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.workload == "spec":
+        print(json.dumps(run_spec(args)), flush=True)
+        return
     out = run_offload(args) if args.workload in OFFLOAD else run(args)
+    if args.workload == "mixtral" and args.prefill:
+        out["prefill"] = prefill_leg(args)
     print(json.dumps(out), flush=True)
+
+
+def prefill_leg(args) -> dict:
+    """The metric's prefill half beside the decode headline: the Kimi-K2-shaped INT4 layer with its
+    shared expert at T = 8192, MFMA utilisation of the routed gate/up kernel, oracle on sampled tokens."""
+    import copy
+    import gc
+
+    import torch
+
+    gc.collect()
+    torch.cuda.empty_cache()
+    pa = copy.copy(args)
+    pa.workload, pa.T, pa.sweep, pa.graph, pa.layers = "kimi", None, False, False, None
+    pre = run(pa)
+    keep = ("metric", "value", "unit", "ms_per_step", "steps", "warmup", "dtype", "data", "config", "roofline",
+            "expert_ffn", "step_tflops", "cpu_baseline")
+    return {k: pre[k] for k in keep if k in pre}
 
 
 if __name__ == "__main__":

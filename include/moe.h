@@ -144,8 +144,10 @@ size_t moe_package_bytes(int H, int I, int fmt);
  *   *_scales  host [rows][K/32] (E8M0 bytes for MXFP4, bf16 bits for INT4); NULL for f32/bf16
  *   package   host, package_bytes >= moe_package_bytes(H, I, fmt) (out)
  * Errors: MOE_ERR_INVALID (null pointers, small package); MOE_ERR_UNSUPPORTED if H or I is not a
- * multiple of 32, or (INT4) a scale is not exactly representable in binary16, the precision the
- * kernels compute INT4 experts in.
+ * multiple of 32, or (INT4) a nonzero scale s lies outside [2^-14, 65504/8] in magnitude: the
+ * kernels compute INT4 experts on binary16 operands, where every q * s (q in [-8, 7]) is then an
+ * exact finite normal-range value (subnormal or NaN scales, and scales whose products overflow,
+ * are refused rather than rounded).
  */
 int moe_pack_expert(int H, int I, int fmt, const void* gate, const void* gate_scales, const void* up,
                     const void* up_scales, const void* down, const void* down_scales, void* package,
@@ -185,12 +187,20 @@ size_t moe_ffn_workspace(const moe_experts* w, int T, int k, int mode);
  *   offsets  device [E+1], perm_src device [T*k] (from moe_permute)
  *   y_perm   device [T*k][H] fp32 (out)
  * Precision: MFMA products of exactly decoded weights (bf16 / MXFP4 -> bf16 operands,
- * INT4 -> fp16 operands with fp16 activations) accumulated in fp32; the intermediate
- * SiLU(g)*u is rounded once to the operand type; f32 experts run in fp32 throughout.
+ * INT4 -> fp16 operands) accumulated in fp32; f32 experts run in fp32 throughout.
+ * Activations: fp32 input for bf16 / MXFP4 experts is rounded to bf16.  For INT4 experts each
+ * token's row is divided by a power of two s_t that puts its largest finite magnitude in [4, 8)
+ * and then rounded to fp16 (so any finite activation magnitude is safe; elements more than 2^19
+ * times smaller than the row's largest lose bits); the gate is evaluated on the unscaled value.
+ * The intermediate SiLU(g)*u is rounded once to the operand type; for INT4 it is SiLU(g)*u / s_t^2
+ * in fp16, bounded by 64 * |W_gate row|_1 * |W_up row|_1 whatever the activations (finite when that
+ * bound is below 65504; typical values are about H times smaller), and the down result is
+ * multiplied back by s_t^2 in fp32.
  * A shared (always-on) expert is the same call with E = 1, offsets = {0, T}, k = 1 and
  * perm_src = {0, 1, ..., T-1}.
  * Errors: MOE_ERR_INVALID (null pointers, sizes), MOE_ERR_UNSUPPORTED (H, I not multiples
- * of 32), MOE_ERR_WORKSPACE (ws smaller than moe_ffn_workspace).
+ * of 32; INT4 experts with activations not 16-byte aligned), MOE_ERR_WORKSPACE (ws smaller
+ * than moe_ffn_workspace).
  */
 int moe_expert_ffn(const moe_experts* w, const void* x, int xdt, int T, int k, const int32_t* offsets,
                    const int32_t* perm_src, float* y_perm, int mode, void* ws, size_t ws_bytes, void* stream);
@@ -235,11 +245,17 @@ int moe_combine(const float* y_perm, const float* topk_w, const int32_t* inv_per
  *     shift); then every key of the group gains 1024; the victim is the one with the
  *     smallest (count, tick, layer*E + expert).  Under a skewed, slowly drifting expert
  *     popularity this keeps the popular experts resident through bursts of one-off lookups.
+ * Pinned keys (moe_cache_pin) are never evicted; a key a prefetch brought in has tick -1 until a
+ * demand lookup uses it (moe_cache_prefetch).
  *
  * The cache object keeps the two pointers of its descriptor (it does not own them) and is
  * host-side state with a single owner (not thread-safe).
  */
 typedef struct moe_cache moe_cache_t;
+
+/* A copy engine: enqueue (or perform) a copy of `bytes` from src to dst on `stream`; return 0 on
+ * success, nonzero on failure.  The default engine is hipMemcpyAsync host -> device. */
+typedef int (*moe_copy_fn)(void* ctx, void* dst, const void* src, size_t bytes, void* stream);
 
 typedef struct {
   const void* host_bank; /* host, page-locked (hipHostMalloc): [L][E] packages, pkg_bytes apart */
@@ -250,6 +266,10 @@ typedef struct {
   int capacity;          /* number of slots (1 .. L*E) */
   int policy;            /* MOE_CACHE_LRU or MOE_CACHE_LFU_DECAY */
   int decay_period;      /* LFU_DECAY: groups between halvings of the counts (0: never) */
+  moe_copy_fn copy;      /* NULL: hipMemcpyAsync (host_bank must then be page-locked); otherwise every
+                            package and slot-table copy of moe_cache_fetch goes through it, and host_bank
+                            and device_pool are whatever memory it understands (not checked) */
+  void* copy_ctx;        /* first argument of `copy` */
 } moe_cache_desc;
 
 enum { MOE_CACHE_LRU = 0, MOE_CACHE_LFU_DECAY = 1 };
@@ -264,8 +284,11 @@ typedef struct {
 } moe_cache_plan_t;
 
 typedef struct {
-  int64_t lookups, hits, misses, evictions;
-  int64_t bytes_fetched;
+  int64_t lookups, hits, misses, evictions; /* demand lookups (moe_cache_plan) and all evictions */
+  int64_t bytes_fetched;                    /* package bytes of every fetch planned (demand, prefetch,
+                                               pin), less those a failed fetch rolled back */
+  int64_t prefetch_fetches;                 /* packages a prefetch brought in */
+  int64_t prefetch_hits;                    /* demand hits on such a package before its eviction */
 } moe_cache_stats_t;
 
 /*
@@ -284,11 +307,42 @@ int moe_cache_create(const moe_cache_desc* desc, moe_cache_t** out);
 int moe_cache_plan(moe_cache_t* c, int layer, const int32_t* host_ids, int n, moe_cache_plan_t* plan);
 
 /*
+ * Host only, synchronous: fetch ahead of use (best effort).  Makes the experts host_ids[0..n) of
+ * `layer` resident if slots allow, without counting demand lookups: each absent one takes a free
+ * slot or evicts the policy's first candidate that is neither in this set nor in the latest demand
+ * group (whose FFN may still be reading its slots); when no such candidate is left the remaining
+ * ones are skipped.  A prefetched expert enters as the first eviction candidate (last use "never",
+ * use count unchanged) until a demand lookup uses it; experts already resident are left as they
+ * are.  *plan lists the fetches (n_hits = already resident); enqueue them with moe_cache_fetch on
+ * the same copy stream as the demand fetches, so that a later demand fetch's event covers them.
+ * The intended use (predictor-free, "Understanding MoE Inference Costs on Galactus" and the Edge0
+ * abstract of the theflow.svmpsp.dev list): while layer l computes, prefetch what layer l + 1 used
+ * at the previous step, or its most used experts.
+ * Errors: MOE_ERR_INVALID (bad layer or id).
+ */
+int moe_cache_prefetch(moe_cache_t* c, int layer, const int32_t* host_ids, int n, moe_cache_plan_t* plan);
+
+/*
+ * Host only, synchronous: pin the experts host_ids[0..n) of `layer`: they become resident (absent
+ * ones take free slots or evict as a prefetch would) and are never evicted afterwards; demand
+ * lookups find them as hits.  A static pin of the popular experts beside the cache policy for the
+ * rest (theflow.svmpsp.dev list, the router-locality study: static-pin hit rate).  *plan lists the
+ * fetches; enqueue them with moe_cache_fetch.
+ * Errors: MOE_ERR_INVALID (bad layer or id); MOE_ERR_CAPACITY if the absent ones do not fit the
+ * free and evictable slots (state unchanged).  moe_cache_plan fails with MOE_ERR_CAPACITY for a
+ * group whose misses do not fit the slots left unpinned.
+ */
+int moe_cache_pin(moe_cache_t* c, int layer, const int32_t* host_ids, int n, moe_cache_plan_t* plan);
+
+/*
  * Enqueue on copy_stream one host->device copy per miss of *plan (bank package ->
  * its slot), then the copy of plan->slot_of_expert to dev_slot_of_expert (device [E],
  * usable as moe_experts.slot_of_expert with packages = device_pool), then record `done`
  * (a hipEvent_t as void*, may be NULL) so the compute stream can wait on it.
  * The plan's table is copied from the plan object: keep *plan alive until done.
+ * A copy that fails to enqueue rolls the plan back from that miss on: those experts are no longer
+ * resident (their slots are free again, and the next lookup of them misses and fetches them
+ * again); the call returns MOE_ERR_HIP and the plan's slot table must not be used.
  */
 int moe_cache_fetch(moe_cache_t* c, const moe_cache_plan_t* plan, int32_t* dev_slot_of_expert, void* copy_stream,
                     void* done);

@@ -21,9 +21,14 @@ class MoeExperts(ctypes.Structure):
                 ("pkg_stride", c_size_t), ("slot_of_expert", vp), ("n_slots", c_int)]
 
 
+# moe_copy_fn: int (*)(void* ctx, void* dst, const void* src, size_t bytes, void* stream)
+COPY_FN = ctypes.CFUNCTYPE(c_int, vp, vp, vp, c_size_t, vp)
+
+
 class MoeCacheDesc(ctypes.Structure):
     _fields_ = [("host_bank", vp), ("pkg_bytes", c_size_t), ("L", c_int), ("E", c_int), ("device_pool", vp),
-                ("slot_stride", c_size_t), ("capacity", c_int), ("policy", c_int), ("decay_period", c_int)]
+                ("slot_stride", c_size_t), ("capacity", c_int), ("policy", c_int), ("decay_period", c_int),
+                ("copy", COPY_FN), ("copy_ctx", vp)]
 
 
 class MoeCachePlan(ctypes.Structure):
@@ -34,7 +39,8 @@ class MoeCachePlan(ctypes.Structure):
 
 class MoeCacheStats(ctypes.Structure):
     _fields_ = [("lookups", ctypes.c_int64), ("hits", ctypes.c_int64), ("misses", ctypes.c_int64),
-                ("evictions", ctypes.c_int64), ("bytes_fetched", ctypes.c_int64)]
+                ("evictions", ctypes.c_int64), ("bytes_fetched", ctypes.c_int64),
+                ("prefetch_fetches", ctypes.c_int64), ("prefetch_hits", ctypes.c_int64)]
 
 
 SIGNATURES = {
@@ -53,6 +59,8 @@ SIGNATURES = {
     "moe_combine": ([f32p, f32p, i32p, c_int, c_int, c_int, f32p, vp, c_int, vp], c_int),
     "moe_cache_create": ([ctypes.POINTER(MoeCacheDesc), ctypes.POINTER(vp)], c_int),
     "moe_cache_plan": ([vp, c_int, i32p, c_int, ctypes.POINTER(MoeCachePlan)], c_int),
+    "moe_cache_prefetch": ([vp, c_int, i32p, c_int, ctypes.POINTER(MoeCachePlan)], c_int),
+    "moe_cache_pin": ([vp, c_int, i32p, c_int, ctypes.POINTER(MoeCachePlan)], c_int),
     "moe_cache_fetch": ([vp, ctypes.POINTER(MoeCachePlan), i32p, vp, vp], c_int),
     "moe_cache_stats": ([vp, ctypes.POINTER(MoeCacheStats)], c_int),
     "moe_cache_destroy": ([vp], None),

@@ -12,7 +12,7 @@ import ctypes
 import numpy as np
 import torch
 
-from ._lib import MoeCacheDesc, MoeCachePlan, MoeCacheStats, MoeExperts, check, lib
+from ._lib import COPY_FN, MoeCacheDesc, MoeCachePlan, MoeCacheStats, MoeExperts, check, lib
 
 FMT = {"f32": 0, "bf16": 1, "mxfp4": 2, "int4g32": 3}
 DT = {"f32": 0, "bf16": 1}
@@ -131,14 +131,21 @@ def moe_combine(y_perm, topk_w, inv_perm, k, shared_y, out, stream=None):
 class ExpertCache:
     """Owner of a moe_cache_t.  `bank` (pinned host tensor) and `pool` (device tensor) must outlive it."""
 
-    def __init__(self, bank, pkg_bytes, L, E, pool, slot_stride, capacity, policy="lru", decay_period=0):
+    def __init__(self, bank, pkg_bytes, L, E, pool, slot_stride, capacity, policy="lru", decay_period=0,
+                 copy=None, bank_ptr=None, pool_ptr=None):
+        """`copy`: optional copy engine, a Python callable (dst, src, bytes, stream) -> int (0 = ok);
+        `bank_ptr` / `pool_ptr` then give the raw addresses it works on."""
         d = MoeCacheDesc()
-        d.host_bank = bank.data_ptr() if bank is not None else None
+        d.host_bank = bank_ptr if bank_ptr is not None else (bank.data_ptr() if bank is not None else None)
         d.pkg_bytes, d.L, d.E = pkg_bytes, L, E
-        d.device_pool = pool.data_ptr() if pool is not None else None
+        d.device_pool = pool_ptr if pool_ptr is not None else (pool.data_ptr() if pool is not None else None)
         d.slot_stride, d.capacity = slot_stride, capacity
         d.policy = POLICY[policy]
         d.decay_period = decay_period
+        self._copy = None
+        if copy is not None:
+            self._copy = COPY_FN(lambda ctx, dst, src, n, stream: int(copy(dst, src, n, stream)))
+            d.copy = self._copy
         self._keep = (bank, pool)
         h = ctypes.c_void_p()
         check(lib().moe_cache_create(ctypes.byref(d), ctypes.byref(h)))
@@ -151,10 +158,25 @@ class ExpertCache:
         check(lib().moe_cache_plan(self.h, layer, _hp(ids), ids.size, ctypes.byref(p)))
         return p
 
+    def prefetch(self, layer, host_ids: np.ndarray) -> MoeCachePlan:
+        ids = np.ascontiguousarray(host_ids, dtype=np.int32).ravel()
+        p = MoeCachePlan()
+        check(lib().moe_cache_prefetch(self.h, layer, _hp(ids), ids.size, ctypes.byref(p)))
+        return p
+
+    def pin(self, layer, host_ids: np.ndarray) -> MoeCachePlan:
+        ids = np.ascontiguousarray(host_ids, dtype=np.int32).ravel()
+        p = MoeCachePlan()
+        check(lib().moe_cache_pin(self.h, layer, _hp(ids), ids.size, ctypes.byref(p)))
+        return p
+
     def fetch(self, plan: MoeCachePlan, dev_slot_of_expert, copy_stream, done_event=None):
+        """`dev_slot_of_expert`: device tensor (or, with a copy engine, a raw address or None)."""
         ev = ctypes.c_void_p(done_event.cuda_event) if done_event is not None else None
-        check(lib().moe_cache_fetch(self.h, ctypes.byref(plan), _dp(dev_slot_of_expert),
-                                    ctypes.c_void_p(copy_stream.cuda_stream), ev))
+        table = (ctypes.c_void_p(dev_slot_of_expert) if isinstance(dev_slot_of_expert, int)
+                 else _dp(dev_slot_of_expert))
+        stream = ctypes.c_void_p(copy_stream.cuda_stream) if copy_stream is not None else None
+        check(lib().moe_cache_fetch(self.h, ctypes.byref(plan), table, stream, ev))
 
     def stats(self) -> dict:
         s = MoeCacheStats()

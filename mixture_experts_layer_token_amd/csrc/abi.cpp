@@ -1,35 +1,12 @@
 // C-ABI entry points of libmoe.so: argument validation, then the launches.  No entry point
 // allocates device memory or synchronises the device.
-#include <stdarg.h>
-#include <stdio.h>
-
 #include "common.hpp"
 
 namespace moe {
 
-static thread_local char g_err[512] = "";
 static thread_local void* const* g_trace = nullptr;
 
 void* const* trace_events() { return g_trace; }
-
-void set_error(const char* fmt, ...) {
-  va_list ap;
-  va_start(ap, fmt);
-  vsnprintf(g_err, sizeof g_err, fmt, ap);
-  va_end(ap);
-}
-
-int fail(int code, const char* fmt, ...) {
-  va_list ap;
-  va_start(ap, fmt);
-  vsnprintf(g_err, sizeof g_err, fmt, ap);
-  va_end(ap);
-  return code;
-}
-
-int hip_fail(hipError_t e, const char* what) {
-  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
-}
 
 bool fmt_valid(int fmt) { return fmt >= MOE_W_F32 && fmt <= MOE_W_INT4G32; }
 bool dtype_valid(int dt) { return dt == MOE_F32 || dt == MOE_BF16; }
@@ -47,8 +24,6 @@ static int check_experts(const moe_experts* w, const char* fn) {
 }  // namespace moe
 
 using namespace moe;
-
-extern "C" const char* moe_last_error(void) { return g_err; }
 
 extern "C" int moe_ffn_trace_events(void* const* events) {
   g_trace = events;

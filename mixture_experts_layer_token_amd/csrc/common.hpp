@@ -23,7 +23,6 @@ typedef __attribute__((__vector_size__(2 * sizeof(unsigned)))) unsigned u32x2;
 constexpr int kWave = 64;
 
 // ------------------------------------------------------------ error state
-void set_error(const char* fmt, ...);
 int fail(int code, const char* fmt, ...);
 int hip_fail(hipError_t e, const char* what);
 

@@ -279,15 +279,23 @@ __global__ __launch_bounds__(NW * 64, FMT == MOE_W_BF16 ? 3 : 2) void ffn_stream
         if (row >= rows) continue;
         const size_t pr = (size_t)(p0 + row);
         if constexpr (GU) {
-          const float h = silu(v[0][r]) * v[1][r];
           unsigned short hb;
-          if constexpr (FMT == MOE_W_INT4G32)
+          if constexpr (FMT == MOE_W_INT4G32) {
+            const float h = args.xscale ? swiglu_scaled(v[0][r], v[1][r], token_scale(args, (int)pr))
+                                        : silu(v[0][r]) * v[1][r];
             hb = __builtin_bit_cast(unsigned short, (_Float16)h);
-          else
-            hb = f32_to_bf16_rne(h);
+          } else {
+            hb = f32_to_bf16_rne(silu(v[0][r]) * v[1][r]);
+          }
           ((unsigned short*)args.out)[pr * N + col] = hb;
         } else {
-          ((float*)args.out)[pr * N + col] = v[0][r];
+          float y = v[0][r];
+          if constexpr (FMT == MOE_W_INT4G32)
+            if (args.xscale) {
+              const float sc = token_scale(args, (int)pr);
+              y = y * sc * sc;
+            }
+          ((float*)args.out)[pr * N + col] = y;
         }
       }
     }
@@ -518,15 +526,23 @@ __global__ __launch_bounds__(NW * 64, 2) void ffn_stream_sa_kernel(FfnArgs args)
         if (row >= rows) continue;
         const size_t pr = (size_t)(p0 + row);
         if constexpr (GU) {
-          const float h = silu(acc[mt][p * 2][r]) * acc[mt][p * 2 + 1][r];
+          const float g = acc[mt][p * 2][r], u = acc[mt][p * 2 + 1][r];
           unsigned short hb;
-          if constexpr (FMT == MOE_W_INT4G32)
+          if constexpr (FMT == MOE_W_INT4G32) {
+            const float h = args.xscale ? swiglu_scaled(g, u, token_scale(args, (int)pr)) : silu(g) * u;
             hb = __builtin_bit_cast(unsigned short, (_Float16)h);
-          else
-            hb = f32_to_bf16_rne(h);
+          } else {
+            hb = f32_to_bf16_rne(silu(g) * u);
+          }
           ((unsigned short*)args.out)[pr * N + col] = hb;
         } else {
-          ((float*)args.out)[pr * N + col] = acc[mt][p][r];
+          float y = acc[mt][p][r];
+          if constexpr (FMT == MOE_W_INT4G32)
+            if (args.xscale) {
+              const float sc = token_scale(args, (int)pr);
+              y = y * sc * sc;
+            }
+          ((float*)args.out)[pr * N + col] = y;
         }
       }
     }
@@ -658,6 +674,56 @@ __global__ __launch_bounds__(256) void cast_act8_kernel(const void* __restrict__
   }
 }
 
+// INT4 experts: each token row of x -> fp16, divided by the power of two s_t that puts the row's
+// largest finite magnitude in [4, 8) (s_t = 1 for a row of zeros or with an infinite largest
+// magnitude); s_t goes to xscale[t] for the epilogues.  One wave per row, 8 elements per lane and
+// step (H a multiple of 8, rows 16-byte aligned); the second pass re-reads the row from cache.
+template <bool SRC_BF16>
+__device__ __forceinline__ void load8(const void* x, size_t i8, float (&v)[8]) {
+  if constexpr (SRC_BF16) {
+    const u32x4 w = ((const u32x4*)x)[i8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[2 * q] = __uint_as_float(w[q] << 16), v[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+  } else {
+    const f32x4 a = ((const f32x4*)x)[2 * i8], b = ((const f32x4*)x)[2 * i8 + 1];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = a[q], v[4 + q] = b[q];
+  }
+}
+template <bool SRC_BF16>
+__global__ __launch_bounds__(256) void cast_rows_scaled_kernel(const void* __restrict__ x, int T, int H,
+                                                               unsigned short* __restrict__ y,
+                                                               float* __restrict__ xscale) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;  // whole wave
+  const int n8 = H / 8;
+  const size_t base = (size_t)t * n8;
+  float m = 0.f;
+  for (int c = lane; c < n8; c += 64) {
+    float v[8];
+    load8<SRC_BF16>(x, base + c, v);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) m = fmaxf(m, fabsf(v[q]));  // (NaN elements ignored)
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  int e = 0;
+  if (m > 0.f && m <= 3.4028235e38f) e = min(max(ilogbf(m) - 2, -126), 127);
+  const float inv = ldexpf(1.f, -e);
+  if (lane == 0) xscale[t] = ldexpf(1.f, e);
+  for (int c = lane; c < n8; c += 64) {
+    float v[8];
+    load8<SRC_BF16>(x, base + c, v);
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      o[q] = (unsigned)__builtin_bit_cast(unsigned short, (_Float16)(v[2 * q] * inv)) |
+             ((unsigned)__builtin_bit_cast(unsigned short, (_Float16)(v[2 * q + 1] * inv)) << 16);
+    ((u32x4*)y)[base + c] = o;
+  }
+}
+
 // ------------------------------------------------------------------ dequant hook
 
 __global__ void dequant_kernel(const char* __restrict__ pkg, int H, int I, int fmt, float* __restrict__ out) {
@@ -717,7 +783,7 @@ __global__ void dequant_f32_kernel(const float* __restrict__ pkg, size_t n, floa
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-  size_t cast_off, cast_bytes, h_off, h_bytes, plan_off, plan_bytes, tplan_off, tplan_bytes, total;
+  size_t cast_off, cast_bytes, xs_off, xs_bytes, h_off, h_bytes, plan_off, plan_bytes, tplan_off, tplan_bytes, total;
 };
 
 WsLayout ws_layout(const moe_experts* w, int T, int k, int xdt) {
@@ -728,7 +794,10 @@ WsLayout ws_layout(const moe_experts* w, int T, int k, int xdt) {
   bool cast = !f32w && (w->fmt == MOE_W_INT4G32 || xdt == MOE_F32);
   L.cast_off = 0;
   L.cast_bytes = cast ? align256((size_t)T * w->H * 2) : 0;
-  L.h_off = L.cast_off + L.cast_bytes;
+  // INT4: the power-of-two scale of every token's fp16 activations
+  L.xs_off = L.cast_off + L.cast_bytes;
+  L.xs_bytes = w->fmt == MOE_W_INT4G32 ? align256((size_t)T * sizeof(float)) : 0;
+  L.h_off = L.xs_off + L.xs_bytes;
   L.h_bytes = align256(n * w->I * (f32w ? 4 : 2));
   // row-tile plan of the streaming kernels: at most n / 16 + min(n, E) tiles
   L.plan_off = L.h_off + L.h_bytes;
@@ -914,25 +983,32 @@ int launch_ffn(const moe_experts* w, const void* x, int xdt, int T, int k, const
   }
 
   const unsigned short* a = (const unsigned short*)x;
-  if (L.cast_bytes) {
+  const float* xscale = nullptr;
+  if (w->fmt == MOE_W_INT4G32) {
+    // fp16 operands: every token row scaled by its own power of two (any finite magnitude fits)
+    unsigned short* xc = (unsigned short*)(wsp + L.cast_off);
+    float* xs = (float*)(wsp + L.xs_off);
+    if ((uintptr_t)x % 16)
+      return fail(MOE_ERR_UNSUPPORTED, "moe_expert_ffn: INT4 experts need 16-byte aligned activations");
+    if (xdt == MOE_BF16)
+      hipLaunchKernelGGL((cast_rows_scaled_kernel<true>), dim3((T + 3) / 4), dim3(256), 0, s, x, T, H, xc, xs);
+    else
+      hipLaunchKernelGGL((cast_rows_scaled_kernel<false>), dim3((T + 3) / 4), dim3(256), 0, s, x, T, H, xc, xs);
+    a = xc;
+    xscale = xs;
+  } else if (L.cast_bytes) {
+    // fp32 activations for bf16 operands: rounded to bf16 (nearest-even)
     unsigned short* xc = (unsigned short*)(wsp + L.cast_off);
     size_t ne = (size_t)T * H;
     int blocks = (int)((ne + 255) / 256);
     if (blocks > 4096) blocks = 4096;
-    const bool f16 = w->fmt == MOE_W_INT4G32;
     if (ne % 8 == 0 && (uintptr_t)x % 16 == 0 && (uintptr_t)xc % 16 == 0) {
       const size_t n8 = ne / 8;
       const unsigned b8 = (unsigned)((n8 + 255) / 256 < 4096 ? (n8 + 255) / 256 : 4096);
-      if (f16 && xdt == MOE_BF16)
-        hipLaunchKernelGGL((cast_act8_kernel<true, true>), dim3(b8), dim3(256), 0, s, x, n8, xc);
-      else if (f16)
-        hipLaunchKernelGGL((cast_act8_kernel<true, false>), dim3(b8), dim3(256), 0, s, x, n8, xc);
-      else if (xdt == MOE_BF16)
+      if (xdt == MOE_BF16)
         hipLaunchKernelGGL((cast_act8_kernel<false, true>), dim3(b8), dim3(256), 0, s, x, n8, xc);
       else
         hipLaunchKernelGGL((cast_act8_kernel<false, false>), dim3(b8), dim3(256), 0, s, x, n8, xc);
-    } else if (f16) {
-      hipLaunchKernelGGL(cast_act_kernel<true>, dim3(blocks), dim3(256), 0, s, x, xdt, ne, xc);
     } else {
       hipLaunchKernelGGL(cast_act_kernel<false>, dim3(blocks), dim3(256), 0, s, x, xdt, ne, xc);
     }
@@ -970,10 +1046,12 @@ int launch_ffn(const moe_experts* w, const void* x, int xdt, int T, int k, const
   const size_t nz = n < (size_t)E ? n : (size_t)E;
   const int S = (int)((n + nz * (mr - 1)) / mr);
   gu.a = a;
+  gu.xscale = xscale;
   gu.out = h;
   gu.region_codes = g.gu_codes;
   gu.region_scales = g.gu_scales;
   dn.a = (const unsigned short*)h;
+  dn.xscale = xscale;
   dn.out = y_perm;
   dn.region_codes = g.d_codes;
   dn.region_scales = g.d_scales;

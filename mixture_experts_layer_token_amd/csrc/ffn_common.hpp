@@ -154,7 +154,18 @@ struct FfnArgs {
   // rows, its slot}, written by the plan kernel from the offsets and the slot table
   const int4* plan;
   int* tcount;  // [8] work counters of the persistent kernels, one per XCD range, zeroed by the plan kernel
+  // INT4 experts: the power of two each token's activations were divided by in the fp16 cast
+  // (xscale[t] = s_t), or null when they were not scaled
+  const float* xscale;
 };
+
+// INT4 experts multiply fp16 activations scaled per token: x' = x / s_t, with s_t a power of two
+// chosen so that the token's largest magnitude lies in [4, 8) (any finite activation then fits
+// binary16 with its bf16 precision).  Gate/up then yield g' = g / s and u' = u / s (exactly: scaling by a
+// power of two commutes with every rounding); the stored intermediate is h' = SiLU(g) u / s^2 =
+// g' u' / (1 + e^(-g' s)), and the down projection yields y' = y / s^2, multiplied back by s twice.
+__device__ __forceinline__ float token_scale(const FfnArgs& a, int p) { return a.xscale[a.perm_src[p] / a.k]; }
+__device__ __forceinline__ float swiglu_scaled(float g, float u, float s) { return g * u / (1.0f + __expf(-(g * s))); }
 
 
 constexpr int kXcds = 8;  // XCDs of an MI355X; workgroup i is dispatched to XCD i % 8

@@ -555,6 +555,14 @@ __device__ __forceinline__ void tile_body(const FfnArgs& args, TileCtx& c, unsig
   // every wave is done with the LDS buffers (the barrier)
   acc_hazard_guard();
   const int p0 = c.p0, rows = c.rows, col = c.col;
+  // INT4: the token scale of each of the lane's result rows (row mt*16 + lane % 16), looked up before
+  // the next item's loads are issued, so that waiting for it does not wait for them
+  float tsc[NMT];
+  const bool scaled = FMT == MOE_W_INT4G32 && args.xscale != nullptr;
+  if (scaled) {
+#pragma unroll
+    for (int mt = 0; mt < NMT; ++mt) tsc[mt] = token_scale(args, p0 + min(mt * 16 + (lane & 15), rows - 1));
+  }
   int nrows[TileCfg<FMT>::IPW_MAX];
   if (next >= 0) {
     tile_set_item<FMT>(args, c, next, ncol);
@@ -590,11 +598,11 @@ __device__ __forceinline__ void tile_body(const FfnArgs& args, TileCtx& c, unsig
         unsigned short hv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float h = silu(acc[mt][2 * p][r]) * acc[mt][2 * p + 1][r];
+          const float g = acc[mt][2 * p][r], u = acc[mt][2 * p + 1][r];
           if constexpr (FMT == MOE_W_INT4G32)
-            hv[r] = __builtin_bit_cast(unsigned short, (_Float16)h);
+            hv[r] = __builtin_bit_cast(unsigned short, (_Float16)(scaled ? swiglu_scaled(g, u, tsc[mt]) : silu(g) * u));
           else
-            hv[r] = f32_to_bf16_rne(h);
+            hv[r] = f32_to_bf16_rne(silu(g) * u);
         }
         const u32x2 pk = {(unsigned)hv[0] | ((unsigned)hv[1] << 16), (unsigned)hv[2] | ((unsigned)hv[3] << 16)};
         if (row_ok && hc < args.I)
@@ -604,8 +612,13 @@ __device__ __forceinline__ void tile_body(const FfnArgs& args, TileCtx& c, unsig
 #pragma unroll
       for (int j = 0; j < kWNS; ++j) {
         const int n = col * (kWNS * kTW * 16) + wave * (kWNS * 16) + j * 16 + q4;
+        f32x4 y = acc[mt][j];
+        if (scaled) {
+          const float s2 = tsc[mt];
+          y = f32x4{y[0] * s2 * s2, y[1] * s2 * s2, y[2] * s2 * s2, y[3] * s2 * s2};
+        }
         if (row_ok && n < c.N)
-          *(__attribute__((address_space(1))) f32x4*)((float*)args.out + (size_t)(p0 + m) * args.H + n) = acc[mt][j];
+          *(__attribute__((address_space(1))) f32x4*)((float*)args.out + (size_t)(p0 + m) * args.H + n) = y;
       }
     }
   }

@@ -9,14 +9,16 @@
 namespace moe {
 namespace {
 
-// binary16 bits of an exactly representable normal-range value, or -1
+// binary16 bits of an INT4 group scale the kernels can use, or -1: the scale must be a normal
+// binary16 number (bf16 has fewer significand bits, so only the range matters) and every product
+// q * s, q in [-8, 7], must stay finite in binary16 (|s| <= 65504 / 8)
 int exact_f16_bits(uint16_t bf16) {
   uint32_t u = (uint32_t)bf16 << 16;
   float f;
   memcpy(&f, &u, 4);
   if (f == 0.0f) return (bf16 & 0x8000) ? 0x8000 : 0;
   float a = fabsf(f);
-  if (!(a >= 0x1.0p-14f && a <= 65504.0f)) return -1;
+  if (!(a >= 0x1.0p-14f && a <= 65504.0f / 8.0f)) return -1;
   int e;
   float m = frexpf(a, &e);  // a = m * 2^e, m in [0.5, 1)
   // 11 significant bits available; bf16 has 8, so only the range matters
@@ -80,7 +82,9 @@ int pack_4bit_matrix(int fmt, const uint8_t* codes, const void* scales, int rows
           sdst[0] = ((const uint8_t*)scales)[(size_t)r * nks + ks];
         } else {
           int h = exact_f16_bits(((const uint16_t*)scales)[(size_t)r * nks + ks]);
-          if (h < 0) return fail(MOE_ERR_UNSUPPORTED, "moe_pack_expert: INT4 scale (row %d, group %d) not exact in binary16", r, ks);
+          if (h < 0)
+            return fail(MOE_ERR_UNSUPPORTED,
+                        "moe_pack_expert: INT4 scale (row %d, group %d) outside [2^-14, 65504/8] (binary16 operands)", r, ks);
           uint16_t hb = (uint16_t)h;
           memcpy(sdst, &hb, 2);
         }

@@ -7,16 +7,23 @@ demand and are addressed through stable logical slots).  Per layer and step:
 
   route (compute stream) -> ids to the host -> moe_cache_plan (host policy) ->
   moe_cache_fetch (one hipMemcpyAsync per miss + the slot table, copy stream,
-  event) -> permute -> grouped FFN over the experts that were already resident
-  (their slots only; the misses' entries are -1) -> the compute stream waits for
-  the event -> grouped FFN over the fetched experts -> combine.
+  event) -> [prefetch for the next layer: moe_cache_prefetch + its copies on the
+  copy stream] -> permute -> grouped FFN over the experts that were already
+  resident (their slots only; the misses' entries are -1) -> the compute stream
+  waits for the event -> grouped FFN over the fetched experts -> combine.
 
 The FFN of the hits runs while the misses stream in (with `overlap=False` the
-whole FFN waits for the copies).
+whole FFN waits for the copies).  Fetching ahead needs no trained predictor
+(the pages' related-abstracts list: an LRU cache, a static pin of popular
+experts, experts fetched before they are needed): while layer l computes, the
+next layer's experts of its previous step ("last") or its most used experts so
+far ("popular") are prefetched; a static pin keeps each layer's most used
+experts of a calibration window resident for the whole run.
 
 Layers run strictly in order.  A slot evicted by a plan is never in use: the
 host waits for the router of the layer being planned, and every earlier FFN
-precedes that router on the compute stream.
+precedes that router on the compute stream; a prefetch never evicts the
+experts of the layer just planned, whose FFN may still be running.
 """
 from __future__ import annotations
 
@@ -63,7 +70,7 @@ class OffloadedModel:
     """L MoE layers whose experts live in a pinned host bank, cached in an HBM slot pool."""
 
     def __init__(self, wl, max_T: int, capacity: int | None = None, device="cuda", fill=True, policy="lru",
-                 decay_period=0, overlap=True):
+                 decay_period=0, overlap=True, prefetch=None):
         from synth import workloads as W
 
         self.wl = wl
@@ -101,27 +108,62 @@ class OffloadedModel:
         self.done = torch.cuda.Event()
         self.done.record(self.copy_stream)  # creates the HIP event the library records into
         self.routed = torch.cuda.Event()
-        self.copy_t0 = torch.cuda.Event(enable_timing=True)
-        self.copy_t1 = torch.cuda.Event(enable_timing=True)
-        self.copy_ms = 0.0
-        self.plans = []
-        self.groups = []
+        self.prefetch = prefetch
+        self._ev_pool = []  # timing events of the copy stream, reused from run to run
         self.filled = {}
+        self._reset_records()
 
-    def reset_cache(self, policy=None, decay_period=None, overlap=None):
-        """Empty the HBM cache (a new planner, optionally with another policy) and the run records."""
+    def _reset_records(self):
+        self.plans, self.groups, self.events, self._copy_windows = [], [], [], []
+        self.prev_ids = [None] * self.L  # distinct experts of each layer's previous step
+        self.use_counts = np.zeros((self.L, self.E), np.int64)  # demand uses of each expert so far
+
+    def _timing_event(self, i):
+        while len(self._ev_pool) <= i:
+            self._ev_pool.append(torch.cuda.Event(enable_timing=True))
+        return self._ev_pool[i]
+
+    def copy_seconds(self) -> float:
+        """Busy time of the copy stream over the run: the windows from before each layer's first copy
+        to after its last (demand, prefetch), read once the run is over."""
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in self._copy_windows) / 1e3
+
+    def reset_cache(self, policy=None, decay_period=None, overlap=None, prefetch="keep", pins=None):
+        """Empty the HBM cache (a new planner, optionally with another policy, prefetch heuristic and
+        static pin) and the run records.  `pins`: {layer: expert ids} pinned (and fetched) at once."""
         if overlap is not None:
             self.overlap = overlap
         if policy is not None:
             self.policy = policy
         if decay_period is not None:
             self.decay_period = decay_period
+        if prefetch != "keep":
+            self.prefetch = prefetch
         self.cache.close()
         self.cache = api.ExpertCache(self.bank, self.pkg_bytes, self.L, self.E, self.pool, self.stride,
                                      self.capacity, self.policy, self.decay_period)
         for t in self.slot_tables:
             t.fill_(-1)
-        self.plans, self.groups, self.copy_ms = [], [], 0.0
+        self._reset_records()
+        for l, ids in sorted((pins or {}).items()):
+            ids = np.asarray(sorted(set(int(e) for e in ids)), dtype=np.int32)
+            plan = self.cache.pin(l, ids)
+            self.events.append(("pin", l, ids))
+            self.cache.fetch(plan, None, self.copy_stream)
+        self.copy_stream.synchronize()
+
+    def prefetch_candidates(self, l: int):
+        """Experts of layer l to fetch ahead of its router, by the current heuristic."""
+        prev = self.prev_ids[l]
+        if self.prefetch is None or prev is None:
+            return None
+        if self.prefetch == "last":
+            return prev
+        if self.prefetch == "popular":  # as many as the layer touched last time, most used first
+            order = np.argsort(-self.use_counts[l], kind="stable")
+            return np.sort(order[:len(prev)]).astype(np.int32)
+        raise ValueError("prefetch heuristic %r" % (self.prefetch,))
 
     def fill(self, l: int, experts):
         """Generate and pack experts of layer l into the host bank."""
@@ -165,6 +207,10 @@ class OffloadedModel:
         plan = self.cache.plan(l, hid)
         self.plans.append((step, l, plan.n_ids, plan.n_hits, plan.n_misses))
         self.groups.append(set((l * self.E + hid.ravel()).tolist()))
+        distinct = np.unique(hid).astype(np.int32)
+        self.events.append(("demand", l, distinct))
+        self.prev_ids[l] = distinct
+        self.use_counts[l][distinct] += 1
         split = self.overlap and plan.n_hits > 0 and plan.n_misses > 0
         if split:
             table = np.ctypeslib.as_array(plan.slot_of_expert)[:self.E]
@@ -177,10 +223,22 @@ class OffloadedModel:
             for dev, host in zip(self.pass_dev[l], self.pass_host[l]):
                 dev.copy_(host, non_blocking=True)
         if time_copies:
-            self.copy_t0.record(self.copy_stream)
+            t0 = self._timing_event(2 * len(self._copy_windows))
+            t0.record(self.copy_stream)
         self.cache.fetch(plan, self.slot_tables[l], self.copy_stream, self.done)
+        # fetch ahead for the next layer: its copies queue behind this layer's on the copy stream (the
+        # next layer's own fetch event covers them); this layer's FFN waits only for its own
+        nl = (l + 1) % self.L
+        cand = self.prefetch_candidates(nl)
+        if cand is not None and len(cand):
+            pf = self.cache.prefetch(nl, cand)
+            self.events.append(("prefetch", nl, np.asarray(cand, np.int32)))
+            if pf.n_misses:
+                self.cache.fetch(pf, None, self.copy_stream)
         if time_copies:
-            self.copy_t1.record(self.copy_stream)
+            t1 = self._timing_event(2 * len(self._copy_windows) + 1)
+            t1.record(self.copy_stream)
+            self._copy_windows.append((t0, t1))
         if split:
             api.moe_permute(ids, self.E, lay.counts, lay.offsets, lay.perm_src[:T * k], lay.inv_perm[:T * k], lay.pws)
             api.moe_expert_ffn(self.pass_desc[l][0], x, k, lay.offsets, lay.perm_src, lay.y_perm, lay.ws)
@@ -191,9 +249,6 @@ class OffloadedModel:
             api.moe_permute(ids, self.E, lay.counts, lay.offsets, lay.perm_src[:T * k], lay.inv_perm[:T * k], lay.pws)
             api.moe_expert_ffn(lay.desc, x, k, lay.offsets, lay.perm_src, lay.y_perm, lay.ws)
         api.moe_combine(lay.y_perm, w, lay.inv_perm, k, None, out)
-        if time_copies:
-            self.copy_t1.synchronize()
-            self.copy_ms += self.copy_t0.elapsed_time(self.copy_t1)
         self.last_plan = plan
         return out
 

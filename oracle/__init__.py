@@ -61,6 +61,8 @@ def lib():
         L.oracle_lfu_decay.restype = i32
         L.oracle_belady.argtypes = [i64, i64, vp, vp, vp, vp]
         L.oracle_belady.restype = i32
+        L.oracle_cache_sim.argtypes = [i64, i32, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp]
+        L.oracle_cache_sim.restype = i32
         for f in ("oracle_decode", "oracle_decode_act", "oracle_router_logits", "oracle_topk_gates",
                   "oracle_permute", "oracle_ffn"):
             getattr(L, f).restype = None
@@ -200,6 +202,28 @@ def lfu_decay(capacity: int, period: int, groups):
         raise ValueError("a group holds more distinct keys than the capacity")
     vo = np.concatenate([[0], np.cumsum(nv)])
     return hits, misses, [victims[vo[g]:vo[g + 1]].copy() for g in range(G)]
+
+
+CACHE_KINDS = {"demand": 0, "prefetch": 1, "pin": 2}
+
+
+def cache_sim(capacity: int, policy: str, period: int, groups, kinds):
+    """The cache with prefetch and pin groups (kinds: 'demand' | 'prefetch' | 'pin' per group;
+    policy 'lru' | 'lfu_decay') -> (hits[g], misses[g], victims per group, prefetch_hits)."""
+    off, keys = _groups(groups)
+    G = len(groups)
+    k = np.array([CACHE_KINDS[x] for x in kinds], dtype=np.int32)
+    hits = np.zeros(G, np.int64)
+    misses = np.zeros(G, np.int64)
+    victims = np.zeros(max(len(keys), 1), np.int64)
+    nv = np.zeros(G, np.int64)
+    ph = np.zeros(1, np.int64)
+    rc = lib().oracle_cache_sim(capacity, {"lru": 0, "lfu_decay": 1}[policy], period, G, _p(off), _p(keys), _p(k),
+                                _p(hits), _p(misses), _p(victims), _p(nv), _p(ph))
+    if rc != 0:
+        raise ValueError("a demand or pin group does not fit the cache")
+    vo = np.concatenate([[0], np.cumsum(nv)])
+    return hits, misses, [victims[vo[g]:vo[g + 1]].copy() for g in range(G)], int(ph[0])
 
 
 def belady(capacity: int, groups):

@@ -504,3 +504,106 @@ int oracle_belady(int64_t capacity, int64_t n_groups, const int64_t* group_off, 
   free(pos);
   return (int)rc;
 }
+
+/*
+ * The cache with fetching ahead and pinning (the planner's moe_cache_prefetch and
+ * moe_cache_pin), groups of three kinds over the same keys:
+ *  kind 0, a demand lookup: as oracle_lru (policy 0) or oracle_lfu_decay (policy 1, counts halved
+ *    every `period` demand groups), counting demand groups only for ticks and decay, and pinned
+ *    keys are never victims.  A group whose absent keys outnumber the free slots plus the
+ *    evictable keys outside the group is an error.
+ *  kind 1, a prefetch: the group's absent keys, ascending, each take a free slot or evict the
+ *    policy's first victim among the keys that are neither pinned, nor in this group, nor in the
+ *    latest demand group; when none is left the rest of the group is skipped.  A key brought in
+ *    this way has last use -1 (its count unchanged) until a demand group uses it.
+ *  kind 2, a pin: as a prefetch, but every key of the group is pinned from then on, and a group
+ *    that does not fit is an error.
+ * Outputs per group: hits (keys already resident), misses (keys fetched), victims as oracle_lru;
+ * *prefetch_hits counts demand hits on keys a prefetch brought in and no demand group used since.
+ * Returns -1 on an error (the group that does not fit), else 0.
+ */
+int oracle_cache_sim(int64_t capacity, int policy, int64_t period, int64_t n_groups, const int64_t* group_off,
+                     const int64_t* keys, const int32_t* kinds, int64_t* hits, int64_t* misses, int64_t* victims,
+                     int64_t* n_victims, int64_t* prefetch_hits) {
+  int64_t max_key = 0;
+  for (int64_t i = 0; i < group_off[n_groups]; ++i)
+    if (keys[i] > max_key) max_key = keys[i];
+  const int64_t nk = max_key + 1;
+  char* res = (char*)calloc((size_t)nk, 1);
+  char* pin = (char*)calloc((size_t)nk, 1);
+  char* fresh = (char*)calloc((size_t)nk, 1);
+  int64_t* last = (int64_t*)malloc(sizeof(int64_t) * (size_t)nk);
+  int64_t* count = (int64_t*)malloc(sizeof(int64_t) * (size_t)nk);
+  int64_t* mark = (int64_t*)malloc(sizeof(int64_t) * (size_t)nk);    /* group index of the latest group naming the key */
+  int64_t* dmark = (int64_t*)malloc(sizeof(int64_t) * (size_t)nk);   /* demand tick + 1 of the latest demand group naming it */
+  for (int64_t i = 0; i < nk; ++i) last[i] = -1, count[i] = 0, mark[i] = -1, dmark[i] = 0;
+  int64_t resident = 0, nv = 0, tick = 0, cur_dmark = 0, rc = 0;
+  *prefetch_hits = 0;
+  for (int64_t g = 0; g < n_groups && rc == 0; ++g) {
+    for (int64_t i = group_off[g]; i < group_off[g + 1]; ++i) mark[keys[i]] = g;
+    const int kind = kinds[g];
+    hits[g] = misses[g] = n_victims[g] = 0;
+    /* may key c be evicted by group g? */
+#define EVICTABLE(c) (res[c] && !pin[c] && mark[c] != g && (kind == 0 || dmark[c] != cur_dmark || cur_dmark == 0))
+    if (kind != 1) { /* demand and pin groups must fit */
+      int64_t absent = 0, evictable = 0;
+      for (int64_t c = 0; c < nk; ++c) {
+        if (mark[c] == g && !res[c]) absent++;
+        if (EVICTABLE(c)) evictable++;
+      }
+      if (absent > capacity - resident + evictable) {
+        rc = -1;
+        break;
+      }
+    }
+    if (kind == 0 && policy == 1) {
+      if (period > 0 && tick > 0 && tick % period == 0)
+        for (int64_t c = 0; c < nk; ++c) count[c] /= 2;
+      for (int64_t c = 0; c < nk; ++c)
+        if (mark[c] == g) count[c] += 1024;
+    }
+    for (int64_t key = 0; key < nk; ++key) {
+      if (mark[key] != g) continue;
+      if (res[key]) {
+        hits[g]++;
+        if (kind == 0 && fresh[key]) (*prefetch_hits)++, fresh[key] = 0;
+      } else {
+        if (resident == capacity) {
+          int64_t best = -1;
+          for (int64_t c = 0; c < nk; ++c) {
+            if (!EVICTABLE(c)) continue;
+            const int64_t pc = policy == 1 ? count[c] : 0, pb = best < 0 ? 0 : (policy == 1 ? count[best] : 0);
+            if (best < 0 || pc < pb || (pc == pb && last[c] < last[best]) || (pc == pb && last[c] == last[best] && c < best))
+              best = c;
+          }
+          if (best < 0) break; /* only a prefetch gets here: skip the rest of the group */
+          res[best] = 0, fresh[best] = 0;
+          resident--;
+          victims[nv++] = best;
+          n_victims[g]++;
+        }
+        res[key] = 1;
+        resident++;
+        misses[g]++;
+        if (kind == 1) last[key] = -1, fresh[key] = 1;
+      }
+      if (kind == 0) last[key] = tick, fresh[key] = 0;
+      if (kind == 2) pin[key] = 1, fresh[key] = 0;
+    }
+#undef EVICTABLE
+    if (kind == 0) {
+      for (int64_t c = 0; c < nk; ++c)
+        if (mark[c] == g) dmark[c] = tick + 1;
+      cur_dmark = tick + 1;
+      tick++;
+    }
+  }
+  free(res);
+  free(pin);
+  free(fresh);
+  free(last);
+  free(count);
+  free(mark);
+  free(dmark);
+  return (int)rc;
+}

@@ -224,3 +224,135 @@ def test_cache_create_rejects_unpinned_bank():
     d.slot_stride, d.capacity = 1024, 4
     h = ctypes.c_void_p()
     assert L.moe_cache_create(ctypes.byref(d), ctypes.byref(h)) == -5
+
+
+def test_pack_int4_scale_domain():
+    """INT4 scales must be normal binary16 values whose products with every code stay finite:
+    |s| in [2^-14, 65504 / 8] (or zero); the largest bf16 below the bound and 2^-14 itself pack."""
+    H = I = 32
+    codes = np.zeros((I, H // 2), np.uint8)
+    ok = np.full((I, 1), 0x3F80, np.uint16)  # 1.0
+
+    def pack_with(bits):
+        s = ok.copy()
+        s[5, 0] = bits
+        return moe.moe_pack_expert(H, I, "int4g32", {"w": [codes, codes, codes], "s": [ok, s, ok]})
+
+    for bits in (0x45FF, 0xC5FF, 0x3880, 0x0000, 0x8000):  # 8160, -8160, 2^-14, +0, -0
+        pack_with(bits)
+    for bits in (0x4600, 0x4700, 0x3800, 0x0001, 0x7FC0, 0x7F80):  # 8192, 32768, 2^-15, subnormal, NaN, inf
+        with pytest.raises(moe.MoeError) as e:
+            pack_with(bits)
+        assert e.value.code == UNSUPPORTED
+
+
+def _run_planner(c, groups, kinds, L_, E):
+    """Feed (layer-major keys) groups of the given kinds to the planner; per group (hits, misses, victims)."""
+    out, prev = [], set()
+    for keys, kind in zip(groups, kinds):
+        layer = keys[0] // E
+        ids = np.array([k - layer * E for k in keys], dtype=np.int32)
+        fn = {"demand": c.plan, "prefetch": c.prefetch, "pin": c.pin}[kind]
+        pl = fn(layer, ids)
+        now = set()
+        for l in range(L_):
+            # every layer's table: the resident set after this call
+            p2 = c.prefetch(l, np.zeros(0, np.int32))
+            now |= {l * E + e for e in range(E) if p2.slot_of_expert[e] >= 0}
+        out.append((pl.n_hits, pl.n_misses, sorted(prev - now)))
+        prev = now
+    return out
+
+
+@pytest.mark.parametrize("policy,period", [("lru", 0), ("lfu_decay", 6)])
+def test_planner_prefetch_and_pin_match_oracle(policy, period):
+    """The planner's demand lookups, prefetches and pins against the oracle's simulator: hits,
+    misses and victims of every group, and the prefetch statistics."""
+    L_, E, cap = 2, 24, 10
+    rng = np.random.default_rng(13)
+    groups, kinds, n_pins = [], [], 0
+    for g in range(300):
+        layer = g % L_
+        r = rng.random()
+        if r < 0.03 and n_pins < 3:
+            n_pins += 1
+            kinds.append("pin")
+            groups.append([layer * E + int(rng.integers(0, E))])
+        elif r < 0.4:
+            kinds.append("prefetch")
+            groups.append((layer * E + rng.integers(0, E, size=3)).tolist())
+        else:
+            kinds.append("demand")
+            groups.append((layer * E + rng.integers(0, E, size=4)).tolist())
+    c = _planner(cap, L_, E, policy, period)
+    got = _run_planner(c, groups, kinds, L_, E)
+    h, m, v, ph = oracle.cache_sim(cap, policy, period, groups, kinds)
+    assert [g[0] for g in got] == list(h)
+    assert [g[1] for g in got] == list(m)
+    assert [g[2] for g in got] == [sorted(a.tolist()) for a in v]
+    st = c.stats()
+    dem = [i for i, k in enumerate(kinds) if k == "demand"]
+    assert st["hits"] == sum(h[i] for i in dem) and st["misses"] == sum(m[i] for i in dem)
+    assert st["prefetch_fetches"] == sum(m[i] for i, k in enumerate(kinds) if k == "prefetch")
+    assert st["prefetch_hits"] == ph
+    assert st["bytes_fetched"] == m.sum() * (1 << 20)
+
+
+def test_planner_hand_worked_prefetch_and_pin():
+    from test_oracle_pins import (CACHE_PIN_GROUPS, CACHE_PIN_HITS, CACHE_PIN_KINDS, CACHE_PIN_VICTIMS,
+                                  CACHE_PREFETCH_GROUPS, CACHE_PREFETCH_HITS, CACHE_PREFETCH_KINDS,
+                                  CACHE_PREFETCH_MISSES, CACHE_PREFETCH_VICTIMS)
+
+    got = _run_planner(_planner(3, 1, 8), CACHE_PREFETCH_GROUPS, CACHE_PREFETCH_KINDS, 1, 8)
+    assert [g[0] for g in got] == CACHE_PREFETCH_HITS and [g[1] for g in got] == CACHE_PREFETCH_MISSES
+    assert [g[2] for g in got] == CACHE_PREFETCH_VICTIMS
+    got = _run_planner(_planner(3, 1, 8), CACHE_PIN_GROUPS, CACHE_PIN_KINDS, 1, 8)
+    assert [g[0] for g in got] == CACHE_PIN_HITS and [g[2] for g in got] == CACHE_PIN_VICTIMS
+    c = _planner(3, 1, 9)
+    c.pin(0, np.array([7, 8]))
+    with pytest.raises(moe.MoeError) as e:
+        c.plan(0, np.array([0, 1]))
+    assert e.value.code == CAPACITY
+
+
+class FakeCopyEngine:
+    """Host memcpy in place of the HIP copy engine; copy number `fail_at` (0-based) fails."""
+
+    def __init__(self, fail_at=None):
+        self.n, self.fail_at, self.log = 0, fail_at, []
+
+    def __call__(self, dst, src, nbytes, stream):
+        i = self.n
+        self.n += 1
+        if self.fail_at is not None and i == self.fail_at:
+            return 1
+        ctypes.memmove(dst, src, nbytes)
+        self.log.append((dst, src, nbytes))
+        return 0
+
+
+def test_fetch_failure_rolls_back_and_refetches():
+    """A copy that fails in the middle of a fetch: the experts whose copies did not run stop being
+    resident, the next lookup misses them and fetches them again; what was copied stays valid."""
+    L_, E, pkg, cap = 1, 8, 512, 4
+    bank = np.random.default_rng(1).integers(0, 256, size=(E, pkg), dtype=np.uint8)
+    pool = np.zeros((cap, pkg), np.uint8)
+    table = np.full(E, -7, np.int32)
+    eng = FakeCopyEngine(fail_at=1)
+    c = ExpertCache(None, pkg, L_, E, None, pkg, cap, copy=eng, bank_ptr=bank.ctypes.data,
+                    pool_ptr=pool.ctypes.data)
+    p = c.plan(0, np.array([2, 5, 6]))
+    assert p.n_misses == 3
+    with pytest.raises(moe.MoeError) as e:
+        c.fetch(p, table.ctypes.data, None)
+    assert e.value.code == -3 and "not resident" in str(e.value)
+    assert (table == -7).all()  # the slot table was not copied
+    st = c.stats()
+    assert st["bytes_fetched"] == pkg  # only the first package was copied
+    eng.fail_at = None
+    p = c.plan(0, np.array([2, 5, 6]))
+    assert (p.n_hits, p.n_misses) == (1, 2) and sorted(p.miss_ids[i] for i in range(2)) == [5, 6]
+    c.fetch(p, table.ctypes.data, None)
+    for e_ in (2, 5, 6):
+        assert table[e_] >= 0 and np.array_equal(pool[table[e_]], bank[e_])
+    assert len(set(table[[2, 5, 6]].tolist())) == 3

@@ -23,14 +23,17 @@ def _gpu():
     moe.lib()
 
 
-def run_and_check(wl, T, steps, check_steps, fill_all=True, capacity=None, policy="lru", period=0, overlap=True):
+def run_and_check(wl, T, steps, check_steps, fill_all=True, capacity=None, policy="lru", period=0, overlap=True,
+                  prefetch=None, pins=None):
     xs = {}
     for s in range(steps):
         for l in range(wl.layers):
             x, _ = oracle.rank_gap_inputs(wl, T, layer=l, step=s)
             xs[(l, s)] = x
     model = OffloadedModel(wl, T, capacity=capacity, fill=fill_all, policy=policy, decay_period=period,
-                           overlap=overlap)
+                           overlap=overlap, prefetch=prefetch)
+    if pins:
+        model.reset_cache(pins=pins)
     if not fill_all:  # only the experts some step routes to (the others are never fetched)
         touched = {l: set() for l in range(wl.layers)}
         for (l, s), x in xs.items():
@@ -56,19 +59,26 @@ def run_and_check(wl, T, steps, check_steps, fill_all=True, capacity=None, polic
                 got_bytes = model.pool[torch.tensor(slots, device="cuda")][:, :model.pkg_bytes].cpu().numpy()
                 for i, e in enumerate(mine):
                     assert np.array_equal(got_bytes[i], model.package(l, e)), (l, s, e)
-    # cache decisions: identical to the oracle's policy
-    if policy == "lru":
-        h, m, v = oracle.lru(model.capacity, groups)
-    else:
-        h, m, v = oracle.lfu_decay(model.capacity, period, groups)
-    got = [(p[3], p[4]) for p in model.plans]
-    assert got == list(zip(h.tolist(), m.tolist()))
+    # cache decisions: identical to the oracle's policy, over every demand lookup, prefetch and pin
+    ev_groups = [(l * wl.E + np.asarray(ids)).tolist() for _, l, ids in model.events]
+    kinds = [kind for kind, _, _ in model.events]
+    h, m, v, ph = oracle.cache_sim(model.capacity, policy, period, ev_groups, kinds)
+    dem = [i for i, kd in enumerate(kinds) if kd == "demand"]
+    assert [(p[3], p[4]) for p in model.plans] == [(int(h[i]), int(m[i])) for i in dem]
+    if prefetch is None and not pins:  # (then also the plain policy simulation)
+        h0, m0, _ = (oracle.lru(model.capacity, groups) if policy == "lru"
+                     else oracle.lfu_decay(model.capacity, period, groups))
+        assert [(p[3], p[4]) for p in model.plans] == list(zip(h0.tolist(), m0.tolist()))
     st = model.cache.stats()
-    assert st["hits"] == h.sum() and st["misses"] == m.sum()
+    assert st["hits"] == sum(h[i] for i in dem) and st["misses"] == sum(m[i] for i in dem)
     assert st["bytes_fetched"] == m.sum() * model.pkg_bytes
+    assert st["prefetch_hits"] == ph
     hb, _ = oracle.belady(model.capacity, groups)
-    assert hb.sum() >= h.sum()
-    say("  %s hits %d / %d lookups (belady %d)" % (policy, h.sum(), h.sum() + m.sum(), hb.sum()))
+    hd = sum(h[i] for i in dem)
+    if prefetch is None and not pins:
+        assert hb.sum() >= hd
+    say("  %s prefetch %s pins %s: hits %d / %d lookups, prefetched %d, prefetch hits %d (belady %d)"
+        % (policy, prefetch, bool(pins), hd, hd + sum(m[i] for i in dem), st["prefetch_fetches"], ph, hb.sum()))
     # outputs of the checked steps
     for (l, s), got_out in outs.items():
         experts = [None] * wl.E
@@ -99,6 +109,25 @@ def test_offload_small_frequency_policy():
     run_and_check(wl, 5, wl.steps, {0, 11, 23}, policy="lfu_decay", period=6)
 
 
+@pytest.mark.parametrize("prefetch,policy", [("last", "lru"), ("popular", "lfu_decay")])
+def test_offload_small_prefetch(prefetch, policy):
+    """Fetching the next layer's likely experts while a layer computes: every step checked (outputs,
+    slot bytes), every lookup, prefetch and eviction against the oracle's simulation."""
+    wl = W.Workload(name="offload-pf", H=224, E=16, k=4, I=352, wfmt="int4g32", xdt="bf16", Ts=(5,), seed=609,
+                    zipf_s=1.2, layers=3, steps=24, rerank_every=8, cache_frac=0.4)
+    say("offload small, prefetch", prefetch, policy)
+    run_and_check(wl, 5, wl.steps, set(range(wl.steps)), policy=policy, period=6 if policy != "lru" else 0,
+                  prefetch=prefetch)
+
+
+def test_offload_small_static_pin():
+    """Two experts of every layer pinned for the whole run, LRU over the other slots."""
+    wl = W.Workload(name="offload-pin", H=224, E=16, k=4, I=352, wfmt="int4g32", xdt="bf16", Ts=(5,), seed=610,
+                    zipf_s=1.2, layers=3, steps=20, rerank_every=8, cache_frac=0.4)
+    say("offload small, static pin")
+    run_and_check(wl, 5, wl.steps, {0, 9, 19}, pins={l: [l, l + 5] for l in range(wl.layers)})
+
+
 def test_offload_small_tight_capacity():
     wl = W.Workload(name="offload-tight", H=96, E=32, k=8, I=160, wfmt="mxfp4", xdt="bf16", Ts=(3,), seed=607,
                     zipf_s=0.8, layers=2, steps=16, rerank_every=4, cache_frac=0.25)
@@ -106,12 +135,12 @@ def test_offload_small_tight_capacity():
     run_and_check(wl, 3, wl.steps, {0, 7, 15}, capacity=24)
 
 
-@pytest.mark.parametrize("T", [1, 16])
-def test_offload_glm_full_size_first_steps(T):
+@pytest.mark.parametrize("T,prefetch", [(1, None), (16, None), (16, "last")])
+def test_offload_glm_full_size_first_steps(T, prefetch):
     """GLM-shaped layers at full size (bank filled with every expert the first steps route to)."""
     wl = W.WORKLOADS["glm"].with_(steps=3)
-    say("offload glm full size T", T)
-    run_and_check(wl, T, 3, {0, 2}, fill_all=False)
+    say("offload glm full size T", T, "prefetch", prefetch)
+    run_and_check(wl, T, 3, {0, 2}, fill_all=False, prefetch=prefetch)
 
 
 @pytest.mark.parametrize("mode", ["decode", "prefill"])

@@ -379,12 +379,37 @@ def test_shared_expert_small():
     assert_output_close(to_f64(out), ref, "bf16", wl.name)
 
 
+@pytest.mark.parametrize("sigma,xdt", [(1e-3, "bf16"), (100.0, "bf16"), (3e4, "bf16"), (3e4, "f32")])
+@pytest.mark.parametrize("mode", ["auto", "decode", "prefill"])
+def test_int4_activation_magnitudes(sigma, xdt, mode):
+    """INT4 experts run on binary16 operands.  Kimi-wide rows (H = 7168) with N(0, sigma)
+    activations: at sigma = 3e4 the activations themselves exceed binary16's range, at sigma = 100
+    the intermediate SiLU(g)*u would (|g| ~ 170), at sigma = 1e-3 it would fall into binary16's
+    subnormals.  Every token's row is scaled by its own power of two, so all stay within tolerance.
+    (The router weights are scaled by 0.02 / sigma, so that logits keep unit scale and a rank gap.)"""
+    wl = W.Workload(name="int4-mag-%g-%s" % (sigma, xdt), H=7168, E=64, k=4, I=512, wfmt="int4g32", xdt=xdt,
+                    Ts=(48,), seed=919, x_sigma=sigma, wg_sigma=0.02 / sigma)
+    T = 48
+    say("int4 activation magnitude", wl.name, mode)
+    x, _ = oracle.rank_gap_inputs(wl, T)
+    layer = build_layer(wl, T)
+    out = layer.forward(to_device_act(x, xdt), mode=mode)
+    torch.cuda.synchronize()
+    ref, ids_ref, _ = oracle_reference(wl, x, np.arange(T))
+    assert np.array_equal(layer.topk_ids[:T].cpu().numpy(), ids_ref)
+    got = to_f64(out)
+    assert np.isfinite(got).all()
+    assert_output_close(got, ref, "bf16", wl.name + " " + mode)
+
+
 # ------------------------------------------------------------------ full-size configurations (sampled tokens)
 
 FULL = [("mixtral", 1, "auto"), ("mixtral", 8, "auto"), ("mixtral", 32, "auto"), ("mixtral", 64, "auto"),
         ("mixtral", 64, "prefill"), ("gptoss", 1, "auto"), ("gptoss", 64, "auto"), ("gptoss", 512, "auto"),
         ("gptoss", 512, "prefill"), ("gptoss", 1024, "auto"),  # 1024: hot experts on the tile kernel
-        ("mixtral", 128, "auto")]  # bf16 from 28 rows per expert on average: the tile kernel alone
+        ("mixtral", 128, "auto"),  # bf16 from 28 rows per expert on average: the tile kernel alone
+        # speculative verification blocks of depth + 1 = 2..4 positions (GLM-shaped INT4 layer, resident)
+        ("glm", 2, "auto"), ("glm", 3, "decode"), ("glm", 4, "auto")]
 
 
 @pytest.mark.parametrize("name,T,mode", FULL)

@@ -402,6 +402,94 @@ def test_lfu_decay_hand_worked_order_of_halving():
     assert [list(a) for a in v] == LFU_HAND_VICTIMS
 
 
+@pytest.mark.parametrize("policy,period", [("lru", 0), ("lfu_decay", 0), ("lfu_decay", 5)])
+def test_cache_sim_demand_only_equals_the_plain_policies(policy, period):
+    """With demand groups only, the simulator with prefetch and pin kinds is the plain policy."""
+    groups = [list(g) for g in _zipf_groups(300, 8, 64, 21)]
+    h, m, v, ph = oracle.cache_sim(16, policy, period, groups, ["demand"] * len(groups))
+    h2, m2, v2 = oracle.lru(16, groups) if policy == "lru" else oracle.lfu_decay(16, period, groups)
+    assert list(h) == list(h2) and list(m) == list(m2) and [list(a) for a in v] == [list(a) for a in v2]
+    assert ph == 0
+
+
+# Hand-worked prefetch sequence, capacity 3, LRU (ticks count demand groups only):
+#   g0 demand  [0 1]   misses 0, 1 (tick 0)
+#   g1 prefetch [2 3]  2 takes the free slot (last use -1); 3 would need a victim outside {2, 3} and
+#                      the latest demand group {0, 1}: none, so it is skipped
+#   g2 demand  [2 4]   2 hits (a prefetch hit); 4 evicts the smallest (last, key) outside {2, 4}:
+#                      0 (last 0) before 1 (last 0, larger key)          (tick 1)
+#   g3 prefetch [5]    victim outside {5} and {2, 4}: 1; 5 enters with last use -1
+#   g4 demand  [0]     victim among 2 (last 1), 4 (last 1), 5 (last -1): 5, the unused prefetch
+CACHE_PREFETCH_GROUPS = [[0, 1], [2, 3], [2, 4], [5], [0]]
+CACHE_PREFETCH_KINDS = ["demand", "prefetch", "demand", "prefetch", "demand"]
+CACHE_PREFETCH_HITS = [0, 0, 1, 0, 0]
+CACHE_PREFETCH_MISSES = [2, 1, 1, 1, 1]
+CACHE_PREFETCH_VICTIMS = [[], [], [0], [1], [5]]
+
+# Hand-worked pin sequence, capacity 3, LRU:
+#   g0 pin     [7]     7 fetched and pinned
+#   g1 demand  [0 1]   misses (tick 0)
+#   g2 demand  [2]     victim among 0, 1 (7 is pinned): 0                   (tick 1)
+#   g3 demand  [7 3]   7 hits; 3 evicts 1 (last 0) before 2 (last 1)        (tick 2)
+#   g4 demand  [4 5]   two misses; 7 is pinned, so 2 (last 1) then 3 (last 2) go         (tick 3)
+CACHE_PIN_GROUPS = [[7], [0, 1], [2], [7, 3], [4, 5]]
+CACHE_PIN_KINDS = ["pin", "demand", "demand", "demand", "demand"]
+CACHE_PIN_HITS = [0, 0, 0, 1, 0]
+CACHE_PIN_VICTIMS = [[], [], [0], [1], [2, 3]]
+
+
+def test_cache_sim_hand_worked_prefetch():
+    h, m, v, ph = oracle.cache_sim(3, "lru", 0, CACHE_PREFETCH_GROUPS, CACHE_PREFETCH_KINDS)
+    assert list(h) == CACHE_PREFETCH_HITS and list(m) == CACHE_PREFETCH_MISSES
+    assert [list(a) for a in v] == CACHE_PREFETCH_VICTIMS
+    assert ph == 1
+
+
+def test_cache_sim_hand_worked_pin():
+    h, m, v, ph = oracle.cache_sim(3, "lru", 0, CACHE_PIN_GROUPS, CACHE_PIN_KINDS)
+    assert list(h) == CACHE_PIN_HITS
+    assert [list(a) for a in v] == CACHE_PIN_VICTIMS
+    # a demand group that needs more slots than the pin leaves is refused
+    with pytest.raises(ValueError):
+        oracle.cache_sim(3, "lru", 0, [[7, 8], [0, 1]], ["pin", "demand"])
+
+
+@pytest.mark.parametrize("policy,period", [("lru", 0), ("lfu_decay", 7)])
+def test_cache_sim_invariants_random(policy, period):
+    """Random mixes: a pinned key is never a victim; a prefetch never evicts a key of the latest
+    demand group; hits + misses of a demand group = its distinct keys; a prefetch fetches at most
+    its absent keys."""
+    rng = np.random.default_rng(5)
+    groups, kinds, pinned = [], [], set()
+    n_pins = 0
+    for g in range(400):
+        r = rng.random()
+        if r < 0.02 and n_pins < 4:  # (at most 4 pinned keys: every demand group of 4 still fits 12 slots)
+            n_pins += 1
+            kinds.append("pin")
+            groups.append([int(rng.integers(0, 40))])
+        elif r < 0.35:
+            kinds.append("prefetch")
+            groups.append(rng.integers(0, 40, size=3).tolist())
+        else:
+            kinds.append("demand")
+            groups.append(rng.integers(0, 40, size=4).tolist())
+    cap = 12
+    h, m, v, ph = oracle.cache_sim(cap, policy, period, groups, kinds)
+    last_demand = set()
+    for g, (grp, kind) in enumerate(zip(groups, kinds)):
+        assert not (set(v[g].tolist()) & pinned)
+        if kind == "prefetch":
+            assert not (set(v[g].tolist()) & last_demand)
+            assert m[g] <= len(set(grp))
+        if kind == "demand":
+            assert h[g] + m[g] == len(set(grp))
+            last_demand = set(grp)
+        if kind == "pin":
+            pinned |= set(grp)
+        assert not (set(v[g].tolist()) & set(grp))
+
+
 def test_belady_at_least_lru_large():
     groups = _zipf_groups(400, 16, 512, 7)
     hb, _ = oracle.belady(64, groups)
