@@ -206,6 +206,22 @@ int moe_expert_ffn(const moe_experts* w, const void* x, int xdt, int T, int k, c
                    const int32_t* perm_src, float* y_perm, int mode, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under stream capture, serving loops and
+ * harnesses that forbid hipMalloc): moe_expert_ffn with its workspace taken from a static device
+ * array of MOE_FFN_NOALLOC_MAX_WORKSPACE bytes that the library holds on every device it runs on
+ * until the process ends.  Same arguments, semantics and results as moe_expert_ffn (the same
+ * kernels); the call allocates nothing.  The array's device address is looked up on the first call
+ * made with a device current.  All calls on one device share its array and nothing of it survives
+ * a call: calls in flight together on one device (several streams or host threads) race on it and
+ * must be serialised by the caller.
+ * Errors: as moe_expert_ffn; MOE_ERR_WORKSPACE when moe_ffn_workspace(w, T, k, mode) exceeds
+ * MOE_FFN_NOALLOC_MAX_WORKSPACE (use moe_expert_ffn with a caller workspace then).
+ */
+#define MOE_FFN_NOALLOC_MAX_WORKSPACE ((size_t)64 << 20)
+int moe_expert_ffn_noalloc(const moe_experts* w, const void* x, int xdt, int T, int k, const int32_t* offsets,
+                           const int32_t* perm_src, float* y_perm, int mode, void* stream);
+
+/*
  * Profiling hook.  While set (on the calling thread), every moe_expert_ffn call records, on its
  * stream, events[0] right before the gate/up GEMM kernel(s) (after any activation cast and
  * row-tile planning), events[1] after the gate/up kernel(s) (before the down kernel(s)) and

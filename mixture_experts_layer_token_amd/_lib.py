@@ -55,6 +55,8 @@ SIGNATURES = {
     "moe_ffn_workspace": ([ctypes.POINTER(MoeExperts), c_int, c_int, c_int], c_size_t),
     "moe_expert_ffn": ([ctypes.POINTER(MoeExperts), vp, c_int, c_int, c_int, i32p, i32p, f32p, c_int, vp, c_size_t,
                         vp], c_int),
+    "moe_expert_ffn_noalloc": ([ctypes.POINTER(MoeExperts), vp, c_int, c_int, c_int, i32p, i32p, f32p, c_int, vp],
+                               c_int),
     "moe_ffn_trace_events": ([vp], c_int),
     "moe_combine": ([f32p, f32p, i32p, c_int, c_int, c_int, f32p, vp, c_int, vp], c_int),
     "moe_cache_create": ([ctypes.POINTER(MoeCacheDesc), ctypes.POINTER(vp)], c_int),

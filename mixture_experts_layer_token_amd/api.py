@@ -122,6 +122,13 @@ def moe_expert_ffn(desc: MoeExperts, x, k, offsets, perm_src, y_perm, ws, mode="
                                _stream(stream)))
 
 
+def moe_expert_ffn_noalloc(desc: MoeExperts, x, k, offsets, perm_src, y_perm, mode="auto", stream=None):
+    """moe_expert_ffn with the library's static per-device scratch as workspace (no allocation)."""
+    T = x.shape[0]
+    check(lib().moe_expert_ffn_noalloc(ctypes.byref(desc), _dp(x), _dt(x), T, k, _dp(offsets), _dp(perm_src),
+                                       _dp(y_perm), MODE[mode], _stream(stream)))
+
+
 def moe_combine(y_perm, topk_w, inv_perm, k, shared_y, out, stream=None):
     T, H = out.shape
     check(lib().moe_combine(_dp(y_perm), _dp(topk_w), _dp(inv_perm), T, k, H, _dp(shared_y), _dp(out), _dt(out),
