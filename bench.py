@@ -64,7 +64,7 @@ def streaming_time(bytes_: float, bandwidth: float) -> float:
 
 # ------------------------------------------------------------------ measurement
 
-def measure(layers, xs, outs, steps: int, warmup: int, trace: bool, max_traced: int = 32):
+def measure(layers, xs, outs, steps: int, warmup: int, trace: bool, max_traced: int = 32, mode: str = "auto"):
     """Time `steps` eager steps between two events; step i runs layer instance i % len(layers) on
     batch i % len(xs).  On up to `max_traced` evenly spaced steps the library also records events
     around the gate/up and down kernels (on the launch stream)."""
@@ -72,7 +72,7 @@ def measure(layers, xs, outs, steps: int, warmup: int, trace: bool, max_traced: 
 
     R, L = len(xs), len(layers)
     for i in range(warmup):
-        layers[i % L].forward(xs[i % R], outs[i % R])
+        layers[i % L].forward(xs[i % R], outs[i % R], mode=mode)
     stride = max(1, steps // max_traced) if trace else steps + 1
     traced = list(range(0, steps, stride)) if trace else []
     ev = {i: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for i in traced}
@@ -86,7 +86,7 @@ def measure(layers, xs, outs, steps: int, warmup: int, trace: bool, max_traced: 
     wall0 = time.perf_counter()
     t0.record()
     for i in range(steps):
-        layers[i % L].forward(xs[i % R], outs[i % R], trace=handles.get(i))
+        layers[i % L].forward(xs[i % R], outs[i % R], mode=mode, trace=handles.get(i))
     t1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -96,7 +96,7 @@ def measure(layers, xs, outs, steps: int, warmup: int, trace: bool, max_traced: 
     return total_ms, wall, gu_ms, dn_ms, traced
 
 
-def measure_graph(layers, xs, outs, steps: int, warmup: int):
+def measure_graph(layers, xs, outs, steps: int, warmup: int, mode: str = "auto"):
     """The same step sequence with every step captured once as a HIP graph (one graph per step of
     a period of the layer and batch rotation) and replayed: exactly `steps` replays are timed.  The
     host launch overhead and inter-kernel gaps of the eager loop are gone.  Returns ms per step."""
@@ -110,14 +110,14 @@ def measure_graph(layers, xs, outs, steps: int, warmup: int):
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):  # warm every instance up off the capture
         for i in range(period):
-            layers[i % L].forward(xs[i % R], outs[i % R])
+            layers[i % L].forward(xs[i % R], outs[i % R], mode=mode)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     graphs = []
     for i in range(period):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            layers[i % L].forward(xs[i % R], outs[i % R])
+            layers[i % L].forward(xs[i % R], outs[i % R], mode=mode)
         graphs.append(g)
     for i in range(warmup):
         graphs[i % period].replay()
@@ -276,8 +276,9 @@ def run(args):
         steps = args.steps if T == args.T else max(20, args.steps // 4)
         if prefill:
             steps = min(steps, args.prefill_steps)
-        total_ms, wall, gu_ms, dn_ms, traced = measure(layers, xs, outs, steps, min(args.warmup, steps), trace=True)
-        graph_ms = (measure_graph(layers, xs, outs, steps, min(args.warmup, steps))
+        total_ms, wall, gu_ms, dn_ms, traced = measure(layers, xs, outs, steps, min(args.warmup, steps), trace=True,
+                                                       mode=args.mode)
+        graph_ms = (measure_graph(layers, xs, outs, steps, min(args.warmup, steps), mode=args.mode)
                     if args.graph and not prefill else None)
         b = [step_bytes(wl, T, touched[i % len(xs)]) for i in range(steps)]
         tot_bytes = sum(x["total"] for x in b)
@@ -313,7 +314,7 @@ def run(args):
         "dtype": "bf16" if wl.wfmt != "f32" else "f32",
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights)",
         "config": {"workload": "%s decode" % wl.name, "T": args.T, "hidden": wl.H, "experts": wl.E, "top_k": wl.k,
-                   "inter": wl.I, "weights": wl.wfmt, "activations": wl.xdt,
+                   "inter": wl.I, "weights": wl.wfmt, "activations": wl.xdt, "ffn_mode": args.mode,
                    "launch": "hipGraph replay" if args.graph else "eager",
                    "layer_instances": head["instances"], "input_batches": args.batches},
         "eager": {"ms_per_step": round(head["eager_ms_per_step"], 5),
@@ -639,6 +640,8 @@ def main():
                     help="decode: report the eager loop only (default: HIP graph replay, eager beside it)")
     ap.add_argument("--no-sweep", dest="sweep", action="store_false")
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
+    ap.add_argument("--mode", default="auto", choices=["auto", "decode", "prefill", "decode_mx"],
+                    help="moe_expert_ffn mode of the timed steps (decode_mx: MXFP4 on the block-scaled MFMA)")
     ap.add_argument("--no-prefill", dest="prefill", action="store_false",
                     help="default (Mixtral decode) run: leave out the Kimi-shaped prefill leg")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -681,7 +684,7 @@ def prefill_leg(args) -> dict:
     gc.collect()
     torch.cuda.empty_cache()
     pa = copy.copy(args)
-    pa.workload, pa.T, pa.sweep, pa.graph, pa.layers = "kimi", None, False, False, None
+    pa.workload, pa.T, pa.sweep, pa.graph, pa.layers, pa.mode = "kimi", None, False, False, None, "auto"
     pre = run(pa)
     keep = ("metric", "value", "unit", "ms_per_step", "steps", "warmup", "dtype", "data", "config", "roofline",
             "expert_ffn", "step_tflops", "cpu_baseline")

@@ -63,7 +63,15 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
  */
 typedef enum { MOE_W_F32 = 0, MOE_W_BF16 = 1, MOE_W_MXFP4 = 2, MOE_W_INT4G32 = 3 } moe_wfmt;
 
-typedef enum { MOE_FFN_AUTO = 0, MOE_FFN_DECODE = 1, MOE_FFN_PREFILL = 2 } moe_ffn_mode;
+/*
+ * moe_expert_ffn variants: AUTO picks per expert from its row count (weight streaming for few rows, the
+ * MFMA tile kernel for many); DECODE streams every expert; PREFILL tiles every expert.
+ * DECODE_MX (MXFP4 experts only) streams every expert on the block-scaled matrix cores
+ * (v_mfma_scale_f32_16x16x128_f8f6f4): the FP4 weights and their E8M0 scales enter the MFMA as stored,
+ * and the activations (x, then h) are first rounded to two MXFP8 (E4M3) terms per 32-element block,
+ * x = 2^e hi + 2^(e-4) lo, which holds each element to within 2^-8 of its magnitude.
+ */
+typedef enum { MOE_FFN_AUTO = 0, MOE_FFN_DECODE = 1, MOE_FFN_PREFILL = 2, MOE_FFN_DECODE_MX = 3 } moe_ffn_mode;
 
 /* Message of the last failing call on this thread ("" if none). Never NULL. */
 const char* moe_last_error(void);
@@ -199,8 +207,8 @@ size_t moe_ffn_workspace(const moe_experts* w, int T, int k, int mode);
  * A shared (always-on) expert is the same call with E = 1, offsets = {0, T}, k = 1 and
  * perm_src = {0, 1, ..., T-1}.
  * Errors: MOE_ERR_INVALID (null pointers, sizes), MOE_ERR_UNSUPPORTED (H, I not multiples
- * of 32; INT4 experts with activations not 16-byte aligned), MOE_ERR_WORKSPACE (ws smaller
- * than moe_ffn_workspace).
+ * of 32; INT4 experts with activations not 16-byte aligned; MOE_FFN_DECODE_MX with experts that
+ * are not MXFP4), MOE_ERR_WORKSPACE (ws smaller than moe_ffn_workspace for this mode).
  */
 int moe_expert_ffn(const moe_experts* w, const void* x, int xdt, int T, int k, const int32_t* offsets,
                    const int32_t* perm_src, float* y_perm, int mode, void* ws, size_t ws_bytes, void* stream);

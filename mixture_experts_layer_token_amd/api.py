@@ -16,7 +16,7 @@ from ._lib import COPY_FN, MoeCacheDesc, MoeCachePlan, MoeCacheStats, MoeExperts
 
 FMT = {"f32": 0, "bf16": 1, "mxfp4": 2, "int4g32": 3}
 DT = {"f32": 0, "bf16": 1}
-MODE = {"auto": 0, "decode": 1, "prefill": 2}
+MODE = {"auto": 0, "decode": 1, "prefill": 2, "decode_mx": 3}
 POLICY = {"lru": 0, "lfu_decay": 1}
 TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
 

@@ -75,7 +75,9 @@ extern "C" int moe_expert_ffn(const moe_experts* w, const void* x, int xdt, int 
   if (!dtype_valid(xdt)) return fail(MOE_ERR_INVALID, "moe_expert_ffn: bad dtype %d", xdt);
   if (T < 0 || k < 1 || k > 16) return fail(MOE_ERR_INVALID, "moe_expert_ffn: T=%d k=%d", T, k);
   if ((long long)T * k > (1LL << 24)) return fail(MOE_ERR_INVALID, "moe_expert_ffn: T*k too large");
-  if (mode < MOE_FFN_AUTO || mode > MOE_FFN_PREFILL) return fail(MOE_ERR_INVALID, "moe_expert_ffn: mode %d", mode);
+  if (mode < MOE_FFN_AUTO || mode > MOE_FFN_DECODE_MX) return fail(MOE_ERR_INVALID, "moe_expert_ffn: mode %d", mode);
+  if (mode == MOE_FFN_DECODE_MX && w->fmt != MOE_W_MXFP4)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_expert_ffn: the block-scaled mode takes MXFP4 experts (format %d)", w->fmt);
   size_t need = moe_package_bytes(w->H, w->I, w->fmt);
   if (w->pkg_stride < need || w->pkg_stride % 256)
     return fail(MOE_ERR_INVALID, "moe_expert_ffn: pkg_stride %zu (need >= %zu, multiple of 256)", w->pkg_stride, need);

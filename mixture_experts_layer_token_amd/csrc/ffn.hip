@@ -783,10 +783,12 @@ __global__ void dequant_f32_kernel(const float* __restrict__ pkg, size_t n, floa
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-  size_t cast_off, cast_bytes, xs_off, xs_bytes, h_off, h_bytes, plan_off, plan_bytes, tplan_off, tplan_bytes, total;
+  size_t cast_off, cast_bytes, xs_off, xs_bytes, h_off, h_bytes, plan_off, plan_bytes, tplan_off, tplan_bytes;
+  size_t mx_off, mx_bytes;  // block-scaled mode: x and h as two MXFP8 terms with their scales
+  size_t total;
 };
 
-WsLayout ws_layout(const moe_experts* w, int T, int k, int xdt) {
+WsLayout ws_layout(const moe_experts* w, int T, int k, int xdt, int mode = MOE_FFN_AUTO) {
   WsLayout L{};
   const size_t n = (size_t)T * k;
   const bool f32w = w->fmt == MOE_W_F32;
@@ -806,7 +808,13 @@ WsLayout ws_layout(const moe_experts* w, int T, int k, int xdt) {
   // counters (8 for gate/up, 8 for down)
   L.tplan_off = L.plan_off + L.plan_bytes;
   L.tplan_bytes = f32w ? 0 : align256((1 + n / kTileRows + (n < (size_t)w->E ? n : (size_t)w->E)) * sizeof(int4)) + 256;
-  L.total = L.tplan_off + L.tplan_bytes;
+  // block-scaled mode: x hi, x lo [T][H], x scales [T][H/32] u16; h hi, h lo [n][I], h scales [n][I/32]
+  L.mx_off = L.tplan_off + L.tplan_bytes;
+  L.mx_bytes = mode == MOE_FFN_DECODE_MX
+                   ? 2 * align256((size_t)T * w->H) + align256((size_t)T * w->H / 16) + 2 * align256(n * w->I) +
+                         align256(n * w->I / 16)
+                   : 0;
+  L.total = L.mx_off + L.mx_bytes;
   return L;
 }
 
@@ -936,9 +944,8 @@ int launch_stream_fmt(int fmt, int mt, bool narrow, bool gate_up, const FfnArgs&
 }  // namespace
 
 size_t ffn_workspace(const moe_experts* w, int T, int k, int mode) {
-  (void)mode;
   // the cast buffer is sized for the worst case (any xdt)
-  WsLayout a = ws_layout(w, T, k, MOE_F32), b = ws_layout(w, T, k, MOE_BF16);
+  WsLayout a = ws_layout(w, T, k, MOE_F32, mode), b = ws_layout(w, T, k, MOE_BF16, mode);
   return a.total > b.total ? a.total : b.total;
 }
 
@@ -946,7 +953,7 @@ int launch_ffn(const moe_experts* w, const void* x, int xdt, int T, int k, const
                const int32_t* perm_src, float* y_perm, int mode, void* ws, size_t ws_bytes, hipStream_t s) {
   if (T == 0) return MOE_OK;
   const int H = w->H, I = w->I, E = w->E;
-  WsLayout L = ws_layout(w, T, k, xdt);
+  WsLayout L = ws_layout(w, T, k, xdt, mode);
   if (!ws || ws_bytes < L.total)
     return fail(MOE_ERR_WORKSPACE, "moe_expert_ffn: workspace %zu bytes < %zu", ws_bytes, L.total);
   char* wsp = (char*)ws;
@@ -979,6 +986,44 @@ int launch_ffn(const moe_experts* w, const void* x, int xdt, int T, int k, const
     hipLaunchKernelGGL((ffn_f32_kernel<float, false>), dim3((H + 3) / 4, S), dim3(256), 0, s, dn);
     trace(2, s);
     MOE_CHECK_LAUNCH("moe_expert_ffn f32 launch");
+    return MOE_OK;
+  }
+
+  if (mode == MOE_FFN_DECODE_MX) {
+    // every expert streamed on the block-scaled MFMA: x -> MXFP8 terms, gate/up, h -> MXFP8 terms, down
+    const int mt = pick_mt(T, k, E), mr = 16 * mt;
+    const size_t nz = n < (size_t)E ? n : (size_t)E;
+    const int S = (int)((n + nz * (mr - 1)) / mr);
+    unsigned char* mx = (unsigned char*)(wsp + L.mx_off);
+    unsigned char* xh = mx;
+    unsigned char* xl = xh + align256((size_t)T * H);
+    unsigned short* xsc = (unsigned short*)(xl + align256((size_t)T * H));
+    unsigned char* hh = (unsigned char*)xsc + align256((size_t)T * H / 16);
+    unsigned char* hl = hh + align256(n * I);
+    unsigned short* hsc = (unsigned short*)(hl + align256(n * I));
+    if ((uintptr_t)x % 16) return fail(MOE_ERR_UNSUPPORTED, "moe_expert_ffn: the block-scaled mode needs 16-byte aligned x");
+    launch_quant_mx8(x, xdt == MOE_BF16, T, H, xh, xl, xsc, s);
+    int4* plan = (int4*)(wsp + L.plan_off);
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, offsets, E, mr, 1, 0x7FFFFFFF, w->slot_of_expert,
+                       gu.n_slots, plan, (int*)nullptr, 0);
+    gu.plan = plan;
+    gu.out = h;
+    gu.region_codes = g.gu_codes, gu.region_scales = g.gu_scales;
+    gu.a_hi = xh, gu.a_lo = xl, gu.a_sc = xsc;
+    gu.min_rows = 1, gu.max_rows = 0x7FFFFFFF;
+    FfnArgs dm = gu;
+    dm.out = y_perm;
+    dm.region_codes = g.d_codes, dm.region_scales = g.d_scales;
+    dm.a_hi = hh, dm.a_lo = hl, dm.a_sc = hsc;
+    trace(0, s);
+    int rc = launch_ffn_mx_part(mt, true, gu, H, I, S, s);
+    if (rc != MOE_OK) return rc;
+    trace(1, s);
+    launch_quant_mx8(h, true, (int)n, I, hh, hl, hsc, s);
+    rc = launch_ffn_mx_part(mt, false, dm, H, I, S, s);
+    if (rc != MOE_OK) return rc;
+    trace(2, s);
+    MOE_CHECK_LAUNCH("moe_expert_ffn block-scaled launch");
     return MOE_OK;
   }
 

@@ -157,6 +157,11 @@ struct FfnArgs {
   // INT4 experts: the power of two each token's activations were divided by in the fp16 cast
   // (xscale[t] = s_t), or null when they were not scaled
   const float* xscale;
+  // block-scaled MXFP4 path: the A operand as two MXFP8 terms, [rows][K] bytes each, and the E8M0
+  // scales of every 32-element block [rows][K/32] (hi byte | lo byte << 8)
+  const unsigned char* a_hi;
+  const unsigned char* a_lo;
+  const unsigned short* a_sc;
 };
 
 // INT4 experts multiply fp16 activations scaled per token: x' = x / s_t, with s_t a power of two
@@ -213,5 +218,11 @@ inline int cu_count() {
 // Prefill (tile) variant, one matrix: gate/up (with SwiGLU) or down, for the experts whose row
 // count lies in [a.min_rows, a.max_rows].
 int launch_ffn_tile_part(int fmt, bool gate_up, const FfnArgs& a, int H, int I, int n, int E, hipStream_t s);
+
+// Block-scaled MXFP4 path: rows of x (bf16 / fp32) or h (bf16) -> two MXFP8 terms and their scales;
+// then one matrix of the streaming FFN on v_mfma_scale_f32_16x16x128_f8f6f4 (a.plan: 16*mt-row tiles).
+void launch_quant_mx8(const void* x, bool src_bf16, int rows, int K, unsigned char* hi, unsigned char* lo,
+                      unsigned short* sc, hipStream_t s);
+int launch_ffn_mx_part(int mt, bool gate_up, const FfnArgs& a, int H, int I, int S, hipStream_t s);
 
 }  // namespace moe

@@ -55,7 +55,9 @@ class MoeLayer:
         self.perm_src = torch.empty(n, **i32)
         self.inv_perm = torch.empty(n, **i32)
         self.y_perm = torch.empty((n, H), dtype=torch.float32, device=d)
-        ws = api.moe_ffn_workspace(self.desc, T, k)
+        # the workspace serves every mode this layer's format has (MXFP4: also the block-scaled one)
+        modes = ("auto", "decode", "prefill") + (("decode_mx",) if self.fmt == "mxfp4" else ())
+        ws = max(api.moe_ffn_workspace(self.desc, T, k, m) for m in modes)
         if self.shared is not None:
             ws = max(ws, api.moe_ffn_workspace(self.shared_desc, T, 1))
             self.sh_offsets = torch.tensor([0, T], **i32)
