@@ -63,6 +63,12 @@ def lib():
         L.oracle_belady.restype = i32
         L.oracle_cache_sim.argtypes = [i64, i32, i64, i64, vp, vp, vp, vp, vp, vp, vp, vp]
         L.oracle_cache_sim.restype = i32
+        L.oracle_xw4_bound.argtypes = [i64]
+        L.oracle_xw4_bound.restype = i64
+        L.oracle_xw4_encode.argtypes = [vp, i64, vp, i64]
+        L.oracle_xw4_encode.restype = i64
+        L.oracle_xw4_decode.argtypes = [vp, i64, vp, i64]
+        L.oracle_xw4_decode.restype = i32
         for f in ("oracle_decode", "oracle_decode_act", "oracle_router_logits", "oracle_topk_gates",
                   "oracle_permute", "oracle_ffn"):
             getattr(L, f).restype = None
@@ -235,6 +241,28 @@ def belady(capacity: int, groups):
     if rc != 0:
         raise ValueError("a group holds more distinct keys than the capacity")
     return hits, misses
+
+
+def xw4_encode(raw: np.ndarray) -> np.ndarray:
+    """Exponent-window code of a bf16 package (uint8 bytes, size a multiple of 1024) -> blob bytes."""
+    raw = np.ascontiguousarray(raw).view(np.uint8).ravel()
+    cap = int(lib().oracle_xw4_bound(raw.size))
+    if cap < 0:
+        raise ValueError("package size %d is not a multiple of 1024" % raw.size)
+    out = np.zeros(cap, np.uint8)
+    n = int(lib().oracle_xw4_encode(_p(raw), raw.size, _p(out), cap))
+    if n < 0:
+        raise ValueError("encode failed")
+    return out[:n].copy()
+
+
+def xw4_decode(blob: np.ndarray, raw_bytes: int) -> np.ndarray:
+    """Blob -> the package's raw_bytes bytes (ValueError if the blob is malformed)."""
+    blob = np.ascontiguousarray(blob).view(np.uint8).ravel()
+    out = np.zeros(raw_bytes, np.uint8)
+    if lib().oracle_xw4_decode(_p(blob), blob.size, _p(out), raw_bytes) != 0:
+        raise ValueError("malformed blob")
+    return out
 
 
 def min_gap(logits: np.ndarray, k: int) -> np.ndarray:

@@ -607,3 +607,128 @@ int oracle_cache_sim(int64_t capacity, int policy, int64_t period, int64_t n_gro
   free(dmark);
   return (int)rc;
 }
+
+/* ------------------------------------------------------------------------------------------
+ * Lossless compression of bf16 expert packages.  The pages place a tier of losslessly
+ * compressed experts in GPU memory beside the host tier, lossless so that no output bit
+ * changes (What expert offloading actually costs, "Inside expert paging"); they name no codec.
+ * Reading: an exponent-window code, from this definition:
+ *
+ *  - The package is read as little-endian bf16 values in chunks of 512 (1024 bytes; the package
+ *    size must be a multiple of 1024).  Value v has sign s = v >> 15, exponent field
+ *    e = (v >> 7) & 255 and mantissa m = v & 127.
+ *  - Chunk window: M = the largest e in the chunk, base b = M - 14 (0 if M < 14); e is in the
+ *    window when b <= e <= b + 14, with code c = e - b + 1 (1..15); any other e is an escape,
+ *    code 0.
+ *  - Coded chunk: 512 bytes s << 7 | m (value order), 256 bytes of codes (byte t holds value
+ *    2t's code in its low nibble, value 2t+1's in its high nibble), then the e of each escaped
+ *    value in value order, zero-padded to a multiple of 16.  Its size is 768 + 16 ceil(n_esc/16).
+ *    A chunk whose coded size would be 1024 or more is stored raw (its 1024 bytes as they are).
+ *  - Blob: a 64-byte header (u32 magic 0x31345758, u32 chunk count n, u64 package bytes, u64
+ *    data offset, u64 blob bytes, zeros), u32 chunk offsets off[0..n] (relative to the data
+ *    offset, off[0] = 0), u8 window bases (0 for raw chunks), zeros up to the data offset (the
+ *    smallest multiple of 256 past the tables), then the chunks back to back.  A chunk of
+ *    off[i+1] - off[i] = 1024 bytes is raw.
+ * ------------------------------------------------------------------------------------------ */
+#define XW4_MAGIC 0x31345758u
+
+static void le_put(uint8_t* p, uint64_t v, int bytes) {
+  for (int i = 0; i < bytes; ++i) p[i] = (uint8_t)(v >> (8 * i));
+}
+static uint64_t le_get(const uint8_t* p, int bytes) {
+  uint64_t v = 0;
+  for (int i = 0; i < bytes; ++i) v |= (uint64_t)p[i] << (8 * i);
+  return v;
+}
+static int64_t xw4_data_offset(int64_t n) { return (64 + 4 * (n + 1) + n + 255) / 256 * 256; }
+
+int64_t oracle_xw4_bound(int64_t raw_bytes) {
+  if (raw_bytes < 0 || raw_bytes % 1024) return -1;
+  return xw4_data_offset(raw_bytes / 1024) + raw_bytes;
+}
+
+/* Returns the blob's size, or -1 (size not a multiple of 1024, or cap too small). */
+int64_t oracle_xw4_encode(const uint8_t* raw, int64_t raw_bytes, uint8_t* out, int64_t cap) {
+  if (raw_bytes < 0 || raw_bytes % 1024 || cap < oracle_xw4_bound(raw_bytes)) return -1;
+  const int64_t n = raw_bytes / 1024, data = xw4_data_offset(n);
+  memset(out, 0, (size_t)data);
+  int64_t pos = 0;
+  for (int64_t i = 0; i < n; ++i) {
+    const uint8_t* src = raw + 1024 * i;
+    uint8_t* dst = out + data + pos;
+    int e[512], M = 0, n_esc = 0;
+    for (int j = 0; j < 512; ++j) {
+      const unsigned v = (unsigned)le_get(src + 2 * j, 2);
+      e[j] = (int)((v >> 7) & 255);
+      if (e[j] > M) M = e[j];
+    }
+    const int b = M < 14 ? 0 : M - 14;
+    for (int j = 0; j < 512; ++j)
+      if (e[j] < b || e[j] > b + 14) n_esc++;
+    const int coded = 768 + 16 * ((n_esc + 15) / 16);
+    if (coded >= 1024) {
+      memcpy(dst, src, 1024);
+      out[64 + 4 * (n + 1) + i] = 0;
+      pos += 1024;
+    } else {
+      memset(dst, 0, (size_t)coded);
+      int k = 0;
+      for (int j = 0; j < 512; ++j) {
+        const unsigned v = (unsigned)le_get(src + 2 * j, 2);
+        dst[j] = (uint8_t)(((v >> 15) << 7) | (v & 127));
+        const int in = e[j] >= b && e[j] <= b + 14;
+        const unsigned c = in ? (unsigned)(e[j] - b + 1) : 0u;
+        dst[512 + j / 2] |= (uint8_t)(c << (4 * (j % 2)));
+        if (!in) dst[768 + k++] = (uint8_t)e[j];
+      }
+      out[64 + 4 * (n + 1) + i] = (uint8_t)b;
+      pos += coded;
+    }
+    le_put(out + 64 + 4 * (i + 1), (uint64_t)pos, 4);
+  }
+  le_put(out, XW4_MAGIC, 4);
+  le_put(out + 4, (uint64_t)n, 4);
+  le_put(out + 8, (uint64_t)raw_bytes, 8);
+  le_put(out + 16, (uint64_t)data, 8);
+  le_put(out + 24, (uint64_t)(data + pos), 8);
+  return data + pos;
+}
+
+/* Decodes a blob into raw_bytes bytes; returns 0, or -1 if the blob is not a well-formed
+ * encoding of a package of that size. */
+int oracle_xw4_decode(const uint8_t* blob, int64_t blob_bytes, uint8_t* raw, int64_t raw_bytes) {
+  if (blob_bytes < 64 || raw_bytes < 0 || raw_bytes % 1024) return -1;
+  const int64_t n = raw_bytes / 1024, data = xw4_data_offset(n);
+  if (le_get(blob, 4) != XW4_MAGIC || (int64_t)le_get(blob + 4, 4) != n || (int64_t)le_get(blob + 8, 8) != raw_bytes ||
+      (int64_t)le_get(blob + 16, 8) != data || blob_bytes < data)
+    return -1;
+  const int64_t total = (int64_t)le_get(blob + 24, 8);
+  if (total > blob_bytes || le_get(blob + 64, 4) != 0 || data + (int64_t)le_get(blob + 64 + 4 * n, 4) != total) return -1;
+  for (int64_t i = 0; i < n; ++i) {
+    const int64_t o0 = (int64_t)le_get(blob + 64 + 4 * i, 4), o1 = (int64_t)le_get(blob + 64 + 4 * (i + 1), 4);
+    const int64_t size = o1 - o0;
+    const uint8_t* src = blob + data + o0;
+    uint8_t* dst = raw + 1024 * i;
+    if (size == 1024) {
+      memcpy(dst, src, 1024);
+      continue;
+    }
+    if (size < 768 || size > 1008 || size % 16) return -1;
+    const int b = blob[64 + 4 * (n + 1) + i];
+    int k = 0;
+    for (int j = 0; j < 512; ++j) {
+      const unsigned c = (src[512 + j / 2] >> (4 * (j % 2))) & 15u;
+      unsigned ex;
+      if (c) {
+        ex = (unsigned)(b + (int)c - 1);
+      } else {
+        if (768 + k >= size) return -1;
+        ex = src[768 + k++];
+      }
+      if (ex > 255) return -1;
+      const unsigned v = ((unsigned)(src[j] >> 7) << 15) | (ex << 7) | (src[j] & 127u);
+      le_put(dst + 2 * j, v, 2);
+    }
+  }
+  return 0;
+}

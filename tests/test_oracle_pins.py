@@ -521,3 +521,132 @@ def test_cost_model_matches_the_printed_worked_example():
     assert round(cm2["tokens_per_s"] / cm["tokens_per_s"] - 1, 2) == m["gain_approx"]
     mr = g["measured_reciprocals"]
     assert round(1000 / mr["kimi_tok_s"]) == mr["kimi_ms"] and round(1000 / mr["glm_tok_s"]) == mr["glm_ms"]
+
+
+# ---- lossless exponent-window code of bf16 packages (the definition is in oracle.c)
+
+def _chunk(vals):
+    v = np.asarray(vals, np.uint16)
+    assert v.size == 512
+    return v.view(np.uint8)
+
+
+def test_xw4_hand_worked_chunk():
+    """One chunk, worked by hand from the definition: values -2.0 (0xC000), +0, 1.5 (0x3FC0), the
+    smallest negative subnormal (0x8001), then 508 x 1.0 (0x3F80).  Largest exponent field 128, so
+    the window base is 114: -2.0 -> code 15, 1.0 and 1.5 -> code 14, the two exponent-0 values are
+    escapes (code 0, escape bytes 0x00 0x00).  Coded size 768 + 16; the tables take 64 + 8 + 1
+    bytes, so the data starts at 256 and the blob is 1040 bytes."""
+    raw = _chunk([0xC000, 0x0000, 0x3FC0, 0x8001] + [0x3F80] * 508)
+    blob = oracle.xw4_encode(raw)
+    assert blob.size == 1040
+    hdr = blob[:64]
+    assert hdr[:4].tobytes() == bytes([0x58, 0x57, 0x34, 0x31])
+    assert int.from_bytes(hdr[4:8].tobytes(), "little") == 1
+    assert int.from_bytes(hdr[8:16].tobytes(), "little") == 1024
+    assert int.from_bytes(hdr[16:24].tobytes(), "little") == 256
+    assert int.from_bytes(hdr[24:32].tobytes(), "little") == 1040
+    assert not hdr[32:].any()
+    assert blob[64:72].view(np.uint32).tolist() == [0, 784]
+    assert blob[72] == 114
+    assert not blob[73:256].any()
+    d = blob[256:]
+    sm = [0x80, 0x00, 0x40, 0x81] + [0x00] * 508
+    codes = [0x0F, 0x0E] + [0xEE] * 254
+    assert d[:512].tolist() == sm
+    assert d[512:768].tolist() == codes
+    assert d[768:784].tolist() == [0] * 16
+    assert np.array_equal(oracle.xw4_decode(blob, 1024), raw)
+
+
+@pytest.mark.parametrize("n_esc,raw_chunk", [(0, False), (1, False), (16, False), (17, False), (240, False),
+                                             (241, True), (400, True)])
+def test_xw4_escape_count_and_raw_fallback(n_esc, raw_chunk):
+    """Largest exponent 200 (0x6400) puts the window at 186..200; exponent-1 values (0x0080) escape
+    and exponent-190 values (0x5F00) do not.  A chunk is coded while 768 + 16 ceil(n_esc / 16) < 1024
+    (at most 240 escapes) and stored raw from there on."""
+    vals = [0x6400] + [0x0080] * n_esc + [0x5F00] * (511 - n_esc)
+    raw = _chunk(vals)
+    blob = oracle.xw4_encode(raw)
+    size = int(blob[68:72].view(np.uint32)[0])
+    if raw_chunk:
+        assert size == 1024 and blob[72] == 0
+        assert np.array_equal(blob[256:256 + 1024], raw)
+    else:
+        assert size == 768 + 16 * ((n_esc + 15) // 16)
+        assert blob[72] == 186
+        d = blob[256:]
+        assert d[768:768 + n_esc].tolist() == [1] * n_esc  # the escaped exponent fields, in value order
+        c = np.concatenate([d[512:768] & 15, d[512:768] >> 4], axis=0).reshape(2, 256).T.ravel()
+        assert c[0] == 15 and (c[1:1 + n_esc] == 0).all() and (c[1 + n_esc:] == 5).all()
+    assert np.array_equal(oracle.xw4_decode(blob, 1024), raw)
+
+
+def test_xw4_small_exponents_window_starts_at_zero():
+    """Largest exponent below 14: the window is 0..14, so zeros and subnormals are coded (code 1)."""
+    raw = _chunk([0x0000, 0x8000, 0x0001, 0x0680] + [0x0000] * 508)  # +0, -0, subnormal, exponent 13
+    blob = oracle.xw4_encode(raw)
+    assert blob.size == 256 + 768 and blob[72] == 0
+    c = blob[256 + 512:256 + 768]
+    assert c[0] == 0x11 and c[1] == 0xE1 and (c[2:] == 0x11).all()
+    assert np.array_equal(oracle.xw4_decode(blob, 1024), raw)
+
+
+def _bf16_bits(a):
+    return (np.asarray(a, np.float32).view(np.uint32) >> 16).astype(np.uint16)  # truncation: any bf16 value
+
+
+@pytest.mark.parametrize("kind", ["normal", "uniform_bits", "specials", "mixed"])
+def test_xw4_round_trip_is_exact(kind):
+    rng = np.random.default_rng(11)
+    n = 512 * 24
+    if kind == "normal":
+        v = _bf16_bits(rng.normal(0, 0.02, n))
+    elif kind == "uniform_bits":
+        v = rng.integers(0, 1 << 16, n, dtype=np.uint16)
+    elif kind == "specials":
+        pool = np.array([0x0000, 0x8000, 0x7F80, 0xFF80, 0x7FC0, 0x7FFF, 0xFFC1, 0x0001, 0x807F, 0x0080, 0x7F7F,
+                         0xFF7F, 0x3F80], np.uint16)
+        v = rng.choice(pool, n)
+    else:
+        v = _bf16_bits(rng.normal(0, 0.02, n))
+        v[rng.integers(0, n, 300)] = rng.integers(0, 1 << 16, 300, dtype=np.uint16)
+        v[5 * 512:6 * 512] = 0
+    raw = v.view(np.uint8)
+    blob = oracle.xw4_encode(raw)
+    assert np.array_equal(oracle.xw4_decode(blob, raw.size), raw)
+    # chunk sizes from the definition, counted with numpy: 768 + 16 ceil(escapes / 16), or raw 1024
+    e = ((v.reshape(-1, 512) >> 7) & 255).astype(np.int64)
+    b = np.maximum(e.max(axis=1) - 14, 0)
+    esc = ((e < b[:, None]) | (e > b[:, None] + 14)).sum(axis=1)
+    coded = 768 + 16 * ((esc + 15) // 16)
+    want = np.where(coded < 1024, coded, 1024)
+    off = blob[64:64 + 4 * 25].view(np.uint32)
+    assert np.array_equal(np.diff(off.astype(np.int64)), want)
+    assert blob.size == 256 + want.sum()
+
+
+def test_xw4_ratio_on_gaussian_weights():
+    """N(0, 0.02) bf16 weights: 12 bits per value plus rare escapes, about 75% of the package."""
+    rng = np.random.default_rng(5)
+    raw = _bf16_bits(rng.normal(0, 0.02, 512 * 2048)).view(np.uint8)
+    blob = oracle.xw4_encode(raw)
+    assert 0.75 <= blob.size / raw.size < 0.76
+
+
+def test_xw4_decode_rejects_malformed_blobs():
+    raw = _chunk([0x3F80] * 512)
+    blob = oracle.xw4_encode(raw)
+    assert np.array_equal(oracle.xw4_decode(blob, 1024), raw)
+    for mutate in (lambda b: b.__setitem__(0, 0), lambda b: b.__setitem__(4, 2),
+                   lambda b: b.__setitem__(68, 0x10)):
+        bad = blob.copy()
+        mutate(bad)
+        with pytest.raises(ValueError):
+            oracle.xw4_decode(bad, 1024)
+    with pytest.raises(ValueError):
+        oracle.xw4_decode(blob, 2048)
+    with pytest.raises(ValueError):
+        oracle.xw4_decode(blob[:600], 1024)
+    with pytest.raises(ValueError):
+        oracle.xw4_encode(np.zeros(1000, np.uint8))
