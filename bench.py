@@ -398,6 +398,182 @@ def static_pins(model, groups_by_layer, per_layer: int):
     return pins
 
 
+def run_offload_compressed(args):
+    """The GLM-shaped offload run with bf16 experts (four layers), plain and with both tiers
+    compressed (the bank and the HBM slots hold exponent-window blobs, decoded into a working pool
+    before each FFN pass), in the same HBM budget: 25% of the bank's plain packages."""
+    import torch
+
+    from synth import workloads as W
+
+    from mixture_experts_layer_token_amd import api
+    from mixture_experts_layer_token_amd.layer import pack_bank, to_device_act
+    from mixture_experts_layer_token_amd.offload import OffloadedModel
+
+    # four of the GLM-shaped layers: their bf16 bank (48 GB) is as much page-locked host memory as the
+    # box grants one process with room to spare (eight layers, 97 GB, are refused)
+    wl = W.WORKLOADS["glm"].with_(wfmt="bf16", name="glm-offload-bf16", layers=4)
+    steps = min(args.offload_steps, wl.steps)
+    Ts = [args.T] if args.T else [16, 1]
+    raw_bytes = api.moe_package_bytes(wl.H, wl.I, "bf16")
+    raw_stride = (raw_bytes + 255) // 256 * 256
+    slots_raw = int(wl.cache_frac * wl.layers * wl.E)
+    budget = slots_raw * raw_stride  # HBM for expert weights, the same in both runs
+    # blob slot: the largest blob of a sample of experts (one per layer and a few more), plus 0.3%;
+    # the fill refuses any blob that does not fit
+    sample = [pack_bank(wl, l, [e])[0, :raw_bytes] for l in range(wl.layers) for e in (0, 97, 211)]
+    largest = max(api.moe_compress_package(p).size for p in sample)
+    blob_bytes = (int(largest * 1.003) + 255) // 256 * 256
+    runs, belady, touched_all = [], {}, {}
+    policies = (("lfu_decay", 32), ("lru", 0))
+    for compressed in (False, True):
+        cap_max = slots_raw if not compressed else (budget - min(wl.E, min(Ts) * wl.k) * raw_stride) // blob_bytes
+        model = OffloadedModel(wl, max(Ts), capacity=cap_max, fill=False, compressed=compressed,
+                               blob_bytes=blob_bytes if compressed else None)
+        for T in Ts:
+            xs = {(l, s): to_device_act(W.activations(wl, T, l, s), wl.xdt) for s in range(steps)
+                  for l in range(wl.layers)}
+            if T not in touched_all:
+                touched = {l: set() for l in range(wl.layers)}
+                ids = torch.empty((T, wl.k), dtype=torch.int32, device="cuda")
+                gw = torch.empty((T, wl.k), dtype=torch.float32, device="cuda")
+                for (l, s), x in xs.items():
+                    api.moe_route(x, model.wg[l], model.bias(l, s), wl.k, ids, gw)
+                    touched[l] |= set(ids.cpu().numpy().ravel().tolist())
+                touched_all[T] = touched
+            for l in range(wl.layers):
+                model.fill(l, touched_all[T][l] - model.filled.get(l, set()))
+                model.filled[l] = model.filled.get(l, set()) | touched_all[T][l]
+            # compressed: the working pool takes min(E, T k) plain packages of the budget
+            n_work = min(wl.E, T * wl.k)
+            cap = slots_raw if not compressed else (budget - n_work * raw_stride) // blob_bytes
+            out = torch.empty((T, wl.H), dtype=torch.bfloat16, device="cuda")
+            model.reset_cache(capacity=cap, prefetch=None)
+            for l in range(wl.layers):  # warm the kernels through the full path
+                model.layer_forward(l, 0, xs[(l, 0)], out)
+            for policy, period in policies:
+                r = offload_variant(model, wl, T, steps, xs, out, policy, period, True, None, None, belady)
+                r["tiers"] = "compressed" if compressed else "plain"
+                r["working_pool_slots"] = n_work if compressed else 0
+                runs.append(r)
+                print("offload %s T=%d %s: %.1f tokens/s, hit %.4f, %d slots" % (
+                    r["tiers"], T, r["policy"], r["tokens_per_s"], r["hit_rate"], r["cache_slots"]), flush=True)
+            del xs
+        if compressed:
+            blob_sizes = model.blob_sizes[model.blob_sizes > 0]
+            dec = time_decoder(model, min(64, model.n_work))
+        model.close()
+        del model
+    head = max((r for r in runs if r["T"] == Ts[0] and r["tiers"] == "compressed"), key=lambda r: r["tokens_per_s"])
+    plain = max((r for r in runs if r["T"] == Ts[0] and r["tiers"] == "plain"), key=lambda r: r["tokens_per_s"])
+    return {
+        "metric": "MoE-layer tokens/s (offloaded expert bank, decode) + expert-cache hit rate + link GB/s",
+        "value": round(head["tokens_per_s"], 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": 1,
+        "ms_per_step": round(head["wall_s"] / steps * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) bf16 weights)",
+        "config": {"workload": wl.name, "T": Ts[0], "layers": wl.layers, "hidden": wl.H, "experts": wl.E,
+                   "top_k": wl.k, "inter": wl.I, "tiers": "compressed (bank and HBM slots)",
+                   "hbm_budget_bytes": budget, "cache_policy": head["policy"],
+                   "reported": "compressed tiers, the faster policy at this T; plain tiers beside"},
+        "vs_plain_tiers": round(head["tokens_per_s"] / plain["tokens_per_s"], 4),
+        "compression": {"raw_bytes": raw_bytes, "blob_slot_bytes": blob_bytes,
+                        "blob_bytes_mean": float(blob_sizes.mean()), "blob_bytes_max": int(blob_sizes.max()),
+                        "ratio_mean": round(float(blob_sizes.mean()) / raw_bytes, 5),
+                        "ratio_slot": round(blob_bytes / raw_bytes, 5), "experts": int(blob_sizes.size)},
+        "roofline": {"bound": "link", "kernel": "hipMemcpyAsync host bank -> HBM slots (copy stream)",
+                     "achieved": round(head["link_gbps_busy"], 2), "peak": PCIE_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(head["link_gbps_busy"] / PCIE_PEAK_GBS, 4), "traffic": None},
+        "decoder_roofline": dec,
+        "runs": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()} for r in runs],
+    }
+
+
+def time_decoder(model, n: int) -> dict:
+    """HBM roofline of the package decoder: n blobs of the bank decoded into the working pool in one
+    launch, timed with HIP events on the stream it runs on; algorithmic bytes = the blobs' bytes
+    read + the packages' bytes written."""
+    import torch
+
+    from mixture_experts_layer_token_amd import api
+
+    keys = [(l, e) for l in range(model.L) for e in range(model.E) if model.blob_sizes[l, e] > 0][:n]
+    n = len(keys)
+    for i, (l, e) in enumerate(keys):
+        model.pool[i].copy_(torch.from_numpy(model.package(l, e).copy()))
+    pairs = torch.tensor([[i, i] for i in range(n)], dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        api.moe_decompress_packages(model.pool, model.stride, model.work, model.raw_stride, pairs, model.raw_bytes)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 20
+    a.record()
+    for _ in range(reps):
+        api.moe_decompress_packages(model.pool, model.stride, model.work, model.raw_stride, pairs, model.raw_bytes)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / reps
+    alg = int(sum(model.blob_sizes[l, e] for l, e in keys)) + n * model.raw_bytes
+    return {"bound": "hbm", "kernel": "xw4_decode_kernel (%d packages per launch)" % n,
+            "achieved": round(alg / us / 1e3, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(alg / us / 1e3 / HBM_PEAK_GBS, 4), "traffic": None, "avg_launch_us": round(us, 2),
+            "algorithmic_bytes_per_launch": alg}
+
+
+def offload_variant(model, wl, T, steps, xs, out, policy, period, overlap, pf, pin, belady):
+    """One timed pass of `steps` decode steps through the model's layers with an empty cache of the
+    given policy, prefetch heuristic and static pin; the run's figures."""
+    import torch
+
+    model.reset_cache(policy, period, overlap, prefetch=pf, pins=pin)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        for l in range(wl.layers):
+            model.layer_forward(l, s, xs[(l, s)], out, time_copies=True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    copy_s = model.copy_seconds()
+    st = model.cache.stats()
+    seen, cold = set(), 0
+    per_epoch = {}
+    for (s, l, n, h, m) in model.plans:
+        a = per_epoch.setdefault(s // wl.rerank_every, [0, 0])
+        a[0] += h
+        a[1] += n
+    # compulsory misses: first lookup of each (layer, expert) key
+    for grp in model.groups:
+        for key in grp:
+            if key not in seen:
+                seen.add(key)
+                cold += 1
+    name = policy if policy == "lru" else "%s/%d" % (policy, period)
+    if pin is not None:
+        name = "static-pin(%d/layer)+%s" % (len(pin[0]), name)
+    bkey = (T, model.capacity)
+    if bkey not in belady:
+        belady[bkey] = belady_hits(model.capacity, model.groups)
+    return {
+        "T": T, "policy": name, "prefetch": pf or "none", "steps": steps,
+        "ffn_of_hits_during_copies": overlap,
+        "layers": wl.layers, "cache_slots": model.capacity, "wall_s": wall, "tokens_per_s": T * steps / wall,
+        "hit_rate": st["hits"] / max(1, st["lookups"]),
+        "hit_rate_cold_excluded": st["hits"] / max(1, st["lookups"] - cold),
+        "hit_rate_per_epoch": [round(v[0] / max(1, v[1]), 4) for _, v in sorted(per_epoch.items())],
+        "hit_rate_belady": belady[bkey] / max(1, st["lookups"]),
+        "lookups": st["lookups"], "misses": st["misses"], "bytes_fetched": st["bytes_fetched"],
+        "prefetch_fetches": st["prefetch_fetches"], "prefetch_hits": st["prefetch_hits"],
+        "copy_busy_s": copy_s,
+        "link_gbps_busy": st["bytes_fetched"] / max(1e-9, copy_s) / 1e9,
+        "link_gbps_wall": st["bytes_fetched"] / wall / 1e9}
+
+
 def run_offload(args):
     """256 decode steps through 8 layers whose experts live in pinned host memory (HBM cache)."""
     import torch
@@ -441,46 +617,8 @@ def run_offload(args):
         if T == Ts[0]:  # the reported policy without the FFN/copy overlap
             variants.append((*POLICIES[-1], False, None, None))
         for policy, period, overlap, pf, pin in variants:
-            model.reset_cache(policy, period, overlap, prefetch=pf, pins=pin)
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            for s in range(steps):
-                for l in range(wl.layers):
-                    model.layer_forward(l, s, xs[(l, s)], out, time_copies=True)
-            torch.cuda.synchronize()
-            wall = time.perf_counter() - t0
-            copy_s = model.copy_seconds()
-            st = model.cache.stats()
-            plans = model.plans
-            seen, cold = set(), 0
-            per_epoch = {}
-            for (s, l, n, h, m) in plans:
-                ep = s // wl.rerank_every
-                a = per_epoch.setdefault(ep, [0, 0])
-                a[0] += h
-                a[1] += n
-            # compulsory misses: first lookup of each (layer, expert) key
-            for (s, l, n, h, m), grp in zip(plans, model.groups):
-                for key in grp:
-                    if key not in seen:
-                        seen.add(key)
-                        cold += 1
-            name = policy if policy == "lru" else "%s/%d" % (policy, period)
-            if pin is not None:
-                name = "static-pin(%d/layer)+%s" % (len(pin[0]), name)
-            runs[(T, name, overlap, pf)] = {
-                "T": T, "policy": name, "prefetch": pf or "none", "steps": steps,
-                "ffn_of_hits_during_copies": overlap,
-                "layers": wl.layers, "wall_s": wall, "tokens_per_s": T * steps / wall,
-                "hit_rate": st["hits"] / max(1, st["lookups"]),
-                "hit_rate_cold_excluded": st["hits"] / max(1, st["lookups"] - cold),
-                "hit_rate_per_epoch": [round(v[0] / max(1, v[1]), 4) for _, v in sorted(per_epoch.items())],
-                "hit_rate_belady": belady.setdefault(T, belady_hits(model.capacity, model.groups)) / max(1, st["lookups"]),
-                "lookups": st["lookups"], "misses": st["misses"], "bytes_fetched": st["bytes_fetched"],
-                "prefetch_fetches": st["prefetch_fetches"], "prefetch_hits": st["prefetch_hits"],
-                "copy_busy_s": copy_s,
-                "link_gbps_busy": st["bytes_fetched"] / max(1e-9, copy_s) / 1e9,
-                "link_gbps_wall": st["bytes_fetched"] / wall / 1e9}
+            r = offload_variant(model, wl, T, steps, xs, out, policy, period, overlap, pf, pin, belady)
+            runs[(T, r["policy"], overlap, pf)] = r
     head = max((r for r in runs.values() if r["T"] == Ts[0] and r["ffn_of_hits_during_copies"]),
                key=lambda r: r["tokens_per_s"])
     out = {
@@ -626,7 +764,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="mixtral", choices=["mixtral", "gptoss", "kimi", "glm", "spec"])
+    ap.add_argument("--workload", default="mixtral", choices=["mixtral", "gptoss", "kimi", "glm", "glm-bf16", "spec"])
     ap.add_argument("--offload-steps", type=int, default=256)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="copy 1 GiB device-to-device before measuring (profiler byte-counter calibration)")
@@ -667,7 +805,10 @@ def main():
     if args.workload == "spec":
         print(json.dumps(run_spec(args)), flush=True)
         return
-    out = run_offload(args) if args.workload in OFFLOAD else run(args)
+    if args.workload == "glm-bf16":
+        out = run_offload_compressed(args)
+    else:
+        out = run_offload(args) if args.workload in OFFLOAD else run(args)
     if args.workload == "mixtral" and args.prefill:
         out["prefill"] = prefill_leg(args)
     print(json.dumps(out), flush=True)

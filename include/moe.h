@@ -133,6 +133,28 @@ size_t moe_permute_workspace(int T, int k, int E);
 int moe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t* counts, int32_t* offsets, int32_t* perm_src,
                 int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream);
 
+/* --------------------------------------------------- router + permutation */
+
+/*
+ * moe_route followed by moe_permute on its ids, in one call: the same outputs, bit for bit, as
+ * those two calls (arguments as there).  Decode batches in bf16 (T <= 64, T*k <= 1024, T*E <= 2^20,
+ * H a multiple of 32) take two launches instead of three: the router's partial logits, then one
+ * workgroup that sums them, selects the top k of every token and groups the pairs.  Other
+ * batches run the two calls' kernels one after the other.  (The routing and grouping steps are
+ * those of "Mixture of experts VRAM: total vs active parameters", section "How current MoE models
+ * route each token", and of "Understanding MoE Inference Costs on Galactus", section "Prompt
+ * processing is a different phase".)
+ *   ws  device workspace of ws_bytes >= moe_route_permute_workspace(T, H, E, k, xdt) bytes
+ * Errors: those of moe_route and moe_permute; MOE_ERR_WORKSPACE if the workspace is too small.
+ */
+int moe_route_permute(const void* x, int xdt, int T, int H, const void* w_router, const float* bias, int E, int k,
+                      int32_t* topk_ids, float* topk_w, float* logits, int32_t* counts, int32_t* offsets,
+                      int32_t* perm_src, int32_t* inv_perm, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes moe_route_permute needs (device, 256-byte aligned): the router's partial logits
+ * on the fused path, else moe_route_workspace and moe_permute_workspace, each rounded up to 256. */
+size_t moe_route_permute_workspace(int T, int H, int E, int k, int xdt);
+
 /* ------------------------------------------------------- expert weight packages */
 
 /*
@@ -166,6 +188,57 @@ int moe_pack_expert(int H, int I, int fmt, const void* gate, const void* gate_sc
  * out = [gate I*H][up I*H][down H*I] (device, 3*H*I floats).  Every value is exact.
  */
 int moe_dequant_expert(const void* package, int H, int I, int fmt, float* out, void* stream);
+
+/* ------------------------------------------------- lossless package compression */
+
+/*
+ * A tier of losslessly compressed experts in GPU memory and in host memory ("What expert
+ * offloading actually costs", section "Inside expert paging": compressed GPU memory beside host
+ * DRAM, lossless so that no output bit changes).  The pages name no codec; this one is an
+ * exponent-window code for bf16 packages, decoded on the GPU into a plain package that the FFN
+ * kernels read as usual:
+ *  - the package is read as little-endian bf16 values in chunks of 512 (1024 bytes; the package
+ *    size must be a multiple of 1024, as every bf16 package is);
+ *  - per chunk, M = the largest exponent field, window base b = max(M - 14, 0); a value whose
+ *    exponent e lies in [b, b + 14] gets the 4-bit code e - b + 1, any other value the code 0
+ *    and an escape byte holding e;
+ *  - a coded chunk is 512 bytes (sign << 7 | 7-bit mantissa, value order), 256 bytes of codes
+ *    (value 2t in the low nibble of byte t, value 2t+1 in the high one), the escape bytes in
+ *    value order, zeros to a multiple of 16: 768 + 16 ceil(escapes / 16) bytes; a chunk for which
+ *    that is 1024 or more is stored raw;
+ *  - the blob: a 64-byte header (u32 magic 0x31345758, u32 chunk count n, u64 package bytes,
+ *    u64 data offset, u64 blob bytes, zeros), u32 chunk offsets off[0..n] relative to the data
+ *    offset, u8 window bases (0 for raw chunks), zeros up to the data offset (the first multiple
+ *    of 256 past the tables), then the chunks back to back; a chunk of off[i+1] - off[i] = 1024
+ *    bytes is raw.
+ * bf16 weights around zero compress to about 75% (12 bits per value); 4-bit packages are already
+ * within a few percent of their codes' entropy and are not compressed.
+ */
+
+/* Largest blob for a package of raw_bytes bytes (0 if raw_bytes is not a multiple of 1024). */
+size_t moe_compress_bound(size_t raw_bytes);
+
+/*
+ * Host, offline: encode one package.
+ *   raw   host, raw_bytes (a multiple of 1024, below 4 GiB)
+ *   blob  host, cap >= moe_compress_bound(raw_bytes) bytes (out); *blob_bytes = its size (out)
+ * Errors: MOE_ERR_INVALID (size, null pointers, small cap).
+ */
+int moe_compress_package(const void* raw, size_t raw_bytes, void* blob, size_t cap, size_t* blob_bytes);
+
+/*
+ * Decode n blobs into packages on the device, in one launch:
+ *   src_base   device, blob j at src_base + pairs[2j] * src_stride (src_stride a multiple of 256)
+ *   dst_base   device, its package at dst_base + pairs[2j+1] * dst_stride (dst_stride a multiple
+ *              of 16, >= raw_bytes)
+ *   pairs      device [n][2] int32 {source slot, destination slot}; a pair with a negative slot
+ *              is skipped (so one slot table can serve several passes)
+ *   raw_bytes  every package's size (a multiple of 1024)
+ * The blobs must come from moe_compress_package (the decoder trusts their tables).
+ * Errors: MOE_ERR_INVALID (sizes, strides, n out of 0..65535, null pointers when n > 0).
+ */
+int moe_decompress_packages(const void* src_base, size_t src_stride, void* dst_base, size_t dst_stride,
+                            const int32_t* pairs, int n, size_t raw_bytes, void* stream);
 
 /* --------------------------------------------------------------- expert FFN */
 

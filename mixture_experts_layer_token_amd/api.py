@@ -78,6 +78,24 @@ def moe_permute(topk_ids, E, counts, offsets, perm_src, inv_perm, ws=None, strea
                             _dp(ws), 0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
 
 
+def moe_route_permute_workspace(T, H, E, k, xdt) -> int:
+    return int(lib().moe_route_permute_workspace(T, H, E, k, DT[xdt]))
+
+
+def moe_route_permute(x, w_router, bias, k, topk_ids, topk_w, counts, offsets, perm_src, inv_perm, logits=None,
+                      ws=None, stream=None):
+    """moe_route then moe_permute in one call.  `ws`: device workspace of at least
+    moe_route_permute_workspace bytes (allocated here if None)."""
+    T, H = x.shape
+    E = w_router.shape[0]
+    if ws is None:
+        need = moe_route_permute_workspace(T, H, E, k, "bf16" if x.dtype == torch.bfloat16 else "f32")
+        ws = torch.empty(need, dtype=torch.uint8, device=x.device) if need else None
+    check(lib().moe_route_permute(_dp(x), _dt(x), T, H, _dp(w_router), _dp(bias), E, k, _dp(topk_ids), _dp(topk_w),
+                                  _dp(logits), _dp(counts), _dp(offsets), _dp(perm_src), _dp(inv_perm), _dp(ws),
+                                  0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
 def moe_package_bytes(H, I, fmt) -> int:
     return int(lib().moe_package_bytes(H, I, FMT[fmt]))
 
@@ -91,6 +109,29 @@ def moe_pack_expert(H, I, fmt, ex: dict, out: np.ndarray | None = None) -> np.nd
     check(lib().moe_pack_expert(H, I, FMT[fmt], _hp(w[0]), _hp(s[0]), _hp(w[1]), _hp(s[1]), _hp(w[2]), _hp(s[2]),
                                 _hp(out), out.nbytes))
     return out
+
+
+def moe_compress_bound(raw_bytes: int) -> int:
+    return int(lib().moe_compress_bound(raw_bytes))
+
+
+def moe_compress_package(raw: np.ndarray, out: np.ndarray | None = None) -> np.ndarray:
+    """Lossless exponent-window code of one bf16 package (host bytes) -> its blob (a view of `out`)."""
+    raw = np.ascontiguousarray(raw).view(np.uint8).ravel()
+    cap = moe_compress_bound(raw.size)
+    if out is None:
+        out = np.empty(max(cap, 1), dtype=np.uint8)
+    n = ctypes.c_size_t(0)
+    check(lib().moe_compress_package(_hp(raw), raw.size, _hp(out), out.nbytes, ctypes.byref(n)))
+    return out[:n.value]
+
+
+def moe_decompress_packages(src, src_stride, dst, dst_stride, pairs, raw_bytes, n=None, stream=None):
+    """Decode blobs into packages on the device: `pairs` is a device int32 [n, 2] tensor of
+    (source slot, destination slot); `src` and `dst` are device tensors holding the slots."""
+    n = pairs.shape[0] if n is None else n
+    check(lib().moe_decompress_packages(_dp(src), src_stride, _dp(dst), dst_stride, _dp(pairs), n, raw_bytes,
+                                        _stream(stream)))
 
 
 def moe_dequant_expert(package, H, I, fmt, out, stream=None):

@@ -62,6 +62,27 @@ extern "C" int moe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t
   return launch_permute(topk_ids, T, k, E, counts, offsets, perm_src, inv_perm, ws, ws_bytes, (hipStream_t)stream);
 }
 
+extern "C" size_t moe_route_permute_workspace(int T, int H, int E, int k, int xdt) {
+  if (T < 0 || H <= 0 || E < 1 || E > 1024 || k < 1 || !dtype_valid(xdt)) return 0;
+  return route_permute_workspace(T, H, E, k, xdt);
+}
+
+extern "C" int moe_route_permute(const void* x, int xdt, int T, int H, const void* w_router, const float* bias, int E,
+                                 int k, int32_t* topk_ids, float* topk_w, float* logits, int32_t* counts,
+                                 int32_t* offsets, int32_t* perm_src, int32_t* inv_perm, void* ws, size_t ws_bytes,
+                                 void* stream) {
+  if (!dtype_valid(xdt)) return fail(MOE_ERR_INVALID, "moe_route_permute: bad dtype %d", xdt);
+  if (T < 0 || H <= 0) return fail(MOE_ERR_INVALID, "moe_route_permute: T=%d H=%d", T, H);
+  if (E < 1 || E > 1024) return fail(MOE_ERR_INVALID, "moe_route_permute: E=%d out of 1..1024", E);
+  if (k < 1 || k > E || k > 16) return fail(MOE_ERR_INVALID, "moe_route_permute: k=%d out of 1..min(E,16)", k);
+  if ((long long)T * k > (1LL << 24)) return fail(MOE_ERR_INVALID, "moe_route_permute: T*k too large");
+  if (!counts || !offsets) return fail(MOE_ERR_INVALID, "moe_route_permute: null counts/offsets");
+  if (T > 0 && (!x || !w_router || !topk_ids || !topk_w || !perm_src || !inv_perm))
+    return fail(MOE_ERR_INVALID, "moe_route_permute: null pointer");
+  return launch_route_permute(x, xdt, T, H, w_router, bias, E, k, topk_ids, topk_w, logits, counts, offsets, perm_src,
+                              inv_perm, ws, ws_bytes, (hipStream_t)stream);
+}
+
 extern "C" size_t moe_ffn_workspace(const moe_experts* w, int T, int k, int mode) {
   if (check_experts(w, "moe_ffn_workspace") != MOE_OK || T < 0 || k < 1) return 0;
   return ffn_workspace(w, T, k, mode);

@@ -94,6 +94,12 @@ bool dtype_valid(int dt);
 size_t route_workspace(int T, int H, int E, int xdt);
 int launch_route(const void* x, int xdt, int T, int H, const void* wg, const float* bias, int E, int k, int32_t* ids,
                  float* w, float* logits, void* ws, size_t ws_bytes, hipStream_t s);
+bool route_split_path(int T, int H, int E, int xdt);
+int route_split_partials(const void* x, int T, int H, const void* wg, int E, float* part, int* ks_out, hipStream_t s);
+size_t route_permute_workspace(int T, int H, int E, int k, int xdt);
+int launch_route_permute(const void* x, int xdt, int T, int H, const void* wg, const float* bias, int E, int k,
+                         int32_t* ids, float* w, float* logits, int32_t* counts, int32_t* offsets, int32_t* perm,
+                         int32_t* inv, void* ws, size_t ws_bytes, hipStream_t s);
 size_t permute_workspace(int T, int k, int E);
 int launch_permute(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_t* offsets, int32_t* perm,
                    int32_t* inv, void* ws, size_t ws_bytes, hipStream_t s);

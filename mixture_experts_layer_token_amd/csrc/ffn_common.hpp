@@ -47,9 +47,10 @@ __device__ __forceinline__ unsigned in_vgpr(unsigned c) {
   return r;
 }
 
-// 8 INT4 elements (nibble n < 4: element 2n, n >= 4: element 2(n-4)+1, stored as q + 8) -> fp16 q*s:
-// the nibble pair becomes 1024 + c in each fp16 half (c = q + 8), minus 1032 gives q, times s;
-// every step is exact in fp16 for s in binary16's normal range.
+// 8 INT4 elements (nibble n < 4: element 2n, n >= 4: element 2(n-4)+1, stored as q + 8) -> fp16 q*s,
+// by the usual "magic number" integer-to-float conversion: fp16 0x6400 is 1024, whose unit in the
+// last place is 1, so OR-ing c = q + 8 into its low mantissa bits gives exactly 1024 + c in each
+// half; minus 1032 gives q, times s; every step is exact in fp16 for s in binary16's normal range.
 __device__ __forceinline__ f16x8 dec_int4(unsigned v, _Float16 s) {
   const f16x2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
   const f16x2 ss = {s, s};

@@ -13,7 +13,11 @@
 // its experts, (2) one workgroup scans the counts per expert over blocks and over experts (the
 // offsets, and each block's starting cursor per expert), (3) every block scatters its indices
 // in order from those cursors with the same in-block ranking.  Same result, block-parallel.
+// Decode batches routed and grouped in one call (moe_route_permute): after the router's partial
+// logits, a single workgroup sums them, selects every token's top k (16 tokens at a time, one per
+// wave) and groups the pairs from an LDS copy of the ids: one launch and one dependent step less.
 #include "common.hpp"
+#include "topk.hpp"
 
 namespace moe {
 namespace {
@@ -21,15 +25,14 @@ namespace {
 constexpr int kPermThreads = 1024;
 constexpr int kBlk = 2048;         // flat indices per block (multi-block path)
 constexpr int kSingleMax = 8192;   // largest T*k done by the single workgroup
+constexpr int kFusedMaxT = 64;     // largest batch routed and grouped by one workgroup (route_permute)
 
-__device__ void scatter_range(const int32_t* __restrict__ ids, int i0, int i1, int E, int* cursor,
-                              int32_t* __restrict__ perm, int32_t* __restrict__ inv);
+__device__ void scatter_range(const int32_t* ids, int i0, int i1, int E, int* cursor, int32_t* __restrict__ perm,
+                              int32_t* __restrict__ inv);
 
-__global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t* __restrict__ ids, int n, int E,
-                                                               int32_t* __restrict__ counts,
-                                                               int32_t* __restrict__ offsets,
-                                                               int32_t* __restrict__ perm,
-                                                               int32_t* __restrict__ inv) {
+// The whole grouping by one workgroup of kPermThreads threads (ids may be in LDS or global memory).
+__device__ void group_pairs(const int32_t* ids, int n, int E, int32_t* __restrict__ counts,
+                            int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
   __shared__ int cnt[1024];
   __shared__ int cursor[1024];
   __shared__ int wsum[16];
@@ -72,8 +75,44 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t* __
   scatter_range(ids, 0, n, E, cursor, perm, inv);
 }
 
+__global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t* __restrict__ ids, int n, int E,
+                                                               int32_t* __restrict__ counts,
+                                                               int32_t* __restrict__ offsets,
+                                                               int32_t* __restrict__ perm,
+                                                               int32_t* __restrict__ inv) {
+  group_pairs(ids, n, E, counts, offsets, perm, inv);
+}
+
+// Decode-sized batches (T <= kFusedMaxT), router and grouping in one workgroup after the router's
+// partial logits (route_split_partials): each of the 16 waves sums the K ranges of a token's logits in
+// range order, adds the bias and selects its top k (as route_topk_kernel does), keeping the ids in
+// LDS as well; then the workgroup groups the pairs as permute_kernel does.
+__global__ __launch_bounds__(kPermThreads) void topk_permute_kernel(
+    const float* __restrict__ part, const float* __restrict__ bias, int T, int E, int KS, int k,
+    int32_t* __restrict__ ids, float* __restrict__ w, float* __restrict__ logits, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+  extern __shared__ float lg_all[];  // [16][E] logit rows, then [T * k] ids
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int32_t* ids_lds = (int32_t*)(lg_all + 16 * E);
+  float* lg = lg_all + (size_t)wave * E;
+  for (int t = wave; t < T; t += kPermThreads / 64) {
+    for (int e = lane; e < E; e += 64) {
+      const float v = split_logit(part, bias, T, E, KS, t, e);
+      lg[e] = v;
+      if (logits) logits[(size_t)t * E + e] = v;
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    wave_topk(lg, E, k, ids + (size_t)t * k, w + (size_t)t * k, ids_lds + t * k);
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  }
+  __syncthreads();
+  group_pairs(ids_lds, T * k, E, counts, offsets, perm, inv);
+}
+
 // Stable scatter of flat indices [i0, i1) (1024 threads), cursor[e] = next position of expert e.
-__device__ void scatter_range(const int32_t* __restrict__ ids, int i0, int i1, int E, int* cursor,
+__device__ void scatter_range(const int32_t* ids, int i0, int i1, int E, int* cursor,
                               int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int nbits = 0;
@@ -95,7 +134,9 @@ __device__ void scatter_range(const int32_t* __restrict__ ids, int i0, int i1, i
     const int rank = __popcll(peers & below);
     const int total = __popcll(peers);
     if (valid && e < 0) inv[i] = -1;  // a dropped pair: its combine term is skipped
-    for (int w = 0; w < 16; ++w) {
+    // only the waves that hold pairs of this chunk take a turn (decode batches: one or a few)
+    const int turns = min(kPermThreads / 64, (i1 - c0 + 63) / 64);
+    for (int w = 0; w < turns; ++w) {
       if (wave == w && e >= 0) {
         // every lane of the wave reads cursor[e] (one LDS instruction) before the last peer
         // advances it (a later instruction of the same wave)
@@ -181,6 +222,50 @@ size_t permute_workspace(int T, int k, int E) {
   if (n <= kSingleMax) return 0;
   const long long B = (n + kBlk - 1) / kBlk;
   return (size_t)(2 * B * E) * sizeof(int32_t);  // bcnt and bbase
+}
+
+bool route_permute_fused(int T, int H, int E, int k, int xdt) {
+  return T <= kFusedMaxT && (long long)T * k <= 1024 && route_split_path(T, H, E, xdt);
+}
+
+size_t route_permute_workspace(int T, int H, int E, int k, int xdt) {
+  auto al = [](size_t b) { return (b + 255) & ~(size_t)255; };
+  if (route_permute_fused(T, H, E, k, xdt)) return al(route_workspace(T, H, E, xdt));
+  return al(route_workspace(T, H, E, xdt)) + al(permute_workspace(T, k, E));
+}
+
+int launch_route_permute(const void* x, int xdt, int T, int H, const void* wg, const float* bias, int E, int k,
+                         int32_t* ids, float* w, float* logits, int32_t* counts, int32_t* offsets, int32_t* perm,
+                         int32_t* inv, void* ws, size_t ws_bytes, hipStream_t s) {
+  const size_t need = route_permute_workspace(T, H, E, k, xdt);
+  if (ws_bytes < need || (need && !ws))
+    return fail(MOE_ERR_WORKSPACE, "moe_route_permute: workspace %zu < %zu", ws_bytes, need);
+  if (E > 1024) return fail(MOE_ERR_INVALID, "moe_route_permute: E=%d exceeds 1024", E);
+  if (!route_permute_fused(T, H, E, k, xdt)) {
+    const size_t rws = (route_workspace(T, H, E, xdt) + 255) & ~(size_t)255;
+    int rc = launch_route(x, xdt, T, H, wg, bias, E, k, ids, w, logits, ws, rws, s);
+    if (rc != MOE_OK) return rc;
+    return launch_permute(ids, T, k, E, counts, offsets, perm, inv, (char*)ws + rws, ws_bytes - rws, s);
+  }
+  if (T == 0) return launch_permute(ids, T, k, E, counts, offsets, perm, inv, nullptr, 0, s);
+  int KS = 0;
+  int rc = route_split_partials(x, T, H, wg, E, (float*)ws, &KS, s);
+  if (rc != MOE_OK) return rc;
+  // 16 logit rows of E <= 1024 floats and T*k <= 1024 ids: at most 68 KiB of dynamic LDS
+  const size_t lds = (size_t)16 * E * sizeof(float) + (size_t)T * k * sizeof(int32_t);
+  static bool attr_set[64];  // per device
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (!attr_set[dev]) {
+    hipError_t e = hipFuncSetAttribute((const void*)topk_permute_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       16 * 1024 * (int)sizeof(float) + 1024 * (int)sizeof(int32_t));
+    if (e != hipSuccess) return hip_fail(e, "moe_route_permute: LDS attribute");
+    attr_set[dev] = true;
+  }
+  hipLaunchKernelGGL(topk_permute_kernel, dim3(1), dim3(kPermThreads), lds, s, (const float*)ws, bias, T, E, KS, k,
+                     ids, w, logits, counts, offsets, perm, inv);
+  MOE_CHECK_LAUNCH("moe_route_permute launch");
+  return MOE_OK;
 }
 
 int launch_permute(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_t* offsets, int32_t* perm,

@@ -11,6 +11,7 @@
 #include <math.h>
 
 #include "ffn_common.hpp"
+#include "topk.hpp"
 
 namespace moe {
 namespace {
@@ -22,63 +23,6 @@ constexpr int kMaxE = 1024;
 // each workgroup re-reads its 16 rows of x and of Wg from L2, which is cheap until the product
 // is large; larger batches use the MFMA tile kernel (one read per 192 x 256 tile).
 constexpr long long kSplitMaxTE = 1 << 20;
-
-// The selection compares unsigned keys that order the logits totally: a larger logit has a larger
-// key (-0 counts as +0), every NaN has key 1, below -inf, and a chosen entry has key 0, below
-// everything.  So a token whose logits hold NaN or infinities still gets k distinct ids in [0, E)
-// (finite and infinite logits first, NaN ones last, equal keys -> lower id), and only its own gate
-// weights carry the NaN.
-__device__ __forceinline__ unsigned logit_key(float v) {
-  if (v != v) return 1u;
-  unsigned u = __float_as_uint(v);
-  if (u == 0x80000000u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float key_logit(unsigned key) {
-  if (key == 1u) return __uint_as_float(0x7FC00000u);
-  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
-}
-
-// top-k of one token's E logits in LDS row `lg`; executed by one full wave.  The row is turned into
-// keys in place (logit_key), chosen entries get key 0.  Lane j keeps the j-th choice and writes
-// ids[j], w[j].
-__device__ void wave_topk(float* lg, int E, int k, int32_t* ids, float* w) {
-  const int lane = threadIdx.x & 63;
-  unsigned* key = (unsigned*)lg;
-  for (int e = lane; e < E; e += 64) key[e] = logit_key(lg[e]);
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  unsigned my_key = 0;
-  int my_e = 0;
-  for (int j = 0; j < k; ++j) {
-    // (key, E - 1 - id) as one 64-bit value: its maximum is the largest key, then the lowest id;
-    // an unchosen entry (key >= 1) always exists because k <= E
-    unsigned long long best = 0;
-    for (int e = lane; e < E; e += 64) {
-      const unsigned long long c = ((unsigned long long)key[e] << 32) | (unsigned)(E - 1 - e);
-      best = c > best ? c : best;
-    }
-    for (int off = 32; off > 0; off >>= 1) {
-      const unsigned long long o = __shfl_xor(best, off, 64);
-      best = o > best ? o : best;
-    }
-    const int be = E - 1 - (int)(unsigned)(best & 0xFFFFFFFFull);
-    if (lane == j) my_key = (unsigned)(best >> 32), my_e = be;
-    if (lane == 0) key[be] = 0u;
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  }
-  const float my_v = key_logit(my_key);
-  // softmax over the k chosen logits (max = the first choice)
-  const float v0 = __shfl(my_v, 0, 64);
-  float p = lane < k ? expf(my_v - v0) : 0.f;
-  float z = p;
-  for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off, 64);
-  if (lane < k) {
-    ids[lane] = my_e;
-    w[lane] = p / z;
-  }
-}
 
 // 8 waves: G groups of expert tiles x R ranges of H (G * R = 8).  Few experts (decode shapes):
 // all waves split H, so every wave has a short run of loads in flight; many experts: waves split
@@ -217,21 +161,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
   if (t >= T) return;  // whole wave; no block barrier below
   float* lg = lds + (size_t)wave * E;
   for (int e = lane; e < E; e += 64) {
-    // the ranges' partials are loaded 16 at a time (independent loads in flight together), then
-    // summed in range order
-    float v = 0.f;
-    for (int r0 = 0; r0 < KS; r0 += 16) {
-      float pv[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = r0 + i < KS ? r0 + i : r0;
-        pv[i] = part[((size_t)r * T + t) * E + e];
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (r0 + i < KS) v = (r0 + i == 0) ? pv[i] : v + pv[i];
-    }
-    v += bias ? bias[e] : 0.f;
+    const float v = split_logit(part, bias, T, E, KS, t, e);
     lg[e] = v;
     if (logits) logits[(size_t)t * E + e] = v;
   }
@@ -331,6 +261,15 @@ size_t route_workspace(int T, int H, int E, int xdt) {
   return (size_t)route_split_ranges(T, H, E) * T * E * sizeof(float);
 }
 
+int route_split_partials(const void* x, int T, int H, const void* wg, int E, float* part, int* ks_out, hipStream_t s) {
+  const int KS = route_split_ranges(T, H, E);
+  *ks_out = KS;
+  hipLaunchKernelGGL(route_partial_kernel, dim3((E + 15) / 16, KS, (T + 15) / 16), dim3(256), 0, s,
+                     (const unsigned short*)x, (const unsigned short*)wg, T, H, E, KS, part);
+  MOE_CHECK_LAUNCH("moe_route launch");
+  return MOE_OK;
+}
+
 int launch_route(const void* x, int xdt, int T, int H, const void* wg, const float* bias, int E, int k, int32_t* ids,
                  float* w, float* logits, void* ws, size_t ws_bytes, hipStream_t s) {
   if (T == 0) return MOE_OK;
@@ -380,9 +319,9 @@ int launch_route(const void* x, int xdt, int T, int H, const void* wg, const flo
   if (route_split_path(T, H, E, xdt)) {
     const size_t need = route_workspace(T, H, E, xdt);
     if (!ws || ws_bytes < need) return fail(MOE_ERR_WORKSPACE, "moe_route: workspace %zu < %zu", ws_bytes, need);
-    const int KS = route_split_ranges(T, H, E);
-    hipLaunchKernelGGL(route_partial_kernel, dim3((E + 15) / 16, KS, (T + 15) / 16), dim3(256), 0, s,
-                       (const unsigned short*)x, (const unsigned short*)wg, T, H, E, KS, (float*)ws);
+    int KS = 0;
+    int rc = route_split_partials(x, T, H, wg, E, (float*)ws, &KS, s);
+    if (rc != MOE_OK) return rc;
     hipLaunchKernelGGL(route_topk_kernel, dim3((T + 3) / 4), dim3(256), (size_t)4 * E * sizeof(float), s,
                        (const float*)ws, bias, T, E, KS, k, ids, w, logits);
     MOE_CHECK_LAUNCH("moe_route launch");

@@ -64,10 +64,8 @@ class MoeLayer:
             self.sh_perm = torch.arange(T, **i32)
             self.sh_y = torch.empty((T, H), dtype=torch.float32, device=d)
         self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=d)
-        pws = api.moe_permute_workspace(T, k, E)
-        self.pws = torch.empty(pws, dtype=torch.uint8, device=d) if pws else None
-        # every batch size up to T may be routed with this buffer
-        rws = max(api.moe_route_workspace(t, H, E, self.xdt) for t in range(1, T + 1))
+        # every batch size up to T may be routed and grouped with this buffer
+        rws = max(api.moe_route_permute_workspace(t, H, E, k, self.xdt) for t in range(1, T + 1))
         self.rws = torch.empty(max(rws, 256), dtype=torch.uint8, device=d)
 
     def forward(self, x: torch.Tensor, out: torch.Tensor | None = None, mode="auto", trace=None) -> torch.Tensor:
@@ -80,9 +78,8 @@ class MoeLayer:
         if out is None:
             out = torch.empty((T, self.H), dtype=x.dtype, device=x.device)
         ids, w = self.topk_ids[:T], self.topk_w[:T]
-        api.moe_route(x, self.w_router, self.bias, k, ids, w, ws=self.rws)
-        api.moe_permute(ids, self.E, self.counts, self.offsets, self.perm_src[:T * k], self.inv_perm[:T * k],
-                        self.pws)
+        api.moe_route_permute(x, self.w_router, self.bias, k, ids, w, self.counts, self.offsets, self.perm_src[:T * k],
+                              self.inv_perm[:T * k], ws=self.rws)
         if trace is not None:
             api.lib().moe_ffn_trace_events(trace)
         try:

@@ -24,6 +24,14 @@ Layers run strictly in order.  A slot evicted by a plan is never in use: the
 host waits for the router of the layer being planned, and every earlier FFN
 precedes that router on the compute stream; a prefetch never evicts the
 experts of the layer just planned, whose FFN may still be running.
+
+With `compressed=True` (bf16 experts) both tiers hold losslessly compressed
+packages (the same page: compressed GPU memory beside host DRAM): the bank and
+the HBM slots hold exponent-window blobs, so a miss moves about 3/4 of the
+bytes and the same HBM holds more experts; before each FFN pass the pass's
+experts are decoded on the compute stream into a working pool of plain
+packages (one slot per distinct expert a layer can touch, shared by all
+layers), which the FFN reads as usual.
 """
 from __future__ import annotations
 
@@ -70,15 +78,26 @@ class OffloadedModel:
     """L MoE layers whose experts live in a pinned host bank, cached in an HBM slot pool."""
 
     def __init__(self, wl, max_T: int, capacity: int | None = None, device="cuda", fill=True, policy="lru",
-                 decay_period=0, overlap=True, prefetch=None):
+                 decay_period=0, overlap=True, prefetch=None, compressed=False, blob_bytes=None):
+        """`compressed`: bank and HBM slots hold blobs of `blob_bytes` bytes (a multiple of 256 that
+        every expert's blob must fit; bf16 experts only)."""
         from synth import workloads as W
 
         self.wl = wl
         self.L, self.E, self.H, self.I, self.k = wl.layers, wl.E, wl.H, wl.I, wl.k
-        self.pkg_bytes = api.moe_package_bytes(wl.H, wl.I, wl.wfmt)
+        self.raw_bytes = api.moe_package_bytes(wl.H, wl.I, wl.wfmt)
+        self.raw_stride = (self.raw_bytes + 255) // 256 * 256
+        self.compressed = compressed
+        if compressed:
+            if wl.wfmt != "bf16" or not blob_bytes or blob_bytes % 256:
+                raise ValueError("compressed banks hold bf16 experts in blob slots of a multiple of 256 bytes")
+            self.pkg_bytes = blob_bytes  # what a miss copies: one blob slot
+        else:
+            self.pkg_bytes = self.raw_bytes
         self.stride = (self.pkg_bytes + 255) // 256 * 256
         self.capacity = capacity or int(wl.cache_frac * wl.layers * wl.E)
         self.bank = PinnedBuffer(self.L * self.E * self.pkg_bytes)
+        self.blob_sizes = np.zeros((self.L, self.E), np.int64)
         if fill:
             for l in range(self.L):
                 self.fill(l, list(range(self.E)))
@@ -94,14 +113,30 @@ class OffloadedModel:
         i32 = dict(dtype=torch.int32)
         self.pass_dev = [[torch.full((self.E,), -1, device=device, **i32) for _ in range(2)] for _ in range(self.L)]
         self.pass_host = [[torch.full((self.E,), -1, pin_memory=True, **i32) for _ in range(2)] for _ in range(self.L)]
-        self.pass_desc = [[api.experts_desc(wl.H, wl.I, wl.E, wl.wfmt, self.pool, self.stride, t, self.capacity)
-                           for t in pd] for pd in self.pass_dev]
+        if compressed:
+            # decoded working pool: one plain package per distinct expert a layer step can touch; the
+            # FFN passes address it through the tables in pass_dev, the decoder through pair lists
+            self.n_work = min(self.E, max_T * self.k)
+            self.work = torch.empty((self.n_work, self.raw_stride), dtype=torch.uint8, device=device)
+            self.pair_dev = [[torch.full((self.E, 2), -1, device=device, **i32) for _ in range(2)]
+                             for _ in range(self.L)]
+            self.pair_host = [[torch.full((self.E, 2), -1, pin_memory=True, **i32) for _ in range(2)]
+                              for _ in range(self.L)]
+            self.pass_desc = [[api.experts_desc(wl.H, wl.I, wl.E, wl.wfmt, self.work, self.raw_stride, t, self.n_work)
+                               for t in pd] for pd in self.pass_dev]
+        else:
+            self.pass_desc = [[api.experts_desc(wl.H, wl.I, wl.E, wl.wfmt, self.pool, self.stride, t, self.capacity)
+                               for t in pd] for pd in self.pass_dev]
         self.wg = [to_device_act(W.router_weights(wl, l), wl.xdt, device) for l in range(self.L)]
         self.bias_cache = {}
         self.layers = []
         for l in range(self.L):
-            lay = MoeLayer(wl.H, wl.I, wl.E, wl.k, wl.wfmt, wl.xdt, self.wg[l], None, self.pool, self.stride,
-                           max_T=max_T, slot_of_expert=self.slot_tables[l], device=device)
+            if compressed:  # the FFN reads the working pool through the pass tables
+                lay = MoeLayer(wl.H, wl.I, wl.E, wl.k, wl.wfmt, wl.xdt, self.wg[l], None, self.work, self.raw_stride,
+                               max_T=max_T, slot_of_expert=self.pass_dev[l][0], device=device)
+            else:
+                lay = MoeLayer(wl.H, wl.I, wl.E, wl.k, wl.wfmt, wl.xdt, self.wg[l], None, self.pool, self.stride,
+                               max_T=max_T, slot_of_expert=self.slot_tables[l], device=device)
             self.layers.append(lay)
         self.copy_stream = torch.cuda.Stream(device=device)
         self.ids_host = torch.empty((max_T, wl.k), dtype=torch.int32, pin_memory=True)
@@ -129,9 +164,14 @@ class OffloadedModel:
         torch.cuda.synchronize()
         return sum(a.elapsed_time(b) for a, b in self._copy_windows) / 1e3
 
-    def reset_cache(self, policy=None, decay_period=None, overlap=None, prefetch="keep", pins=None):
+    def reset_cache(self, policy=None, decay_period=None, overlap=None, prefetch="keep", pins=None, capacity=None):
         """Empty the HBM cache (a new planner, optionally with another policy, prefetch heuristic and
-        static pin) and the run records.  `pins`: {layer: expert ids} pinned (and fetched) at once."""
+        static pin) and the run records.  `pins`: {layer: expert ids} pinned (and fetched) at once;
+        `capacity`: slots the planner may use (at most the pool's)."""
+        if capacity is not None:
+            if capacity > self.pool.shape[0]:
+                raise ValueError("capacity %d exceeds the pool's %d slots" % (capacity, self.pool.shape[0]))
+            self.capacity = capacity
         if overlap is not None:
             self.overlap = overlap
         if policy is not None:
@@ -166,18 +206,37 @@ class OffloadedModel:
         raise ValueError("prefetch heuristic %r" % (self.prefetch,))
 
     def fill(self, l: int, experts):
-        """Generate and pack experts of layer l into the host bank."""
-        from .layer import pack_bank
+        """Generate and pack experts of layer l into the host bank (compressed: their blobs)."""
+        import concurrent.futures as cf
+
+        from .layer import _workers, pack_bank
 
         experts = sorted(experts)
         for i in range(0, len(experts), 64):
             ids = experts[i:i + 64]
-            host = pack_bank(self.wl, l, ids, stride=self.pkg_bytes)
-            for j, e in enumerate(ids):
+            host = pack_bank(self.wl, l, ids, stride=self.raw_bytes)
+            if not self.compressed:
+                for j, e in enumerate(ids):
+                    o = (l * self.E + e) * self.pkg_bytes
+                    self.bank.array[o:o + self.pkg_bytes] = host[j]
+                continue
+
+            def one(j):
+                e = ids[j]
+                blob = api.moe_compress_package(host[j])
+                if blob.size > self.pkg_bytes:
+                    raise ValueError("layer %d expert %d: blob of %d bytes exceeds the %d-byte slot"
+                                     % (l, e, blob.size, self.pkg_bytes))
                 o = (l * self.E + e) * self.pkg_bytes
-                self.bank.array[o:o + self.pkg_bytes] = host[j]
+                self.bank.array[o:o + blob.size] = blob
+                self.bank.array[o + blob.size:o + self.pkg_bytes] = 0
+                self.blob_sizes[l, e] = blob.size
+
+            with cf.ThreadPoolExecutor(max_workers=_workers()) as pool:
+                list(pool.map(one, range(len(ids))))
 
     def package(self, l: int, e: int) -> np.ndarray:
+        """The bank's bytes of expert e of layer l (compressed: its blob slot)."""
         o = (l * self.E + e) * self.pkg_bytes
         return self.bank.array[o:o + self.pkg_bytes]
 
@@ -198,7 +257,8 @@ class OffloadedModel:
         if out is None:
             out = torch.empty((T, self.H), dtype=x.dtype, device=x.device)
         ids, w = lay.topk_ids[:T], lay.topk_w[:T]
-        api.moe_route(x, self.wg[l], self.bias(l, step), k, ids, w, ws=lay.rws)
+        api.moe_route_permute(x, self.wg[l], self.bias(l, step), k, ids, w, lay.counts, lay.offsets,
+                              lay.perm_src[:T * k], lay.inv_perm[:T * k], ws=lay.rws)
         host_ids = self.ids_host[:T]
         host_ids.copy_(ids, non_blocking=True)
         self.routed.record()
@@ -212,7 +272,9 @@ class OffloadedModel:
         self.prev_ids[l] = distinct
         self.use_counts[l][distinct] += 1
         split = self.overlap and plan.n_hits > 0 and plan.n_misses > 0
-        if split:
+        if self.compressed:
+            n_pairs = self._stage_decode(l, plan, distinct, split)
+        elif split:
             table = np.ctypeslib.as_array(plan.slot_of_expert)[:self.E]
             miss = np.ctypeslib.as_array(plan.miss_ids)[:plan.n_misses]
             hit_t, miss_t = (h.numpy() for h in self.pass_host[l])
@@ -239,18 +301,57 @@ class OffloadedModel:
             t1 = self._timing_event(2 * len(self._copy_windows) + 1)
             t1.record(self.copy_stream)
             self._copy_windows.append((t0, t1))
-        if split:
-            api.moe_permute(ids, self.E, lay.counts, lay.offsets, lay.perm_src[:T * k], lay.inv_perm[:T * k], lay.pws)
+        if self.compressed:
+            # decode each pass's experts into the working pool, then its FFN; the misses' pass after
+            # their copies landed
+            if split:
+                self._decode(l, 0, n_pairs[0])
+                api.moe_expert_ffn(self.pass_desc[l][0], x, k, lay.offsets, lay.perm_src, lay.y_perm, lay.ws)
+                torch.cuda.current_stream().wait_event(self.done)
+                self._decode(l, 1, n_pairs[1])
+                api.moe_expert_ffn(self.pass_desc[l][1], x, k, lay.offsets, lay.perm_src, lay.y_perm, lay.ws)
+            else:
+                torch.cuda.current_stream().wait_event(self.done)
+                self._decode(l, 0, n_pairs[0])
+                api.moe_expert_ffn(self.pass_desc[l][0], x, k, lay.offsets, lay.perm_src, lay.y_perm, lay.ws)
+        elif split:
             api.moe_expert_ffn(self.pass_desc[l][0], x, k, lay.offsets, lay.perm_src, lay.y_perm, lay.ws)
             torch.cuda.current_stream().wait_event(self.done)
             api.moe_expert_ffn(self.pass_desc[l][1], x, k, lay.offsets, lay.perm_src, lay.y_perm, lay.ws)
         else:
             torch.cuda.current_stream().wait_event(self.done)
-            api.moe_permute(ids, self.E, lay.counts, lay.offsets, lay.perm_src[:T * k], lay.inv_perm[:T * k], lay.pws)
             api.moe_expert_ffn(lay.desc, x, k, lay.offsets, lay.perm_src, lay.y_perm, lay.ws)
         api.moe_combine(lay.y_perm, w, lay.inv_perm, k, None, out)
         self.last_plan = plan
         return out
+
+    def _stage_decode(self, l, plan, distinct, split):
+        """Compressed tiers: working-pool slot of each of the layer's experts (its rank among them),
+        the FFN passes' tables over the pool and the decoder's (blob slot, pool slot) pairs; staged
+        through pinned memory to the device on the compute stream.  Returns the pairs per pass."""
+        blob_slot = np.ctypeslib.as_array(plan.slot_of_expert)[:self.E]
+        is_miss = np.zeros(self.E, bool)
+        is_miss[np.ctypeslib.as_array(plan.miss_ids)[:plan.n_misses]] = True
+        passes = ([distinct[~is_miss[distinct]], distinct[is_miss[distinct]]] if split else [distinct, distinct[:0]])
+        rank = np.full(self.E, -1, np.int32)
+        rank[distinct] = np.arange(len(distinct), dtype=np.int32)
+        n_pairs = []
+        for j, ids in enumerate(passes):
+            t = self.pass_host[l][j].numpy()
+            t[:] = -1
+            t[ids] = rank[ids]
+            pr = self.pair_host[l][j].numpy()
+            pr[:len(ids), 0] = blob_slot[ids]
+            pr[:len(ids), 1] = rank[ids]
+            n_pairs.append(len(ids))
+            self.pass_dev[l][j].copy_(self.pass_host[l][j], non_blocking=True)
+            self.pair_dev[l][j].copy_(self.pair_host[l][j], non_blocking=True)
+        return n_pairs
+
+    def _decode(self, l, j, n):
+        if n:
+            api.moe_decompress_packages(self.pool, self.stride, self.work, self.raw_stride, self.pair_dev[l][j],
+                                        self.raw_bytes, n=n)
 
     def close(self):
         self.cache.close()

@@ -55,6 +55,31 @@ def test_permute_workspace_sizes():
     assert moe.api.moe_permute_workspace(1025, 8, 16) == 8 * 5 * 16
 
 
+def test_route_permute_workspace_sizes():
+    al = lambda b: (b + 255) // 256 * 256
+    # decode batches in bf16: only the router's partial logits (the single workgroup needs none)
+    for T, H, E, k in ((1, 2880, 128, 4), (64, 7168, 384, 8), (16, 4096, 8, 2), (3, 64, 24, 2)):
+        assert moe.api.moe_route_permute_workspace(T, H, E, k, "bf16") == al(moe.api.moe_route_workspace(T, H, E, "bf16"))
+    # larger batches (T > 64, or T * k > 1024), fp32, or H not a multiple of 32: route then permute
+    for T, H, E, k, dt in ((65, 2880, 128, 4, "bf16"), (8192, 7168, 384, 8, "bf16"), (64, 4096, 64, 17, "bf16"),
+                           (16, 256, 8, 2, "f32"), (4, 48, 8, 2, "bf16")):
+        want = al(moe.api.moe_route_workspace(T, H, E, dt)) + al(moe.api.moe_permute_workspace(T, k, E))
+        assert moe.api.moe_route_permute_workspace(T, H, E, k, dt) == want, (T, H, E, k, dt)
+    assert moe.api.moe_route_permute_workspace(4, 64, 0, 2, "bf16") == 0
+
+
+def test_route_permute_validation():
+    n = [None] * 8
+    assert L.moe_route_permute(None, 1, 4, 64, None, None, 0, 1, *n, 0, None) == INVALID
+    assert b"E=0" in L.moe_last_error()
+    assert L.moe_route_permute(None, 1, 4, 64, None, None, 8, 9, *n, 0, None) == INVALID  # k > E
+    assert L.moe_route_permute(None, 1, 4, 64, None, None, 64, 17, *n, 0, None) == INVALID  # k > 16
+    assert L.moe_route_permute(None, 7, 4, 64, None, None, 8, 2, *n, 0, None) == INVALID  # dtype
+    assert L.moe_route_permute(None, 1, 4, 64, None, None, 8, 2, *n, 0, None) == INVALID  # null counts
+    assert b"counts" in L.moe_last_error()
+    assert L.moe_route_permute(None, 1, -1, 64, None, None, 8, 2, *n, 0, None) == INVALID
+
+
 def test_permute_and_combine_validation():
     assert L.moe_permute(None, 4, 2, 0, None, None, None, None, None, 0, None) == INVALID
     assert L.moe_permute(None, 4, 0, 8, None, None, None, None, None, 0, None) == INVALID
@@ -356,3 +381,53 @@ def test_fetch_failure_rolls_back_and_refetches():
     for e_ in (2, 5, 6):
         assert table[e_] >= 0 and np.array_equal(pool[table[e_]], bank[e_])
     assert len(set(table[[2, 5, 6]].tolist())) == 3
+
+
+# ---- lossless package compression: the library's host encoder against the oracle's
+
+def _bf16(a):
+    return (np.asarray(a, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("kind", ["gaussian", "bits", "specials", "escapes", "package"])
+def test_compress_package_equals_oracle_blob(kind):
+    rng = np.random.default_rng(3)
+    n = 512 * 40
+    if kind == "gaussian":
+        v = _bf16(rng.normal(0, 0.02, n))
+    elif kind == "bits":
+        v = rng.integers(0, 1 << 16, n, dtype=np.uint16)
+    elif kind == "specials":
+        v = rng.choice(np.array([0, 0x8000, 0x7F80, 0xFF80, 0x7FC1, 0x0001, 0x8080, 0x3F80], np.uint16), n)
+    elif kind == "escapes":  # chunks with 0..300 escapes around the raw-fallback boundary
+        v = np.full(n, 0x5F00, np.uint16)
+        for c in range(40):
+            v[c * 512] = 0x6400
+            v[c * 512 + 1:c * 512 + 1 + 8 * c] = 0x0080
+    else:  # a real bf16 package of a small expert
+        wl = W.Workload(name="cz", H=256, E=1, k=1, I=512, wfmt="bf16", xdt="bf16", Ts=(1,), seed=4)
+        v = moe.moe_pack_expert(wl.H, wl.I, "bf16", W.expert_weights(wl, 0, 0)).view(np.uint16)
+    raw = v.view(np.uint8)
+    got = moe.moe_compress_package(raw)
+    want = oracle.xw4_encode(raw)
+    assert got.size == want.size and np.array_equal(got, want)
+    assert np.array_equal(oracle.xw4_decode(got, raw.size), raw)
+    assert moe.moe_compress_bound(raw.size) >= got.size
+
+
+def test_compress_validation():
+    assert moe.moe_compress_bound(1000) == 0
+    assert moe.moe_compress_bound(0) == 256
+    assert moe.moe_compress_bound(1 << 20) == 256 * ((64 + 4 * 1025 + 1024 + 255) // 256) + (1 << 20)
+    with pytest.raises(moe.MoeError):
+        moe.moe_compress_package(np.zeros(1000, np.uint8))
+    with pytest.raises(moe.MoeError):
+        moe.moe_compress_package(np.zeros(2048, np.uint8), out=np.zeros(100, np.uint8))
+    assert moe.moe_compress_package(np.zeros(0, np.uint8)).size == 256
+    # device decoder: argument checks before any pointer is touched
+    assert L.moe_decompress_packages(None, 256, None, 1024, None, 1, 1000, None) == INVALID
+    assert L.moe_decompress_packages(None, 100, None, 1024, None, 1, 1024, None) == INVALID
+    assert L.moe_decompress_packages(None, 256, None, 512, None, 1, 1024, None) == INVALID
+    assert L.moe_decompress_packages(None, 256, None, 1024, None, -1, 1024, None) == INVALID
+    assert L.moe_decompress_packages(None, 256, None, 1024, None, 1, 1024, None) == INVALID  # null pointers
+    assert L.moe_decompress_packages(None, 256, None, 1024, None, 0, 1024, None) == OK

@@ -24,14 +24,16 @@ def _gpu():
 
 
 def run_and_check(wl, T, steps, check_steps, fill_all=True, capacity=None, policy="lru", period=0, overlap=True,
-                  prefetch=None, pins=None):
+                  prefetch=None, pins=None, blob_bytes=None):
+    """`blob_bytes`: compressed tiers with blob slots of that size."""
     xs = {}
     for s in range(steps):
         for l in range(wl.layers):
             x, _ = oracle.rank_gap_inputs(wl, T, layer=l, step=s)
             xs[(l, s)] = x
     model = OffloadedModel(wl, T, capacity=capacity, fill=fill_all, policy=policy, decay_period=period,
-                           overlap=overlap, prefetch=prefetch)
+                           overlap=overlap, prefetch=prefetch, compressed=blob_bytes is not None,
+                           blob_bytes=blob_bytes)
     if pins:
         model.reset_cache(pins=pins)
     if not fill_all:  # only the experts some step routes to (the others are never fetched)
@@ -59,6 +61,12 @@ def run_and_check(wl, T, steps, check_steps, fill_all=True, capacity=None, polic
                 got_bytes = model.pool[torch.tensor(slots, device="cuda")][:, :model.pkg_bytes].cpu().numpy()
                 for i, e in enumerate(mine):
                     assert np.array_equal(got_bytes[i], model.package(l, e)), (l, s, e)
+                if blob_bytes is not None:
+                    # the working pool the FFN read: expert e's package, decoded by the oracle from its blob
+                    work = model.work[:len(mine), :model.raw_bytes].cpu().numpy()
+                    for i, e in enumerate(mine):
+                        want = oracle.xw4_decode(model.package(l, e), model.raw_bytes)
+                        assert np.array_equal(work[i], want), ("decoded", l, s, e)
     # cache decisions: identical to the oracle's policy, over every demand lookup, prefetch and pin
     ev_groups = [(l * wl.E + np.asarray(ids)).tolist() for _, l, ids in model.events]
     kinds = [kind for kind, _, _ in model.events]
@@ -141,6 +149,31 @@ def test_offload_glm_full_size_first_steps(T, prefetch):
     wl = W.WORKLOADS["glm"].with_(steps=3)
     say("offload glm full size T", T, "prefetch", prefetch)
     run_and_check(wl, T, 3, {0, 2}, fill_all=False, prefetch=prefetch)
+
+
+@pytest.mark.parametrize("overlap", [True, False])
+def test_offload_compressed_small_all_steps(overlap):
+    """bf16 experts in compressed tiers: blobs in the bank and in the HBM slots, decoded into the
+    working pool before each FFN pass; every step checked (slot bytes, decoded packages, outputs)."""
+    from mixture_experts_layer_token_amd import api
+
+    wl = W.Workload(name="offload-z", H=224, E=16, k=4, I=352, wfmt="bf16", xdt="bf16", Ts=(5,), seed=611,
+                    zipf_s=1.2, layers=3, steps=16, rerank_every=8, cache_frac=0.25)
+    blob = (api.moe_compress_bound(api.moe_package_bytes(wl.H, wl.I, "bf16")) + 255) // 256 * 256
+    say("offload compressed small, overlap", overlap)
+    run_and_check(wl, 5, wl.steps, set(range(wl.steps)), overlap=overlap, blob_bytes=blob)
+
+
+def test_offload_compressed_glm_bf16_full_size_first_steps():
+    """GLM-shaped bf16 experts at full size (two layers), compressed tiers with blob slots of 77% of
+    the package, frequency-with-decay policy."""
+    from mixture_experts_layer_token_amd import api
+
+    wl = W.WORKLOADS["glm"].with_(wfmt="bf16", layers=2, steps=3, name="glm-bf16")
+    raw = api.moe_package_bytes(wl.H, wl.I, "bf16")
+    blob = (int(raw * 0.77) + 255) // 256 * 256
+    say("offload compressed glm bf16")
+    run_and_check(wl, 4, 3, {0, 2}, fill_all=False, policy="lfu_decay", period=4, blob_bytes=blob)
 
 
 @pytest.mark.parametrize("mode", ["decode", "prefill"])

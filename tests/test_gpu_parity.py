@@ -241,6 +241,79 @@ def test_permute_all_tokens_one_expert():
     assert counts.cpu().numpy()[11] == T and np.array_equal(perm.cpu().numpy(), np.arange(T))
 
 
+# ------------------------------------------------------------------ router + permutation in one call
+
+# (workload, T, overrides, poisoned rows): decode batches on the one-workgroup path (T <= 64,
+# T*k <= 1024), the largest it takes (E = 1024 logits rows, T*k = 1024), and batches beyond it
+ROUTE_PERMUTE_CASES = [
+    ("gptoss", 1, {}, ()), ("gptoss", 3, {}, ()), ("gptoss", 64, {}, ()), ("gptoss", 65, {}, ()),
+    ("mixtral", 16, {}, ()), ("kimi", 1, {}, ()), ("kimi", 64, {}, ()), ("kimi", 128, {}, ()),
+    ("glm", 16, {}, ()),
+    ("tiny", 64, dict(E=1024, k=16, H=64, name="e1024k16", xdt="bf16"), ()),
+    ("tiny", 65, dict(E=1024, k=16, H=64, name="e1024k16", xdt="bf16"), ()),
+    ("tiny", 7, dict(E=1, k=1, name="e1k1", xdt="bf16"), ()),
+    ("tiny", 16, {}, ()),  # fp32 activations: the two calls' kernels
+    ("tiny", 0, dict(xdt="bf16", name="empty"), ()),
+    ("gptoss", 40, dict(name="nonfinite"), (1, 20, 39)),
+]
+
+
+@pytest.mark.parametrize("name,T,kw,bad", ROUTE_PERMUTE_CASES,
+                         ids=["%s-%d%s" % (c[0], c[1], c[2].get("name", "")) for c in ROUTE_PERMUTE_CASES])
+def test_route_permute_exact(name, T, kw, bad):
+    """moe_route_permute: ids and grouping equal the oracle's, bit for bit; ids, gates, logits and
+    grouping equal those of moe_route followed by moe_permute, bit for bit."""
+    wl = W.WORKLOADS[name].with_(**kw)
+    k, E = wl.k, wl.E
+    say("route+permute", wl.name, "T", T, "E", E, "k", k, wl.xdt)
+    if T:
+        x, _ = oracle.rank_gap_inputs(wl, T)
+    else:
+        x = np.zeros((0, wl.H), np.float32 if wl.xdt == "f32" else np.uint16)
+    if bad:
+        x = _poison(x, wl.xdt, list(bad))
+    wg, bias = W.router_weights(wl), W.router_bias(wl)
+    xd, wgd = to_device_act(x, wl.xdt), to_device_act(wg, wl.xdt)
+    bd = torch.from_numpy(bias).cuda() if bias is not None else None
+    n = max(T * k, 1)
+
+    def outs():
+        i32 = dict(dtype=torch.int32, device="cuda")
+        return (torch.full((T, k), -7, **i32), torch.full((T, k), -7.0, device="cuda"),
+                torch.full((T, E), -7.0, device="cuda"), torch.full((E,), -7, **i32),
+                torch.full((E + 1,), -7, **i32), torch.full((n,), -7, **i32), torch.full((n,), -7, **i32))
+
+    ids, w, lg, counts, offsets, perm, inv = a = outs()
+    moe.moe_route_permute(xd, wgd, bd, k, ids, w, counts, offsets, perm, inv, logits=lg)
+    ids2, w2, lg2, counts2, offsets2, perm2, inv2 = b = outs()
+    moe.moe_route(xd, wgd, bd, k, ids2, w2, lg2)
+    moe.moe_permute(ids2, E, counts2, offsets2, perm2, inv2)
+    torch.cuda.synchronize()
+    for u, v, what in zip(a, b, ("ids", "gates", "logits", "counts", "offsets", "perm", "inv")):
+        un, vn = u.cpu().numpy(), v.cpu().numpy()
+        if u.dtype == torch.float32:
+            un, vn = un.view(np.uint32), vn.view(np.uint32)  # bit patterns (NaN included)
+        if what in ("perm", "inv"):
+            un, vn = un[:T * k], vn[:T * k]
+        assert np.array_equal(un, vn), what
+    got = ids.cpu().numpy()
+    c_ref, o_ref, p_ref, i_ref = oracle.permute(got, E)
+    assert np.array_equal(counts.cpu().numpy(), c_ref)
+    assert np.array_equal(offsets.cpu().numpy(), o_ref)
+    assert np.array_equal(perm.cpu().numpy()[:T * k], p_ref)
+    assert np.array_equal(inv.cpu().numpy()[:T * k], i_ref)
+    if T == 0:
+        return
+    good = np.setdiff1d(np.arange(T), np.asarray(bad, np.int64))
+    lgr = oracle.router_logits(wl.xdt, x[good], wg, bias)
+    ids_ref, w_ref = oracle.topk_gates(lgr, k)
+    assert np.array_equal(got[good], ids_ref)
+    np.testing.assert_allclose(w.cpu().numpy()[good], w_ref, rtol=GATE_RTOL, atol=GATE_ATOL)
+    if bad:
+        assert got.min() >= 0 and got.max() < E and all(len(set(r.tolist())) == k for r in got)
+        assert got[bad[0]].tolist() == list(range(k))
+
+
 # ------------------------------------------------------------------ whole layer, reduced shapes
 
 SMALL = [("f32", "f32"), ("f32", "bf16"), ("bf16", "bf16"), ("mxfp4", "bf16"), ("int4g32", "bf16"),
