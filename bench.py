@@ -426,10 +426,11 @@ def run_offload_compressed(args):
     blob_bytes = (int(largest * 1.003) + 255) // 256 * 256
     runs, belady, touched_all = [], {}, {}
     policies = (("lfu_decay", 32), ("lru", 0))
+    work_slots = 16  # plain packages the compressed run decodes into, a layer's experts a group at a time
     for compressed in (False, True):
-        cap_max = slots_raw if not compressed else (budget - min(wl.E, min(Ts) * wl.k) * raw_stride) // blob_bytes
+        cap_max = slots_raw if not compressed else (budget - min(wl.E, min(Ts) * wl.k, work_slots) * raw_stride) // blob_bytes
         model = OffloadedModel(wl, max(Ts), capacity=cap_max, fill=False, compressed=compressed,
-                               blob_bytes=blob_bytes if compressed else None)
+                               blob_bytes=blob_bytes if compressed else None, work_slots=work_slots)
         for T in Ts:
             xs = {(l, s): to_device_act(W.activations(wl, T, l, s), wl.xdt) for s in range(steps)
                   for l in range(wl.layers)}
@@ -444,8 +445,8 @@ def run_offload_compressed(args):
             for l in range(wl.layers):
                 model.fill(l, touched_all[T][l] - model.filled.get(l, set()))
                 model.filled[l] = model.filled.get(l, set()) | touched_all[T][l]
-            # compressed: the working pool takes min(E, T k) plain packages of the budget
-            n_work = min(wl.E, T * wl.k)
+            # compressed: the working pool takes min(E, T k, work_slots) plain packages of the budget
+            n_work = min(wl.E, T * wl.k, work_slots)
             cap = slots_raw if not compressed else (budget - n_work * raw_stride) // blob_bytes
             out = torch.empty((T, wl.H), dtype=torch.bfloat16, device="cuda")
             model.reset_cache(capacity=cap, prefetch=None)

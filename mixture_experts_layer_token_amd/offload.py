@@ -28,10 +28,11 @@ experts of the layer just planned, whose FFN may still be running.
 With `compressed=True` (bf16 experts) both tiers hold losslessly compressed
 packages (the same page: compressed GPU memory beside host DRAM): the bank and
 the HBM slots hold exponent-window blobs, so a miss moves about 3/4 of the
-bytes and the same HBM holds more experts; before each FFN pass the pass's
-experts are decoded on the compute stream into a working pool of plain
-packages (one slot per distinct expert a layer can touch, shared by all
-layers), which the FFN reads as usual.
+bytes and the same HBM holds more experts.  A layer's experts are decoded on
+the compute stream into a small working pool of plain packages (`work_slots`,
+shared by all layers), a group of at most that many at a time, each group
+followed by its FFN pass: the hits' groups first, the misses' groups once
+their copies landed.
 """
 from __future__ import annotations
 
@@ -78,9 +79,10 @@ class OffloadedModel:
     """L MoE layers whose experts live in a pinned host bank, cached in an HBM slot pool."""
 
     def __init__(self, wl, max_T: int, capacity: int | None = None, device="cuda", fill=True, policy="lru",
-                 decay_period=0, overlap=True, prefetch=None, compressed=False, blob_bytes=None):
+                 decay_period=0, overlap=True, prefetch=None, compressed=False, blob_bytes=None, work_slots=16):
         """`compressed`: bank and HBM slots hold blobs of `blob_bytes` bytes (a multiple of 256 that
-        every expert's blob must fit; bf16 experts only)."""
+        every expert's blob must fit; bf16 experts only), decoded through a working pool of
+        `work_slots` plain packages."""
         from synth import workloads as W
 
         self.wl = wl
@@ -114,16 +116,23 @@ class OffloadedModel:
         self.pass_dev = [[torch.full((self.E,), -1, device=device, **i32) for _ in range(2)] for _ in range(self.L)]
         self.pass_host = [[torch.full((self.E,), -1, pin_memory=True, **i32) for _ in range(2)] for _ in range(self.L)]
         if compressed:
-            # decoded working pool: one plain package per distinct expert a layer step can touch; the
-            # FFN passes address it through the tables in pass_dev, the decoder through pair lists
-            self.n_work = min(self.E, max_T * self.k)
+            # decoded working pool of plain packages, shared by the layers
+            self.n_work = min(self.E, max_T * self.k, work_slots)
             self.work = torch.empty((self.n_work, self.raw_stride), dtype=torch.uint8, device=device)
-            self.pair_dev = [[torch.full((self.E, 2), -1, device=device, **i32) for _ in range(2)]
+            # per layer, up to n_groups groups (the hits' and the misses' experts in groups of n_work):
+            # a table over the working pool for the group's FFN pass and the decoder's pair list
+            d_max = min(self.E, max_T * self.k)
+            self.n_groups = (d_max + self.n_work - 1) // self.n_work + 1
+            self.group_dev = [torch.full((self.n_groups, self.E), -1, device=device, **i32) for _ in range(self.L)]
+            self.group_host = [torch.full((self.n_groups, self.E), -1, pin_memory=True, **i32) for _ in range(self.L)]
+            self.pair_dev = [torch.full((self.n_groups, self.n_work, 2), -1, device=device, **i32)
                              for _ in range(self.L)]
-            self.pair_host = [[torch.full((self.E, 2), -1, pin_memory=True, **i32) for _ in range(2)]
+            self.pair_host = [torch.full((self.n_groups, self.n_work, 2), -1, pin_memory=True, **i32)
                               for _ in range(self.L)]
-            self.pass_desc = [[api.experts_desc(wl.H, wl.I, wl.E, wl.wfmt, self.work, self.raw_stride, t, self.n_work)
-                               for t in pd] for pd in self.pass_dev]
+            self.group_desc = [[api.experts_desc(wl.H, wl.I, wl.E, wl.wfmt, self.work, self.raw_stride, t, self.n_work)
+                                for t in gd] for gd in self.group_dev]
+            self.pass_desc = None
+            self.last_group = []
         else:
             self.pass_desc = [[api.experts_desc(wl.H, wl.I, wl.E, wl.wfmt, self.pool, self.stride, t, self.capacity)
                                for t in pd] for pd in self.pass_dev]
@@ -131,9 +140,9 @@ class OffloadedModel:
         self.bias_cache = {}
         self.layers = []
         for l in range(self.L):
-            if compressed:  # the FFN reads the working pool through the pass tables
+            if compressed:  # the FFN reads the working pool through the group tables
                 lay = MoeLayer(wl.H, wl.I, wl.E, wl.k, wl.wfmt, wl.xdt, self.wg[l], None, self.work, self.raw_stride,
-                               max_T=max_T, slot_of_expert=self.pass_dev[l][0], device=device)
+                               max_T=max_T, slot_of_expert=self.group_dev[l][0], device=device)
             else:
                 lay = MoeLayer(wl.H, wl.I, wl.E, wl.k, wl.wfmt, wl.xdt, self.wg[l], None, self.pool, self.stride,
                                max_T=max_T, slot_of_expert=self.slot_tables[l], device=device)
@@ -273,7 +282,7 @@ class OffloadedModel:
         self.use_counts[l][distinct] += 1
         split = self.overlap and plan.n_hits > 0 and plan.n_misses > 0
         if self.compressed:
-            n_pairs = self._stage_decode(l, plan, distinct, split)
+            groups = self._stage_decode(l, plan, distinct)
         elif split:
             table = np.ctypeslib.as_array(plan.slot_of_expert)[:self.E]
             miss = np.ctypeslib.as_array(plan.miss_ids)[:plan.n_misses]
@@ -302,18 +311,19 @@ class OffloadedModel:
             t1.record(self.copy_stream)
             self._copy_windows.append((t0, t1))
         if self.compressed:
-            # decode each pass's experts into the working pool, then its FFN; the misses' pass after
-            # their copies landed
-            if split:
-                self._decode(l, 0, n_pairs[0])
-                api.moe_expert_ffn(self.pass_desc[l][0], x, k, lay.offsets, lay.perm_src, lay.y_perm, lay.ws)
+            # each group: decode its experts into the working pool, then their FFN pass (the next
+            # group's decode follows that FFN on the stream); the misses' groups after their copies
+            # (all groups after them without the overlap)
+            waited = False
+            for j, (is_miss, n) in enumerate(groups):
+                if not waited and (is_miss or not self.overlap):
+                    torch.cuda.current_stream().wait_event(self.done)
+                    waited = True
+                api.moe_decompress_packages(self.pool, self.stride, self.work, self.raw_stride, self.pair_dev[l][j],
+                                            self.raw_bytes, n=n)
+                api.moe_expert_ffn(self.group_desc[l][j], x, k, lay.offsets, lay.perm_src, lay.y_perm, lay.ws)
+            if not waited:
                 torch.cuda.current_stream().wait_event(self.done)
-                self._decode(l, 1, n_pairs[1])
-                api.moe_expert_ffn(self.pass_desc[l][1], x, k, lay.offsets, lay.perm_src, lay.y_perm, lay.ws)
-            else:
-                torch.cuda.current_stream().wait_event(self.done)
-                self._decode(l, 0, n_pairs[0])
-                api.moe_expert_ffn(self.pass_desc[l][0], x, k, lay.offsets, lay.perm_src, lay.y_perm, lay.ws)
         elif split:
             api.moe_expert_ffn(self.pass_desc[l][0], x, k, lay.offsets, lay.perm_src, lay.y_perm, lay.ws)
             torch.cuda.current_stream().wait_event(self.done)
@@ -325,33 +335,30 @@ class OffloadedModel:
         self.last_plan = plan
         return out
 
-    def _stage_decode(self, l, plan, distinct, split):
-        """Compressed tiers: working-pool slot of each of the layer's experts (its rank among them),
-        the FFN passes' tables over the pool and the decoder's (blob slot, pool slot) pairs; staged
-        through pinned memory to the device on the compute stream.  Returns the pairs per pass."""
+    def _stage_decode(self, l, plan, distinct):
+        """Compressed tiers: the layer's experts in groups of at most n_work (the hits' first, then
+        the misses'); per group, a table over the working pool (expert -> its rank in the group) and
+        the decoder's (blob slot, pool slot) pairs, staged through pinned memory to the device on the
+        compute stream.  Returns [(group of misses?, experts in it)]."""
         blob_slot = np.ctypeslib.as_array(plan.slot_of_expert)[:self.E]
         is_miss = np.zeros(self.E, bool)
         is_miss[np.ctypeslib.as_array(plan.miss_ids)[:plan.n_misses]] = True
-        passes = ([distinct[~is_miss[distinct]], distinct[is_miss[distinct]]] if split else [distinct, distinct[:0]])
-        rank = np.full(self.E, -1, np.int32)
-        rank[distinct] = np.arange(len(distinct), dtype=np.int32)
-        n_pairs = []
-        for j, ids in enumerate(passes):
-            t = self.pass_host[l][j].numpy()
-            t[:] = -1
-            t[ids] = rank[ids]
-            pr = self.pair_host[l][j].numpy()
-            pr[:len(ids), 0] = blob_slot[ids]
-            pr[:len(ids), 1] = rank[ids]
-            n_pairs.append(len(ids))
-            self.pass_dev[l][j].copy_(self.pass_host[l][j], non_blocking=True)
-            self.pair_dev[l][j].copy_(self.pair_host[l][j], non_blocking=True)
-        return n_pairs
-
-    def _decode(self, l, j, n):
-        if n:
-            api.moe_decompress_packages(self.pool, self.stride, self.work, self.raw_stride, self.pair_dev[l][j],
-                                        self.raw_bytes, n=n)
+        tables, pairs = self.group_host[l].numpy(), self.pair_host[l].numpy()
+        tables[:] = -1
+        groups = []
+        for miss in (False, True):
+            ids = distinct[is_miss[distinct] == miss]
+            for g0 in range(0, len(ids), self.n_work):
+                g = ids[g0:g0 + self.n_work]
+                j = len(groups)
+                tables[j, g] = np.arange(len(g), dtype=np.int32)
+                pairs[j, :len(g), 0] = blob_slot[g]
+                pairs[j, :len(g), 1] = np.arange(len(g), dtype=np.int32)
+                groups.append((miss, len(g)))
+                self.last_group = g.tolist()
+        self.group_dev[l].copy_(self.group_host[l], non_blocking=True)
+        self.pair_dev[l].copy_(self.pair_host[l], non_blocking=True)
+        return groups
 
     def close(self):
         self.cache.close()

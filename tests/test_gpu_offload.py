@@ -24,7 +24,7 @@ def _gpu():
 
 
 def run_and_check(wl, T, steps, check_steps, fill_all=True, capacity=None, policy="lru", period=0, overlap=True,
-                  prefetch=None, pins=None, blob_bytes=None):
+                  prefetch=None, pins=None, blob_bytes=None, work_slots=16):
     """`blob_bytes`: compressed tiers with blob slots of that size."""
     xs = {}
     for s in range(steps):
@@ -33,7 +33,7 @@ def run_and_check(wl, T, steps, check_steps, fill_all=True, capacity=None, polic
             xs[(l, s)] = x
     model = OffloadedModel(wl, T, capacity=capacity, fill=fill_all, policy=policy, decay_period=period,
                            overlap=overlap, prefetch=prefetch, compressed=blob_bytes is not None,
-                           blob_bytes=blob_bytes)
+                           blob_bytes=blob_bytes, work_slots=work_slots)
     if pins:
         model.reset_cache(pins=pins)
     if not fill_all:  # only the experts some step routes to (the others are never fetched)
@@ -62,9 +62,10 @@ def run_and_check(wl, T, steps, check_steps, fill_all=True, capacity=None, polic
                 for i, e in enumerate(mine):
                     assert np.array_equal(got_bytes[i], model.package(l, e)), (l, s, e)
                 if blob_bytes is not None:
-                    # the working pool the FFN read: expert e's package, decoded by the oracle from its blob
-                    work = model.work[:len(mine), :model.raw_bytes].cpu().numpy()
-                    for i, e in enumerate(mine):
+                    # the working pool after the layer's last group: each of its experts' packages as the
+                    # oracle decodes them from the blob
+                    work = model.work[:len(model.last_group), :model.raw_bytes].cpu().numpy()
+                    for i, e in enumerate(model.last_group):
                         want = oracle.xw4_decode(model.package(l, e), model.raw_bytes)
                         assert np.array_equal(work[i], want), ("decoded", l, s, e)
     # cache decisions: identical to the oracle's policy, over every demand lookup, prefetch and pin
@@ -151,17 +152,18 @@ def test_offload_glm_full_size_first_steps(T, prefetch):
     run_and_check(wl, T, 3, {0, 2}, fill_all=False, prefetch=prefetch)
 
 
-@pytest.mark.parametrize("overlap", [True, False])
-def test_offload_compressed_small_all_steps(overlap):
+@pytest.mark.parametrize("overlap,work_slots", [(True, 16), (False, 16), (True, 3), (False, 1)])
+def test_offload_compressed_small_all_steps(overlap, work_slots):
     """bf16 experts in compressed tiers: blobs in the bank and in the HBM slots, decoded into the
-    working pool before each FFN pass; every step checked (slot bytes, decoded packages, outputs)."""
+    working pool in groups of at most `work_slots` experts, each followed by its FFN pass; every
+    step checked (slot bytes, decoded packages, outputs)."""
     from mixture_experts_layer_token_amd import api
 
     wl = W.Workload(name="offload-z", H=224, E=16, k=4, I=352, wfmt="bf16", xdt="bf16", Ts=(5,), seed=611,
                     zipf_s=1.2, layers=3, steps=16, rerank_every=8, cache_frac=0.25)
     blob = (api.moe_compress_bound(api.moe_package_bytes(wl.H, wl.I, "bf16")) + 255) // 256 * 256
-    say("offload compressed small, overlap", overlap)
-    run_and_check(wl, 5, wl.steps, set(range(wl.steps)), overlap=overlap, blob_bytes=blob)
+    say("offload compressed small, overlap", overlap, "work slots", work_slots)
+    run_and_check(wl, 5, wl.steps, set(range(wl.steps)), overlap=overlap, blob_bytes=blob, work_slots=work_slots)
 
 
 def test_offload_compressed_glm_bf16_full_size_first_steps():
