@@ -498,33 +498,76 @@ def run_offload_compressed(args):
 
 
 def time_decoder(model, n: int) -> dict:
-    """HBM roofline of the package decoder: n blobs of the bank decoded into the working pool in one
-    launch, timed with HIP events on the stream it runs on; algorithmic bytes = the blobs' bytes
-    read + the packages' bytes written."""
+    """HBM roofline of the package decoder on n blobs of the model's bank (decoded into its working
+    pool in one launch)."""
+    import torch
+
+    keys = [(l, e) for l in range(model.L) for e in range(model.E) if model.blob_sizes[l, e] > 0][:n]
+    for i, (l, e) in enumerate(keys):
+        model.pool[i].copy_(torch.from_numpy(model.package(l, e).copy()))
+    sizes = [int(model.blob_sizes[l, e]) for l, e in keys]
+    return decoder_roofline(model.pool, model.stride, model.work, model.raw_stride, sizes, model.raw_bytes)
+
+
+def decoder_roofline(pool, stride, work, raw_stride, sizes, raw_bytes, reps=20) -> dict:
+    """Blobs in pool slots 0..n-1 decoded into work slots 0..n-1 in one launch, timed with HIP events
+    on the stream it runs on; algorithmic bytes = the blobs' bytes read + the packages' bytes written."""
     import torch
 
     from mixture_experts_layer_token_amd import api
 
-    keys = [(l, e) for l in range(model.L) for e in range(model.E) if model.blob_sizes[l, e] > 0][:n]
-    n = len(keys)
-    for i, (l, e) in enumerate(keys):
-        model.pool[i].copy_(torch.from_numpy(model.package(l, e).copy()))
+    n = len(sizes)
     pairs = torch.tensor([[i, i] for i in range(n)], dtype=torch.int32, device="cuda")
     for _ in range(3):
-        api.moe_decompress_packages(model.pool, model.stride, model.work, model.raw_stride, pairs, model.raw_bytes)
+        api.moe_decompress_packages(pool, stride, work, raw_stride, pairs, raw_bytes)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    reps = 20
     a.record()
     for _ in range(reps):
-        api.moe_decompress_packages(model.pool, model.stride, model.work, model.raw_stride, pairs, model.raw_bytes)
+        api.moe_decompress_packages(pool, stride, work, raw_stride, pairs, raw_bytes)
     b.record()
     torch.cuda.synchronize()
     us = a.elapsed_time(b) * 1e3 / reps
-    alg = int(sum(model.blob_sizes[l, e] for l, e in keys)) + n * model.raw_bytes
+    alg = int(sum(sizes)) + n * raw_bytes
     return {"bound": "hbm", "kernel": "xw4_decode_kernel (%d packages per launch)" % n,
             "achieved": round(alg / us / 1e3, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(alg / us / 1e3 / HBM_PEAK_GBS, 4), "traffic": None, "avg_launch_us": round(us, 2),
-            "algorithmic_bytes_per_launch": alg}
+            "algorithmic_bytes_per_launch": alg, "timed_launches": reps}
+
+
+def run_decoder(args):
+    """The package decoder alone: 16 GLM-shaped bf16 experts (47 MB each) encoded on the host, their
+    blobs decoded on the GPU in one launch per repetition; decoded bytes checked against the packages."""
+    import numpy as np
+    import torch
+
+    from synth import workloads as W
+
+    from mixture_experts_layer_token_amd import api
+    from mixture_experts_layer_token_amd.layer import pack_bank
+
+    wl = W.WORKLOADS["glm"].with_(wfmt="bf16", name="glm-bf16")
+    raw_bytes = api.moe_package_bytes(wl.H, wl.I, "bf16")
+    n = 16
+    host = pack_bank(wl, 0, list(range(n)), stride=raw_bytes)
+    blobs = [api.moe_compress_package(host[i]) for i in range(n)]
+    stride = (max(b.size for b in blobs) + 255) // 256 * 256
+    pool = torch.zeros((n, stride), dtype=torch.uint8, device="cuda")
+    for i, b in enumerate(blobs):
+        pool[i, :b.size].copy_(torch.from_numpy(b))
+    work = torch.empty((n, raw_bytes), dtype=torch.uint8, device="cuda")
+    roof = decoder_roofline(pool, stride, work, raw_bytes, [b.size for b in blobs], raw_bytes, reps=args.steps)
+    ok = all(np.array_equal(work[i].cpu().numpy(), host[i]) for i in range(n))
+    if not ok:
+        raise RuntimeError("decoded packages differ from the originals")
+    us = roof["avg_launch_us"]
+    return {"metric": "lossless package decode GB/s (blobs read + packages written)", "value": roof["achieved"],
+            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": 3, "ms_per_step": round(us / 1e3, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (N(0,0.02) bf16 weights of GLM-shaped experts)",
+            "config": {"workload": "xw4 decode of %d glm-bf16 packages" % n, "raw_bytes": raw_bytes,
+                       "blob_bytes_mean": float(np.mean([b.size for b in blobs]))},
+            "roofline": roof, "decoded_equal": ok}
+
 
 
 def offload_variant(model, wl, T, steps, xs, out, policy, period, overlap, pf, pin, belady):
@@ -765,7 +808,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="mixtral", choices=["mixtral", "gptoss", "kimi", "glm", "glm-bf16", "spec"])
+    ap.add_argument("--workload", default="mixtral",
+                    choices=["mixtral", "gptoss", "kimi", "glm", "glm-bf16", "spec", "decoder"])
     ap.add_argument("--offload-steps", type=int, default=256)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="copy 1 GiB device-to-device before measuring (profiler byte-counter calibration)")
@@ -808,6 +852,8 @@ def main():
         return
     if args.workload == "glm-bf16":
         out = run_offload_compressed(args)
+    elif args.workload == "decoder":
+        out = run_decoder(args)
     else:
         out = run_offload(args) if args.workload in OFFLOAD else run(args)
     if args.workload == "mixtral" and args.prefill:

@@ -137,7 +137,7 @@ int moe_permute(const int32_t* topk_ids, int T, int k, int E, int32_t* counts, i
 
 /*
  * moe_route followed by moe_permute on its ids, in one call: the same outputs, bit for bit, as
- * those two calls (arguments as there).  Decode batches in bf16 (T <= 64, T*k <= 1024, T*E <= 2^20,
+ * those two calls (arguments as there).  Decode batches in bf16 (T <= 16, T*k <= 1024, T*E <= 2^20,
  * H a multiple of 32) take two launches instead of three: the router's partial logits, then one
  * workgroup that sums them, selects the top k of every token and groups the pairs.  Other
  * batches run the two calls' kernels one after the other.  (The routing and grouping steps are

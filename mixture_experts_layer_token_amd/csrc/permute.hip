@@ -14,7 +14,7 @@
 // offsets, and each block's starting cursor per expert), (3) every block scatters its indices
 // in order from those cursors with the same in-block ranking.  Same result, block-parallel.
 // Decode batches routed and grouped in one call (moe_route_permute): after the router's partial
-// logits, a single workgroup sums them, selects every token's top k (16 tokens at a time, one per
+// logits, a single workgroup sums them, selects every token's top k (at most 16 tokens, one per
 // wave) and groups the pairs from an LDS copy of the ids: one launch and one dependent step less.
 #include "common.hpp"
 #include "topk.hpp"
@@ -25,7 +25,8 @@ namespace {
 constexpr int kPermThreads = 1024;
 constexpr int kBlk = 2048;         // flat indices per block (multi-block path)
 constexpr int kSingleMax = 8192;   // largest T*k done by the single workgroup
-constexpr int kFusedMaxT = 64;     // largest batch routed and grouped by one workgroup (route_permute)
+constexpr int kFusedMaxT = 16;     // largest batch routed and grouped by one workgroup (route_permute):
+                                   // one token per wave
 
 __device__ void scatter_range(const int32_t* ids, int i0, int i1, int E, int* cursor, int32_t* __restrict__ perm,
                               int32_t* __restrict__ inv);

@@ -243,17 +243,18 @@ def test_permute_all_tokens_one_expert():
 
 # ------------------------------------------------------------------ router + permutation in one call
 
-# (workload, T, overrides, poisoned rows): decode batches on the one-workgroup path (T <= 64,
-# T*k <= 1024), the largest it takes (E = 1024 logits rows, T*k = 1024), and batches beyond it
+# (workload, T, overrides, poisoned rows): decode batches on the one-workgroup path (T <= 16,
+# T*k <= 1024), the largest rows it takes (E = 1024 with k = 16), and batches beyond it
 ROUTE_PERMUTE_CASES = [
-    ("gptoss", 1, {}, ()), ("gptoss", 3, {}, ()), ("gptoss", 64, {}, ()), ("gptoss", 65, {}, ()),
-    ("mixtral", 16, {}, ()), ("kimi", 1, {}, ()), ("kimi", 64, {}, ()), ("kimi", 128, {}, ()),
-    ("glm", 16, {}, ()),
-    ("tiny", 64, dict(E=1024, k=16, H=64, name="e1024k16", xdt="bf16"), ()),
-    ("tiny", 65, dict(E=1024, k=16, H=64, name="e1024k16", xdt="bf16"), ()),
+    ("gptoss", 1, {}, ()), ("gptoss", 3, {}, ()), ("gptoss", 16, {}, ()), ("gptoss", 17, {}, ()),
+    ("gptoss", 64, {}, ()), ("mixtral", 16, {}, ()), ("kimi", 1, {}, ()), ("kimi", 16, {}, ()),
+    ("kimi", 128, {}, ()), ("glm", 16, {}, ()),
+    ("tiny", 16, dict(E=1024, k=16, H=64, name="e1024k16", xdt="bf16"), ()),
+    ("tiny", 17, dict(E=1024, k=16, H=64, name="e1024k16", xdt="bf16"), ()),
     ("tiny", 7, dict(E=1, k=1, name="e1k1", xdt="bf16"), ()),
     ("tiny", 16, {}, ()),  # fp32 activations: the two calls' kernels
     ("tiny", 0, dict(xdt="bf16", name="empty"), ()),
+    ("gptoss", 12, dict(name="nonfinite"), (1, 6, 11)),
     ("gptoss", 40, dict(name="nonfinite"), (1, 20, 39)),
 ]
 
