@@ -211,8 +211,8 @@ int moe_dequant_expert(const void* package, int H, int I, int fmt, float* out, v
  *    offset, u8 window bases (0 for raw chunks), zeros up to the data offset (the first multiple
  *    of 256 past the tables), then the chunks back to back; a chunk of off[i+1] - off[i] = 1024
  *    bytes is raw.
- * bf16 weights around zero compress to about 75% (12 bits per value); 4-bit packages are already
- * within a few percent of their codes' entropy and are not compressed.
+ * bf16 weights around zero compress to about 75% (12 bits per value).  4-bit packages are not
+ * compressed: their codes carry 3.6-3.9 bits of entropy each, which no fixed-width code can use.
  */
 
 /* Largest blob for a package of raw_bytes bytes (0 if raw_bytes is not a multiple of 1024). */

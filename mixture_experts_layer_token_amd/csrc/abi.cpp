@@ -91,6 +91,12 @@ extern "C" size_t moe_ffn_workspace(const moe_experts* w, int T, int k, int mode
 extern "C" int moe_expert_ffn(const moe_experts* w, const void* x, int xdt, int T, int k, const int32_t* offsets,
                               const int32_t* perm_src, float* y_perm, int mode, void* ws, size_t ws_bytes,
                               void* stream) {
+  return expert_ffn(w, x, xdt, T, k, offsets, perm_src, y_perm, mode, ws, ws_bytes, stream, true);
+}
+
+int moe::expert_ffn(const moe_experts* w, const void* x, int xdt, int T, int k, const int32_t* offsets,
+                    const int32_t* perm_src, float* y_perm, int mode, void* ws, size_t ws_bytes, void* stream,
+                    bool helper_stream) {
   int rc = check_experts(w, "moe_expert_ffn");
   if (rc != MOE_OK) return rc;
   if (!dtype_valid(xdt)) return fail(MOE_ERR_INVALID, "moe_expert_ffn: bad dtype %d", xdt);
@@ -106,7 +112,8 @@ extern "C" int moe_expert_ffn(const moe_experts* w, const void* x, int xdt, int 
     return fail(MOE_ERR_INVALID, "moe_expert_ffn: null pointer");
   if (w->slot_of_expert && w->n_slots < 1)
     return fail(MOE_ERR_INVALID, "moe_expert_ffn: n_slots=%d with a slot table", w->n_slots);
-  return launch_ffn(w, x, xdt, T, k, offsets, perm_src, y_perm, mode, ws, ws_bytes, (hipStream_t)stream);
+  return launch_ffn(w, x, xdt, T, k, offsets, perm_src, y_perm, mode, ws, ws_bytes, (hipStream_t)stream,
+                    helper_stream);
 }
 
 extern "C" int moe_combine(const float* y_perm, const float* topk_w, const int32_t* inv_perm, int T, int k, int H,

@@ -107,7 +107,14 @@ int launch_combine(const float* y, const float* w, const int32_t* inv, int T, in
                    void* out, int odt, hipStream_t s);
 int launch_dequant(const void* pkg, int H, int I, int fmt, float* out, hipStream_t s);
 size_t ffn_workspace(const moe_experts* w, int T, int k, int mode);
+// helper_stream: the AUTO hybrid may run its tile-kernel share on a library-owned helper stream
+// (created once per device), beside the streaming kernels
 int launch_ffn(const moe_experts* w, const void* x, int xdt, int T, int k, const int32_t* offsets,
-               const int32_t* perm_src, float* y_perm, int mode, void* ws, size_t ws_bytes, hipStream_t s);
+               const int32_t* perm_src, float* y_perm, int mode, void* ws, size_t ws_bytes, hipStream_t s,
+               bool helper_stream);
+// moe_expert_ffn's validation, then launch_ffn
+int expert_ffn(const moe_experts* w, const void* x, int xdt, int T, int k, const int32_t* offsets,
+               const int32_t* perm_src, float* y_perm, int mode, void* ws, size_t ws_bytes, void* stream,
+               bool helper_stream);
 
 }  // namespace moe

@@ -21,6 +21,8 @@
 // host never reads the routing back.
 #include <math.h>
 
+#include <mutex>
+
 #include "ffn_common.hpp"
 
 namespace moe {
@@ -837,6 +839,10 @@ void trace(int i, hipStream_t s) {
 // NARROW: few experts can be touched (small batches), so the workgroups cover fewer strips and
 // there are enough of them to occupy every CU.
 // (MOE_CFG_* macros override the defaults when tuning.)
+#ifndef MOE_CFG_HYBRID_4BIT_MIN_AVG
+#define MOE_CFG_HYBRID_4BIT_MIN_AVG 24.0  // AUTO, 4-bit: average rows per expert from which hot experts go to
+                                          // the tile kernel
+#endif
 #ifndef MOE_CFG_Q4_GU_NP
 #define MOE_CFG_Q4_GU_NP 2  // 4-bit gate/up units per workgroup at one M tile (wide)
 #endif
@@ -949,8 +955,35 @@ size_t ffn_workspace(const moe_experts* w, int T, int k, int mode) {
   return a.total > b.total ? a.total : b.total;
 }
 
+// The helper stream of a device (default priority, non-blocking) and the two events that fork it
+// from the caller's stream and join it back; created on first use, kept until the process ends.
+// The mutex also covers each fork / launch / join sequence, so host threads do not interleave theirs.
+struct Helper {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_helper_mu;
+Helper g_helper[64];
+
+int helper_for_current_device(Helper** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "moe_expert_ffn: hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(MOE_ERR_UNSUPPORTED, "moe_expert_ffn: device %d", dev);
+  Helper& h = g_helper[dev];
+  if (!h.s) {
+    if ((e = hipStreamCreateWithFlags(&h.s, hipStreamNonBlocking)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&h.fork, hipEventDisableTiming)) != hipSuccess ||
+        (e = hipEventCreateWithFlags(&h.join, hipEventDisableTiming)) != hipSuccess)
+      return hip_fail(e, "moe_expert_ffn: helper stream");
+  }
+  *out = &h;
+  return MOE_OK;
+}
+
 int launch_ffn(const moe_experts* w, const void* x, int xdt, int T, int k, const int32_t* offsets,
-               const int32_t* perm_src, float* y_perm, int mode, void* ws, size_t ws_bytes, hipStream_t s) {
+               const int32_t* perm_src, float* y_perm, int mode, void* ws, size_t ws_bytes, hipStream_t s,
+               bool helper_stream) {
   if (T == 0) return MOE_OK;
   const int H = w->H, I = w->I, E = w->E;
   WsLayout L = ws_layout(w, T, k, xdt, mode);
@@ -1075,7 +1108,7 @@ int launch_ffn(const moe_experts* w, const void* x, int xdt, int T, int k, const
     // than sending the hot ones to the tile kernel, which runs after the streaming kernel with too
     // few tiles to fill the GPU (gpt-oss-shaped MXFP4, 128 experts, top-4: T = 256 / 512 / 1024,
     // 223 vs 294, 317 vs 368, 488 vs 469 us per layer step)
-    const double min_avg_rows = w->fmt == MOE_W_BF16 ? 0.0 : 24.0;
+    const double min_avg_rows = w->fmt == MOE_W_BF16 ? 0.0 : MOE_CFG_HYBRID_4BIT_MIN_AVG;
     // bf16 experts from 28 rows per expert on average: the tile kernel for every expert (a second
     // streaming row tile re-reads a whole expert from HBM; Mixtral-shaped, 8 experts, top-2:
     // T = 96 / 128, streaming 531 / 693 us, tile kernel 568 / 576 us per layer step)
@@ -1114,17 +1147,48 @@ int launch_ffn(const moe_experts* w, const void* x, int xdt, int T, int k, const
                        gu.n_slots, plan, (int*)nullptr, 0);
     gu_s.plan = dn_s.plan = plan;
   }
+  // the hybrid's two shares touch disjoint experts (their h and y_perm rows too): the tile share
+  // runs on the helper stream beside the streaming share, forked after the activation cast
+  const bool concurrent = use_stream && use_tile && helper_stream;
+  Helper* hp = nullptr;
+  std::unique_lock<std::mutex> lock(g_helper_mu, std::defer_lock);
+  hipStream_t ts = s;
+  if (concurrent) {
+    lock.lock();
+    int rc = helper_for_current_device(&hp);
+    if (rc != MOE_OK) return rc;
+    hipError_t e;
+    if ((e = hipEventRecord(hp->fork, s)) != hipSuccess || (e = hipStreamWaitEvent(hp->s, hp->fork, 0)) != hipSuccess)
+      return hip_fail(e, "moe_expert_ffn: fork to the helper stream");
+    ts = hp->s;
+  }
   if (use_tile) {
     int4* tplan = (int4*)(wsp + L.tplan_off);
     int* counters = (int*)(wsp + L.tplan_off + L.tplan_bytes - 256);
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, offsets, E, kTileRows, gu_t.min_rows, 0x7FFFFFFF,
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, ts, offsets, E, kTileRows, gu_t.min_rows, 0x7FFFFFFF,
                        w->slot_of_expert, gu.n_slots, tplan, counters, 16);
     gu_t.plan = dn_t.plan = tplan;
     gu_t.tcount = counters;
     dn_t.tcount = counters + 8;
   }
-  trace(0, s);
   int rc = MOE_OK;
+  if (concurrent) {
+    rc = launch_ffn_tile_part(w->fmt, true, gu_t, H, I, (int)n, E, ts);
+    if (rc == MOE_OK) rc = launch_ffn_tile_part(w->fmt, false, dn_t, H, I, (int)n, E, ts);
+    hipError_t e = hipEventRecord(hp->join, ts);
+    trace(0, s);
+    if (rc == MOE_OK) rc = launch_stream_fmt(w->fmt, mt, narrow, true, gu_s, H, I, S, s);
+    trace(1, s);
+    if (rc == MOE_OK) rc = launch_stream_fmt(w->fmt, mt, narrow, false, dn_s, H, I, S, s);
+    // the caller's stream waits for the helper's share whatever happened above
+    if (e == hipSuccess) e = hipStreamWaitEvent(s, hp->join, 0);
+    if (rc != MOE_OK) return rc;
+    if (e != hipSuccess) return hip_fail(e, "moe_expert_ffn: join from the helper stream");
+    trace(2, s);
+    MOE_CHECK_LAUNCH("moe_expert_ffn launch");
+    return MOE_OK;
+  }
+  trace(0, s);
   if (use_stream) rc = launch_stream_fmt(w->fmt, mt, narrow, true, gu_s, H, I, S, s);
   if (rc == MOE_OK && use_tile) rc = launch_ffn_tile_part(w->fmt, true, gu_t, H, I, (int)n, E, s);
   if (rc != MOE_OK) return rc;

@@ -56,5 +56,6 @@ extern "C" int moe_expert_ffn_noalloc(const moe_experts* w, const void* x, int x
   void* ws = nullptr;
   int rc = scratch_for_current_device(&ws);
   if (rc != MOE_OK) return rc;
-  return moe_expert_ffn(w, x, xdt, T, k, offsets, perm_src, y_perm, mode, ws, kScratchBytes, stream);
+  // (no helper stream: the first use of one would create it)
+  return expert_ffn(w, x, xdt, T, k, offsets, perm_src, y_perm, mode, ws, kScratchBytes, stream, false);
 }
