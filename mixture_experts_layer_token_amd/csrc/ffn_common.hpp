@@ -50,18 +50,21 @@ __device__ __forceinline__ unsigned in_vgpr(unsigned c) {
 // 8 INT4 elements (nibble n < 4: element 2n, n >= 4: element 2(n-4)+1, stored as q + 8) -> fp16 q*s,
 // by the usual "magic number" integer-to-float conversion: fp16 0x6400 is 1024, whose unit in the
 // last place is 1, so OR-ing c = q + 8 into its low mantissa bits gives exactly 1024 + c in each
-// half; minus 1032 gives q, times s; every step is exact in fp16 for s in binary16's normal range.
+// half; minus 1032 gives q, times s.  The nibble pairs at bits 4-7 of each half need no shift:
+// fp16 0x5400 is 64, whose unit in the last place is 1/16, so OR-ing c << 4 into it gives exactly
+// 64 + c, minus 72 gives q.  Pairs 0 and 1 come from v, pairs 2 and 3 from v >> 8 (one shift for
+// the eight elements).  Every step is exact in fp16 for s in binary16's normal range.
 __device__ __forceinline__ f16x8 dec_int4(unsigned v, _Float16 s) {
-  const f16x2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
+  const f16x2 bias_lo = {(_Float16)1032.0f, (_Float16)1032.0f}, bias_hi = {(_Float16)72.0f, (_Float16)72.0f};
   const f16x2 ss = {s, s};
-  const unsigned mask = in_vgpr(0x000F000Fu), magic = in_vgpr(0x64006400u);
+  const unsigned mask_lo = in_vgpr(0x000F000Fu), magic_lo = in_vgpr(0x64006400u);
+  const unsigned mask_hi = in_vgpr(0x00F000F0u), magic_hi = in_vgpr(0x54005400u);
+  const unsigned v8 = v >> 8;
   f16x2 r[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    unsigned p = ((v >> (4 * j)) & mask) | magic;
-    f16x2 h = __builtin_bit_cast(f16x2, p);
-    r[j] = (h - bias) * ss;
-  }
+  r[0] = (__builtin_bit_cast(f16x2, (v & mask_lo) | magic_lo) - bias_lo) * ss;
+  r[1] = (__builtin_bit_cast(f16x2, (v & mask_hi) | magic_hi) - bias_hi) * ss;
+  r[2] = (__builtin_bit_cast(f16x2, (v8 & mask_lo) | magic_lo) - bias_lo) * ss;
+  r[3] = (__builtin_bit_cast(f16x2, (v8 & mask_hi) | magic_hi) - bias_hi) * ss;
   return f16x8{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
 }
 

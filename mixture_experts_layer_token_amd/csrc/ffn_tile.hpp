@@ -371,29 +371,31 @@ __device__ __forceinline__ void tile_body(const FfnArgs& args, TileCtx& c, unsig
         out[st / 2] = pin(__builtin_bit_cast(unsigned, r));
       }
     } else if constexpr (FMT == MOE_W_INT4G32) {
-      // the INT4 decode of dec_int4, one nibble pair p at a time: (v >> 4p) & mask | magic,
-      // minus 1032, times the scale
+      // the INT4 decode of dec_int4, one nibble pair at a time: pairs 0 and 2 (bits 0-3 of each
+      // half of v and of v >> 8) as (w & 0x000F000F) | 0x6400 per half, minus 1032; pairs 1 and 3
+      // (bits 4-7) as (w & 0x00F000F0) | 0x5400, minus 72; then times the scale
       const _Float16 sc = __builtin_bit_cast(_Float16, (unsigned short)(B.sc[j] >> (16 * q)));
-      const f16x2 bias = {(_Float16)1032.0f, (_Float16)1032.0f};
+      const f16x2 bias_lo = {(_Float16)1032.0f, (_Float16)1032.0f}, bias_hi = {(_Float16)72.0f, (_Float16)72.0f};
       const f16x2 ss = {sc, sc};
-      const unsigned mask = in_vgpr(0x000F000Fu), magic = in_vgpr(0x64006400u);
+      const unsigned mask_lo = in_vgpr(0x000F000Fu), magic_lo = in_vgpr(0x64006400u);
+      const unsigned mask_hi = in_vgpr(0x00F000F0u), magic_hi = in_vgpr(0x54005400u);
       const unsigned v = B.v[j][q];
-      auto sub = [&](unsigned w) { return __builtin_bit_cast(unsigned, __builtin_bit_cast(f16x2, w) - bias); };
+      auto sub = [&](unsigned w, const f16x2& b) {
+        return __builtin_bit_cast(unsigned, __builtin_bit_cast(f16x2, w) - b);
+      };
       auto mul = [&](unsigned w) { return __builtin_bit_cast(unsigned, __builtin_bit_cast(f16x2, w) * ss); };
-      // Two dependency chains, one instruction of each per sub-step, the longer chain first: an
-      // instruction never follows its producer with only MFMA code in between (the compiler
-      // would insert a wait state there: it cannot see that the assembly is not a vector op).
-      //   chain a (pairs 1, 3): shift, and-or, subtract, multiply, then the same for pair 3
-      //   chain b (pairs 0, 2): and-or, subtract, multiply, then shift, and-or, subtract, multiply
+      // 13 instructions in 8 sub-steps, ordered so that no instruction reads the result of the
+      // instruction right before it with only MFMA code in between (the compiler would insert a
+      // wait state there: it cannot see that the assembly is not a vector op).
       switch (st) {
-        case 0: t[1] = pin(v >> 4); t[0] = pin((v & mask) | magic); break;
-        case 1: t[1] = pin((t[1] & mask) | magic); t[0] = pin(sub(t[0])); break;
-        case 2: t[1] = pin(sub(t[1])); out[0] = pin(mul(t[0])); break;
-        case 3: out[1] = pin(mul(t[1])); t[2] = pin(v >> 8); break;
-        case 4: t[3] = pin(v >> 12); t[2] = pin((t[2] & mask) | magic); break;
-        case 5: t[3] = pin((t[3] & mask) | magic); t[2] = pin(sub(t[2])); break;
-        case 6: t[3] = pin(sub(t[3])); out[2] = pin(mul(t[2])); break;
-        default: out[3] = pin(mul(t[3])); break;
+        case 0: t[1] = pin((v & mask_hi) | magic_hi); t[0] = pin((v & mask_lo) | magic_lo); break;
+        case 1: t[1] = pin(sub(t[1], bias_hi)); t[0] = pin(sub(t[0], bias_lo)); break;
+        case 2: out[1] = pin(mul(t[1])); t[2] = pin(v >> 8); break;
+        case 3: out[0] = pin(mul(t[0])); break;
+        case 4: t[3] = pin((t[2] & mask_hi) | magic_hi); t[2] = pin((t[2] & mask_lo) | magic_lo); break;
+        case 5: t[3] = pin(sub(t[3], bias_hi)); t[2] = pin(sub(t[2], bias_lo)); break;
+        case 6: out[3] = pin(mul(t[3])); out[2] = pin(mul(t[2])); break;
+        default: break;
       }
     }
   };
