@@ -706,6 +706,7 @@ int oracle_xw4_decode(const uint8_t* blob, int64_t blob_bytes, uint8_t* raw, int
   if (total > blob_bytes || le_get(blob + 64, 4) != 0 || data + (int64_t)le_get(blob + 64 + 4 * n, 4) != total) return -1;
   for (int64_t i = 0; i < n; ++i) {
     const int64_t o0 = (int64_t)le_get(blob + 64 + 4 * i, 4), o1 = (int64_t)le_get(blob + 64 + 4 * (i + 1), 4);
+    if (o1 < o0 || data + o1 > total) return -1; /* chunks lie in order inside the blob */
     const int64_t size = o1 - o0;
     const uint8_t* src = blob + data + o0;
     uint8_t* dst = raw + 1024 * i;

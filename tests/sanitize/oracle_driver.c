@@ -40,6 +40,34 @@ static void* xmalloc(size_t n) {
   return p;
 }
 
+int64_t oracle_xw4_bound(int64_t);
+int64_t oracle_xw4_encode(const uint8_t*, int64_t, uint8_t*, int64_t);
+int oracle_xw4_decode(const uint8_t*, int64_t, uint8_t*, int64_t);
+
+/* the lossless code on gaussian, random and escape-heavy chunks, round trip and malformed blobs */
+static int xw4_checks(void) {
+  enum { N = 1024 * 24 };
+  uint16_t* v = xmalloc(N);
+  uint8_t* back = xmalloc(N);
+  synth_normal_bf16(7, 1, 0, N / 2, 0.02, v);
+  for (int i = 0; i < 512; ++i) v[4 * 512 + i] = (uint16_t)(i * 2654435761u >> 16); /* a random-bits chunk */
+  for (int i = 0; i < 300; ++i) v[6 * 512 + i] = 0x0080;                         /* many escapes: raw */
+  for (int i = 0; i < 40; ++i) v[8 * 512 + 3 * i] = 0;                           /* a few escapes */
+  const int64_t cap = oracle_xw4_bound(N);
+  uint8_t* blob = xmalloc((size_t)cap);
+  const int64_t n = oracle_xw4_encode((const uint8_t*)v, N, blob, cap);
+  if (n <= 0 || n > cap) return 1;
+  if (oracle_xw4_decode(blob, n, back, N) != 0 || memcmp(back, v, N) != 0) return 2;
+  if (oracle_xw4_decode(blob, 100, back, N) == 0) return 3; /* truncated */
+  blob[64 + 4] ^= 0x40;                                      /* a corrupt chunk offset */
+  (void)oracle_xw4_decode(blob, n, back, N);
+  if (oracle_xw4_encode((const uint8_t*)v, 1000, blob, cap) != -1) return 4;
+  free(v);
+  free(back);
+  free(blob);
+  return 0;
+}
+
 int main(void) {
   /* experts in all four formats */
   oracle_expert ex[4];
@@ -102,6 +130,7 @@ int main(void) {
   /* (group 3 pins three keys: 8 slots leave room for every demand group of three) */
   if (oracle_cache_sim(8, 0, 0, G, off, keys, kinds, hits, misses, victims, nv, &ph) != 0) return 6;
   if (oracle_cache_sim(8, 1, 4, G, off, keys, kinds, hits, misses, victims, nv, &ph) != 0) return 7;
+  if (xw4_checks() != 0) return 8;
   for (int i = 0; i < nk; ++i) free(keep[i]);
   free(x);
   free(wg);

@@ -50,6 +50,23 @@ int main() {
     delete p;
     moe_cache_destroy(c);
   }
-  printf("planner: ok (%d copies)\n", copies);
+  // the host encoder of the lossless code: a hand-worked chunk (largest exponent 128, two escapes)
+  // and random bit patterns, sizes and the refusals
+  {
+    std::vector<uint16_t> v(512 * 6);
+    for (size_t i = 0; i < v.size(); ++i) v[i] = (uint16_t)((i * 2654435761u) >> 13);
+    v[0] = 0xC000, v[1] = 0x0000, v[2] = 0x3FC0, v[3] = 0x8001;
+    for (int i = 4; i < 512; ++i) v[i] = 0x3F80;
+    const size_t raw = v.size() * 2, cap = moe_compress_bound(raw);
+    std::vector<uint8_t> blob(cap);
+    size_t n = 0;
+    if (moe_compress_package(v.data(), raw, blob.data(), cap, &n) != MOE_OK || n > cap) return 9;
+    uint32_t off1;
+    memcpy(&off1, blob.data() + 68, 4);
+    if (off1 != 784 || blob[64 + 4 * 7] != 114) return 10;  // first chunk: 768 + 16 bytes, window base 114
+    if (moe_compress_package(v.data(), raw, blob.data(), cap - 1, &n) != MOE_ERR_INVALID) return 11;
+    if (moe_compress_package(v.data(), 1000, blob.data(), cap, &n) != MOE_ERR_INVALID) return 12;
+  }
+  printf("planner and encoder: ok (%d copies)\n", copies);
   return 0;
 }

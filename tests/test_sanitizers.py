@@ -1,7 +1,7 @@
 """AddressSanitizer and UndefinedBehaviorSanitizer builds of the host-side C/C++ code: the oracle and
-the input generator (gcc), and the expert-cache planner with the library's error state (hipcc,
-sanitizers on the host code only); each runs a driver that exercises every function and fails on
-any report."""
+the input generator (gcc), and the expert-cache planner, the lossless encoder and the library's error
+state (hipcc, sanitizers on the host code only); each runs a driver that exercises every function and
+fails on any report."""
 import os
 import shutil
 import subprocess
@@ -32,7 +32,7 @@ def test_oracle_and_generator_under_sanitizers(tmp_path):
 @pytest.mark.skipif(shutil.which("hipcc") is None, reason="needs hipcc")
 def test_planner_under_sanitizers(tmp_path):
     objs = []
-    for src in ("cache.cpp", "errors.cpp"):
+    for src in ("cache.cpp", "errors.cpp", "compress.cpp"):
         o = str(tmp_path / (src + ".o"))
         host_san = [a for f in SAN for a in ("-Xarch_host", f)]
         _run(["hipcc", "-x", "hip", "--offload-arch=gfx950", "-O1", "-g", "-std=c++17", *host_san, "-c",
