@@ -69,6 +69,12 @@ def lib():
         L.oracle_xw4_encode.restype = i64
         L.oracle_xw4_decode.argtypes = [vp, i64, vp, i64]
         L.oracle_xw4_decode.restype = i32
+        L.oracle_rns_bound.argtypes = [i64]
+        L.oracle_rns_bound.restype = i64
+        L.oracle_rns_encode.argtypes = [vp, i64, i64, vp, i64]
+        L.oracle_rns_encode.restype = i64
+        L.oracle_rns_decode.argtypes = [vp, i64, vp, i64]
+        L.oracle_rns_decode.restype = i32
         for f in ("oracle_decode", "oracle_decode_act", "oracle_router_logits", "oracle_topk_gates",
                   "oracle_permute", "oracle_ffn"):
             getattr(L, f).restype = None
@@ -261,6 +267,25 @@ def xw4_decode(blob: np.ndarray, raw_bytes: int) -> np.ndarray:
     blob = np.ascontiguousarray(blob).view(np.uint8).ravel()
     out = np.zeros(raw_bytes, np.uint8)
     if lib().oracle_xw4_decode(_p(blob), blob.size, _p(out), raw_bytes) != 0:
+        raise ValueError("malformed blob")
+    return out
+
+
+def rns_encode(raw: np.ndarray, q: int) -> np.ndarray:
+    """Order-0 rANS code of a package (uint8 bytes) cut at byte q into two regions -> blob bytes."""
+    raw = np.ascontiguousarray(raw).view(np.uint8).ravel()
+    cap = int(lib().oracle_rns_bound(raw.size))
+    out = np.zeros(cap, np.uint8)
+    n = int(lib().oracle_rns_encode(_p(raw), raw.size, q, _p(out), cap))
+    if n < 0:
+        raise ValueError("encode failed")
+    return out[:n].copy()
+
+
+def rns_decode(blob: np.ndarray, raw_bytes: int) -> np.ndarray:
+    blob = np.ascontiguousarray(blob).view(np.uint8).ravel()
+    out = np.zeros(raw_bytes, np.uint8)
+    if lib().oracle_rns_decode(_p(blob), blob.size, _p(out), raw_bytes) != 0:
         raise ValueError("malformed blob")
     return out
 

@@ -733,3 +733,164 @@ int oracle_xw4_decode(const uint8_t* blob, int64_t blob_bytes, uint8_t* raw, int
   }
   return 0;
 }
+
+/* ------------------------------------------------------------------------------------------
+ * Lossless compression of any package (4-bit ones included): an order-0 range-asymmetric-numeral-
+ * system (rANS) code of its bytes, from this definition (the pages name no codec; see the
+ * exponent-window code above for the lossless tier they describe):
+ *
+ *  - The package of n bytes is cut at byte q into two regions (the codes, then the scales); each
+ *    region is coded on its own.
+ *  - Region model: h[s] = occurrences of byte s; f[s] = max(1, floor(4096 h[s] / m)) for every
+ *    present s (m the region's length), 0 otherwise; while the f sum to more than 4096 the largest
+ *    f (smallest s among equals) loses one, while they sum to less the largest gains the rest.
+ *    c[s] = f[0] + ... + f[s-1].
+ *  - Streams: region byte j belongs to stream j mod S (S = 8192), as its (j div S)-th symbol.  A
+ *    stream is coded last symbol first from x = 2^16: before a symbol s, while x >= 2^20 f[s] the
+ *    low 16 bits of x are emitted and x shifts right by 16; then x = 4096 (x div f[s]) +
+ *    (x mod f[s]) + c[s].  The final x is the stream's state; its words are stored in the reverse
+ *    of their emission order, so decoding reads them forward: a symbol is the s with
+ *    c[s] <= x mod 4096 < c[s] + f[s], then x = f[s] (x div 4096) + (x mod 4096) - c[s], and while
+ *    x < 2^16, x = 2^16 x + the next word.  Decoding a whole stream returns x to 2^16.
+ *  - Blob: a 64-byte header (u32 magic 0x31534E52, u32 S, u64 n, u64 q, u64 blob bytes, zeros),
+ *    then per region (region 0 first): u16 f[256], u32 states[S], u32 word offsets off[0..S]
+ *    (stream i's words are words off[i] .. off[i+1]-1 of the region), the u16 words, zeros up to a
+ *    multiple of 16 bytes.
+ * ------------------------------------------------------------------------------------------ */
+#define RNS_MAGIC 0x31534E52u
+#define RNS_S 8192
+
+static void rns_model(const uint8_t* r, int64_t m, uint32_t* f) {
+  int64_t h[256] = {0};
+  for (int64_t j = 0; j < m; ++j) h[r[j]]++;
+  int64_t sum = 0;
+  for (int s = 0; s < 256; ++s) {
+    f[s] = 0;
+    if (h[s]) {
+      const int64_t v = (int64_t)(h[s] * 4096 / m);
+      f[s] = (uint32_t)(v < 1 ? 1 : v);
+    }
+    sum += f[s];
+  }
+  while (m > 0 && sum != 4096) {
+    int best = 0;
+    for (int s = 1; s < 256; ++s)
+      if (f[s] > f[best]) best = s;
+    if (sum > 4096) {
+      f[best] -= 1;
+      sum -= 1;
+    } else {
+      f[best] += (uint32_t)(4096 - sum);
+      sum = 4096;
+    }
+  }
+}
+
+static int64_t rns_region_bound(int64_t m) { return 512 + 4 * RNS_S + 4 * (RNS_S + 1) + 2 * (m + 2 * RNS_S) + 16; }
+
+int64_t oracle_rns_bound(int64_t n) { return 64 + rns_region_bound(n) * 2; }
+
+/* codes region r (m bytes) at out; returns its bytes (a multiple of 16) */
+static int64_t rns_encode_region(const uint8_t* r, int64_t m, uint8_t* out) {
+  uint32_t f[256], c[256];
+  rns_model(r, m, f);
+  c[0] = 0;
+  for (int s = 1; s < 256; ++s) c[s] = c[s - 1] + f[s - 1];
+  for (int s = 0; s < 256; ++s) le_put(out + 2 * s, f[s], 2);
+  uint8_t* states = out + 512;
+  uint8_t* offs = states + 4 * RNS_S;
+  uint8_t* words = offs + 4 * (RNS_S + 1);
+  uint16_t* tmp = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(2 * (m / RNS_S + 1) + 2));
+  int64_t w = 0;
+  for (int i = 0; i < RNS_S; ++i) {
+    le_put(offs + 4 * i, (uint64_t)w, 4);
+    const int64_t count = i < m ? (m - i + RNS_S - 1) / RNS_S : 0;
+    uint64_t x = 1u << 16;
+    int64_t nw = 0;
+    for (int64_t j = count - 1; j >= 0; --j) {
+      const uint8_t s = r[i + j * RNS_S];
+      while (x >= ((uint64_t)f[s] << 20)) {
+        tmp[nw++] = (uint16_t)(x & 0xFFFF);
+        x >>= 16;
+      }
+      x = (x / f[s]) * 4096 + (x % f[s]) + c[s];
+    }
+    le_put(states + 4 * i, x, 4);
+    for (int64_t k = 0; k < nw; ++k) le_put(words + 2 * (w + k), tmp[nw - 1 - k], 2);
+    w += nw;
+  }
+  le_put(offs + 4 * RNS_S, (uint64_t)w, 4);
+  free(tmp);
+  int64_t bytes = 512 + 4 * RNS_S + 4 * (RNS_S + 1) + 2 * w;
+  const int64_t padded = (bytes + 15) / 16 * 16;
+  memset(out + bytes, 0, (size_t)(padded - bytes));
+  return padded;
+}
+
+/* Returns the blob's size, or -1 (q > n, or cap too small). */
+int64_t oracle_rns_encode(const uint8_t* raw, int64_t n, int64_t q, uint8_t* out, int64_t cap) {
+  if (n < 0 || q < 0 || q > n || cap < oracle_rns_bound(n)) return -1;
+  memset(out, 0, 64);
+  int64_t pos = 64;
+  pos += rns_encode_region(raw, q, out + pos);
+  pos += rns_encode_region(raw + q, n - q, out + pos);
+  le_put(out, RNS_MAGIC, 4);
+  le_put(out + 4, RNS_S, 4);
+  le_put(out + 8, (uint64_t)n, 8);
+  le_put(out + 16, (uint64_t)q, 8);
+  le_put(out + 24, (uint64_t)pos, 8);
+  return pos;
+}
+
+/* decodes region r (m bytes) from its section at in (avail bytes); returns the section's bytes or -1 */
+static int64_t rns_decode_region(const uint8_t* in, int64_t avail, uint8_t* r, int64_t m) {
+  const int64_t head = 512 + 4 * RNS_S + 4 * (RNS_S + 1);
+  if (avail < head) return -1;
+  uint32_t f[256], c[256];
+  int64_t sum = 0;
+  for (int s = 0; s < 256; ++s) f[s] = (uint32_t)le_get(in + 2 * s, 2), sum += f[s];
+  if (m > 0 && sum != 4096) return -1;
+  c[0] = 0;
+  for (int s = 1; s < 256; ++s) c[s] = c[s - 1] + f[s - 1];
+  const uint8_t* states = in + 512;
+  const uint8_t* offs = states + 4 * RNS_S;
+  const uint8_t* words = offs + 4 * (RNS_S + 1);
+  const int64_t total_w = (int64_t)le_get(offs + 4 * RNS_S, 4);
+  if (head + 2 * total_w > avail) return -1;
+  for (int i = 0; i < RNS_S; ++i) {
+    const int64_t count = i < m ? (m - i + RNS_S - 1) / RNS_S : 0;
+    int64_t k = (int64_t)le_get(offs + 4 * i, 4);
+    const int64_t kend = (int64_t)le_get(offs + 4 * (i + 1), 4);
+    if (k > kend || kend > total_w) return -1;
+    uint64_t x = le_get(states + 4 * i, 4);
+    for (int64_t j = 0; j < count; ++j) {
+      const uint32_t slot = (uint32_t)(x & 4095);
+      int s = 0;
+      while (s < 255 && !(c[s] <= slot && slot < c[s] + f[s])) ++s;
+      if (!(c[s] <= slot && slot < c[s] + f[s])) return -1;
+      r[i + j * RNS_S] = (uint8_t)s;
+      x = (uint64_t)f[s] * (x >> 12) + slot - c[s];
+      while (x < (1u << 16)) {
+        if (k >= kend) return -1;
+        x = (x << 16) | le_get(words + 2 * k, 2);
+        ++k;
+      }
+    }
+    if (x != (1u << 16) || k != kend) return -1;
+  }
+  return (head + 2 * total_w + 15) / 16 * 16;
+}
+
+/* Decodes a blob into n bytes; 0, or -1 if the blob is not a well-formed encoding of n bytes. */
+int oracle_rns_decode(const uint8_t* blob, int64_t blob_bytes, uint8_t* raw, int64_t n) {
+  if (blob_bytes < 64 || le_get(blob, 4) != RNS_MAGIC || le_get(blob + 4, 4) != RNS_S ||
+      (int64_t)le_get(blob + 8, 8) != n)
+    return -1;
+  const int64_t q = (int64_t)le_get(blob + 16, 8), total = (int64_t)le_get(blob + 24, 8);
+  if (q < 0 || q > n || total > blob_bytes) return -1;
+  const int64_t a = rns_decode_region(blob + 64, total - 64, raw, q);
+  if (a < 0) return -1;
+  const int64_t b = rns_decode_region(blob + 64 + a, total - 64 - a, raw + q, n - q);
+  if (b < 0 || 64 + a + b != total) return -1;
+  return 0;
+}

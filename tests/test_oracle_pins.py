@@ -650,3 +650,117 @@ def test_xw4_decode_rejects_malformed_blobs():
         oracle.xw4_decode(blob[:600], 1024)
     with pytest.raises(ValueError):
         oracle.xw4_encode(np.zeros(1000, np.uint8))
+
+
+# ---- order-0 rANS code of packages (the definition is in oracle.c)
+
+RNS_S = 8192
+RNS_REGION_HEAD = 512 + 4 * RNS_S + 4 * (RNS_S + 1)
+
+
+def _rns_region(blob, off):
+    f = blob[off:off + 512].view(np.uint16)
+    states = blob[off + 512:off + 512 + 4 * RNS_S].view(np.uint32)
+    offs = blob[off + 512 + 4 * RNS_S:off + RNS_REGION_HEAD].view(np.uint32)
+    return f, states, offs
+
+
+def test_rns_hand_worked_region():
+    """Bytes [0, 0, 1] as one region, worked by hand: h = {0: 2, 1: 1}, m = 3, so f[0] = floor(8192/3)
+    = 2730 and f[1] = 1365 sum to 4095 and the larger, f[0], takes the missing one: 2731; c[1] = 2731.
+    Streams 0, 1, 2 hold one symbol each.  From x = 65536 no word is emitted (65536 < 2^20 f), and
+    x = 4096 (x div f) + (x mod f) + c: symbol 0 -> 4096 * 23 + 2723 = 96931, symbol 1 -> 4096 * 48 +
+    16 + 2731 = 199355.  Every other stream keeps 65536; no words; each region section is 66052
+    bytes padded to 66064; the second region is empty."""
+    raw = np.array([0, 0, 1], np.uint8)
+    blob = oracle.rns_encode(raw, 3)
+    assert blob.size == 64 + 2 * 66064
+    assert blob[:4].tobytes() == bytes([0x52, 0x4E, 0x53, 0x31])
+    assert blob[4:8].view(np.uint32)[0] == RNS_S
+    assert blob[8:16].view(np.uint64)[0] == 3 and blob[16:24].view(np.uint64)[0] == 3
+    assert blob[24:32].view(np.uint64)[0] == blob.size
+    f, states, offs = _rns_region(blob, 64)
+    assert f[0] == 2731 and f[1] == 1365 and f[2:].sum() == 0
+    assert states[:3].tolist() == [96931, 96931, 199355]
+    assert (states[3:] == 65536).all() and (offs == 0).all()
+    f2, states2, offs2 = _rns_region(blob, 64 + 66064)
+    assert f2.sum() == 0 and (states2 == 65536).all() and (offs2 == 0).all()
+    assert np.array_equal(oracle.rns_decode(blob, 3), raw)
+
+
+@pytest.mark.parametrize("kind", ["single", "uniform256", "rare"])
+def test_rns_model_normalisation(kind):
+    """Frequencies sum to 4096 with every present byte at least 1: a single byte value takes all
+    4096; 256 equally frequent values take 16 each; a value seen once in 10,000 bytes gets 1 and
+    the largest value gives up the excess."""
+    if kind == "single":
+        raw, want = np.full(1000, 7, np.uint8), {7: 4096}
+    elif kind == "uniform256":
+        raw, want = np.tile(np.arange(256, dtype=np.uint8), 40), {s: 16 for s in range(256)}
+    else:
+        raw = np.zeros(10000, np.uint8)
+        raw[:6000] = 3
+        raw[6000:9999] = 9
+        raw[9999] = 200
+        # floor(6000*4096/10000) = 2457, floor(3999*4096/10000) = 1637, 200 -> max(1, 0) = 1: sum 4095,
+        # the largest (3) takes the missing one
+        want = {3: 2458, 9: 1637, 200: 1}
+    blob = oracle.rns_encode(raw, raw.size)
+    f, _, _ = _rns_region(blob, 64)
+    assert {s: int(v) for s, v in enumerate(f) if v} == want
+    assert np.array_equal(oracle.rns_decode(blob, raw.size), raw)
+
+
+def test_rns_streams_interleave_and_emit_words():
+    """Region byte j is symbol j div S of stream j mod S: a region where only stream 5 carries
+    information (every other byte 0) emits words for stream 5 alone."""
+    m = RNS_S * 40
+    raw = np.zeros(m, np.uint8)
+    rng = np.random.default_rng(2)
+    raw[5::RNS_S] = rng.integers(1, 256, 40)
+    blob = oracle.rns_encode(raw, m)
+    f, states, offs = _rns_region(blob, 64)
+    words = np.diff(offs.astype(np.int64))
+    assert words[5] > 0 and words.sum() == words[5]
+    assert np.array_equal(oracle.rns_decode(blob, m), raw)
+
+
+def test_rns_size_within_the_entropy_bound():
+    """Independent bytes of a known distribution: every emitted word carries 16 bits of the code,
+    so the words are at most the order-0 information of the symbols under the model's frequencies
+    plus 16 bits per stream (the final state holds the rest)."""
+    rng = np.random.default_rng(3)
+    p = np.array([0.5, 0.25, 0.125, 0.0625, 0.0625])
+    m = RNS_S * 64
+    raw = rng.choice(5, m, p=p).astype(np.uint8)
+    blob = oracle.rns_encode(raw, m)
+    f, _, offs = _rns_region(blob, 64)
+    info_bits = -np.log2(f[raw] / 4096.0).sum()
+    words = int(offs[-1])
+    assert 16 * words <= info_bits + 16 * RNS_S
+    assert 16 * words >= info_bits - 32 * RNS_S
+    assert np.array_equal(oracle.rns_decode(blob, m), raw)
+
+
+@pytest.mark.parametrize("n,q", [(0, 0), (1, 0), (1, 1), (5000, 1234), (RNS_S * 3 + 7, RNS_S + 1)])
+def test_rns_round_trip(n, q):
+    rng = np.random.default_rng(n + q)
+    raw = (rng.normal(0, 30, n).astype(np.int64) & 255).astype(np.uint8)
+    blob = oracle.rns_encode(raw, q)
+    assert np.array_equal(oracle.rns_decode(blob, n), raw)
+
+
+def test_rns_decode_rejects_malformed_blobs():
+    rng = np.random.default_rng(4)
+    raw = rng.integers(0, 16, RNS_S * 40).astype(np.uint8)
+    blob = oracle.rns_encode(raw, RNS_S * 20)
+    words0 = int(_rns_region(blob, 64)[2][-1])
+    second = 64 + (RNS_REGION_HEAD + 2 * words0 + 15) // 16 * 16
+    # the magic, the size, a state and a word of region 0, the model of region 1
+    for where in (0, 8, 64 + 512 + 4 * 3, 64 + RNS_REGION_HEAD + 2 * (words0 // 2), second + 2):
+        bad = blob.copy()
+        bad[where] ^= 0x5A
+        with pytest.raises(ValueError):
+            oracle.rns_decode(bad, raw.size)
+    with pytest.raises(ValueError):
+        oracle.rns_decode(blob[:1000], raw.size)
