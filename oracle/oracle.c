@@ -746,15 +746,19 @@ int oracle_xw4_decode(const uint8_t* blob, int64_t blob_bytes, uint8_t* raw, int
  *    f (smallest s among equals) loses one, while they sum to less the largest gains the rest.
  *    c[s] = f[0] + ... + f[s-1].
  *  - Streams: region byte j belongs to stream j mod S (S = 8192), as its (j div S)-th symbol.  A
- *    stream is coded last symbol first from x = 2^16: before a symbol s, while x >= 2^20 f[s] the
- *    low 16 bits of x are emitted and x shifts right by 16; then x = 4096 (x div f[s]) +
- *    (x mod f[s]) + c[s].  The final x is the stream's state; its words are stored in the reverse
- *    of their emission order, so decoding reads them forward: a symbol is the s with
- *    c[s] <= x mod 4096 < c[s] + f[s], then x = f[s] (x div 4096) + (x mod 4096) - c[s], and while
- *    x < 2^16, x = 2^16 x + the next word.  Decoding a whole stream returns x to 2^16.
+ *    stream is coded from x = 2^16, last symbol first: before a symbol s, if x >= 2^20 f[s] a word
+ *    (the low 16 bits of x) is emitted and x shifts right by 16; then
+ *    x = 4096 (x div f[s]) + (x mod f[s]) + c[s].  The final x is the stream's state.  Decoding: the
+ *    symbol is the s with c[s] <= x mod 4096 < c[s] + f[s], then x = f[s] (x div 4096) +
+ *    (x mod 4096) - c[s], and if x < 2^16, x = 2^16 x + the next word.  Decoding a whole stream
+ *    returns x to 2^16.
+ *  - Words: streams 64g .. 64g+63 form group g and share one word sequence, in decoding order: for
+ *    each symbol index j ascending, the words the group's streams read after their j-th symbol, in
+ *    stream order.  (So the coder runs the group's streams in step, j descending and streams in
+ *    descending order, and stores the emitted words reversed.)
  *  - Blob: a 64-byte header (u32 magic 0x31534E52, u32 S, u64 n, u64 q, u64 blob bytes, zeros),
- *    then per region (region 0 first): u16 f[256], u32 states[S], u32 word offsets off[0..S]
- *    (stream i's words are words off[i] .. off[i+1]-1 of the region), the u16 words, zeros up to a
+ *    then per region (region 0 first): u16 f[256], u32 states[S], u32 word offsets off[0..S/64]
+ *    (group g's words are words off[g] .. off[g+1]-1 of the region), the u16 words, zeros up to a
  *    multiple of 16 bytes.
  * ------------------------------------------------------------------------------------------ */
 #define RNS_MAGIC 0x31534E52u
@@ -786,9 +790,12 @@ static void rns_model(const uint8_t* r, int64_t m, uint32_t* f) {
   }
 }
 
-static int64_t rns_region_bound(int64_t m) { return 512 + 4 * RNS_S + 4 * (RNS_S + 1) + 2 * (m + 2 * RNS_S) + 16; }
+#define RNS_G (RNS_S / 64)
+static int64_t rns_region_bound(int64_t m) { return 512 + 4 * RNS_S + 4 * (RNS_G + 1) + 2 * (m + 2 * RNS_S) + 16; }
 
 int64_t oracle_rns_bound(int64_t n) { return 64 + rns_region_bound(n) * 2; }
+
+static int64_t rns_count(int64_t m, int64_t i) { return i < m ? (m - i + RNS_S - 1) / RNS_S : 0; }
 
 /* codes region r (m bytes) at out; returns its bytes (a multiple of 16) */
 static int64_t rns_encode_region(const uint8_t* r, int64_t m, uint8_t* out) {
@@ -799,29 +806,33 @@ static int64_t rns_encode_region(const uint8_t* r, int64_t m, uint8_t* out) {
   for (int s = 0; s < 256; ++s) le_put(out + 2 * s, f[s], 2);
   uint8_t* states = out + 512;
   uint8_t* offs = states + 4 * RNS_S;
-  uint8_t* words = offs + 4 * (RNS_S + 1);
-  uint16_t* tmp = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(2 * (m / RNS_S + 1) + 2));
+  uint8_t* words = offs + 4 * (RNS_G + 1);
+  uint16_t* tmp = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(64 * (m / RNS_S + 2)));
   int64_t w = 0;
-  for (int i = 0; i < RNS_S; ++i) {
-    le_put(offs + 4 * i, (uint64_t)w, 4);
-    const int64_t count = i < m ? (m - i + RNS_S - 1) / RNS_S : 0;
-    uint64_t x = 1u << 16;
+  for (int g = 0; g < RNS_G; ++g) {
+    le_put(offs + 4 * g, (uint64_t)w, 4);
+    uint64_t x[64];
+    for (int l = 0; l < 64; ++l) x[l] = 1u << 16;
     int64_t nw = 0;
-    for (int64_t j = count - 1; j >= 0; --j) {
-      const uint8_t s = r[i + j * RNS_S];
-      while (x >= ((uint64_t)f[s] << 20)) {
-        tmp[nw++] = (uint16_t)(x & 0xFFFF);
-        x >>= 16;
+    for (int64_t j = rns_count(m, 64 * g) - 1; j >= 0; --j) {
+      for (int l = 63; l >= 0; --l) {
+        const int64_t i = 64 * g + l;
+        if (j >= rns_count(m, i)) continue;
+        const uint8_t s = r[i + j * RNS_S];
+        if (x[l] >= ((uint64_t)f[s] << 20)) {
+          tmp[nw++] = (uint16_t)(x[l] & 0xFFFF);
+          x[l] >>= 16;
+        }
+        x[l] = (x[l] / f[s]) * 4096 + (x[l] % f[s]) + c[s];
       }
-      x = (x / f[s]) * 4096 + (x % f[s]) + c[s];
     }
-    le_put(states + 4 * i, x, 4);
+    for (int l = 0; l < 64; ++l) le_put(states + 4 * (64 * g + l), x[l], 4);
     for (int64_t k = 0; k < nw; ++k) le_put(words + 2 * (w + k), tmp[nw - 1 - k], 2);
     w += nw;
   }
-  le_put(offs + 4 * RNS_S, (uint64_t)w, 4);
+  le_put(offs + 4 * RNS_G, (uint64_t)w, 4);
   free(tmp);
-  int64_t bytes = 512 + 4 * RNS_S + 4 * (RNS_S + 1) + 2 * w;
+  int64_t bytes = 512 + 4 * RNS_S + 4 * (RNS_G + 1) + 2 * w;
   const int64_t padded = (bytes + 15) / 16 * 16;
   memset(out + bytes, 0, (size_t)(padded - bytes));
   return padded;
@@ -844,7 +855,7 @@ int64_t oracle_rns_encode(const uint8_t* raw, int64_t n, int64_t q, uint8_t* out
 
 /* decodes region r (m bytes) from its section at in (avail bytes); returns the section's bytes or -1 */
 static int64_t rns_decode_region(const uint8_t* in, int64_t avail, uint8_t* r, int64_t m) {
-  const int64_t head = 512 + 4 * RNS_S + 4 * (RNS_S + 1);
+  const int64_t head = 512 + 4 * RNS_S + 4 * (RNS_G + 1);
   if (avail < head) return -1;
   uint32_t f[256], c[256];
   int64_t sum = 0;
@@ -854,29 +865,36 @@ static int64_t rns_decode_region(const uint8_t* in, int64_t avail, uint8_t* r, i
   for (int s = 1; s < 256; ++s) c[s] = c[s - 1] + f[s - 1];
   const uint8_t* states = in + 512;
   const uint8_t* offs = states + 4 * RNS_S;
-  const uint8_t* words = offs + 4 * (RNS_S + 1);
-  const int64_t total_w = (int64_t)le_get(offs + 4 * RNS_S, 4);
+  const uint8_t* words = offs + 4 * (RNS_G + 1);
+  const int64_t total_w = (int64_t)le_get(offs + 4 * RNS_G, 4);
   if (head + 2 * total_w > avail) return -1;
-  for (int i = 0; i < RNS_S; ++i) {
-    const int64_t count = i < m ? (m - i + RNS_S - 1) / RNS_S : 0;
-    int64_t k = (int64_t)le_get(offs + 4 * i, 4);
-    const int64_t kend = (int64_t)le_get(offs + 4 * (i + 1), 4);
+  for (int g = 0; g < RNS_G; ++g) {
+    int64_t k = (int64_t)le_get(offs + 4 * g, 4);
+    const int64_t kend = (int64_t)le_get(offs + 4 * (g + 1), 4);
     if (k > kend || kend > total_w) return -1;
-    uint64_t x = le_get(states + 4 * i, 4);
-    for (int64_t j = 0; j < count; ++j) {
-      const uint32_t slot = (uint32_t)(x & 4095);
-      int s = 0;
-      while (s < 255 && !(c[s] <= slot && slot < c[s] + f[s])) ++s;
-      if (!(c[s] <= slot && slot < c[s] + f[s])) return -1;
-      r[i + j * RNS_S] = (uint8_t)s;
-      x = (uint64_t)f[s] * (x >> 12) + slot - c[s];
-      while (x < (1u << 16)) {
+    uint64_t x[64];
+    for (int l = 0; l < 64; ++l) x[l] = le_get(states + 4 * (64 * g + l), 4);
+    for (int64_t j = 0; j < rns_count(m, 64 * g); ++j) {
+      for (int l = 0; l < 64; ++l) {
+        const int64_t i = 64 * g + l;
+        if (j >= rns_count(m, i)) continue;
+        const uint32_t slot = (uint32_t)(x[l] & 4095);
+        int s = 0;
+        while (s < 255 && !(c[s] <= slot && slot < c[s] + f[s])) ++s;
+        if (!(c[s] <= slot && slot < c[s] + f[s])) return -1;
+        r[i + j * RNS_S] = (uint8_t)s;
+        x[l] = (uint64_t)f[s] * (x[l] >> 12) + slot - c[s];
+      }
+      for (int l = 0; l < 64; ++l) {
+        if (j >= rns_count(m, 64 * g + l) || x[l] >= (1u << 16)) continue;
         if (k >= kend) return -1;
-        x = (x << 16) | le_get(words + 2 * k, 2);
+        x[l] = (x[l] << 16) | le_get(words + 2 * k, 2);
         ++k;
       }
     }
-    if (x != (1u << 16) || k != kend) return -1;
+    for (int l = 0; l < 64; ++l)
+      if (x[l] != (1u << 16)) return -1;
+    if (k != kend) return -1;
   }
   return (head + 2 * total_w + 15) / 16 * 16;
 }

@@ -655,13 +655,14 @@ def test_xw4_decode_rejects_malformed_blobs():
 # ---- order-0 rANS code of packages (the definition is in oracle.c)
 
 RNS_S = 8192
-RNS_REGION_HEAD = 512 + 4 * RNS_S + 4 * (RNS_S + 1)
+RNS_G = RNS_S // 64
+RNS_REGION_HEAD = 512 + 4 * RNS_S + 4 * (RNS_G + 1)
 
 
 def _rns_region(blob, off):
     f = blob[off:off + 512].view(np.uint16)
     states = blob[off + 512:off + 512 + 4 * RNS_S].view(np.uint32)
-    offs = blob[off + 512 + 4 * RNS_S:off + RNS_REGION_HEAD].view(np.uint32)
+    offs = blob[off + 512 + 4 * RNS_S:off + RNS_REGION_HEAD].view(np.uint32)  # per group of 64 streams
     return f, states, offs
 
 
@@ -670,11 +671,11 @@ def test_rns_hand_worked_region():
     = 2730 and f[1] = 1365 sum to 4095 and the larger, f[0], takes the missing one: 2731; c[1] = 2731.
     Streams 0, 1, 2 hold one symbol each.  From x = 65536 no word is emitted (65536 < 2^20 f), and
     x = 4096 (x div f) + (x mod f) + c: symbol 0 -> 4096 * 23 + 2723 = 96931, symbol 1 -> 4096 * 48 +
-    16 + 2731 = 199355.  Every other stream keeps 65536; no words; each region section is 66052
-    bytes padded to 66064; the second region is empty."""
+    16 + 2731 = 199355.  Every other stream keeps 65536; no words; each region section is
+    512 + 4 * 8192 + 4 * 129 = 33796 bytes padded to 33808; the second region is empty."""
     raw = np.array([0, 0, 1], np.uint8)
     blob = oracle.rns_encode(raw, 3)
-    assert blob.size == 64 + 2 * 66064
+    assert blob.size == 64 + 2 * 33808
     assert blob[:4].tobytes() == bytes([0x52, 0x4E, 0x53, 0x31])
     assert blob[4:8].view(np.uint32)[0] == RNS_S
     assert blob[8:16].view(np.uint64)[0] == 3 and blob[16:24].view(np.uint64)[0] == 3
@@ -683,7 +684,7 @@ def test_rns_hand_worked_region():
     assert f[0] == 2731 and f[1] == 1365 and f[2:].sum() == 0
     assert states[:3].tolist() == [96931, 96931, 199355]
     assert (states[3:] == 65536).all() and (offs == 0).all()
-    f2, states2, offs2 = _rns_region(blob, 64 + 66064)
+    f2, states2, offs2 = _rns_region(blob, 64 + 33808)
     assert f2.sum() == 0 and (states2 == 65536).all() and (offs2 == 0).all()
     assert np.array_equal(oracle.rns_decode(blob, 3), raw)
 
@@ -712,17 +713,50 @@ def test_rns_model_normalisation(kind):
 
 
 def test_rns_streams_interleave_and_emit_words():
-    """Region byte j is symbol j div S of stream j mod S: a region where only stream 5 carries
-    information (every other byte 0) emits words for stream 5 alone."""
+    """Region byte j is symbol j div S of stream j mod S, and streams 64g .. 64g+63 share group g's
+    words: a region where only stream 200 (group 3) carries information (every other byte 0)
+    emits words in group 3 alone."""
     m = RNS_S * 40
     raw = np.zeros(m, np.uint8)
     rng = np.random.default_rng(2)
-    raw[5::RNS_S] = rng.integers(1, 256, 40)
+    raw[200::RNS_S] = rng.integers(1, 256, 40)
     blob = oracle.rns_encode(raw, m)
     f, states, offs = _rns_region(blob, 64)
     words = np.diff(offs.astype(np.int64))
-    assert words[5] > 0 and words.sum() == words[5]
+    assert words[3] > 0 and words.sum() == words[3]
     assert np.array_equal(oracle.rns_decode(blob, m), raw)
+
+
+def test_rns_group_words_in_lane_order():
+    """Two streams of one group: 9 symbols each, alternating 1 and 2 in stream 0 and all 3 in
+    stream 1, in a region of mostly 0 bytes (f[1], f[2], f[3] are a few units of 4096, so each of
+    these symbols carries about 10 bits and words are emitted at most steps; the other streams of
+    the group hold only 0 bytes and emit none).  A decoder written here from the definition --
+    symbols of the step for every stream, then the words in stream order -- reads the oracle's
+    blob back to the bytes, ending on state 2^16 with every word of the group consumed."""
+    m = RNS_S * 9
+    raw = np.zeros(m, np.uint8)
+    raw[0::RNS_S] = [1, 2] * 4 + [1]
+    raw[1::RNS_S] = 3
+    blob = oracle.rns_encode(raw, m)
+    f, states, offs = _rns_region(blob, 64)
+    assert offs[1] > 2  # group 0 emitted several words
+    words = blob[64 + RNS_REGION_HEAD:64 + RNS_REGION_HEAD + 2 * int(offs[1])].view(np.uint16).astype(np.int64)
+    c = np.concatenate([[0], np.cumsum(f.astype(np.int64))])
+    x = [int(states[0]), int(states[1])]
+    k, out = 0, [[], []]
+    for j in range(9):
+        for lane in (0, 1):
+            slot = x[lane] & 4095
+            sym = int(np.searchsorted(c, slot, side="right") - 1)
+            out[lane].append(sym)
+            x[lane] = int(f[sym]) * (x[lane] >> 12) + slot - int(c[sym])
+        for lane in (0, 1):
+            if x[lane] < 65536:
+                x[lane] = (x[lane] << 16) | int(words[k])
+                k += 1
+    assert out[0] == [1, 2] * 4 + [1] and out[1] == [3] * 9
+    assert x == [65536, 65536] and k == int(offs[1])
 
 
 def test_rns_size_within_the_entropy_bound():
