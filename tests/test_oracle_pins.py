@@ -729,8 +729,8 @@ def test_rns_streams_interleave_and_emit_words():
 
 def test_rns_group_words_in_lane_order():
     """Two streams of one group: 9 symbols each, alternating 1 and 2 in stream 0 and all 3 in
-    stream 1, in a region of mostly 0 bytes (f[1], f[2], f[3] are a few units of 4096, so each of
-    these symbols carries about 10 bits and words are emitted at most steps; the other streams of
+    stream 1, in a region of mostly 0 bytes (f[1] = f[2] = f[3] = 1 of 4096, so each of these
+    symbols carries 12 bits and words are emitted at most steps; the other streams of
     the group hold only 0 bytes and emit none).  A decoder written here from the definition --
     symbols of the step for every stream, then the words in stream order -- reads the oracle's
     blob back to the bytes, ending on state 2^16 with every word of the group consumed."""
