@@ -745,7 +745,7 @@ int oracle_xw4_decode(const uint8_t* blob, int64_t blob_bytes, uint8_t* raw, int
  *    present s (m the region's length), 0 otherwise; while the f sum to more than 4096 the largest
  *    f (smallest s among equals) loses one, while they sum to less the largest gains the rest.
  *    c[s] = f[0] + ... + f[s-1].
- *  - Streams: region byte j belongs to stream j mod S (S = 8192), as its (j div S)-th symbol.  A
+ *  - Streams: region byte j belongs to stream j mod S (S = 32768), as its (j div S)-th symbol.  A
  *    stream is coded from x = 2^16, last symbol first: before a symbol s, if x >= 2^20 f[s] a word
  *    (the low 16 bits of x) is emitted and x shifts right by 16; then
  *    x = 4096 (x div f[s]) + (x mod f[s]) + c[s].  The final x is the stream's state.  Decoding: the
@@ -762,7 +762,7 @@ int oracle_xw4_decode(const uint8_t* blob, int64_t blob_bytes, uint8_t* raw, int
  *    multiple of 16 bytes.
  * ------------------------------------------------------------------------------------------ */
 #define RNS_MAGIC 0x31534E52u
-#define RNS_S 8192
+#define RNS_S 32768
 
 static void rns_model(const uint8_t* r, int64_t m, uint32_t* f) {
   int64_t h[256] = {0};

@@ -654,7 +654,7 @@ def test_xw4_decode_rejects_malformed_blobs():
 
 # ---- order-0 rANS code of packages (the definition is in oracle.c)
 
-RNS_S = 8192
+RNS_S = 32768
 RNS_G = RNS_S // 64
 RNS_REGION_HEAD = 512 + 4 * RNS_S + 4 * (RNS_G + 1)
 
@@ -672,10 +672,10 @@ def test_rns_hand_worked_region():
     Streams 0, 1, 2 hold one symbol each.  From x = 65536 no word is emitted (65536 < 2^20 f), and
     x = 4096 (x div f) + (x mod f) + c: symbol 0 -> 4096 * 23 + 2723 = 96931, symbol 1 -> 4096 * 48 +
     16 + 2731 = 199355.  Every other stream keeps 65536; no words; each region section is
-    512 + 4 * 8192 + 4 * 129 = 33796 bytes padded to 33808; the second region is empty."""
+    512 + 4 * 32768 + 4 * 513 = 133636 bytes padded to 133648; the second region is empty."""
     raw = np.array([0, 0, 1], np.uint8)
     blob = oracle.rns_encode(raw, 3)
-    assert blob.size == 64 + 2 * 33808
+    assert blob.size == 64 + 2 * 133648
     assert blob[:4].tobytes() == bytes([0x52, 0x4E, 0x53, 0x31])
     assert blob[4:8].view(np.uint32)[0] == RNS_S
     assert blob[8:16].view(np.uint64)[0] == 3 and blob[16:24].view(np.uint64)[0] == 3
@@ -684,7 +684,7 @@ def test_rns_hand_worked_region():
     assert f[0] == 2731 and f[1] == 1365 and f[2:].sum() == 0
     assert states[:3].tolist() == [96931, 96931, 199355]
     assert (states[3:] == 65536).all() and (offs == 0).all()
-    f2, states2, offs2 = _rns_region(blob, 64 + 33808)
+    f2, states2, offs2 = _rns_region(blob, 64 + 133648)
     assert f2.sum() == 0 and (states2 == 65536).all() and (offs2 == 0).all()
     assert np.array_equal(oracle.rns_decode(blob, 3), raw)
 
