@@ -509,7 +509,7 @@ def time_decoder(model, n: int) -> dict:
     return decoder_roofline(model.pool, model.stride, model.work, model.raw_stride, sizes, model.raw_bytes)
 
 
-def decoder_roofline(pool, stride, work, raw_stride, sizes, raw_bytes, reps=20) -> dict:
+def decoder_roofline(pool, stride, work, raw_stride, sizes, raw_bytes, reps=20, codec="xw4") -> dict:
     """Blobs in pool slots 0..n-1 decoded into work slots 0..n-1 in one launch, timed with HIP events
     on the stream it runs on; algorithmic bytes = the blobs' bytes read + the packages' bytes written."""
     import torch
@@ -518,25 +518,29 @@ def decoder_roofline(pool, stride, work, raw_stride, sizes, raw_bytes, reps=20) 
 
     n = len(sizes)
     pairs = torch.tensor([[i, i] for i in range(n)], dtype=torch.int32, device="cuda")
+    decode = api.moe_decompress_packages if codec == "xw4" else api.moe_decompress_rans
     for _ in range(3):
-        api.moe_decompress_packages(pool, stride, work, raw_stride, pairs, raw_bytes)
+        decode(pool, stride, work, raw_stride, pairs, raw_bytes)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for _ in range(reps):
-        api.moe_decompress_packages(pool, stride, work, raw_stride, pairs, raw_bytes)
+        decode(pool, stride, work, raw_stride, pairs, raw_bytes)
     b.record()
     torch.cuda.synchronize()
     us = a.elapsed_time(b) * 1e3 / reps
     alg = int(sum(sizes)) + n * raw_bytes
-    return {"bound": "hbm", "kernel": "xw4_decode_kernel (%d packages per launch)" % n,
+    kernel = "xw4_decode_kernel" if codec == "xw4" else "rns_decode_kernel"
+    return {"bound": "hbm", "kernel": "%s (%d packages per launch)" % (kernel, n),
             "achieved": round(alg / us / 1e3, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(alg / us / 1e3 / HBM_PEAK_GBS, 4), "traffic": None, "avg_launch_us": round(us, 2),
             "algorithmic_bytes_per_launch": alg, "timed_launches": reps}
 
 
 def run_decoder(args):
-    """The package decoder alone: 16 GLM-shaped bf16 experts (47 MB each) encoded on the host, their
-    blobs decoded on the GPU in one launch per repetition; decoded bytes checked against the packages."""
+    """A package decoder alone: 16 GLM-shaped experts encoded on the host (bf16 ones with the
+    exponent-window code, 47 MB each; with --codec rans, INT4 ones with the rANS code, 12.6 MB each),
+    their blobs decoded on the GPU in one launch per repetition; decoded bytes checked against the
+    packages."""
     import numpy as np
     import torch
 
@@ -545,27 +549,35 @@ def run_decoder(args):
     from mixture_experts_layer_token_amd import api
     from mixture_experts_layer_token_amd.layer import pack_bank
 
-    wl = W.WORKLOADS["glm"].with_(wfmt="bf16", name="glm-bf16")
-    raw_bytes = api.moe_package_bytes(wl.H, wl.I, "bf16")
+    codec = args.codec
+    wfmt = "bf16" if codec == "xw4" else "int4g32"
+    wl = W.WORKLOADS["glm"].with_(wfmt=wfmt, name="glm-" + wfmt)
+    raw_bytes = api.moe_package_bytes(wl.H, wl.I, wfmt)
     n = 16
     host = pack_bank(wl, 0, list(range(n)), stride=raw_bytes)
-    blobs = [api.moe_compress_package(host[i]) for i in range(n)]
+    if codec == "xw4":
+        blobs = [api.moe_compress_package(host[i]) for i in range(n)]
+    else:
+        split = api.package_split(wl.H, wl.I, wfmt)
+        blobs = [api.moe_compress_rans(host[i], split) for i in range(n)]
     stride = (max(b.size for b in blobs) + 255) // 256 * 256
     pool = torch.zeros((n, stride), dtype=torch.uint8, device="cuda")
     for i, b in enumerate(blobs):
         pool[i, :b.size].copy_(torch.from_numpy(b))
     work = torch.empty((n, raw_bytes), dtype=torch.uint8, device="cuda")
-    roof = decoder_roofline(pool, stride, work, raw_bytes, [b.size for b in blobs], raw_bytes, reps=args.steps)
+    roof = decoder_roofline(pool, stride, work, raw_bytes, [b.size for b in blobs], raw_bytes, reps=args.steps,
+                            codec=codec)
     ok = all(np.array_equal(work[i].cpu().numpy(), host[i]) for i in range(n))
     if not ok:
         raise RuntimeError("decoded packages differ from the originals")
     us = roof["avg_launch_us"]
     return {"metric": "lossless package decode GB/s (blobs read + packages written)", "value": roof["achieved"],
             "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": 3, "ms_per_step": round(us / 1e3, 4),
-            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-            "data": "synthetic (N(0,0.02) bf16 weights of GLM-shaped experts)",
-            "config": {"workload": "xw4 decode of %d glm-bf16 packages" % n, "raw_bytes": raw_bytes,
-                       "blob_bytes_mean": float(np.mean([b.size for b in blobs]))},
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u8" if codec == "rans" else "bf16",
+            "data": "synthetic (N(0,0.02) weights of GLM-shaped experts, %s)" % wfmt,
+            "config": {"workload": "%s decode of %d glm-%s packages" % (codec, n, wfmt), "raw_bytes": raw_bytes,
+                       "blob_bytes_mean": float(np.mean([b.size for b in blobs])),
+                       "ratio": round(float(np.mean([b.size for b in blobs])) / raw_bytes, 5)},
             "roofline": roof, "decoded_equal": ok}
 
 
@@ -810,6 +822,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="mixtral",
                     choices=["mixtral", "gptoss", "kimi", "glm", "glm-bf16", "spec", "decoder"])
+    ap.add_argument("--codec", default="xw4", choices=["xw4", "rans"],
+                    help="decoder workload: exponent-window code of bf16 packages, or rANS code of INT4 ones")
     ap.add_argument("--offload-steps", type=int, default=256)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="copy 1 GiB device-to-device before measuring (profiler byte-counter calibration)")

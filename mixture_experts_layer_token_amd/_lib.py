@@ -55,6 +55,9 @@ SIGNATURES = {
     "moe_compress_bound": ([c_size_t], c_size_t),
     "moe_compress_package": ([vp, c_size_t, vp, c_size_t, ctypes.POINTER(c_size_t)], c_int),
     "moe_decompress_packages": ([vp, c_size_t, vp, c_size_t, i32p, c_int, c_size_t, vp], c_int),
+    "moe_compress_rans_bound": ([c_size_t], c_size_t),
+    "moe_compress_rans": ([vp, c_size_t, c_size_t, vp, c_size_t, ctypes.POINTER(c_size_t)], c_int),
+    "moe_decompress_rans": ([vp, c_size_t, vp, c_size_t, i32p, c_int, c_size_t, vp], c_int),
     "moe_package_bytes": ([c_int, c_int, c_int], c_size_t),
     "moe_pack_expert": ([c_int, c_int, c_int, vp, vp, vp, vp, vp, vp, vp, c_size_t], c_int),
     "moe_dequant_expert": ([vp, c_int, c_int, c_int, f32p, vp], c_int),

@@ -134,6 +134,34 @@ def moe_decompress_packages(src, src_stride, dst, dst_stride, pairs, raw_bytes, 
                                         _stream(stream)))
 
 
+def moe_compress_rans_bound(raw_bytes: int) -> int:
+    return int(lib().moe_compress_rans_bound(raw_bytes))
+
+
+def moe_compress_rans(raw: np.ndarray, split: int, out: np.ndarray | None = None) -> np.ndarray:
+    """Order-0 rANS code of one package (host bytes, cut into regions at byte `split`) -> its blob."""
+    raw = np.ascontiguousarray(raw).view(np.uint8).ravel()
+    cap = int(lib().moe_compress_rans_bound(raw.size))
+    if out is None:
+        out = np.empty(cap, dtype=np.uint8)
+    n = ctypes.c_size_t(0)
+    check(lib().moe_compress_rans(_hp(raw), raw.size, split, _hp(out), out.nbytes, ctypes.byref(n)))
+    return out[:n.value]
+
+
+def moe_decompress_rans(src, src_stride, dst, dst_stride, pairs, raw_bytes, n=None, stream=None):
+    n = pairs.shape[0] if n is None else n
+    check(lib().moe_decompress_rans(_dp(src), src_stride, _dp(dst), dst_stride, _dp(pairs), n, raw_bytes,
+                                    _stream(stream)))
+
+
+def package_split(H, I, fmt) -> int:
+    """Bytes of a package's first region for the rANS code: its weight codes (4-bit formats), all
+    of it otherwise."""
+    nb = moe_package_bytes(H, I, fmt)
+    return 3 * H * I // 2 if fmt in ("mxfp4", "int4g32") else nb
+
+
 def moe_dequant_expert(package, H, I, fmt, out, stream=None):
     check(lib().moe_dequant_expert(_dp(package), H, I, FMT[fmt], _dp(out), _stream(stream)))
 

@@ -116,6 +116,125 @@ __global__ __launch_bounds__(kDecThreads) void xw4_decode_kernel(const uint8_t* 
   }
 }
 
+
+// ---------------------------------------------------------------- order-0 rANS decoder
+//
+// One wave per group of 64 streams: the lanes decode their streams in step (one symbol each per
+// step, written as 64 consecutive bytes of the region), then the lanes whose state fell below 2^16
+// take the next words of the group's sequence in lane order (ballot and bit count).  The words go
+// through a 1024-word ring in LDS, refilled 256 words at a time from a chunk prefetched into
+// registers one refill ahead.  The workgroup's four waves share the region's model: frequencies and
+// cumulative counts, and a 4096-entry table from the low 12 bits of the state to the symbol.
+
+constexpr int kRnsThreads = 256;
+constexpr int kRnsRing = 1024;  // words per wave
+constexpr int kRnsChunk = 256;  // words per refill (4 per lane)
+
+__global__ __launch_bounds__(kRnsThreads) void rns_decode_kernel(const uint8_t* __restrict__ src_base,
+                                                                 size_t src_stride, uint8_t* __restrict__ dst_base,
+                                                                 size_t dst_stride, const int32_t* __restrict__ pairs,
+                                                                 long long raw_bytes) {
+  __shared__ uint32_t fc[256];  // f | c << 16
+  __shared__ uint8_t lut[4096];
+  __shared__ uint16_t ring[kRnsThreads / 64][kRnsRing];
+  __shared__ uint32_t wsum[kRnsThreads / 64];
+  const int ss = __builtin_amdgcn_readfirstlane(pairs[2 * blockIdx.y]);
+  const int ds = __builtin_amdgcn_readfirstlane(pairs[2 * blockIdx.y + 1]);
+  if (ss < 0 || ds < 0) return;
+  const uint8_t* blob = src_base + (size_t)ss * src_stride;
+  uint8_t* out = dst_base + (size_t)ds * dst_stride;
+  const long long n = (long long)*(const uint64_t*)(blob + 8), q = (long long)*(const uint64_t*)(blob + 16);
+  if (n != raw_bytes || q > n) return;  // not a blob of this package size: nothing is written
+  constexpr int kWgPerRegion = kRnsGroups / (kRnsThreads / 64);
+  const int region = blockIdx.x / kWgPerRegion;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = (blockIdx.x % kWgPerRegion) * (kRnsThreads / 64) + wave;
+  size_t sec_off = 64;
+  if (region == 1) {
+    const uint32_t w0 = *(const uint32_t*)(blob + 64 + 512 + 4 * (size_t)kRnsStreams + 4 * (size_t)kRnsGroups);
+    sec_off += (rns_section_head() + 2 * (size_t)w0 + 15) & ~(size_t)15;
+  }
+  const uint8_t* sec = blob + sec_off;
+  const long long m = region ? n - q : q;
+  uint8_t* dst = out + (region ? q : 0);
+  if (m == 0) return;  // (whole workgroup: no barrier below is skipped by part of it)
+
+  // model: cumulative counts by a scan over the 256 frequencies, then the slot -> symbol table
+  const uint32_t f = *(const uint16_t*)(sec + 2 * tid);
+  uint32_t incl = f;
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t t = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += t;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  uint32_t base = 0;
+  for (int w = 0; w < wave; ++w) base += wsum[w];
+  const uint32_t c = base + incl - f;
+  fc[tid] = f | (c << 16);
+  __syncthreads();
+  for (int slot = tid; slot < 4096; slot += kRnsThreads) {
+    int lo = 0, hi = 255;  // largest symbol whose cumulative count is <= slot (it has f > 0)
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((fc[mid] >> 16) <= (uint32_t)slot) lo = mid;
+      else hi = mid - 1;
+    }
+    lut[slot] = (uint8_t)lo;
+  }
+  __syncthreads();
+
+  // this wave's group
+  const long long i = 64LL * g + lane;
+  const long long cnt = rns_count(m, i);
+  const int steps = (int)__builtin_amdgcn_readfirstlane((int)rns_count(m, 64LL * g));
+  uint32_t x = *(const uint32_t*)(sec + 512 + 4 * (size_t)i);
+  const uint32_t* offs = (const uint32_t*)(sec + 512 + 4 * (size_t)kRnsStreams);
+  const uint32_t w_begin = __builtin_amdgcn_readfirstlane(offs[g]);
+  const uint32_t n_words = __builtin_amdgcn_readfirstlane(offs[g + 1]) - w_begin;
+  const uint16_t* words = (const uint16_t*)(sec + rns_section_head()) + w_begin;
+  uint16_t* rw = ring[wave];
+  // words [fetched, fetched + 256) of the sequence, 4 per lane (lanes past the end load nothing)
+  uint16_t pre[4];
+  auto prefetch = [&](uint32_t fetched) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t wi = fetched + (uint32_t)(k * 64 + lane);
+      pre[k] = wi < n_words ? words[wi] : (uint16_t)0;
+    }
+  };
+  uint32_t loaded = 0, consumed = 0;  // words in the ring so far; words taken
+  prefetch(0);
+  for (int j = 0; j < steps; ++j) {
+    if (loaded - consumed < 64 && loaded < n_words) {  // (wave-uniform) a step takes at most 64 words
+#pragma unroll
+      for (int k = 0; k < 4; ++k) rw[(loaded + k * 64 + lane) & (kRnsRing - 1)] = pre[k];
+      loaded += kRnsChunk;
+      if (loaded < n_words) prefetch(loaded);
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    }
+    const bool act = j < cnt;
+    if (act) {
+      const uint32_t slot = x & 4095u;
+      const uint32_t sym = lut[slot];
+      const uint32_t e = fc[sym];
+      x = (e & 0xFFFFu) * (x >> 12) + slot - (e >> 16);
+      dst[i + (long long)j * kRnsStreams] = (uint8_t)sym;
+    }
+    const bool need = act && x < kRnsLow;
+    const unsigned long long b = __ballot(need);
+    if (need) {
+      const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0));
+      x = (x << 16) | rw[(consumed + rank) & (kRnsRing - 1)];
+    }
+    consumed += (uint32_t)__popcll(b);
+    // every lane has read its word before a later refill overwrites the ring
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  }
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -140,5 +259,20 @@ extern "C" int moe_decompress_packages(const void* src_base, size_t src_stride, 
                      (hipStream_t)stream, (const uint8_t*)src_base, src_stride, (uint8_t*)dst_base, dst_stride, pairs,
                      n_chunks);
   MOE_CHECK_LAUNCH("moe_decompress_packages launch");
+  return MOE_OK;
+}
+
+extern "C" int moe_decompress_rans(const void* src_base, size_t src_stride, void* dst_base, size_t dst_stride,
+                                   const int32_t* pairs, int n, size_t raw_bytes, void* stream) {
+  if (n < 0 || n > 65535) return fail(MOE_ERR_INVALID, "moe_decompress_rans: n=%d out of 0..65535", n);
+  if (src_stride % 256 || dst_stride < raw_bytes)
+    return fail(MOE_ERR_INVALID, "moe_decompress_rans: strides %zu / %zu for %zu bytes (source a multiple of 256)",
+                src_stride, dst_stride, raw_bytes);
+  if (n == 0 || raw_bytes == 0) return MOE_OK;
+  if (!src_base || !dst_base || !pairs) return fail(MOE_ERR_INVALID, "moe_decompress_rans: null pointer");
+  hipLaunchKernelGGL(rns_decode_kernel, dim3(2 * kRnsGroups / (kRnsThreads / 64), n), dim3(kRnsThreads), 0,
+                     (hipStream_t)stream, (const uint8_t*)src_base, src_stride, (uint8_t*)dst_base, dst_stride, pairs,
+                     (long long)raw_bytes);
+  MOE_CHECK_LAUNCH("moe_decompress_rans launch");
   return MOE_OK;
 }

@@ -22,3 +22,22 @@ __host__ __device__ inline size_t xw4_offsets_at() { return kXw4HeaderBytes; }
 __host__ __device__ inline size_t xw4_bases_at(size_t n_chunks) { return kXw4HeaderBytes + 4 * (n_chunks + 1); }
 
 }  // namespace moe
+
+namespace moe {
+
+// Blob layout of the order-0 rANS code (encoder: compress.cpp, decoder kernel: decompress.hip);
+// the format is specified in moe.h beside moe_compress_rans.
+constexpr uint32_t kRnsMagic = 0x31534E52u;
+constexpr int kRnsStreams = 32768;             // per region
+constexpr int kRnsGroups = kRnsStreams / 64;   // streams of a group share one word sequence
+constexpr int kRnsProb = 12;                   // frequencies sum to 2^12
+constexpr uint32_t kRnsLow = 1u << 16;         // state interval [2^16, 2^32)
+
+// bytes of a region section before its words: frequencies, states, group word offsets
+__host__ __device__ inline size_t rns_section_head() { return 512 + 4 * (size_t)kRnsStreams + 4 * (size_t)(kRnsGroups + 1); }
+// symbols of stream i in a region of m bytes
+__host__ __device__ inline long long rns_count(long long m, long long i) {
+  return i < m ? (m - i + kRnsStreams - 1) / kRnsStreams : 0;
+}
+
+}  // namespace moe

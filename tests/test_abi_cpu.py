@@ -431,3 +431,47 @@ def test_compress_validation():
     assert L.moe_decompress_packages(None, 256, None, 1024, None, -1, 1024, None) == INVALID
     assert L.moe_decompress_packages(None, 256, None, 1024, None, 1, 1024, None) == INVALID  # null pointers
     assert L.moe_decompress_packages(None, 256, None, 1024, None, 0, 1024, None) == OK
+
+
+# ---- order-0 rANS code: the library's host encoder against the oracle's
+
+@pytest.mark.parametrize("kind", ["skewed", "uniform", "single", "empty_first", "empty_second", "int4", "mxfp4"])
+def test_compress_rans_equals_oracle_blob(kind):
+    rng = np.random.default_rng(5)
+    n, q = 3 * 32768 + 999, 40000
+    if kind == "skewed":
+        raw = (rng.normal(0, 6, n).astype(np.int64) & 255).astype(np.uint8)
+    elif kind == "uniform":
+        raw = rng.integers(0, 256, n, dtype=np.uint8)
+    elif kind == "single":
+        raw = np.full(n, 7, np.uint8)
+    elif kind in ("empty_first", "empty_second"):
+        raw = (rng.normal(0, 20, n).astype(np.int64) & 255).astype(np.uint8)
+        q = 0 if kind == "empty_first" else n
+    else:  # a 4-bit package of a small expert, cut after its codes
+        fmt = "int4g32" if kind == "int4" else "mxfp4"
+        wl = W.Workload(name="cr", H=256, E=1, k=1, I=512, wfmt=fmt, xdt="bf16", Ts=(1,), seed=4)
+        raw = moe.moe_pack_expert(wl.H, wl.I, fmt, W.expert_weights(wl, 0, 0))
+        n, q = raw.size, moe.api.package_split(wl.H, wl.I, fmt)
+        assert q == 3 * wl.H * wl.I // 2
+    got = moe.moe_compress_rans(raw, q)
+    want = oracle.rns_encode(raw, q)
+    assert got.size == want.size and np.array_equal(got, want)
+    assert np.array_equal(oracle.rns_decode(got, n), raw)
+    assert moe.moe_compress_rans_bound(n) >= got.size
+
+
+def test_compress_rans_validation():
+    raw = np.zeros(100, np.uint8)
+    with pytest.raises(moe.MoeError):
+        moe.moe_compress_rans(raw, 101)  # split past the end
+    with pytest.raises(moe.MoeError):
+        moe.moe_compress_rans(raw, 10, out=np.zeros(1000, np.uint8))  # below the bound
+    assert moe.moe_compress_rans(np.zeros(0, np.uint8), 0).size == 64 + 2 * 133648
+    # device decoder: argument checks before any pointer is touched
+    assert L.moe_decompress_rans(None, 100, None, 1024, None, 1, 1024, None) == INVALID
+    assert L.moe_decompress_rans(None, 256, None, 512, None, 1, 1024, None) == INVALID
+    assert L.moe_decompress_rans(None, 256, None, 1024, None, -1, 1024, None) == INVALID
+    assert L.moe_decompress_rans(None, 256, None, 1024, None, 65536, 1024, None) == INVALID
+    assert L.moe_decompress_rans(None, 256, None, 1024, None, 1, 1024, None) == INVALID  # null pointers
+    assert L.moe_decompress_rans(None, 256, None, 1024, None, 0, 1024, None) == OK

@@ -1,0 +1,98 @@
+"""GPU parity of the rANS package decoder (moe_decompress_rans): every decoded package equals the
+original bytes exactly.  Blobs are the oracle encoder's (the library's host encoder matches it byte
+for byte in test_abi_cpu.py); the expected output is the input package itself."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import oracle  # noqa: E402
+from synth import workloads as W  # noqa: E402
+
+import mixture_experts_layer_token_amd as moe  # noqa: E402
+from mixture_experts_layer_token_amd import api  # noqa: E402
+
+from helpers import say  # noqa: E402
+
+S = 32768  # streams per region
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    moe.lib()
+
+
+def _raw(kind, n, seed):
+    rng = np.random.default_rng(seed)
+    if kind == "skewed":  # a peaked byte distribution: many streams read words at the same step
+        return (rng.normal(0, 6, n).astype(np.int64) & 255).astype(np.uint8)
+    if kind == "uniform":  # incompressible: about one word per two symbols
+        return rng.integers(0, 256, n, dtype=np.uint8)
+    if kind == "two":  # two symbols, one of them rare (a frequency at the minimum of 1)
+        r = np.zeros(n, np.uint8)
+        r[rng.integers(0, n, max(1, n // 5000))] = 0xFF
+        return r
+    return np.full(n, 0x5A, np.uint8)  # "single": one symbol, no words at all
+
+
+def _run(raws, splits, pairs_host, n_dst, stride_dst, encode=oracle.rns_encode):
+    blobs = [encode(r, q) for r, q in zip(raws, splits)]
+    stride = (max(b.size for b in blobs) + 255) // 256 * 256
+    src = np.zeros((len(blobs), stride), np.uint8)
+    for i, b in enumerate(blobs):
+        src[i, :b.size] = b
+    d_src = torch.from_numpy(src).cuda()
+    d_dst = torch.full((n_dst, stride_dst), 0xAB, dtype=torch.uint8, device="cuda")
+    pairs = torch.tensor(pairs_host, dtype=torch.int32, device="cuda").reshape(-1, 2)
+    moe.moe_decompress_rans(d_src, stride, d_dst, stride_dst, pairs, raws[0].size)
+    torch.cuda.synchronize()
+    return d_dst.cpu().numpy(), [b.size / max(1, r.size) for b, r in zip(blobs, raws)]
+
+
+@pytest.mark.parametrize("kind", ["skewed", "uniform", "two", "single"])
+@pytest.mark.parametrize("n,q", [(3 * S + 1234, S + 17), (5000, 1234), (2 * S, 0), (70001, 70001), (1, 1)])
+def test_rans_decode_bit_exact(kind, n, q):
+    """Regions longer than the 32768 streams (ragged last step), shorter than one group of streams,
+    empty first or second regions, one byte."""
+    raws = [_raw(kind, n, seed) for seed in range(4)]
+    stride_dst = n + 4096
+    pairs = [0, 2, 1, 0, -1, 1, 3, 3, 2, -5]  # as for the other decoder: skipped pairs write nothing
+    say("rans decode", kind, n, q)
+    got, ratios = _run(raws, [q] * 4, pairs, 5, stride_dst)
+    for src_i, dst_i in ((0, 2), (1, 0), (3, 3)):
+        assert np.array_equal(got[dst_i, :n], raws[src_i]), (src_i, dst_i)
+        assert (got[dst_i, n:] == 0xAB).all()
+    assert (got[1] == 0xAB).all() and (got[4] == 0xAB).all()
+
+
+def test_rans_decode_refuses_other_sizes():
+    """A blob whose header names another package size writes nothing."""
+    raw = _raw("skewed", 5000, 7)
+    got, _ = _run([raw, raw[:4096]], [1000, 1000], [1, 0], 1, 8192)
+    assert (got == 0xAB).all()
+
+
+@pytest.mark.parametrize("fmt,model", [("int4g32", "glm"), ("mxfp4", "gptoss")])
+def test_rans_decode_full_size_packages(fmt, model):
+    """Real 4-bit packages at full size, encoded by the library's host encoder."""
+    wl = W.WORKLOADS[model].with_(wfmt=fmt)
+    raws = [np.ascontiguousarray(moe.moe_pack_expert(wl.H, wl.I, fmt, W.expert_weights(wl, 0, e)))
+            .view(np.uint8).ravel() for e in range(3)]
+    split = api.package_split(wl.H, wl.I, fmt)
+    got, ratios = _run(raws, [split] * 3, [0, 1, 1, 2, 2, 0], 3, raws[0].size,
+                       encode=lambda r, q: moe.moe_compress_rans(r, q).copy())
+    say("rans decode", model, fmt, "ratios", ["%.4f" % r for r in ratios])
+    assert all(r < 0.95 for r in ratios)
+    for src_i, dst_i in ((0, 1), (1, 2), (2, 0)):
+        assert np.array_equal(got[dst_i], raws[src_i])
+
+
+def test_rans_decode_nothing_to_do():
+    d = torch.zeros(1024, dtype=torch.uint8, device="cuda")
+    pairs = torch.zeros((0, 2), dtype=torch.int32, device="cuda")
+    moe.moe_decompress_rans(d, 1024, d, 1024, pairs, 1024)
+    torch.cuda.synchronize()
+    assert int(d.sum()) == 0
