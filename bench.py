@@ -530,7 +530,9 @@ def decoder_roofline(pool, stride, work, raw_stride, sizes, raw_bytes, reps=20, 
     us = a.elapsed_time(b) * 1e3 / reps
     alg = int(sum(sizes)) + n * raw_bytes
     kernel = "xw4_decode_kernel" if codec == "xw4" else "rns_decode_kernel"
-    return {"bound": "hbm", "kernel": "%s (%d packages per launch)" % (kernel, n),
+    # (the rANS decoder is bound by each stream's serial chain of LDS lookups; its HBM fraction is
+    # given for scale)
+    return {"bound": "hbm" if codec == "xw4" else "latency", "kernel": "%s (%d packages per launch)" % (kernel, n),
             "achieved": round(alg / us / 1e3, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(alg / us / 1e3 / HBM_PEAK_GBS, 4), "traffic": None, "avg_launch_us": round(us, 2),
             "algorithmic_bytes_per_launch": alg, "timed_launches": reps}
@@ -644,6 +646,17 @@ def run_offload(args):
     steps = min(args.offload_steps, wl.steps)
     Ts = [args.T] if args.T else [16, 1]
     model = OffloadedModel(wl, max(Ts), fill=False)
+    rans = args.host_codec == "rans"
+    if rans:
+        # a second bank of rANS blobs of the same packages, in slots of the largest blob of a sample
+        # plus 0.3% (the fill refuses any blob that does not fit), plain packages in the same HBM pool
+        from mixture_experts_layer_token_amd.layer import pack_bank
+
+        raw = model.raw_bytes
+        sample = [pack_bank(wl, l, [e])[0, :raw] for l in range(wl.layers) for e in (0, 97)]
+        largest = max(api.moe_compress_rans(p, model.split).size for p in sample)
+        model_r = OffloadedModel(wl, max(Ts), capacity=model.capacity, fill=False, host_codec="rans",
+                                 blob_bytes=(int(largest * 1.003) + 255) // 256 * 256)
     runs, belady = {}, {}
     for T in Ts:
         xs = {(l, s): to_device_act(W.activations(wl, T, l, s), wl.xdt) for s in range(steps) for l in range(wl.layers)}
@@ -662,21 +675,37 @@ def run_offload(args):
         for l in range(wl.layers):
             model.fill(l, touched[l] - model.filled.get(l, set()))
             model.filled[l] = model.filled.get(l, set()) | touched[l]
+            if rans:  # the same packages, from the plain bank
+                model_r.fill(l, touched[l] - model_r.filled.get(l, set()),
+                             source=lambda l_, ids: np.stack([model.package(l_, e) for e in ids]))
+                model_r.filled[l] = model_r.filled.get(l, set()) | touched[l]
         out = torch.empty((T, wl.H), dtype=torch.bfloat16, device="cuda")
-        model.reset_cache(prefetch=None)
-        for l in range(wl.layers):  # warm the kernels through the full path (the cache is reset below)
-            model.layer_forward(l, 0, xs[(l, 0)], out)
         # half the slots pinned (the layers' most used experts over the first popularity epoch), LRU on the rest
         pins = static_pins(model, calib, model.capacity // 2 // wl.layers)
-        variants = [(p, d, True, pf, None) for p, d in POLICIES for pf in PREFETCH]
-        variants += [("lru", 0, True, None, pins)]
-        if T == Ts[0]:  # the reported policy without the FFN/copy overlap
-            variants.append((*POLICIES[-1], False, None, None))
-        for policy, period, overlap, pf, pin in variants:
-            r = offload_variant(model, wl, T, steps, xs, out, policy, period, overlap, pf, pin, belady)
-            runs[(T, r["policy"], overlap, pf)] = r
-    head = max((r for r in runs.values() if r["T"] == Ts[0] and r["ffn_of_hits_during_copies"]),
-               key=lambda r: r["tokens_per_s"])
+        if rans:  # both banks under the two policies, no prefetch
+            variants = [(p, d, True, None, None) for p, d in POLICIES]
+        else:
+            variants = [(p, d, True, pf, None) for p, d in POLICIES for pf in PREFETCH]
+            variants += [("lru", 0, True, None, pins)]
+            if T == Ts[0]:  # the reported policy without the FFN/copy overlap
+                variants.append((*POLICIES[-1], False, None, None))
+        for bank, m in (("plain", model), ("rans", model_r if rans else None)):
+            if m is None:
+                continue
+            m.reset_cache(prefetch=None)
+            for l in range(wl.layers):  # warm the kernels through the full path (the cache is reset below)
+                m.layer_forward(l, 0, xs[(l, 0)], out)
+            for policy, period, overlap, pf, pin in variants:
+                r = offload_variant(m, wl, T, steps, xs, out, policy, period, overlap, pf, pin, belady)
+                r["bank"] = bank
+                if bank == "rans":  # package bytes the blobs delivered per second of copy-stream time
+                    r["packages_gbps_busy"] = r["misses"] * m.raw_bytes / max(1e-9, r["copy_busy_s"]) / 1e9
+                runs[(T, bank, r["policy"], overlap, pf)] = r
+                print("offload %s bank T=%d %s prefetch %s: %.1f tokens/s, hit %.4f" % (
+                    bank, T, r["policy"], pf, r["tokens_per_s"], r["hit_rate"]), flush=True)
+    head_bank = "rans" if rans else "plain"
+    head = max((r for r in runs.values() if r["T"] == Ts[0] and r["ffn_of_hits_during_copies"]
+                and r["bank"] == head_bank), key=lambda r: r["tokens_per_s"])
     out = {
         "metric": "MoE-layer tokens/s (offloaded expert bank, decode) + expert-cache hit rate + link GB/s",
         "value": round(head["tokens_per_s"], 2),
@@ -694,12 +723,33 @@ def run_offload(args):
                    "top_k": wl.k, "inter": wl.I, "cache_slots": model.capacity,
                    "cache_policy": head["policy"], "prefetch": head["prefetch"], "ffn_of_hits_during_copies": True,
                    "reported": "the fastest policy / prefetch combination at this T",
-                   "bank_bytes": wl.layers * wl.E * model.pkg_bytes},
+                   "bank": "rANS blobs (plain packages in HBM)" if rans else "plain packages",
+                   "bank_bytes": wl.layers * wl.E * (model_r if rans else model).pkg_bytes},
         "roofline": {"bound": "link", "kernel": "hipMemcpyAsync host bank -> HBM slots (copy stream)",
                      "achieved": round(head["link_gbps_busy"], 2), "peak": PCIE_PEAK_GBS, "unit": "GB/s",
                      "frac": round(head["link_gbps_busy"] / PCIE_PEAK_GBS, 4), "traffic": None},
         "runs": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()} for r in runs.values()],
     }
+    if rans:
+        plain = max((r for r in runs.values() if r["T"] == Ts[0] and r["bank"] == "plain"),
+                    key=lambda r: r["tokens_per_s"])
+        sizes = model_r.blob_sizes[model_r.blob_sizes > 0]
+        out["vs_plain_bank"] = round(head["tokens_per_s"] / plain["tokens_per_s"], 4)
+        out["compression"] = {"codec": "rans", "raw_bytes": model.raw_bytes, "blob_slot_bytes": model_r.pkg_bytes,
+                              "ratio_mean": round(float(sizes.mean()) / model.raw_bytes, 5),
+                              "ratio_max": round(float(sizes.max()) / model.raw_bytes, 5),
+                              "experts": int(sizes.size)}
+        n_dec = 16
+        keys = [(l, e) for l in range(wl.layers) for e in range(wl.E) if model_r.blob_sizes[l, e] > 0][:n_dec]
+        blob_stride = model_r.pkg_bytes
+        pool = torch.zeros((len(keys), blob_stride), dtype=torch.uint8, device="cuda")
+        for i, (l, e) in enumerate(keys):
+            pool[i].copy_(torch.from_numpy(model_r.package(l, e).copy()))
+        work = torch.empty((len(keys), model.raw_bytes), dtype=torch.uint8, device="cuda")
+        out["decoder_roofline"] = decoder_roofline(pool, blob_stride, work, model.raw_bytes,
+                                                   [int(model_r.blob_sizes[k]) for k in keys], model.raw_bytes,
+                                                   codec="rans")
+        model_r.close()
     model.close()
     return out
 
@@ -822,6 +872,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="mixtral",
                     choices=["mixtral", "gptoss", "kimi", "glm", "glm-bf16", "spec", "decoder"])
+    ap.add_argument("--host-codec", default="none", choices=["none", "rans"],
+                    help="glm offload: also run a bank of rANS blobs (decoded into plain HBM slots) and report it")
     ap.add_argument("--codec", default="xw4", choices=["xw4", "rans"],
                     help="decoder workload: exponent-window code of bf16 packages, or rANS code of INT4 ones")
     ap.add_argument("--offload-steps", type=int, default=256)

@@ -424,7 +424,9 @@ typedef struct {
 typedef struct {
   int64_t lookups, hits, misses, evictions; /* demand lookups (moe_cache_plan) and all evictions */
   int64_t bytes_fetched;                    /* package bytes of every fetch planned (demand, prefetch,
-                                               pin), less those a failed fetch rolled back */
+                                               pin), less those a failed fetch rolled back; with a
+                                               rANS bank read by hipMemcpyAsync, each fetched blob's
+                                               own bytes */
   int64_t prefetch_fetches;                 /* packages a prefetch brought in */
   int64_t prefetch_hits;                    /* demand hits on such a package before its eviction */
 } moe_cache_stats_t;
@@ -484,6 +486,26 @@ int moe_cache_pin(moe_cache_t* c, int layer, const int32_t* host_ids, int n, moe
  */
 int moe_cache_fetch(moe_cache_t* c, const moe_cache_plan_t* plan, int32_t* dev_slot_of_expert, void* copy_stream,
                     void* done);
+
+/*
+ * Declare the bank's packages rANS blobs (moe_compress_rans, one per bank slot of pkg_bytes) of
+ * packages of raw_bytes bytes (<= slot_stride): the host tier holds the compressed bytes and the
+ * pool plain packages ("Understanding MoE Inference Costs on Galactus": compressed memory beside
+ * host DRAM as the cheaper tier), so a miss moves the blob (GLM-shaped INT4 experts: 88.5% of the
+ * package) and hits cost nothing extra.  From then on moe_cache_fetch copies each miss's blob into
+ * one of `staging_slots` device staging slots (staging: device, staging_slots * staging_stride
+ * bytes, staging_stride >= pkg_bytes and a multiple of 256; the cache uses it, the caller owns it)
+ * and a decode stream created here (on the current device, default priority) decodes it into the
+ * pool slot while the copy stream moves on to the next blob; before `done` the copy stream waits
+ * for the fetch's last decode, so `done` (and any later event of the copy stream) covers the
+ * decoded packages.  A staging slot is rewritten only after the decode that read it.  With the
+ * default copy engine only the blob's own bytes cross the link, and a bank slot whose header is
+ * not a rANS blob of raw_bytes fails the fetch (MOE_ERR_INVALID, rolled back as a failed copy).
+ * Call once, before the first fetch; moe_cache_destroy waits for the decode stream.
+ * Errors: MOE_ERR_INVALID (null pointers, sizes, a planning-only cache, a second call);
+ * MOE_ERR_HIP (stream or event creation).
+ */
+int moe_cache_set_rans(moe_cache_t* c, void* staging, size_t staging_stride, int staging_slots, size_t raw_bytes);
 
 int moe_cache_stats(const moe_cache_t* c, moe_cache_stats_t* out);
 void moe_cache_destroy(moe_cache_t* c);

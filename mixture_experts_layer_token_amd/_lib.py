@@ -73,6 +73,7 @@ SIGNATURES = {
     "moe_cache_prefetch": ([vp, c_int, i32p, c_int, ctypes.POINTER(MoeCachePlan)], c_int),
     "moe_cache_pin": ([vp, c_int, i32p, c_int, ctypes.POINTER(MoeCachePlan)], c_int),
     "moe_cache_fetch": ([vp, ctypes.POINTER(MoeCachePlan), i32p, vp, vp], c_int),
+    "moe_cache_set_rans": ([vp, vp, c_size_t, c_int, c_size_t], c_int),
     "moe_cache_stats": ([vp, ctypes.POINTER(MoeCacheStats)], c_int),
     "moe_cache_destroy": ([vp], None),
 }

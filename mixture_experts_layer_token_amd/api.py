@@ -228,6 +228,12 @@ class ExpertCache:
         self.h = h
         self.E = E
 
+    def set_rans(self, staging, staging_stride: int, raw_bytes: int):
+        """The bank holds rANS blobs of raw_bytes packages; `staging` (device uint8 [slots, stride])
+        takes each fetched blob before the cache's decode stream decodes it into its pool slot."""
+        check(lib().moe_cache_set_rans(self.h, _dp(staging), staging_stride, staging.shape[0], raw_bytes))
+        self._keep = self._keep + (staging,)
+
     def plan(self, layer, host_ids: np.ndarray) -> MoeCachePlan:
         ids = np.ascontiguousarray(host_ids, dtype=np.int32).ravel()
         p = MoeCachePlan()

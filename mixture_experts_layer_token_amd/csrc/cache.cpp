@@ -10,7 +10,12 @@
 //
 // Planning is host work on host ids (the router's choice copied back); fetching enqueues copies
 // from the page-locked bank (hipMemcpyAsync, or the caller's copy engine) plus one small copy of
-// the slot table.
+// the slot table.  A bank of rANS blobs (moe_cache_set_rans) moves fewer bytes over the link: each
+// blob lands in a device staging slot and a decode stream owned by the cache turns it into the plain
+// package in its pool slot, while the copy stream carries on with the next blob; the copy stream
+// waits for the last decode before it records the fetch's event.
+#include <string.h>
+
 #include <algorithm>
 #include <set>
 #include <tuple>
@@ -37,6 +42,26 @@ struct moe_cache {
   std::vector<int32_t> last_group;   // keys of the latest demand group (sorted): a prefetch keeps them
   int64_t n_pinned = 0;
   moe_cache_stats_t st{};
+  // rANS bank (moe_cache_set_rans): staging ring, decode stream and its events
+  bool rans = false;
+  char* staging = nullptr;
+  size_t staging_stride = 0, raw_bytes = 0;
+  int n_stage = 0, next_stage = 0, device = -1;
+  hipStream_t dec = nullptr;
+  std::vector<hipEvent_t> copied, decoded;  // per staging slot: its blob landed; its decode finished
+  std::vector<char> stage_used;             // the slot's `decoded` event has been recorded
+
+  ~moe_cache() {
+    if (!dec) return;
+    int cur = -1;
+    (void)hipGetDevice(&cur);
+    if (cur != device) (void)hipSetDevice(device);
+    (void)hipStreamSynchronize(dec);
+    for (hipEvent_t e : copied) (void)hipEventDestroy(e);
+    for (hipEvent_t e : decoded) (void)hipEventDestroy(e);
+    (void)hipStreamDestroy(dec);
+    if (cur != device && cur >= 0) (void)hipSetDevice(cur);
+  }
 
   bool lfu() const { return d.policy == MOE_CACHE_LFU_DECAY; }
   Prio prio(int32_t key) const { return Prio(lfu() ? count[key] : 0, last[key], key); }
@@ -287,6 +312,81 @@ extern "C" int moe_cache_pin(moe_cache_t* c, int layer, const int32_t* host_ids,
   return MOE_OK;
 }
 
+extern "C" int moe_cache_set_rans(moe_cache_t* c, void* staging, size_t staging_stride, int staging_slots,
+                                  size_t raw_bytes) {
+  if (!c || !staging) return fail(MOE_ERR_INVALID, "moe_cache_set_rans: null pointer");
+  if (!c->d.host_bank) return fail(MOE_ERR_INVALID, "moe_cache_set_rans: planning-only cache has no bank");
+  if (c->rans) return fail(MOE_ERR_INVALID, "moe_cache_set_rans: already set");
+  if (staging_slots < 1 || staging_slots > 64)
+    return fail(MOE_ERR_INVALID, "moe_cache_set_rans: %d staging slots (1..64)", staging_slots);
+  if (staging_stride < c->d.pkg_bytes || staging_stride % 256)
+    return fail(MOE_ERR_INVALID, "moe_cache_set_rans: staging_stride %zu (a multiple of 256, >= pkg_bytes %zu)",
+                staging_stride, c->d.pkg_bytes);
+  if (raw_bytes == 0 || raw_bytes > c->d.slot_stride)
+    return fail(MOE_ERR_INVALID, "moe_cache_set_rans: raw_bytes %zu (1..slot_stride %zu)", raw_bytes,
+                c->d.slot_stride);
+  hipError_t e = hipGetDevice(&c->device);
+  if (e == hipSuccess) e = hipStreamCreateWithFlags(&c->dec, hipStreamNonBlocking);
+  if (e != hipSuccess) {
+    c->dec = nullptr;
+    return hip_fail(e, "moe_cache_set_rans: decode stream");
+  }
+  c->copied.assign(staging_slots, nullptr);
+  c->decoded.assign(staging_slots, nullptr);
+  for (int r = 0; r < staging_slots && e == hipSuccess; ++r) {
+    e = hipEventCreateWithFlags(&c->copied[r], hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&c->decoded[r], hipEventDisableTiming);
+  }
+  if (e != hipSuccess) return hip_fail(e, "moe_cache_set_rans: events");  // (the destructor frees them)
+  c->stage_used.assign(staging_slots, 0);
+  c->staging = (char*)staging;
+  c->staging_stride = staging_stride;
+  c->n_stage = staging_slots;
+  c->raw_bytes = raw_bytes;
+  c->rans = true;
+  return MOE_OK;
+}
+
+namespace {
+
+// rANS bank: blob -> staging slot (copy stream) -> decode into the pool slot (decode stream)
+int fetch_rans_one(moe_cache* c, moe_copy_fn copy, void* ctx, const char* blob, char* dst, hipStream_t cs) {
+  size_t bytes = c->d.pkg_bytes;
+  if (!c->d.copy) {  // the bank is host memory: copy the blob's own bytes, not its whole slot
+    uint32_t magic;
+    uint64_t n, total;
+    memcpy(&magic, blob, 4);
+    memcpy(&n, blob + 8, 8);
+    memcpy(&total, blob + 24, 8);
+    if (magic != 0x31534E52u || n != c->raw_bytes || total > bytes || total < 64) return MOE_ERR_INVALID;
+    bytes = (size_t)total;
+  }
+  const int r = c->next_stage;
+  c->next_stage = (r + 1) % c->n_stage;
+  char* stage = c->staging + (size_t)r * c->staging_stride;
+  // the staging slot is free once the decode that read it has finished (a wait on the copy stream
+  // costs the link a gap, so none is enqueued for a decode already over)
+  if (c->stage_used[r]) {
+    const hipError_t q = hipEventQuery(c->decoded[r]);
+    if (q == hipErrorNotReady) {
+      (void)hipGetLastError();  // (not an error: keep it out of the next launch check)
+      if (hipStreamWaitEvent(cs, c->decoded[r], 0) != hipSuccess) return MOE_ERR_HIP;
+    } else if (q != hipSuccess) {
+      return MOE_ERR_HIP;
+    }
+  }
+  if (copy(ctx, stage, blob, bytes, cs) != 0) return MOE_ERR_HIP;
+  if (hipEventRecord(c->copied[r], cs) != hipSuccess || hipStreamWaitEvent(c->dec, c->copied[r], 0) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (moe::launch_rns_decode_one(stage, dst, c->raw_bytes, c->dec) != MOE_OK) return MOE_ERR_HIP;
+  if (hipEventRecord(c->decoded[r], c->dec) != hipSuccess) return MOE_ERR_HIP;
+  c->stage_used[r] = 1;
+  c->st.bytes_fetched -= (int64_t)(c->d.pkg_bytes - bytes);  // (the stats count the bytes that cross the link)
+  return MOE_OK;
+}
+
+}  // namespace
+
 extern "C" int moe_cache_fetch(moe_cache_t* c, const moe_cache_plan_t* plan, int32_t* dev_slot_of_expert,
                                void* copy_stream, void* done) {
   if (!c || !plan) return fail(MOE_ERR_INVALID, "moe_cache_fetch: null pointer");
@@ -302,16 +402,32 @@ extern "C" int moe_cache_fetch(moe_cache_t* c, const moe_cache_plan_t* plan, int
   void* ctx = c->d.copy ? c->d.copy_ctx : nullptr;
   const char* bank = (const char*)c->d.host_bank;
   char* pool = (char*)c->d.device_pool;
+  int last_stage = -1;
   for (int i = 0; i < plan->n_misses; ++i) {
     const size_t key = (size_t)plan->layer * c->d.E + plan->miss_ids[i];
-    if (copy(ctx, pool + (size_t)plan->miss_slots[i] * c->d.slot_stride, bank + key * c->d.pkg_bytes, c->d.pkg_bytes,
-             copy_stream) != 0) {
+    char* dst = pool + (size_t)plan->miss_slots[i] * c->d.slot_stride;
+    const char* src = bank + key * c->d.pkg_bytes;
+    int rc = MOE_OK;
+    if (c->rans) {
+      const int r = c->next_stage;
+      rc = fetch_rans_one(c, copy, ctx, src, dst, (hipStream_t)copy_stream);
+      if (rc == MOE_OK) last_stage = r;
+    } else if (copy(ctx, dst, src, c->d.pkg_bytes, copy_stream) != 0) {
+      rc = MOE_ERR_HIP;
+    }
+    if (rc != MOE_OK) {
       (void)hipGetLastError();
       roll_back(c, plan, i);
-      return fail(MOE_ERR_HIP, "moe_cache_fetch: copy of expert %d of layer %d failed; it and the %d misses after it "
-                  "are not resident", plan->miss_ids[i], plan->layer, plan->n_misses - i - 1);
+      if (last_stage >= 0)  // the decodes already launched still finish before later events of the copy stream
+        (void)hipStreamWaitEvent((hipStream_t)copy_stream, c->decoded[last_stage], 0);
+      return fail(rc, "moe_cache_fetch: %s of expert %d of layer %d failed; it and the %d misses after it are not "
+                  "resident", rc == MOE_ERR_INVALID ? "blob header" : "copy", plan->miss_ids[i], plan->layer,
+                  plan->n_misses - i - 1);
     }
   }
+  // the pool slots hold the decoded packages once the last decode has finished
+  if (last_stage >= 0 && hipStreamWaitEvent((hipStream_t)copy_stream, c->decoded[last_stage], 0) != hipSuccess)
+    return fail(MOE_ERR_HIP, "moe_cache_fetch: wait for the decode stream");
   if (dev_slot_of_expert &&
       copy(ctx, dev_slot_of_expert, plan->slot_of_expert, sizeof(int32_t) * c->d.E, copy_stream) != 0) {
     (void)hipGetLastError();

@@ -106,6 +106,8 @@ int launch_permute(const int32_t* ids, int T, int k, int E, int32_t* counts, int
 int launch_combine(const float* y, const float* w, const int32_t* inv, int T, int k, int H, const float* shared,
                    void* out, int odt, hipStream_t s);
 int launch_dequant(const void* pkg, int H, int I, int fmt, float* out, hipStream_t s);
+// one rANS blob (moe_compress_rans) of a raw_bytes package decoded into dst
+int launch_rns_decode_one(const void* blob, void* dst, size_t raw_bytes, hipStream_t s);
 size_t ffn_workspace(const moe_experts* w, int T, int k, int mode);
 // helper_stream: the AUTO hybrid may run its tile-kernel share on a library-owned helper stream
 // (created once per device), beside the streaming kernels

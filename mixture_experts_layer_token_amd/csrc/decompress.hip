@@ -120,35 +120,41 @@ __global__ __launch_bounds__(kDecThreads) void xw4_decode_kernel(const uint8_t* 
 // ---------------------------------------------------------------- order-0 rANS decoder
 //
 // One wave per group of 64 streams: the lanes decode their streams in step (one symbol each per
-// step, written as 64 consecutive bytes of the region), then the lanes whose state fell below 2^16
-// take the next words of the group's sequence in lane order (ballot and bit count).  The words go
-// through a 1024-word ring in LDS, refilled 256 words at a time from a chunk prefetched into
-// registers one refill ahead.  The workgroup's four waves share the region's model: frequencies and
-// cumulative counts, and a 4096-entry table from the low 12 bits of the state to the symbol.
+// step), then the lanes whose state fell below 2^16 take the next words of the group's sequence in
+// lane order (ballot and bit count).  A symbol costs one LDS lookup: a 4096-entry table from the low
+// 12 bits of the state to (symbol, f - 1, slot - c), built per workgroup from the region's model.
+// The words go through a 512-word ring in LDS, refilled 256 at a time from registers loaded one
+// refill ahead; the decoded bytes collect in LDS, 16 steps of 64 streams per wave, and leave as one
+// 16-byte store per lane every 16 steps.  The step itself waits on no global memory access, so even
+// a lone package (1024 waves, one per SIMD) steps at LDS latency.
 
 constexpr int kRnsThreads = 256;
-constexpr int kRnsRing = 1024;  // words per wave
+constexpr int kRnsWaves = kRnsThreads / 64;
+constexpr int kRnsRing = 512;   // words per wave
 constexpr int kRnsChunk = 256;  // words per refill (4 per lane)
+constexpr int kRnsRows = 16;    // steps per output flush
 
 __global__ __launch_bounds__(kRnsThreads) void rns_decode_kernel(const uint8_t* __restrict__ src_base,
                                                                  size_t src_stride, uint8_t* __restrict__ dst_base,
                                                                  size_t dst_stride, const int32_t* __restrict__ pairs,
                                                                  long long raw_bytes) {
-  __shared__ uint32_t fc[256];  // f | c << 16
-  __shared__ uint8_t lut[4096];
-  __shared__ uint16_t ring[kRnsThreads / 64][kRnsRing];
-  __shared__ uint32_t wsum[kRnsThreads / 64];
-  const int ss = __builtin_amdgcn_readfirstlane(pairs[2 * blockIdx.y]);
-  const int ds = __builtin_amdgcn_readfirstlane(pairs[2 * blockIdx.y + 1]);
+  __shared__ uint32_t tab[4096];  // slot -> symbol | (f - 1) << 8 | (slot - c) << 20
+  __shared__ uint32_t fc[256];    // f | c << 16
+  __shared__ uint16_t ring[kRnsWaves][kRnsRing];
+  __shared__ __align__(16) uint8_t ob[kRnsWaves][kRnsRows * 64];
+  __shared__ uint32_t wsum[kRnsWaves];
+  // (pairs == nullptr: one package, the blob at src_base decoded to dst_base)
+  const int ss = pairs ? __builtin_amdgcn_readfirstlane(pairs[2 * blockIdx.y]) : 0;
+  const int ds = pairs ? __builtin_amdgcn_readfirstlane(pairs[2 * blockIdx.y + 1]) : 0;
   if (ss < 0 || ds < 0) return;
   const uint8_t* blob = src_base + (size_t)ss * src_stride;
   uint8_t* out = dst_base + (size_t)ds * dst_stride;
   const long long n = (long long)*(const uint64_t*)(blob + 8), q = (long long)*(const uint64_t*)(blob + 16);
   if (n != raw_bytes || q > n) return;  // not a blob of this package size: nothing is written
-  constexpr int kWgPerRegion = kRnsGroups / (kRnsThreads / 64);
+  constexpr int kWgPerRegion = kRnsGroups / kRnsWaves;
   const int region = blockIdx.x / kWgPerRegion;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = (blockIdx.x % kWgPerRegion) * (kRnsThreads / 64) + wave;
+  const int g = (blockIdx.x % kWgPerRegion) * kRnsWaves + wave;
   size_t sec_off = 64;
   if (region == 1) {
     const uint32_t w0 = *(const uint32_t*)(blob + 64 + 512 + 4 * (size_t)kRnsStreams + 4 * (size_t)kRnsGroups);
@@ -159,7 +165,15 @@ __global__ __launch_bounds__(kRnsThreads) void rns_decode_kernel(const uint8_t* 
   uint8_t* dst = out + (region ? q : 0);
   if (m == 0) return;  // (whole workgroup: no barrier below is skipped by part of it)
 
-  // model: cumulative counts by a scan over the 256 frequencies, then the slot -> symbol table
+  // this wave's group: its states and word range, loaded ahead of the model's barriers
+  const long long i = 64LL * g + lane;
+  uint32_t x = *(const uint32_t*)(sec + 512 + 4 * (size_t)i);
+  const uint32_t* offs = (const uint32_t*)(sec + 512 + 4 * (size_t)kRnsStreams);
+  const uint32_t w_begin = __builtin_amdgcn_readfirstlane(offs[g]);
+  const uint32_t n_words = __builtin_amdgcn_readfirstlane(offs[g + 1]) - w_begin;
+  const uint16_t* words = (const uint16_t*)(sec + rns_section_head()) + w_begin;
+
+  // model: cumulative counts by a scan over the 256 frequencies
   const uint32_t f = *(const uint16_t*)(sec + 2 * tid);
   uint32_t incl = f;
   for (int off = 1; off < 64; off <<= 1) {
@@ -172,28 +186,46 @@ __global__ __launch_bounds__(kRnsThreads) void rns_decode_kernel(const uint8_t* 
   for (int w = 0; w < wave; ++w) base += wsum[w];
   const uint32_t c = base + incl - f;
   fc[tid] = f | (c << 16);
+#pragma unroll
+  for (int k = 0; k < 4096 / kRnsThreads; ++k) tab[tid + k * kRnsThreads] = 0;
   __syncthreads();
-  for (int slot = tid; slot < 4096; slot += kRnsThreads) {
-    int lo = 0, hi = 255;  // largest symbol whose cumulative count is <= slot (it has f > 0)
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if ((fc[mid] >> 16) <= (uint32_t)slot) lo = mid;
-      else hi = mid - 1;
-    }
-    lut[slot] = (uint8_t)lo;
+  // slot -> symbol: the first slot of each present symbol names it, and a running maximum over the
+  // slots gives every slot the largest present symbol starting at or before it (present symbols
+  // start at increasing slots)
+  if (f && c < 4096) tab[c] = tid;
+  __syncthreads();
+  constexpr int kPer = 4096 / kRnsThreads;  // 16 slots per thread
+  uint32_t v[kPer], run = 0;
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    run = max(run, tab[kPer * tid + k]);
+    v[k] = run;
+  }
+  uint32_t mx = run;
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t t = __shfl_up(mx, off, 64);
+    if (lane >= off) mx = max(mx, t);
+  }
+  if (lane == 63) wsum[wave] = mx;  // (its sums were read before the previous barrier)
+  __syncthreads();
+  uint32_t before = __shfl_up(mx, 1, 64);
+  if (lane == 0) before = 0;
+  for (int w = 0; w < wave; ++w) before = max(before, wsum[w]);
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const uint32_t slot = kPer * tid + k, sym = max(before, v[k]), e = fc[sym];
+    tab[slot] = sym | (((e & 0xFFFFu) - 1u) & 0xFFFu) << 8 | ((slot - (e >> 16)) & 0xFFFu) << 20;
   }
   __syncthreads();
 
-  // this wave's group
-  const long long i = 64LL * g + lane;
+  // the state's load completes here, once: inside the loop the compiler could no longer tell it
+  // apart from the ring's prefetches and the flushes, and would wait for all of them every step
+  asm volatile("" : "+v"(x));
   const long long cnt = rns_count(m, i);
   const int steps = (int)__builtin_amdgcn_readfirstlane((int)rns_count(m, 64LL * g));
-  uint32_t x = *(const uint32_t*)(sec + 512 + 4 * (size_t)i);
-  const uint32_t* offs = (const uint32_t*)(sec + 512 + 4 * (size_t)kRnsStreams);
-  const uint32_t w_begin = __builtin_amdgcn_readfirstlane(offs[g]);
-  const uint32_t n_words = __builtin_amdgcn_readfirstlane(offs[g + 1]) - w_begin;
-  const uint16_t* words = (const uint16_t*)(sec + rns_section_head()) + w_begin;
   uint16_t* rw = ring[wave];
+  uint8_t* ow = ob[wave];
+  const bool aligned = ((uintptr_t)dst & 15) == 0;
   // words [fetched, fetched + 256) of the sequence, 4 per lane (lanes past the end load nothing)
   uint16_t pre[4];
   auto prefetch = [&](uint32_t fetched) {
@@ -216,11 +248,9 @@ __global__ __launch_bounds__(kRnsThreads) void rns_decode_kernel(const uint8_t* 
     }
     const bool act = j < cnt;
     if (act) {
-      const uint32_t slot = x & 4095u;
-      const uint32_t sym = lut[slot];
-      const uint32_t e = fc[sym];
-      x = (e & 0xFFFFu) * (x >> 12) + slot - (e >> 16);
-      dst[i + (long long)j * kRnsStreams] = (uint8_t)sym;
+      const uint32_t e = tab[x & 4095u];
+      x = (((e >> 8) & 0xFFFu) + 1u) * (x >> 12) + (e >> 20);
+      ow[(j & (kRnsRows - 1)) * 64 + lane] = (uint8_t)e;
     }
     const bool need = act && x < kRnsLow;
     const unsigned long long b = __ballot(need);
@@ -229,13 +259,41 @@ __global__ __launch_bounds__(kRnsThreads) void rns_decode_kernel(const uint8_t* 
       x = (x << 16) | rw[(consumed + rank) & (kRnsRing - 1)];
     }
     consumed += (uint32_t)__popcll(b);
-    // every lane has read its word before a later refill overwrites the ring
+    if ((j & (kRnsRows - 1)) == kRnsRows - 1 || j == steps - 1) {
+      // flush: lane l stores bytes 16 (l % 4) .. +15 of row l / 4 (16 streams at one step)
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      const int rows = (j & (kRnsRows - 1)) + 1, r = lane >> 2, part = lane & 3;
+      if (r < rows) {
+        const long long pos = 64LL * g + 16 * part + (long long)((j & ~(kRnsRows - 1)) + r) * kRnsStreams;
+        const uint8_t* src = ow + r * 64 + 16 * part;
+        if (aligned && pos + 16 <= m) {
+          *(uint4*)(dst + pos) = *(const uint4*)src;
+        } else {
+          for (int k = 0; k < 16; ++k)
+            if (pos + k < m) dst[pos + k] = src[k];
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    }
+    // (LDS accesses of one wave complete in order: a ring word is read before a later refill
+    // rewrites it)
     __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   }
 }
 
 }  // namespace
+
+int launch_rns_decode_one(const void* blob, void* dst, size_t raw_bytes, hipStream_t s) {
+  if (raw_bytes == 0) return MOE_OK;
+  hipLaunchKernelGGL(rns_decode_kernel, dim3(2 * kRnsGroups / kRnsWaves, 1), dim3(kRnsThreads), 0, s,
+                     (const uint8_t*)blob, (size_t)0, (uint8_t*)dst, (size_t)0, (const int32_t*)nullptr,
+                     (long long)raw_bytes);
+  MOE_CHECK_LAUNCH("rANS decode launch");
+  return MOE_OK;
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -270,7 +328,7 @@ extern "C" int moe_decompress_rans(const void* src_base, size_t src_stride, void
                 src_stride, dst_stride, raw_bytes);
   if (n == 0 || raw_bytes == 0) return MOE_OK;
   if (!src_base || !dst_base || !pairs) return fail(MOE_ERR_INVALID, "moe_decompress_rans: null pointer");
-  hipLaunchKernelGGL(rns_decode_kernel, dim3(2 * kRnsGroups / (kRnsThreads / 64), n), dim3(kRnsThreads), 0,
+  hipLaunchKernelGGL(rns_decode_kernel, dim3(2 * kRnsGroups / kRnsWaves, n), dim3(kRnsThreads), 0,
                      (hipStream_t)stream, (const uint8_t*)src_base, src_stride, (uint8_t*)dst_base, dst_stride, pairs,
                      (long long)raw_bytes);
   MOE_CHECK_LAUNCH("moe_decompress_rans launch");

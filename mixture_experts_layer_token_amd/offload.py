@@ -33,6 +33,13 @@ the compute stream into a small working pool of plain packages (`work_slots`,
 shared by all layers), a group of at most that many at a time, each group
 followed by its FFN pass: the hits' groups first, the misses' groups once
 their copies landed.
+
+With `host_codec="rans"` (meant for 4-bit experts, whose codes no fixed-width
+code shrinks) only the host tier is compressed: the bank holds order-0 rANS
+blobs, the HBM slots plain packages.  A miss copies its blob into a small
+staging ring and the cache's decode stream writes the plain package into the
+slot (moe_cache_set_rans), so the link carries fewer bytes, hits cost nothing
+extra and the FFN reads the pool as in the plain case.
 """
 from __future__ import annotations
 
@@ -79,10 +86,13 @@ class OffloadedModel:
     """L MoE layers whose experts live in a pinned host bank, cached in an HBM slot pool."""
 
     def __init__(self, wl, max_T: int, capacity: int | None = None, device="cuda", fill=True, policy="lru",
-                 decay_period=0, overlap=True, prefetch=None, compressed=False, blob_bytes=None, work_slots=16):
+                 decay_period=0, overlap=True, prefetch=None, compressed=False, blob_bytes=None, work_slots=16,
+                 host_codec=None, staging_slots=16):
         """`compressed`: bank and HBM slots hold blobs of `blob_bytes` bytes (a multiple of 256 that
         every expert's blob must fit; bf16 experts only), decoded through a working pool of
-        `work_slots` plain packages."""
+        `work_slots` plain packages.  `host_codec="rans"`: the bank holds rANS blobs in slots of
+        `blob_bytes` bytes, decoded into the plain HBM slots as they arrive (through
+        `staging_slots` device staging slots)."""
         from synth import workloads as W
 
         self.wl = wl
@@ -90,13 +100,21 @@ class OffloadedModel:
         self.raw_bytes = api.moe_package_bytes(wl.H, wl.I, wl.wfmt)
         self.raw_stride = (self.raw_bytes + 255) // 256 * 256
         self.compressed = compressed
-        if compressed:
-            if wl.wfmt != "bf16" or not blob_bytes or blob_bytes % 256:
-                raise ValueError("compressed banks hold bf16 experts in blob slots of a multiple of 256 bytes")
-            self.pkg_bytes = blob_bytes  # what a miss copies: one blob slot
+        self.host_codec = host_codec
+        if host_codec not in (None, "rans") or (host_codec and compressed):
+            raise ValueError("host_codec: None or 'rans' (not with compressed tiers)")
+        if compressed or host_codec:
+            if (compressed and wl.wfmt != "bf16") or not blob_bytes or blob_bytes % 256:
+                raise ValueError("compressed banks hold blob slots of a multiple of 256 bytes (bf16 experts "
+                                 "for compressed tiers)")
+            self.pkg_bytes = blob_bytes  # bank stride; a miss copies at most one blob slot
         else:
             self.pkg_bytes = self.raw_bytes
-        self.stride = (self.pkg_bytes + 255) // 256 * 256
+        # pool slots: blobs (compressed tiers) or plain packages; the cache wants them >= the bank slot
+        self.stride = (max(self.pkg_bytes, self.raw_bytes if host_codec else 0) + 255) // 256 * 256
+        self.split = api.package_split(wl.H, wl.I, wl.wfmt)
+        self.staging = (torch.empty((staging_slots, self.pkg_bytes), dtype=torch.uint8, device=device)
+                        if host_codec else None)
         self.capacity = capacity or int(wl.cache_frac * wl.layers * wl.E)
         self.bank = PinnedBuffer(self.L * self.E * self.pkg_bytes)
         self.blob_sizes = np.zeros((self.L, self.E), np.int64)
@@ -105,8 +123,7 @@ class OffloadedModel:
                 self.fill(l, list(range(self.E)))
         self.pool = torch.empty((self.capacity, self.stride), dtype=torch.uint8, device=device)
         self.policy, self.decay_period = policy, decay_period
-        self.cache = api.ExpertCache(self.bank, self.pkg_bytes, self.L, self.E, self.pool, self.stride,
-                                     self.capacity, policy, decay_period)
+        self.cache = self._new_cache()
         self.slot_tables = [torch.full((self.E,), -1, dtype=torch.int32, device=device) for _ in range(self.L)]
         # slot tables of the two FFN passes (hits only, misses only), staged from pinned host memory;
         # a layer's staging buffers are rewritten only after its previous copies ran (the host waits
@@ -157,6 +174,13 @@ class OffloadedModel:
         self.filled = {}
         self._reset_records()
 
+    def _new_cache(self):
+        c = api.ExpertCache(self.bank, self.pkg_bytes, self.L, self.E, self.pool, self.stride, self.capacity,
+                            self.policy, self.decay_period)
+        if self.host_codec:
+            c.set_rans(self.staging, self.pkg_bytes, self.raw_bytes)
+        return c
+
     def _reset_records(self):
         self.plans, self.groups, self.events, self._copy_windows = [], [], [], []
         self.prev_ids = [None] * self.L  # distinct experts of each layer's previous step
@@ -189,9 +213,9 @@ class OffloadedModel:
             self.decay_period = decay_period
         if prefetch != "keep":
             self.prefetch = prefetch
+        self.copy_stream.synchronize()  # (the old cache's copies and decodes are over)
         self.cache.close()
-        self.cache = api.ExpertCache(self.bank, self.pkg_bytes, self.L, self.E, self.pool, self.stride,
-                                     self.capacity, self.policy, self.decay_period)
+        self.cache = self._new_cache()
         for t in self.slot_tables:
             t.fill_(-1)
         self._reset_records()
@@ -214,8 +238,9 @@ class OffloadedModel:
             return np.sort(order[:len(prev)]).astype(np.int32)
         raise ValueError("prefetch heuristic %r" % (self.prefetch,))
 
-    def fill(self, l: int, experts):
-        """Generate and pack experts of layer l into the host bank (compressed: their blobs)."""
+    def fill(self, l: int, experts, source=None):
+        """Generate and pack experts of layer l into the host bank (compressed: their blobs).
+        `source(l, ids)`: the packages ([len(ids), raw_bytes] uint8) in place of generating them."""
         import concurrent.futures as cf
 
         from .layer import _workers, pack_bank
@@ -223,8 +248,8 @@ class OffloadedModel:
         experts = sorted(experts)
         for i in range(0, len(experts), 64):
             ids = experts[i:i + 64]
-            host = pack_bank(self.wl, l, ids, stride=self.raw_bytes)
-            if not self.compressed:
+            host = source(l, ids) if source else pack_bank(self.wl, l, ids, stride=self.raw_bytes)
+            if not self.compressed and not self.host_codec:
                 for j, e in enumerate(ids):
                     o = (l * self.E + e) * self.pkg_bytes
                     self.bank.array[o:o + self.pkg_bytes] = host[j]
@@ -232,7 +257,8 @@ class OffloadedModel:
 
             def one(j):
                 e = ids[j]
-                blob = api.moe_compress_package(host[j])
+                blob = (api.moe_compress_package(host[j]) if self.compressed
+                        else api.moe_compress_rans(host[j], self.split))
                 if blob.size > self.pkg_bytes:
                     raise ValueError("layer %d expert %d: blob of %d bytes exceeds the %d-byte slot"
                                      % (l, e, blob.size, self.pkg_bytes))

@@ -1,12 +1,20 @@
 // Drives the expert-cache planner (demand lookups of both policies, prefetches, pins, a fetch
-// through a copy engine that fails halfway, the error paths) for builds with AddressSanitizer and
-// UndefinedBehaviorSanitizer; no GPU is touched.
+// through a copy engine that fails halfway, the error paths) and the host encoders, for builds
+// with AddressSanitizer and UndefinedBehaviorSanitizer; no GPU is touched.
 #include <stdio.h>
 #include <string.h>
 
 #include <vector>
 
+#include <hip/hip_runtime.h>
+
 #include "../../include/moe.h"
+
+// the cache's rANS bank mode launches a GPU decoder; this host-only build links no kernels, and the
+// mode itself is never switched on here (it needs a device stream), so a stand-in that refuses
+namespace moe {
+int launch_rns_decode_one(const void*, void*, size_t, hipStream_t) { return MOE_ERR_UNSUPPORTED; }
+}  // namespace moe
 
 static int copies = 0;
 static int fake_copy(void*, void* dst, const void* src, size_t n, void*) {
@@ -47,6 +55,12 @@ int main() {
     if (moe_cache_plan(c, L, ids, 1, p) != MOE_ERR_INVALID) return 7;
     moe_cache_stats_t st;
     if (moe_cache_stats(c, &st) != MOE_OK || st.lookups <= 0) return 8;
+    // the rANS bank mode's argument checks (all before a stream would be created)
+    unsigned char stage_stub[1];
+    if (moe_cache_set_rans(c, nullptr, 256, 4, pkg) != MOE_ERR_INVALID) return 13;
+    if (moe_cache_set_rans(c, stage_stub, 128, 4, pkg) != MOE_ERR_INVALID) return 14;
+    if (moe_cache_set_rans(c, stage_stub, 256, 0, pkg) != MOE_ERR_INVALID) return 15;
+    if (moe_cache_set_rans(c, stage_stub, 256, 4, pkg + 1) != MOE_ERR_INVALID) return 16;
     delete p;
     moe_cache_destroy(c);
   }
@@ -67,6 +81,30 @@ int main() {
     if (moe_compress_package(v.data(), raw, blob.data(), cap - 1, &n) != MOE_ERR_INVALID) return 11;
     if (moe_compress_package(v.data(), 1000, blob.data(), cap, &n) != MOE_ERR_INVALID) return 12;
   }
-  printf("planner and encoder: ok (%d copies)\n", copies);
+  // the host rANS encoder over regions shorter and longer than its 32768 streams, empty regions and
+  // one-symbol regions: the blob stays within the bound and its header names what was encoded
+  {
+    const size_t sizes[] = {0, 1, 1000, 32768 + 5, 3 * 32768 + 999};
+    for (size_t raw : sizes) {
+      std::vector<uint8_t> r(raw);
+      for (size_t i = 0; i < raw; ++i) r[i] = (uint8_t)(((i * 2654435761u) >> 20) % 9 == 0 ? i * 7 : 3);
+      const size_t cap = moe_compress_rans_bound(raw);
+      std::vector<uint8_t> blob(cap);
+      const size_t splits[] = {0, raw / 3, raw};
+      for (size_t q : splits) {
+        size_t n = 0;
+        if (moe_compress_rans(r.data(), raw, q, blob.data(), cap, &n) != MOE_OK || n > cap || n % 16) return 17;
+        uint64_t hn, hq, ht;
+        memcpy(&hn, blob.data() + 8, 8);
+        memcpy(&hq, blob.data() + 16, 8);
+        memcpy(&ht, blob.data() + 24, 8);
+        if (hn != raw || hq != q || ht != n) return 18;
+      }
+      size_t n = 0;
+      if (moe_compress_rans(r.data(), raw, raw + 1, blob.data(), cap, &n) != MOE_ERR_INVALID) return 19;
+      if (moe_compress_rans(r.data(), raw, 0, blob.data(), cap - 1, &n) != MOE_ERR_INVALID) return 20;
+    }
+  }
+  printf("planner and encoders: ok (%d copies)\n", copies);
   return 0;
 }

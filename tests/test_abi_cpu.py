@@ -475,3 +475,23 @@ def test_compress_rans_validation():
     assert L.moe_decompress_rans(None, 256, None, 1024, None, 65536, 1024, None) == INVALID
     assert L.moe_decompress_rans(None, 256, None, 1024, None, 1, 1024, None) == INVALID  # null pointers
     assert L.moe_decompress_rans(None, 256, None, 1024, None, 0, 1024, None) == OK
+
+
+def test_cache_set_rans_validation():
+    """Argument checks of the rANS bank mode, all taken before any stream is created."""
+    L_, E, pkg, cap = 1, 8, 512, 4
+    bank = np.zeros((E, pkg), np.uint8)
+    pool = np.zeros((cap, 1024), np.uint8)
+    c = ExpertCache(None, pkg, L_, E, None, 1024, cap, copy=FakeCopyEngine(), bank_ptr=bank.ctypes.data,
+                    pool_ptr=pool.ctypes.data)
+    st = ctypes.c_void_p(0x1000)
+    assert L.moe_cache_set_rans(c.h, None, 512, 4, 1024) == INVALID        # no staging
+    assert L.moe_cache_set_rans(c.h, st, 256, 4, 1024) == INVALID          # staging slot below pkg_bytes
+    assert L.moe_cache_set_rans(c.h, st, 600, 4, 1024) == INVALID          # not a multiple of 256
+    assert L.moe_cache_set_rans(c.h, st, 512, 0, 1024) == INVALID          # no staging slots
+    assert L.moe_cache_set_rans(c.h, st, 512, 65, 1024) == INVALID
+    assert L.moe_cache_set_rans(c.h, st, 512, 4, 1025) == INVALID          # package larger than a pool slot
+    assert L.moe_cache_set_rans(c.h, st, 512, 4, 0) == INVALID
+    assert L.moe_cache_set_rans(None, st, 512, 4, 1024) == INVALID
+    planning = ExpertCache(None, 1 << 20, L_, E, None, 0, cap)
+    assert L.moe_cache_set_rans(planning.h, st, 1 << 20, 4, 1024) == INVALID  # no bank

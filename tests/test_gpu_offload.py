@@ -24,16 +24,18 @@ def _gpu():
 
 
 def run_and_check(wl, T, steps, check_steps, fill_all=True, capacity=None, policy="lru", period=0, overlap=True,
-                  prefetch=None, pins=None, blob_bytes=None, work_slots=16):
-    """`blob_bytes`: compressed tiers with blob slots of that size."""
+                  prefetch=None, pins=None, blob_bytes=None, work_slots=16, host_codec=None):
+    """`blob_bytes`: compressed tiers with blob slots of that size (with `host_codec`: a bank of
+    blobs of that codec in slots of that size, plain packages in HBM)."""
+    tiers = blob_bytes is not None and host_codec is None
     xs = {}
     for s in range(steps):
         for l in range(wl.layers):
             x, _ = oracle.rank_gap_inputs(wl, T, layer=l, step=s)
             xs[(l, s)] = x
     model = OffloadedModel(wl, T, capacity=capacity, fill=fill_all, policy=policy, decay_period=period,
-                           overlap=overlap, prefetch=prefetch, compressed=blob_bytes is not None,
-                           blob_bytes=blob_bytes, work_slots=work_slots)
+                           overlap=overlap, prefetch=prefetch, compressed=tiers,
+                           blob_bytes=blob_bytes, work_slots=work_slots, host_codec=host_codec)
     if pins:
         model.reset_cache(pins=pins)
     if not fill_all:  # only the experts some step routes to (the others are never fetched)
@@ -58,10 +60,16 @@ def run_and_check(wl, T, steps, check_steps, fill_all=True, capacity=None, polic
                 mine = sorted(set(ids.ravel().tolist()))
                 slots = [int(tab[e]) for e in mine]
                 assert min(slots) >= 0 and len(set(slots)) == len(slots)
-                got_bytes = model.pool[torch.tensor(slots, device="cuda")][:, :model.pkg_bytes].cpu().numpy()
-                for i, e in enumerate(mine):
-                    assert np.array_equal(got_bytes[i], model.package(l, e)), (l, s, e)
-                if blob_bytes is not None:
+                if host_codec:  # the slot holds the package the oracle decodes from the bank's blob
+                    got_bytes = model.pool[torch.tensor(slots, device="cuda")][:, :model.raw_bytes].cpu().numpy()
+                    for i, e in enumerate(mine):
+                        want = oracle.rns_decode(model.package(l, e)[:model.blob_sizes[l, e]], model.raw_bytes)
+                        assert np.array_equal(got_bytes[i], want), ("decoded", l, s, e)
+                else:
+                    got_bytes = model.pool[torch.tensor(slots, device="cuda")][:, :model.pkg_bytes].cpu().numpy()
+                    for i, e in enumerate(mine):
+                        assert np.array_equal(got_bytes[i], model.package(l, e)), (l, s, e)
+                if tiers:
                     # the working pool after the layer's last group: each of its experts' packages as the
                     # oracle decodes them from the blob
                     work = model.work[:len(model.last_group), :model.raw_bytes].cpu().numpy()
@@ -80,7 +88,12 @@ def run_and_check(wl, T, steps, check_steps, fill_all=True, capacity=None, polic
         assert [(p[3], p[4]) for p in model.plans] == list(zip(h0.tolist(), m0.tolist()))
     st = model.cache.stats()
     assert st["hits"] == sum(h[i] for i in dem) and st["misses"] == sum(m[i] for i in dem)
-    assert st["bytes_fetched"] == m.sum() * model.pkg_bytes
+    if host_codec:  # each fetch moved its blob's own bytes
+        sizes = model.blob_sizes[model.blob_sizes > 0]
+        assert m.sum() * sizes.min() <= st["bytes_fetched"] <= m.sum() * sizes.max()
+        assert st["bytes_fetched"] % 16 == 0 and sizes.max() <= model.pkg_bytes
+    else:
+        assert st["bytes_fetched"] == m.sum() * model.pkg_bytes
     assert st["prefetch_hits"] == ph
     hb, _ = oracle.belady(model.capacity, groups)
     hd = sum(h[i] for i in dem)
@@ -176,6 +189,32 @@ def test_offload_compressed_glm_bf16_full_size_first_steps():
     blob = (int(raw * 0.77) + 255) // 256 * 256
     say("offload compressed glm bf16")
     run_and_check(wl, 4, 3, {0, 2}, fill_all=False, policy="lfu_decay", period=4, blob_bytes=blob)
+
+
+@pytest.mark.parametrize("overlap,prefetch,fmt", [(True, None, "int4g32"), (False, "last", "mxfp4")])
+def test_offload_rans_bank_small_all_steps(overlap, prefetch, fmt):
+    """4-bit experts with a bank of rANS blobs: every miss decoded into its plain HBM slot on the
+    cache's decode stream; every step checked (slot bytes against the oracle's decode, outputs)."""
+    from mixture_experts_layer_token_amd import api
+
+    wl = W.Workload(name="offload-r", H=224, E=16, k=4, I=352, wfmt=fmt, xdt="bf16", Ts=(5,), seed=612,
+                    zipf_s=1.2, layers=3, steps=16, rerank_every=8, cache_frac=0.3)
+    blob = (api.moe_compress_rans_bound(api.moe_package_bytes(wl.H, wl.I, fmt)) + 255) // 256 * 256
+    say("offload rans bank small", fmt, "overlap", overlap, "prefetch", prefetch)
+    run_and_check(wl, 5, wl.steps, set(range(wl.steps)), overlap=overlap, prefetch=prefetch, blob_bytes=blob,
+                  host_codec="rans")
+
+
+@pytest.mark.parametrize("T", [1, 16])
+def test_offload_rans_bank_glm_full_size_first_steps(T):
+    """GLM-shaped INT4 layers at full size with a bank of rANS blobs in slots of 90% of the package."""
+    from mixture_experts_layer_token_amd import api
+
+    wl = W.WORKLOADS["glm"].with_(layers=2, steps=3)
+    raw = api.moe_package_bytes(wl.H, wl.I, wl.wfmt)
+    blob = (int(raw * 0.9) + 255) // 256 * 256
+    say("offload rans bank glm T", T)
+    run_and_check(wl, T, 3, {0, 2}, fill_all=False, blob_bytes=blob, host_codec="rans")
 
 
 @pytest.mark.parametrize("mode", ["decode", "prefill"])
