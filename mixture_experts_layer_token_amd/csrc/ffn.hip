@@ -820,8 +820,12 @@ WsLayout ws_layout(const moe_experts* w, int T, int k, int xdt, int mode = MOE_F
   return L;
 }
 
-int pick_mt(int T, int k, int E) {
-  double avg = (double)T * k / E;
+// M tiles per streaming row tile, from the average rows per expert (the counts are on the device):
+// bf16 from 4 rows (Mixtral T = 16 / 32: 428 -> 423, 459 -> 440 us per step; T = 8 the same), 4-bit
+// only from about 11 (two M tiles measured slower for the 4-bit kernels at gpt-oss T = 32 .. 128)
+int pick_mt(int T, int k, int E, int fmt) {
+  const double avg = (double)T * k / E;
+  if (fmt == MOE_W_BF16) return avg >= 4.0 ? 2 : 1;
   return 1.5 * avg > 16.0 ? 2 : 1;
 }
 
@@ -1030,7 +1034,7 @@ int launch_ffn(const moe_experts* w, const void* x, int xdt, int T, int k, const
 
   if (mode == MOE_FFN_DECODE_MX) {
     // every expert streamed on the block-scaled MFMA: x -> MXFP8 terms, gate/up, h -> MXFP8 terms, down
-    const int mt = pick_mt(T, k, E), mr = 16 * mt;
+    const int mt = pick_mt(T, k, E, w->fmt), mr = 16 * mt;
     const size_t nz = n < (size_t)E ? n : (size_t)E;
     const int S = (int)((n + nz * (mr - 1)) / mr);
     unsigned char* mx = (unsigned char*)(wsp + L.mx_off);
@@ -1102,7 +1106,7 @@ int launch_ffn(const moe_experts* w, const void* x, int xdt, int T, int k, const
   // go to the weight-streaming kernel, the others to the MFMA tile kernel (one weight read per 192
   // rows instead of one per 16 * mt rows).  AUTO launches only the variants that can have work; DECODE
   // and PREFILL force one variant for every expert.
-  const int kHot = 4 * 16 * pick_mt(T, k, E);  // at most 4 streaming row tiles per expert
+  const int kHot = 4 * 16 * pick_mt(T, k, E, w->fmt);  // at most 4 streaming row tiles per expert
   // (the tile kernel addresses activation rows with 32-bit element offsets)
   const bool tile_ok = (double)((size_t)T > n ? T : n) * (H > I ? H : I) < 2147483648.0;
   bool use_stream = true, use_tile = false;
@@ -1125,7 +1129,7 @@ int launch_ffn(const moe_experts* w, const void* x, int xdt, int T, int k, const
       use_tile = true, split = kHot;
     }
   }
-  const int mt = pick_mt(T, k, E);
+  const int mt = pick_mt(T, k, E, w->fmt);
   const int mr = 16 * mt;
   const size_t nz = n < (size_t)E ? n : (size_t)E;
   const int S = (int)((n + nz * (mr - 1)) / mr);
