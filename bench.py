@@ -572,6 +572,9 @@ def run_decoder(args):
     ok = all(np.array_equal(work[i].cpu().numpy(), host[i]) for i in range(n))
     if not ok:
         raise RuntimeError("decoded packages differ from the originals")
+    # one package per launch (what the expert cache's decode of a single miss costs)
+    one = decoder_roofline(pool, stride, work, raw_bytes, [blobs[0].size], raw_bytes, reps=args.steps, codec=codec)
+    roof["one_package_us"] = one["avg_launch_us"]
     us = roof["avg_launch_us"]
     return {"metric": "lossless package decode GB/s (blobs read + packages written)", "value": roof["achieved"],
             "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": 3, "ms_per_step": round(us / 1e3, 4),
