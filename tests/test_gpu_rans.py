@@ -96,3 +96,54 @@ def test_rans_decode_nothing_to_do():
     moe.moe_decompress_rans(d, 1024, d, 1024, pairs, 1024)
     torch.cuda.synchronize()
     assert int(d.sum()) == 0
+
+
+def test_cache_rans_bank_refuses_a_corrupt_blob_and_rolls_back():
+    """Expert cache over a bank of rANS blobs: each miss lands in a staging slot and is decoded into
+    its pool slot.  A bank slot whose header is not a blob of the package size fails the fetch
+    before anything of it moves; it and the misses after it are not resident (the ones before stay
+    valid), the stats count only the blobs that crossed, and once the slot holds a good blob the
+    next lookup fetches the rest."""
+    from mixture_experts_layer_token_amd.offload import PinnedBuffer
+
+    n, q, E = 40000, 30000, 4
+    raws = [_raw("skewed", n, 20 + e) for e in range(E)]
+    blobs = [oracle.rns_encode(r, q) for r in raws]
+    pkg = (max(b.size for b in blobs) + 255) // 256 * 256
+    bank = PinnedBuffer(E * pkg)
+    for e, b in enumerate(blobs):
+        bank.array[e * pkg:e * pkg + b.size] = b
+        bank.array[e * pkg + b.size:(e + 1) * pkg] = 0
+    bank.array[2 * pkg] ^= 0xFF  # expert 2: not a rANS blob
+    pool = torch.full((E, pkg), 0xAB, dtype=torch.uint8, device="cuda")
+    staging = torch.empty((2, pkg), dtype=torch.uint8, device="cuda")  # fewer staging slots than misses
+    table = torch.full((E,), -1, dtype=torch.int32, device="cuda")
+    cs, done = torch.cuda.Stream(), torch.cuda.Event()
+    done.record(cs)
+    cache = api.ExpertCache(bank, pkg, 1, E, pool, pkg, E)
+    cache.set_rans(staging, pkg, n)
+    try:
+        plan = cache.plan(0, np.arange(E, dtype=np.int32))
+        assert plan.n_misses == E
+        slots = [plan.miss_slots[i] for i in range(E)]
+        with pytest.raises(moe.MoeError) as err:
+            cache.fetch(plan, table, cs, done)
+        assert err.value.code == -1 and "blob header" in str(err.value)
+        cs.synchronize()
+        got = pool.cpu().numpy()
+        for e in (0, 1):  # fetched and decoded before the bad slot
+            assert np.array_equal(got[slots[e], :n], raws[e])
+        assert cache.stats()["bytes_fetched"] == blobs[0].size + blobs[1].size
+        bank.array[2 * pkg] ^= 0xFF
+        plan = cache.plan(0, np.array([2, 3], dtype=np.int32))
+        assert (plan.n_hits, plan.n_misses) == (0, 2)
+        cache.fetch(plan, table, cs, done)
+        done.synchronize()
+        got = pool.cpu().numpy()
+        tab = table.cpu().numpy()
+        for e in range(E):
+            assert np.array_equal(got[tab[e], :n], raws[e]), e
+        assert cache.stats()["bytes_fetched"] == sum(b.size for b in blobs)
+    finally:
+        cache.close()
+        bank.close()
