@@ -68,11 +68,13 @@ __global__ __launch_bounds__(NW * 64, FMT == MOE_W_BF16 ? 3 : 2) void ffn_stream
   const int gx = (n_units + NP - 1) / NP;  // unit groups
   // work item (uniform: scalar loads).  plan[0].x = row tiles; plan[1 + t] = {first tile of the
   // expert, its first grouped row, its rows, its slot} for every tile t of that expert
-  const int n_items = args.plan[0].x * gx;
+  DirectTiles dt;
+  if (!args.plan) dt.scan(args, MR);
+  const int n_items = (args.plan ? args.plan[0].x : dt.total) * gx;
   const int per_xcd = (n_items + 7) / 8;
   const int j = (int)blockIdx.x / 8, item = (int)(blockIdx.x % 8) * per_xcd + j;
   if (j >= per_xcd || item >= n_items) return;
-  const int4 td = args.plan[1 + item / gx];
+  const int4 td = args.plan ? args.plan[1 + item / gx] : dt.entry(MR, item / gx);
   const int nt = (td.z + MR - 1) / MR;
   const int local = item - gx * td.x;
   const int t = local % nt;
@@ -335,11 +337,13 @@ __global__ __launch_bounds__(NW * 64, 2) void ffn_stream_sa_kernel(FfnArgs args)
   constexpr int UPW = NW * NPW;        // units per workgroup
   const int gx = (n_units + UPW - 1) / UPW;
   // work item, as in ffn_stream_kernel
-  const int n_items = args.plan[0].x * gx;
+  DirectTiles dt;
+  if (!args.plan) dt.scan(args, MR);
+  const int n_items = (args.plan ? args.plan[0].x : dt.total) * gx;
   const int per_xcd = (n_items + 7) / 8;
   const int j = (int)blockIdx.x / 8, item = (int)(blockIdx.x % 8) * per_xcd + j;
   if (j >= per_xcd || item >= n_items) return;
-  const int4 td = args.plan[1 + item / gx];
+  const int4 td = args.plan ? args.plan[1 + item / gx] : dt.entry(MR, item / gx);
   const int nt = (td.z + MR - 1) / MR;
   const int local = item - gx * td.x;
   const int t = local % nt;
@@ -823,6 +827,12 @@ WsLayout ws_layout(const moe_experts* w, int T, int k, int xdt, int mode = MOE_F
 // M tiles per streaming row tile, from the average rows per expert (the counts are on the device):
 // bf16 from 4 rows (Mixtral T = 16 / 32: 428 -> 423, 459 -> 440 us per step; T = 8 the same), 4-bit
 // only from about 11 (two M tiles measured slower for the 4-bit kernels at gpt-oss T = 32 .. 128)
+// routed rows up to which the streaming kernels find their row tiles themselves (no plan kernel)
+#ifndef MOE_CFG_DIRECT_ROWS
+#define MOE_CFG_DIRECT_ROWS 64
+#endif
+constexpr size_t kDirectRows = MOE_CFG_DIRECT_ROWS;
+
 int pick_mt(int T, int k, int E, int fmt) {
   const double avg = (double)T * k / E;
   if (fmt == MOE_W_BF16) return avg >= 4.0 ? 2 : 1;
@@ -918,16 +928,16 @@ void launch_stream_cfg(bool gate_up, const FfnArgs& a, int H, int I, int S, hipS
       hipLaunchKernelGGL((ffn_stream_sa_kernel<FMT, MT, NW, D_NPW, PF, false>), dim3(grid8(dx, S)), dim3(64 * NW), 0,
                          s, a);
     }
-    return;
-  }
-  if (gate_up) {
-    const int gx = (I / 16 + C::GU_NP - 1) / C::GU_NP;
-    hipLaunchKernelGGL((ffn_stream_kernel<FMT, MT, C::GU_NW, C::GU_NP, C::GU_PF, true>), dim3(grid8(gx, S)),
-                       dim3(64 * C::GU_NW), 0, s, a);
-  } else {
-    const int dx = (H / 16 + C::D_NP - 1) / C::D_NP;
-    hipLaunchKernelGGL((ffn_stream_kernel<FMT, MT, C::D_NW, C::D_NP, C::D_PF, false>), dim3(grid8(dx, S)),
-                       dim3(64 * C::D_NW), 0, s, a);
+  } else {  // (an else, so that no wide 4-bit shape of this kernel is instantiated)
+    if (gate_up) {
+      const int gx = (I / 16 + C::GU_NP - 1) / C::GU_NP;
+      hipLaunchKernelGGL((ffn_stream_kernel<FMT, MT, C::GU_NW, C::GU_NP, C::GU_PF, true>), dim3(grid8(gx, S)),
+                         dim3(64 * C::GU_NW), 0, s, a);
+    } else {
+      const int dx = (H / 16 + C::D_NP - 1) / C::D_NP;
+      hipLaunchKernelGGL((ffn_stream_kernel<FMT, MT, C::D_NW, C::D_NP, C::D_PF, false>), dim3(grid8(dx, S)),
+                         dim3(64 * C::D_NW), 0, s, a);
+    }
   }
 }
 
@@ -1151,7 +1161,11 @@ int launch_ffn(const moe_experts* w, const void* x, int xdt, int T, int k, const
   const long long wide_wgs = (long long)nz * ((I / 16 + Cfg<MOE_W_MXFP4, 1, false>::GU_NP - 1) /
                                               Cfg<MOE_W_MXFP4, 1, false>::GU_NP);
   const bool narrow = wide_wgs < 1024;
-  if (use_stream) {
+  if (use_stream && n <= kDirectRows && E <= 64 * kDirectPer) {
+    // few routed rows, so few row tiles: each streaming workgroup finds its own from the offsets
+    // (DirectTiles), one dependent launch less (gpt-oss T = 1: the plan kernel took 3.1 us)
+    gu_s.plan = dn_s.plan = nullptr;
+  } else if (use_stream) {
     int4* plan = (int4*)(wsp + L.plan_off);
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, offsets, E, mr, 1, split, w->slot_of_expert,
                        gu.n_slots, plan, (int*)nullptr, 0);

@@ -155,7 +155,8 @@ struct FfnArgs {
   size_t region_codes, region_scales;  // byte offsets of this matrix's codes / scales in a package
   // row tiles (16 * mt rows for the streaming variant, 192 for the tile variant): plan[0].x =
   // tiles; plan[1 + t] = {first tile of the expert of tile t, the expert's first grouped row, its
-  // rows, its slot}, written by the plan kernel from the offsets and the slot table
+  // rows, its slot}, written by the plan kernel from the offsets and the slot table (streaming
+  // variant: null when the kernel finds its tile itself, see DirectTiles)
   const int4* plan;
   int* tcount;  // [8] work counters of the persistent kernels, one per XCD range, zeroed by the plan kernel
   // INT4 experts: the power of two each token's activations were divided by in the fp16 cast
@@ -176,6 +177,64 @@ struct FfnArgs {
 __device__ __forceinline__ float token_scale(const FfnArgs& a, int p) { return a.xscale[a.perm_src[p] / a.k]; }
 __device__ __forceinline__ float swiglu_scaled(float g, float u, float s) { return g * u / (1.0f + __expf(-(g * s))); }
 
+
+// The streaming kernels' row tiles without a plan kernel (launches with few routed rows): the tiles
+// plan_kernel would write -- mr rows at a time over the experts in order, counting the experts whose
+// row count lies in [min_rows, max_rows] and whose slot is resident -- found by each wave on its own
+// from the offsets, so the results are wave-uniform and no LDS or barrier is involved.  Lane l
+// covers experts [l * per, (l + 1) * per), per <= kDirectPer (E <= 512), and keeps their first row,
+// row count and slot in registers; scan() gives its tiles' range [excl, incl) and the total.
+constexpr int kDirectPer = 8;
+struct DirectTiles {
+  int per, excl, incl, total;
+  int o0[kDirectPer], c[kDirectPer], slot[kDirectPer];
+
+  __device__ void scan(const FfnArgs& a, int mr) {
+    const int lane = threadIdx.x & 63;
+    per = (a.E + 63) / 64;
+    int local = 0;
+#pragma unroll
+    for (int i = 0; i < kDirectPer; ++i) {
+      const int e = lane * per + i;
+      o0[i] = 0, c[i] = 0, slot[i] = -1;
+      if (i < per && e < a.E) {
+        o0[i] = a.offsets[e];
+        c[i] = a.offsets[e + 1] - o0[i];
+        slot[i] = a.slot_of_expert ? a.slot_of_expert[e] : e;
+        if (c[i] < a.min_rows || c[i] > a.max_rows || (unsigned)slot[i] >= (unsigned)a.n_slots) c[i] = 0;
+      }
+      local += (c[i] + mr - 1) / mr;
+    }
+    incl = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += t;
+    }
+    excl = incl - local;
+    total = __builtin_amdgcn_readlane(incl, 63);
+  }
+  // the plan entry of tile `tile` (uniform, < total): {first tile of its expert, the expert's first
+  // grouped row, its rows, its slot}
+  __device__ int4 entry(int mr, int tile) const {
+    const unsigned long long b = __ballot(tile >= excl && tile < incl);
+    const int owner = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(b));
+    int4 r = make_int4(0, 0, 0, 0);
+    int acc = excl;
+    bool found = false;
+#pragma unroll
+    for (int i = 0; i < kDirectPer; ++i) {
+      const int nt = (c[i] + mr - 1) / mr;
+      if (!found && tile < acc + nt) {
+        r = make_int4(acc, o0[i], c[i], slot[i]);
+        found = true;
+      }
+      acc += nt;
+    }
+    return make_int4(__builtin_amdgcn_readlane(r.x, owner), __builtin_amdgcn_readlane(r.y, owner),
+                     __builtin_amdgcn_readlane(r.z, owner), __builtin_amdgcn_readlane(r.w, owner));
+  }
+};
 
 constexpr int kXcds = 8;  // XCDs of an MI355X; workgroup i is dispatched to XCD i % 8
 // Rows of a tile of the prefill (MFMA tile) kernel at most: its plans cut an expert with n rows
