@@ -316,7 +316,17 @@ __global__ __launch_bounds__(NW * 64, FMT == MOE_W_BF16 ? 3 : 2) void ffn_stream
 // each wave, and read back by every wave.  Stage st lives in LDS buffer st % (PF + 1): the loads
 // of stage st + PF, issued after stage st's barrier, go to the buffer of stage st - 1, which every
 // wave has finished reading once it reached that barrier.
-template <int FMT, int MT, int NW, int NPW, int PF, bool GU>
+// KiB of LDS that hold one wave's scales in the shared-activation kernel: nstr strips of nks k-steps,
+// 16 rows and sb bytes per scale
+__host__ __device__ constexpr int sl_kib(int nks, int nstr, int sb) { return (nstr * 16 * nks * sb + 1023) / 1024; }
+// LDS per workgroup up to which the scales go to LDS: 4 workgroups still fit a CU's 160 KiB
+constexpr size_t kSlMaxLds = 40 * 1024;
+
+// SL: the block scales of a wave's strips are copied into LDS once, with direct-to-LDS loads issued
+// ahead of the first stage (one contiguous run per strip), and every stage reads its scales from
+// there; otherwise each stage loads its 64 (MXFP4) or 128 (INT4) scale bytes per strip from HBM
+// beside its codes.  The launch passes NW * sl_kib(K) KiB of dynamic LDS for them.
+template <int FMT, int MT, int NW, int NPW, int PF, bool GU, bool SL>
 __global__ __launch_bounds__(NW * 64, 2) void ffn_stream_sa_kernel(FfnArgs args) {
   typedef typename Op<FMT>::T OpT;
   constexpr int SPU = GU ? 2 : 1;  // strips per unit
@@ -328,8 +338,9 @@ __global__ __launch_bounds__(NW * 64, 2) void ffn_stream_sa_kernel(FfnArgs args)
   static_assert(FMT != MOE_W_BF16 && NW == KPS, "4-bit weights; wave q loads k-step q's fragments");
   constexpr int NAW = MT;        // activation loads per wave and stage
   constexpr int NBUF = PF + 1;   // LDS stage buffers
-  constexpr int L = 2 * NSTR + NAW;  // vector loads per wave and stage
+  constexpr int L = (SL ? 1 : 2) * NSTR + NAW;  // vector loads per wave and stage
   __shared__ __align__(16) unsigned char a_lds[NBUF * NA * 1024];
+  extern __shared__ __align__(16) unsigned char s_lds[];  // SL: the scales, sl_kib KiB per wave
 
   const int K = GU ? args.H : args.I;
   const int N = GU ? args.I : args.H;  // output features of this matrix
@@ -372,6 +383,22 @@ __global__ __launch_bounds__(NW * 64, 2) void ffn_stream_sa_kernel(FfnArgs args)
   typedef const __attribute__((address_space(1))) char* gptr;
   gptr zpage = (gptr)g_zero_page;
   asm volatile("" : "+s"(zpage));
+  // SL: the wave's NSTR scale runs of R bytes each, back to back from sl (R is a multiple of 16);
+  // KiB i of that copy is one direct-to-LDS load, lanes past the end read the zero page
+  const int R = 16 * nks * SB;
+  unsigned char* const sl = s_lds + (size_t)wave * sl_kib(nks, NSTR, SB) * 1024;
+  if constexpr (SL) {
+    const int nkib = sl_kib(nks, NSTR, SB);
+    for (int i = 0; i < nkib; ++i) {
+      const int o = i * 1024 + (int)lane16;
+      gptr g = zpage + lane16;
+#pragma unroll
+      for (int s = 0; s < NSTR; ++s)
+        if (o >= s * R && o < (s + 1) * R) g = (gptr)(sbase[s] + (o - s * R));
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                       (__attribute__((address_space(3))) void*)(sl + i * 1024), 16, 0, 0);
+    }
+  }
   // this lane's activation row of every M tile (rows past the tile repeat its last row)
   const unsigned short* arow[MT];
 #pragma unroll
@@ -399,6 +426,7 @@ __global__ __launch_bounds__(NW * 64, 2) void ffn_stream_sa_kernel(FfnArgs args)
     for (int s = 0; s < NSTR; ++s) {
       gptr cb = valid ? (gptr)(cbase[s] + (size_t)st * 1024) : zpage;
       S.code[s] = __builtin_nontemporal_load((const __attribute__((address_space(1))) u32x4*)(cb + lane16));
+      if constexpr (SL) continue;
       gptr sc = valid ? (gptr)(sbase[s] + (size_t)st * 64 * SB) : zpage;
       sc += lrow * 4 * SB;
       if constexpr (SB == 1) {
@@ -422,20 +450,33 @@ __global__ __launch_bounds__(NW * 64, 2) void ffn_stream_sa_kernel(FfnArgs args)
                                        (__attribute__((address_space(3))) void*)l, 16, 0, 0);
     }
   };
-  auto compute = [&](const WStage& S, const OpT (&a)[KPS][MT]) {
+  auto compute = [&](const WStage& S, const unsigned (&scale)[NSTR][SB], const OpT (&a)[KPS][MT]) {
 #pragma unroll
     for (int q = 0; q < KPS; ++q) {
 #pragma unroll
       for (int s = 0; s < NSTR; ++s) {
         OpT b;
         if constexpr (FMT == MOE_W_MXFP4) {
-          b = dec_mxfp4(S.code[s][q], (S.scale[s][0] >> (8 * q)) & 255);
+          b = dec_mxfp4(S.code[s][q], (scale[s][0] >> (8 * q)) & 255);
         } else {
-          const unsigned sw = S.scale[s][q >> 1];
+          const unsigned sw = scale[s][q >> 1];
           b = dec_int4(S.code[s][q], __builtin_bit_cast(_Float16, (unsigned short)(sw >> (16 * (q & 1)))));
         }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) acc[mt][s] = mfma(a[q][mt], b, acc[mt][s]);
+      }
+    }
+  };
+  // SL: stage st's scales of every strip (the stage-st copy of a full chunk: 4 * SB bytes of row lrow)
+  auto read_s = [&](unsigned (&scale)[NSTR][SB], int st) {
+#pragma unroll
+    for (int s = 0; s < NSTR; ++s) {
+      const unsigned char* p = sl + s * R + (st * 64 + (int)lrow * 4) * SB;
+      if constexpr (SB == 1) {
+        scale[s][0] = *(const unsigned*)p;
+      } else {
+        const u32x2 v = *(const u32x2*)p;
+        scale[s][0] = v[0], scale[s][1] = v[1];
       }
     }
   };
@@ -455,6 +496,20 @@ __global__ __launch_bounds__(NW * 64, 2) void ffn_stream_sa_kernel(FfnArgs args)
     load_a(i, i < nfull);
     __builtin_amdgcn_sched_barrier(0);
   }
+  // SL: the scales of the next stage to compute, read from LDS one stage ahead of their use (the
+  // copy was issued before every stage, so once it has landed it stays valid for the whole call)
+  unsigned scn[NSTR][SB];
+  if constexpr (SL) {
+    MOE_WAIT_VMCNT(PF * L);  // the scale copy has landed (the stages' loads may not have)
+    read_s(scn, 0);
+  }
+  auto next_scales = [&](unsigned (&sc)[NSTR][SB], int st) {
+#pragma unroll
+    for (int s = 0; s < NSTR; ++s)
+#pragma unroll
+      for (int b = 0; b < SB; ++b) sc[s][b] = scn[s][b];
+    read_s(scn, st + 1 < nfull ? st + 1 : st);
+  };
   int base = 0;
   for (; base + PF <= nfull; base += PF) {
 #pragma unroll
@@ -465,7 +520,13 @@ __global__ __launch_bounds__(NW * 64, 2) void ffn_stream_sa_kernel(FfnArgs args)
       __builtin_amdgcn_sched_barrier(0);
       OpT a[KPS][MT];
       read_a(a, st);
-      compute(ring[i], a);
+      if constexpr (SL) {
+        unsigned sc[NSTR][SB];
+        next_scales(sc, st);
+        compute(ring[i], sc, a);
+      } else {
+        compute(ring[i], ring[i].scale, a);
+      }
       load_w(ring[i], st + PF, st + PF < nfull);
       load_a(st + PF, st + PF < nfull);
       __builtin_amdgcn_sched_barrier(0);
@@ -479,7 +540,13 @@ __global__ __launch_bounds__(NW * 64, 2) void ffn_stream_sa_kernel(FfnArgs args)
     if (base + i < nfull) {
       OpT a[KPS][MT];
       read_a(a, base + i);
-      compute(ring[i], a);
+      if constexpr (SL) {
+        unsigned sc[NSTR][SB];
+        next_scales(sc, base + i);
+        compute(ring[i], sc, a);
+      } else {
+        compute(ring[i], ring[i].scale, a);
+      }
     }
   }
   // the partial last chunk: ns k-steps packed 4 * ns bytes per lane; the missing k-steps get
@@ -490,7 +557,7 @@ __global__ __launch_bounds__(NW * 64, 2) void ffn_stream_sa_kernel(FfnArgs args)
 #pragma unroll
     for (int s = 0; s < NSTR; ++s) {
       const char* cb = cbase[s] + (size_t)st * 1024 + (size_t)lane * 4 * ns;
-      const char* sb = sbase[s] + ((size_t)st * 64 + lrow * ns) * SB;
+      const char* sb = (SL ? (const char*)sl + s * R : sbase[s]) + ((size_t)st * 64 + lrow * ns) * SB;
       unsigned c[4] = {0, 0, 0, 0}, sc[4] = {0, 0, 0, 0};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -516,7 +583,7 @@ __global__ __launch_bounds__(NW * 64, 2) void ffn_stream_sa_kernel(FfnArgs args)
         if (q < ns) v = *(const OpT*)(arow[mt] + (KPS * st + q) * 32);
         a[q][mt] = v;
       }
-    compute(S, a);
+    compute(S, S.scale, a);
   }
   // ---- epilogue: this wave's strips
 #pragma unroll
@@ -919,14 +986,26 @@ void launch_stream_cfg(bool gate_up, const FfnArgs& a, int H, int I, int S, hipS
     // 4-bit weights, many experts touched: shared activations (4 waves, each with its gate/up
     // units or down strips over the whole contraction)
     constexpr int NW = 4, GU_NPW = MOE_CFG_Q4S_GU_NPW, D_NPW = MOE_CFG_Q4S_D_NPW, PF = MOE_CFG_Q4S_PF;
+    constexpr int SB = FMT == MOE_W_MXFP4 ? 1 : 2;
+    constexpr size_t stat = (size_t)(PF + 1) * 4 * MT * 1024;  // the activation stages
     if (gate_up) {
       const int gx = (I / 16 + NW * GU_NPW - 1) / (NW * GU_NPW);
-      hipLaunchKernelGGL((ffn_stream_sa_kernel<FMT, MT, NW, GU_NPW, PF, true>), dim3(grid8(gx, S)), dim3(64 * NW), 0,
-                         s, a);
+      const size_t dyn = (size_t)NW * sl_kib(H / 32, 2 * GU_NPW, SB) * 1024;
+      if (stat + dyn <= kSlMaxLds)
+        hipLaunchKernelGGL((ffn_stream_sa_kernel<FMT, MT, NW, GU_NPW, PF, true, true>), dim3(grid8(gx, S)),
+                           dim3(64 * NW), dyn, s, a);
+      else
+        hipLaunchKernelGGL((ffn_stream_sa_kernel<FMT, MT, NW, GU_NPW, PF, true, false>), dim3(grid8(gx, S)),
+                           dim3(64 * NW), 0, s, a);
     } else {
       const int dx = (H / 16 + NW * D_NPW - 1) / (NW * D_NPW);
-      hipLaunchKernelGGL((ffn_stream_sa_kernel<FMT, MT, NW, D_NPW, PF, false>), dim3(grid8(dx, S)), dim3(64 * NW), 0,
-                         s, a);
+      const size_t dyn = (size_t)NW * sl_kib(I / 32, D_NPW, SB) * 1024;
+      if (stat + dyn <= kSlMaxLds)
+        hipLaunchKernelGGL((ffn_stream_sa_kernel<FMT, MT, NW, D_NPW, PF, false, true>), dim3(grid8(dx, S)),
+                           dim3(64 * NW), dyn, s, a);
+      else
+        hipLaunchKernelGGL((ffn_stream_sa_kernel<FMT, MT, NW, D_NPW, PF, false, false>), dim3(grid8(dx, S)),
+                           dim3(64 * NW), 0, s, a);
     }
   } else {  // (an else, so that no wide 4-bit shape of this kernel is instantiated)
     if (gate_up) {

@@ -131,6 +131,10 @@ def test_route_exact(name, T, kw):
     torch.cuda.synchronize()
     assert np.array_equal(ids.cpu().numpy(), ids_ref)
     np.testing.assert_allclose(w.cpu().numpy(), w_ref, rtol=GATE_RTOL, atol=GATE_ATOL)
+    # a token's gates sum to one up to fp32 rounding: k exponentials of relative error <= 2^-23,
+    # their fp32 sum (<= (k - 1) roundings of 2^-24) and one division (2^-24) per gate
+    wsum = w.cpu().numpy().astype(np.float64).sum(axis=1)
+    assert np.abs(wsum - 1.0).max() <= (wl.k + 3) * 2.0 ** -23, np.abs(wsum - 1.0).max()
     np.testing.assert_allclose(logits.cpu().numpy(), lg, rtol=1e-4, atol=1e-4 * np.abs(lg).max())
 
 
