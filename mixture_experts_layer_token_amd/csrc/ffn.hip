@@ -1192,7 +1192,7 @@ int launch_ffn(const moe_experts* w, const void* x, int xdt, int T, int k, const
     a = xc;
   }
   // Variant per expert, decided on the device from its row count: experts with at most kHot rows
-  // go to the weight-streaming kernel, the others to the MFMA tile kernel (one weight read per 192
+  // go to the weight-streaming kernel, the others to the MFMA tile kernel (one weight read per kTileRows
   // rows instead of one per 16 * mt rows).  AUTO launches only the variants that can have work; DECODE
   // and PREFILL force one variant for every expert.
   const int kHot = 4 * 16 * pick_mt(T, k, E, w->fmt);  // at most 4 streaming row tiles per expert

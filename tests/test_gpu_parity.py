@@ -104,7 +104,7 @@ ROUTE_CASES = [
     ("tiny", 16, dict(k=8, name="k-eq-e")),
     ("tiny", 37, dict(E=1024, k=16, H=64, name="e1024", xdt="bf16")),
     ("tiny", 300, dict(E=24, k=3, name="e24-bf16", xdt="bf16")),  # large T, E not a multiple of 16
-    ("tiny", 700, dict(E=48, k=5, H=96, name="e48-bf16", xdt="bf16")),  # large T, ragged 192-row tile
+    ("tiny", 700, dict(E=48, k=5, H=96, name="e48-bf16", xdt="bf16")),  # large T, ragged row tile
     # T * E > 2^20: the MFMA tile kernel in short row tiles (the last one ragged), two column tiles
     ("tiny", 3000, dict(E=400, k=6, H=96, name="e400-bf16-tile", xdt="bf16")),
     # T * E > 2^20 with E not a multiple of 16: the one-kernel bf16 router (16 tokens per workgroup)
@@ -487,7 +487,10 @@ FULL = [("mixtral", 1, "auto"), ("mixtral", 8, "auto"), ("mixtral", 32, "auto"),
         ("gptoss", 512, "prefill"), ("gptoss", 1024, "auto"),  # 1024: hot experts on the tile kernel
         ("mixtral", 128, "auto"),  # bf16 from 28 rows per expert on average: the tile kernel alone
         # speculative verification blocks of depth + 1 = 2..4 positions (GLM-shaped INT4 layer, resident)
-        ("glm", 2, "auto"), ("glm", 3, "decode"), ("glm", 4, "auto")]
+        ("glm", 2, "auto"), ("glm", 3, "decode"), ("glm", 4, "auto"),
+        # about 100 experts touched: the shared-activation 4-bit kernel, its INT4 gate/up scales
+        # (K = 5120) streamed per stage, its down scales (K = 1536) copied to LDS
+        ("glm", 16, "decode")]
 
 
 @pytest.mark.parametrize("name,T,mode", FULL)
