@@ -319,8 +319,15 @@ __global__ __launch_bounds__(NW * 64, FMT == MOE_W_BF16 ? 3 : 2) void ffn_stream
 // KiB of LDS that hold one wave's scales in the shared-activation kernel: nstr strips of nks k-steps,
 // 16 rows and sb bytes per scale
 __host__ __device__ constexpr int sl_kib(int nks, int nstr, int sb) { return (nstr * 16 * nks * sb + 1023) / 1024; }
-// LDS per workgroup up to which the scales go to LDS: 4 workgroups still fit a CU's 160 KiB
-constexpr size_t kSlMaxLds = 40 * 1024;
+// The scales go to LDS while they take at most this much of it per workgroup (measured:
+// gpt-oss-shaped MXFP4, at one M tile
+// gate/up 12 KiB and down 24 KiB leave 4 workgroups per CU; at two M tiles they leave 3 instead of 4,
+// and the step still gained 4%, T = 512: 329.8 -> 315.5 us; INT4 gate/up at H = 5120, 40 KiB, is left
+// to the per-stage loads)
+#ifndef MOE_CFG_SL_MAX_KIB
+#define MOE_CFG_SL_MAX_KIB 24
+#endif
+constexpr size_t kSlMaxLds = MOE_CFG_SL_MAX_KIB * 1024;
 
 // SL: the block scales of a wave's strips are copied into LDS once, with direct-to-LDS loads issued
 // ahead of the first stage (one contiguous run per strip), and every stage reads its scales from
@@ -987,11 +994,10 @@ void launch_stream_cfg(bool gate_up, const FfnArgs& a, int H, int I, int S, hipS
     // units or down strips over the whole contraction)
     constexpr int NW = 4, GU_NPW = MOE_CFG_Q4S_GU_NPW, D_NPW = MOE_CFG_Q4S_D_NPW, PF = MOE_CFG_Q4S_PF;
     constexpr int SB = FMT == MOE_W_MXFP4 ? 1 : 2;
-    constexpr size_t stat = (size_t)(PF + 1) * 4 * MT * 1024;  // the activation stages
     if (gate_up) {
       const int gx = (I / 16 + NW * GU_NPW - 1) / (NW * GU_NPW);
       const size_t dyn = (size_t)NW * sl_kib(H / 32, 2 * GU_NPW, SB) * 1024;
-      if (stat + dyn <= kSlMaxLds)
+      if (dyn <= kSlMaxLds)
         hipLaunchKernelGGL((ffn_stream_sa_kernel<FMT, MT, NW, GU_NPW, PF, true, true>), dim3(grid8(gx, S)),
                            dim3(64 * NW), dyn, s, a);
       else
@@ -1000,7 +1006,7 @@ void launch_stream_cfg(bool gate_up, const FfnArgs& a, int H, int I, int S, hipS
     } else {
       const int dx = (H / 16 + NW * D_NPW - 1) / (NW * D_NPW);
       const size_t dyn = (size_t)NW * sl_kib(I / 32, D_NPW, SB) * 1024;
-      if (stat + dyn <= kSlMaxLds)
+      if (dyn <= kSlMaxLds)
         hipLaunchKernelGGL((ffn_stream_sa_kernel<FMT, MT, NW, D_NPW, PF, false, true>), dim3(grid8(dx, S)),
                            dim3(64 * NW), dyn, s, a);
       else
