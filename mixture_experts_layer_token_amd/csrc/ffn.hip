@@ -432,7 +432,15 @@ __global__ __launch_bounds__(NW * 64, 2) void ffn_stream_sa_kernel(FfnArgs args)
 #pragma unroll
     for (int s = 0; s < NSTR; ++s) {
       gptr cb = valid ? (gptr)(cbase[s] + (size_t)st * 1024) : zpage;
-      S.code[s] = __builtin_nontemporal_load((const __attribute__((address_space(1))) u32x4*)(cb + lane16));
+      // one M tile (few rows per expert: most experts have one row tile) streams the weights past
+      // the cache; at two M tiles hot experts have several row tiles on one XCD, and ordinary loads
+      // let the later ones find the weights in L2 (gpt-oss-shaped MXFP4: T = 64, 111.4 against 113.5
+      // us per step with ordinary loads; T = 512, 317.5 against 304.7 us)
+      typedef const __attribute__((address_space(1))) u32x4* gv4;
+      if constexpr (MT == 1)
+        S.code[s] = __builtin_nontemporal_load((gv4)(cb + lane16));
+      else
+        S.code[s] = *(gv4)(cb + lane16);
       if constexpr (SL) continue;
       gptr sc = valid ? (gptr)(sbase[s] + (size_t)st * 64 * SB) : zpage;
       sc += lrow * 4 * SB;
