@@ -308,6 +308,18 @@ __global__ __launch_bounds__(NW * 64, FMT == MOE_W_BF16 ? 3 : 2) void ffn_stream
 
 // ------------------------------------------------------------------ 4-bit streaming, shared activations
 
+// KiB of LDS that hold one wave's scales in the shared-activation kernel: nstr strips of nks k-steps,
+// 16 rows and sb bytes per scale
+__host__ __device__ constexpr int sl_kib(int nks, int nstr, int sb) { return (nstr * 16 * nks * sb + 1023) / 1024; }
+// The scales go to LDS while they take at most this much of it per workgroup (measured on the
+// gpt-oss-shaped MXFP4 layer: at one M tile, gate/up 12 KiB and down 24 KiB leave 4 workgroups per CU;
+// at two M tiles they leave 3 instead of 4, and the step still gained 4%, T = 512: 329.8 -> 315.5 us;
+// INT4 gate/up at H = 5120, 40 KiB, is left to the per-stage loads)
+#ifndef MOE_CFG_SL_MAX_KIB
+#define MOE_CFG_SL_MAX_KIB 24
+#endif
+constexpr size_t kSlMaxLds = MOE_CFG_SL_MAX_KIB * 1024;
+
 // 4-bit weights carry as many activation bytes per stage as weight bytes (16 rows x 2 B per k
 // against 4 strips x 16 rows x 0.5 B per k), and every unit group of a row tile loads them again.
 // This variant shares them: a workgroup's NW waves each own NPW units over the whole
@@ -316,19 +328,6 @@ __global__ __launch_bounds__(NW * 64, FMT == MOE_W_BF16 ? 3 : 2) void ffn_stream
 // each wave, and read back by every wave.  Stage st lives in LDS buffer st % (PF + 1): the loads
 // of stage st + PF, issued after stage st's barrier, go to the buffer of stage st - 1, which every
 // wave has finished reading once it reached that barrier.
-// KiB of LDS that hold one wave's scales in the shared-activation kernel: nstr strips of nks k-steps,
-// 16 rows and sb bytes per scale
-__host__ __device__ constexpr int sl_kib(int nks, int nstr, int sb) { return (nstr * 16 * nks * sb + 1023) / 1024; }
-// The scales go to LDS while they take at most this much of it per workgroup (measured:
-// gpt-oss-shaped MXFP4, at one M tile
-// gate/up 12 KiB and down 24 KiB leave 4 workgroups per CU; at two M tiles they leave 3 instead of 4,
-// and the step still gained 4%, T = 512: 329.8 -> 315.5 us; INT4 gate/up at H = 5120, 40 KiB, is left
-// to the per-stage loads)
-#ifndef MOE_CFG_SL_MAX_KIB
-#define MOE_CFG_SL_MAX_KIB 24
-#endif
-constexpr size_t kSlMaxLds = MOE_CFG_SL_MAX_KIB * 1024;
-
 // SL: the block scales of a wave's strips are copied into LDS once, with direct-to-LDS loads issued
 // ahead of the first stage (one contiguous run per strip), and every stage reads its scales from
 // there; otherwise each stage loads its 64 (MXFP4) or 128 (INT4) scale bytes per strip from HBM
